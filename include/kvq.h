@@ -1,0 +1,304 @@
+/*
+ * kvq.h -- C ABI of libkvq.so: quantized KV cache and decode attention for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * What the library computes (sources are the pages' titles and sections):
+ *
+ *  - Symmetric absmax rule ("KV quantization axes: why Key and Value need
+ *    separate reasoning", section "What rows and columns mean"): for a group
+ *    x, scale = max|x| / qmax, code = clip(round(x / scale), -qmax, qmax),
+ *    x_hat = code * scale.  Here qmax = 2^(b-1) - 1 for b in {8, 4, 3, 2},
+ *    round is round-half-to-even, and both divisions are IEEE float32
+ *    divisions.  A zero group uses scale 1; NaN/Inf input is rejected (same
+ *    page, closing troubleshooting paragraph).
+ *  - Grouping axes ("KVQuant: Towards 10 Million Context Length LLM
+ *    Inference with KV Cache Quantization", table "Measured effects"; the
+ *    page above, "What rows and columns mean"): keys per channel, grouped
+ *    along G tokens; values per token, grouped along Gv channels.
+ *  - Residual tail and sink ("MixKVQ: Query-Aware Mixed-Precision KV Cache
+ *    Quantization for Long-Context Reasoning", Figure 4; "KVQuant ...",
+ *    summary): recent tokens stay in fp16 in a buffer of R tokens; the first
+ *    S tokens stay fp16 as attention sinks.
+ *  - Salience ("MixKVQ ...", Figure 3): A_d = I_d * S_d (query intensity
+ *    times key scale); the top channels stay bf16, the next int4, the rest
+ *    int2.
+ *  - Decode attention ("KV quantization axes ...", section "Separate the two
+ *    error paths"): out = softmax(q K_hat^T * sm_scale) V_hat per query
+ *    head, over every cached token (no mask).
+ *
+ * Conventions for every call:
+ *  - All data pointers are DEVICE pointers unless the comment says host.
+ *    The caller allocates every device buffer; the library never allocates
+ *    device memory.  Host handles (kvq_cache) are malloc'ed by
+ *    kvq_cache_init and released by kvq_cache_free.
+ *  - `stream` is a hipStream_t (NULL = the default stream).  Calls only
+ *    enqueue work and return; results are valid once the stream reaches
+ *    them.  Calls on one cache or one output buffer must be ordered by the
+ *    caller (same stream or explicit events).
+ *  - Argument errors return at once and enqueue nothing.  Data errors
+ *    (NaN/Inf input) are found on the device: the kernel sets a sticky flag
+ *    and the outputs are unspecified; read the flag with kvq_poll_error or
+ *    kvq_cache_check.
+ *  - Outputs are deterministic: equal inputs give equal bytes.
+ *  - Packed codes: offset binary u = code + 2^(b-1), b bits each,
+ *    LSB-first in little-endian uint32 words, floor(32/b) fields per word,
+ *    one row per token padded to whole words ("words(n, b)" below), unused
+ *    bits zero.
+ */
+#ifndef KVQ_H
+#define KVQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  KVQ_OK = 0,
+  KVQ_E_ARG = 1,        /* invalid argument; nothing was enqueued */
+  KVQ_E_CAPACITY = 2,   /* append would exceed the cache's max_tokens */
+  KVQ_E_NONFINITE = 3,  /* a kernel saw NaN/Inf input (sticky flag set) */
+  KVQ_E_HIP = 4,        /* a HIP runtime call failed */
+  KVQ_E_POISONED = 5,   /* cache saw NaN/Inf earlier; re-initialise it */
+  KVQ_E_UNSUPPORTED = 6 /* valid request the library does not implement */
+} kvq_status;
+
+typedef enum { KVQ_F32 = 0, KVQ_F16 = 1 } kvq_dtype;
+typedef enum { KVQ_PER_CHANNEL = 0, KVQ_PER_TOKEN = 1 } kvq_axis;
+
+/* Layout of value codes inside a cache (kvq_kv_view.v_layout). */
+typedef enum {
+  KVQ_V_ROWS = 0,   /* one packed row per token, as described above */
+  KVQ_V_TILE32 = 1  /* 32-token tiles ordered for the matrix-core decode;
+                       kvq_export converts to rows */
+} kvq_v_layout;
+
+/* Number of uint32 words of one packed row of n fields of b bits. */
+int kvq_words(int n_fields, int bits);
+
+/* ---------------------------------------------------------------------
+ * Stateless quantizers.
+ * ------------------------------------------------------------------ */
+
+/* Per-channel key quantization ("KVQuant ...", table "Measured effects":
+ * keys per channel; "KV quantization axes ...", "What rows and columns
+ * mean": the rule and the (1, D) channel-scale shape).
+ *   k       [n_mats][n_tok][d], dtype KVQ_F32 or KVQ_F16
+ *   codes   [n_mats][n_tok][kvq_words(d, bits)] uint32 (written)
+ *   scales  [n_mats][ceil(n_tok / group_tok)][d] float32 (written); the
+ *           group of channel c and token t is t / group_tok; a final partial
+ *           group uses its own absmax.
+ *   err_flag  device uint32, nullable; bit 0 is OR-ed in on NaN/Inf.
+ * Requires 1 <= d <= 256, group_tok >= 1, bits in {8,4,3,2}, 4-byte aligned
+ * pointers.  n_mats or n_tok == 0 is a no-op.                           */
+kvq_status kvq_quantize_k(const void* k, int dtype, int64_t n_mats,
+                          int64_t n_tok, int d, int bits, int group_tok,
+                          uint32_t* codes, float* scales, uint32_t* err_flag,
+                          void* stream);
+
+/* Per-token value quantization (same sources; token-scale shape (N, 1)
+ * generalised to one scale per group of group_ch channels).
+ *   v       [n_mats][n_tok][d]
+ *   codes   [n_mats][n_tok][kvq_words(d, bits)]
+ *   scales  [n_mats][n_tok][d / group_ch]
+ * Requires group_ch to divide d, 1 <= d <= 256.                          */
+kvq_status kvq_quantize_v(const void* v, int dtype, int64_t n_mats,
+                          int64_t n_tok, int d, int bits, int group_ch,
+                          uint32_t* codes, float* scales, uint32_t* err_flag,
+                          void* stream);
+
+/* Reconstruction x_hat = fl32(code * scale) ("KV quantization axes ...",
+ * "What rows and columns mean").
+ *   codes [n_mats][n_tok][kvq_words(d, bits)]; out [n_mats][n_tok][d] f32.
+ *   axis KVQ_PER_CHANNEL: scales [n_mats][ceil(n_tok/group)][d];
+ *   axis KVQ_PER_TOKEN:   scales [n_mats][n_tok][d/group].               */
+kvq_status kvq_dequant(const uint32_t* codes, const float* scales,
+                       int64_t n_mats, int64_t n_tok, int d, int bits,
+                       int axis, int group, float* out, void* stream);
+
+/* ---------------------------------------------------------------------
+ * Cache.
+ * ------------------------------------------------------------------ */
+
+typedef struct {
+  int32_t batch;      /* B */
+  int32_t kv_heads;   /* Hkv */
+  int32_t head_dim;   /* D, 1..256 */
+  int32_t k_bits;     /* uniform keys: 8|4|3|2 (ignored when k_mixed) */
+  int32_t v_bits;     /* 8|4|3|2 */
+  int32_t group_tok;  /* G: key group, tokens */
+  int32_t group_ch;   /* Gv: value group, channels; divides D */
+  int32_t residual;   /* R: fp16 tail capacity, a positive multiple of G */
+  int32_t sink;       /* S: leading tokens kept in fp16 */
+  int32_t k_mixed;    /* 1: MixKVQ key classes bf16 / int4 / int2 */
+  int32_t n_bf16;     /* mixed: channels kept bf16 per group */
+  int32_t n_int4;     /* mixed: channels at int4 per group (rest int2) */
+  int64_t max_tokens; /* capacity, tokens per (batch, KV head) */
+} kvq_cache_cfg;
+
+typedef struct kvq_cache kvq_cache;
+
+/* Device bytes the cache needs for cfg (0 if cfg is invalid). */
+size_t kvq_cache_bytes(const kvq_cache_cfg* cfg);
+
+/* Bind a cache to a caller-owned device buffer of kvq_cache_bytes(cfg)
+ * bytes (256-byte aligned).  n_tokens == 0 starts empty: the error flag is
+ * cleared and the salience intensity set to 1 for every channel (ranking by
+ * key scale alone until kvq_salience_select).  n_tokens > 0 re-attaches a
+ * buffer that already holds that many tokens (checkpoint resume: the buffer
+ * is the whole state).  *out receives a host handle.                    */
+kvq_status kvq_cache_init(const kvq_cache_cfg* cfg, void* dev_buf,
+                          size_t bytes, int64_t n_tokens, kvq_cache** out,
+                          void* stream);
+
+/* Release the host handle (the device buffer stays the caller's). */
+void kvq_cache_free(kvq_cache* c);
+
+/* Tokens appended so far (host counter). */
+int64_t kvq_cache_tokens(const kvq_cache* c);
+
+/* Append n_new tokens of every (batch, KV head) stream ("MixKVQ ...",
+ * Figure 4; "KVQuant ...", summary):
+ *   k_new, v_new  [B][Hkv][n_new][D] float16
+ * The first S tokens ever appended go to the fp16 sink.  Later tokens join
+ * the fp16 tail; whenever the tail would exceed R tokens, its oldest G
+ * tokens are quantized as one key group (per channel; MixKVQ classes when
+ * k_mixed) and per token for values.  Returns KVQ_E_CAPACITY if the cache
+ * would exceed max_tokens, KVQ_E_POISONED after a data error.          */
+kvq_status kvq_append(kvq_cache* c, const void* k_new, const void* v_new,
+                      int dtype, int64_t n_new, void* stream);
+
+/* MixKVQ query intensity ("MixKVQ ...", Figure 3; refreshed per the
+ * Figure 4 window):
+ *   q_win  [B][w_rows][n_q_heads][D] float16, the last w_rows query rows.
+ * I[b][kvh][d] = sum over the rows and the query heads kvh*g .. kvh*g+g-1
+ * (g = n_q_heads / Hkv) of |q|, in float64 (exact).  Applies to every later
+ * key-group flush.  Requires k_mixed.                                   */
+kvq_status kvq_salience_select(kvq_cache* c, const void* q_win, int dtype,
+                               int w_rows, int n_q_heads, void* stream);
+
+/* Sync `stream`, read the cache's sticky data-error flag; on NaN/Inf the
+ * cache is poisoned (every later call returns KVQ_E_POISONED) and
+ * KVQ_E_NONFINITE is returned.                                          */
+kvq_status kvq_cache_check(kvq_cache* c, void* stream);
+
+/* Read-only description of a cache's device arrays.  Strides are in
+ * elements of the array's type, per (batch, KV head) stream s = b*Hkv + h.
+ * A view may also be filled in by hand from kvq_quantize_k/v outputs
+ * (rows layout, uniform keys, no sink or tail).                          */
+typedef struct {
+  int32_t batch, kv_heads, head_dim;
+  int32_t k_bits, v_bits, group_tok, group_ch;
+  int32_t k_mixed, n_bf16, n_int4;
+  int32_t v_layout;   /* kvq_v_layout */
+  int32_t residual;   /* ring capacity of the tail arrays */
+  int64_t n_sink;     /* fp16 sink tokens */
+  int64_t n_quant;    /* quantized tokens (past-sink indices 0..n_quant-1) */
+  int64_t n_tail;     /* fp16 tail tokens; past-sink index p sits in ring
+                         row p % residual */
+  const uint16_t* sink_k; const uint16_t* sink_v; int64_t sink_stride;
+  const uint16_t* tail_k; const uint16_t* tail_v; int64_t tail_stride;
+  /* uniform keys: codes [n_quant][kvq_words(D, k_bits)], scales [groups][D] */
+  const uint32_t* k_codes; int64_t k_codes_stride;
+  const float* k_scales; int64_t k_scales_stride;
+  /* largest |K| of each key group (float32), nullable */
+  const float* k_gmax; int64_t k_gmax_stride;
+  /* mixed keys: per group, k_pos[d] = position of channel d in the order
+     [bf16 channels | int4 channels | int2 channels], each ascending;
+     k_scales [groups][n_int4 + n_int2] in that order;
+     bf16 [n_quant][n_bf16]; int4 [n_quant][words(n_int4,4)];
+     int2 [n_quant][words(n_int2,2)] */
+  const uint8_t* k_pos; int64_t k_pos_stride;
+  const uint16_t* k_bf16; int64_t k_bf16_stride;
+  const uint32_t* k_int4; int64_t k_int4_stride;
+  const uint32_t* k_int2; int64_t k_int2_stride;
+  /* values: codes (v_layout), scales [n_quant][D / group_ch] */
+  const uint32_t* v_codes; int64_t v_codes_stride;
+  const float* v_scales; int64_t v_scales_stride;
+  uint32_t* err_flag;   /* the cache's sticky data-error flag */
+} kvq_kv_view;
+
+kvq_status kvq_cache_view(const kvq_cache* c, kvq_kv_view* v);
+
+/* Canonical dense copies of a cache (tests, audits, checkpoints).  Every
+ * pointer is a device buffer; shapes with ns, nq, nt = n_sink, n_quant,
+ * n_tail and ng = nq / G:
+ *   sink_k, sink_v [B][Hkv][ns][D] f16;  tail_k, tail_v [B][Hkv][nt][D]
+ *   f16 in token order; v_codes [B][Hkv][nq][words(D, v_bits)] rows;
+ *   v_scales [B][Hkv][nq][D/Gv];
+ *   uniform: k_codes [B][Hkv][nq][words(D, k_bits)], k_scales [..][ng][D];
+ *   mixed: k_class [B][Hkv][ng][D] u8 (0 bf16, 1 int4, 2 int2), k_bf16,
+ *   k_int4, k_int2, k_scales as in kvq_kv_view, densely per stream.
+ * Pointers the layout does not use may be NULL.                         */
+typedef struct {
+  void* sink_k; void* sink_v; void* tail_k; void* tail_v;
+  uint32_t* k_codes; float* k_scales;
+  uint8_t* k_class; uint16_t* k_bf16; uint32_t* k_int4; uint32_t* k_int2;
+  uint32_t* v_codes; float* v_scales;
+} kvq_export_bufs;
+
+kvq_status kvq_export(const kvq_kv_view* v, const kvq_export_bufs* out,
+                      void* stream);
+
+/* ---------------------------------------------------------------------
+ * Decode attention.
+ * ------------------------------------------------------------------ */
+
+enum {
+  KVQ_DECODE_AUTO = 0,     /* matrix-core kernel when the view allows it */
+  KVQ_DECODE_GENERIC = 1   /* always the general vector kernel */
+};
+
+/* Bytes of the split workspace for n_splits (0 = automatic). */
+size_t kvq_decode_workspace_bytes(const kvq_kv_view* v, int n_q_heads,
+                                  int n_splits);
+
+/* Decode attention over every token of the view ("KV quantization axes
+ * ...", section "Separate the two error paths"; "KVQuant ...", key
+ * results: key and value matvecs over the quantized cache):
+ *   q    [B][n_q_heads][D], KVQ_F16 or KVQ_F32
+ *   out  [B][n_q_heads][D] float32 (written)
+ * Query head h reads KV head h / (n_q_heads / Hkv).  The context is split
+ * into n_splits ranges (0 = automatic) whose softmax partials are merged
+ * with the log-sum-exp rule.  workspace >= kvq_decode_workspace_bytes.
+ * An empty view (no tokens) is KVQ_E_ARG.                               */
+kvq_status kvq_decode_attention(const kvq_kv_view* v, const void* q,
+                                int dtype, int n_q_heads, float sm_scale,
+                                float* out, int n_splits, int flags,
+                                void* workspace, size_t ws_bytes,
+                                void* stream);
+
+/* ---------------------------------------------------------------------
+ * Errors and utilities.
+ * ------------------------------------------------------------------ */
+
+/* Sync `stream`, then read a device error flag: KVQ_E_NONFINITE if set. */
+kvq_status kvq_poll_error(const uint32_t* err_flag, void* stream);
+
+const char* kvq_strerror(kvq_status s);
+
+/* Fill a device uint32 buffer with a value (a kernel, so the call is safe
+ * inside captured graphs). */
+kvq_status kvq_fill_u32(uint32_t* dst, uint32_t value, int64_t n,
+                        void* stream);
+
+/* Seeded synthetic fp16 data for benchmarks too large to draw on the host:
+ * element (head, token, channel) of `tensor` (0 K, 1 V, 2 q) in `layer` is
+ * the counter-th output of a SplitMix64 stream (Steele, Lea and Flood,
+ * OOPSLA 2014) seeded with `seed`, counter = ((((tensor*256 + layer)*256 +
+ * head) << 32) + token)*256 + channel; its four 16-bit lanes are summed,
+ * centred at 131070, multiplied by the float32 nearest 1/sqrt((2^32-1)/3)
+ * and rounded to fp16.
+ *   out [n_heads][n_tok][d] with head stride head_stride halves.        */
+kvq_status kvq_synth_normal_f16(void* out, uint64_t seed, int tensor,
+                                int layer, int head0, int n_heads,
+                                int64_t t0, int64_t n_tok, int d,
+                                int64_t head_stride, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVQ_H */

@@ -1,0 +1,222 @@
+// General decode attention of libkvq (any bit width, layout, D <= 256,
+// mixed keys) and the cross-split merge.
+//
+// Computes, per query head h reading KV head h / g, the stable softmax of
+// q . k_hat_t * sm_scale over every cached token and the weighted sum of
+// v_hat_t ("KV quantization axes ...", section "Separate the two error
+// paths").  Scores are kept in log2 units (q pre-multiplied by
+// sm_scale * log2(e)), so exp2 replaces exp.  Each split writes a partial
+// (m, l, o): m the largest score, l = sum 2^(s - m), o = sum 2^(s - m) v_hat;
+// the merge combines partials with the log-sum-exp rule.
+#include <hip/hip_runtime.h>
+
+#include "kvq_internal.h"
+
+namespace kvq {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kChunkTok = 128;
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ inline float h2f(uint16_t u) {
+  return (float)__builtin_bit_cast(_Float16, u);
+}
+__device__ inline float bf2f(uint16_t u) {
+  return __builtin_bit_cast(float, (uint32_t)u << 16);
+}
+
+__device__ inline uint32_t field(uint32_t w, int j, int bits) {
+  return (w >> (j * bits)) & ((1u << bits) - 1u);
+}
+
+// Dequantized key of token t (cache order: sink, quantized, tail) channel d.
+__device__ float kdeq(const kvq_kv_view& v, int64_t s, int64_t t, int d) {
+  const int D = v.head_dim;
+  if (t < v.n_sink) return h2f(v.sink_k[s * v.sink_stride + t * D + d]);
+  t -= v.n_sink;
+  if (t < v.n_quant) {
+    const int64_t g = t / v.group_tok;
+    if (!v.k_mixed) {
+      const int kb = v.k_bits, pw = fields_per_word(kb), wk = words_of(D, kb);
+      uint32_t w = v.k_codes[s * v.k_codes_stride + t * wk + d / pw];
+      int u = (int)field(w, d % pw, kb);
+      return (float)(u - qmax_of(kb) - 1) *
+             v.k_scales[s * v.k_scales_stride + g * D + d];
+    }
+    const int nb = v.n_bf16, n4 = v.n_int4, n2 = D - nb - n4;
+    const int pos = v.k_pos[s * v.k_pos_stride + g * D + d];
+    if (pos < nb) return bf2f(v.k_bf16[s * v.k_bf16_stride + t * nb + pos]);
+    const float sc = v.k_scales[s * v.k_scales_stride + g * (n4 + n2) + (pos - nb)];
+    if (pos < nb + n4) {
+      const int k = pos - nb, w4 = words_of(n4, 4);
+      uint32_t w = v.k_int4[s * v.k_int4_stride + t * w4 + k / 8];
+      return (float)((int)field(w, k % 8, 4) - 8) * sc;
+    }
+    const int k = pos - nb - n4, w2 = words_of(n2, 2);
+    uint32_t w = v.k_int2[s * v.k_int2_stride + t * w2 + k / 16];
+    return (float)((int)field(w, k % 16, 2) - 2) * sc;
+  }
+  t -= v.n_quant;
+  return h2f(v.tail_k[s * v.tail_stride + ((v.n_quant + t) % v.residual) * D + d]);
+}
+
+__device__ float vdeq(const kvq_kv_view& v, int64_t s, int64_t t, int d) {
+  const int D = v.head_dim;
+  if (t < v.n_sink) return h2f(v.sink_v[s * v.sink_stride + t * D + d]);
+  t -= v.n_sink;
+  if (t < v.n_quant) {
+    const int vb = v.v_bits;
+    uint32_t u;
+    if (v.v_layout == KVQ_V_ROWS) {
+      const int pw = fields_per_word(vb), wv = words_of(D, vb);
+      u = field(v.v_codes[s * v.v_codes_stride + t * wv + d / pw], d % pw, vb);
+    } else {
+      int64_t widx;
+      int bit;
+      v_tile_pos(t, d, D, vb, &widx, &bit);
+      u = (v.v_codes[s * v.v_codes_stride + widx] >> bit) & ((1u << vb) - 1u);
+    }
+    const int ng = D / v.group_ch;
+    return (float)((int)u - qmax_of(vb) - 1) *
+           v.v_scales[s * v.v_scales_stride + t * ng + d / v.group_ch];
+  }
+  t -= v.n_quant;
+  return h2f(v.tail_v[s * v.tail_stride + ((v.n_quant + t) % v.residual) * D + d]);
+}
+
+template <typename T> __device__ inline float ldq(const T* p, int64_t i);
+template <> __device__ inline float ldq<float>(const float* p, int64_t i) { return p[i]; }
+template <> __device__ inline float ldq<uint16_t>(const uint16_t* p, int64_t i) {
+  return h2f(p[i]);
+}
+
+template <typename QT>
+__global__ void __launch_bounds__(kThreads)
+decode_generic_kernel(kvq_kv_view v, const QT* __restrict__ q, int Hq,
+                      float qscale, float* __restrict__ partials, int n_parts) {
+  extern __shared__ float smem[];
+  const int D = v.head_dim;
+  const int g = Hq / v.kv_heads;
+  float* qs = smem;                  // [g][D]
+  float* ps = qs + g * D;            // [g][kChunkTok]
+  float* os = ps + g * kChunkTok;    // [g][D]
+  float* ms = os + g * D;            // [g]
+  float* ls = ms + g;                // [g]
+  float* as = ls + g;                // [g]
+  const int tid = threadIdx.x;
+  const int part = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  const int64_t s = (int64_t)b * v.kv_heads + kvh;
+  const int64_t N = v.n_sink + v.n_quant + v.n_tail;
+  const int64_t per = (N + n_parts - 1) / n_parts;
+  const int64_t t_lo = min(N, (int64_t)part * per), t_hi = min(N, t_lo + per);
+
+  for (int i = tid; i < g * D; i += kThreads) {
+    const int h = i / D, d = i % D;
+    qs[i] = ldq(q, ((int64_t)b * Hq + kvh * g + h) * D + d) * qscale;
+    os[i] = 0.0f;
+  }
+  if (tid < g) {
+    ms[tid] = -INFINITY;
+    ls[tid] = 0.0f;
+  }
+  __syncthreads();
+
+  for (int64_t c0 = t_lo; c0 < t_hi; c0 += kChunkTok) {
+    const int n = (int)min((int64_t)kChunkTok, t_hi - c0);
+    for (int i = tid; i < n * g; i += kThreads) {
+      const int t = i % n, h = i / n;
+      float acc = 0.0f;
+      for (int d = 0; d < D; ++d) acc += qs[h * D + d] * kdeq(v, s, c0 + t, d);
+      ps[h * kChunkTok + t] = acc;
+    }
+    __syncthreads();
+    if (tid < g) {
+      float mx = -INFINITY;
+      for (int t = 0; t < n; ++t) mx = fmaxf(mx, ps[tid * kChunkTok + t]);
+      const float mnew = fmaxf(ms[tid], mx);
+      as[tid] = exp2f(ms[tid] - mnew);
+      ms[tid] = mnew;
+    }
+    __syncthreads();
+    for (int i = tid; i < n * g; i += kThreads) {
+      const int t = i % n, h = i / n;
+      ps[h * kChunkTok + t] = exp2f(ps[h * kChunkTok + t] - ms[h]);
+    }
+    __syncthreads();
+    if (tid < g) {
+      float l = ls[tid] * as[tid];
+      for (int t = 0; t < n; ++t) l += ps[tid * kChunkTok + t];
+      ls[tid] = l;
+    }
+    for (int i = tid; i < g * D; i += kThreads) {
+      const int h = i / D, d = i % D;
+      float acc = os[i] * as[h];
+      for (int t = 0; t < n; ++t) acc += ps[h * kChunkTok + t] * vdeq(v, s, c0 + t, d);
+      os[i] = acc;
+    }
+    __syncthreads();
+  }
+  for (int i = tid; i < g * (D + 2); i += kThreads) {
+    const int h = i / (D + 2), j = i % (D + 2);
+    float val = j == 0 ? ms[h] : (j == 1 ? ls[h] : os[h * D + j - 2]);
+    partials[(((int64_t)b * Hq + kvh * g + h) * n_parts + part) * (D + 2) + j] = val;
+  }
+}
+
+// out[b][h][:] = sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) l_p.
+__global__ void merge_kernel(const float* __restrict__ partials, int D,
+                             int n_parts, float* __restrict__ out) {
+  const int64_t bh = blockIdx.x;
+  const float* p = partials + bh * n_parts * (int64_t)(D + 2);
+  float M = -INFINITY;
+  for (int i = 0; i < n_parts; ++i)
+    if (p[i * (D + 2) + 1] > 0.0f) M = fmaxf(M, p[i * (D + 2)]);
+  float L = 0.0f;
+  for (int i = 0; i < n_parts; ++i) {
+    const float l = p[i * (D + 2) + 1];
+    if (l > 0.0f) L += l * exp2f(p[i * (D + 2)] - M);
+  }
+  for (int d = threadIdx.x; d < D; d += blockDim.x) {
+    float acc = 0.0f;
+    for (int i = 0; i < n_parts; ++i) {
+      const float l = p[i * (D + 2) + 1];
+      if (l > 0.0f) acc += p[i * (D + 2) + 2 + d] * exp2f(p[i * (D + 2)] - M);
+    }
+    out[bh * D + d] = acc / L;
+  }
+}
+
+}  // namespace
+
+hipError_t launch_decode_generic(const kvq_kv_view& v, const void* q, int f16,
+                                 int Hq, float sm_scale, float* partials,
+                                 int n_parts, hipStream_t s) {
+  const int g = Hq / v.kv_heads;
+  const size_t lds = sizeof(float) * ((size_t)g * v.head_dim * 2 +
+                                      (size_t)g * kChunkTok + 3 * (size_t)g);
+  dim3 grid((unsigned)n_parts, (unsigned)v.kv_heads, (unsigned)v.batch);
+  const float qscale = sm_scale * kLog2e;
+  if (lds > 64 * 1024) {
+    hipError_t e = f16 ? hipFuncSetAttribute((const void*)decode_generic_kernel<uint16_t>,
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds)
+                       : hipFuncSetAttribute((const void*)decode_generic_kernel<float>,
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  if (f16)
+    decode_generic_kernel<uint16_t><<<grid, kThreads, lds, s>>>(
+        v, (const uint16_t*)q, Hq, qscale, partials, n_parts);
+  else
+    decode_generic_kernel<float><<<grid, kThreads, lds, s>>>(
+        v, (const float*)q, Hq, qscale, partials, n_parts);
+  return hipGetLastError();
+}
+
+hipError_t launch_merge(const float* partials, int B, int Hq, int D,
+                        int n_parts, float* out, hipStream_t s) {
+  merge_kernel<<<dim3((unsigned)(B * Hq)), 128, 0, s>>>(partials, D, n_parts, out);
+  return hipGetLastError();
+}
+
+}  // namespace kvq

@@ -1,0 +1,753 @@
+// Quantize, append (sink / tail / flush), salience, export and synthetic-data
+// kernels of libkvq for gfx950.
+//
+// The rule ("KV quantization axes: why Key and Value need separate
+// reasoning", section "What rows and columns mean"): scale = max|x| / qmax,
+// code = clip(round_half_even(x / scale), -qmax, qmax), with both divisions
+// IEEE float32 (__fdiv_rn) so codes are bit-exact; a zero group (or a scale
+// that underflows to 0) uses scale 1; NaN/Inf input sets the sticky error
+// flag (closing troubleshooting paragraph of the same page).
+#include <hip/hip_runtime.h>
+
+#include "kvq_internal.h"
+
+namespace kvq {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kChunk = 32;   // token rows staged in LDS per step
+
+__device__ inline float h2f(uint16_t u) {
+  return (float)__builtin_bit_cast(_Float16, u);
+}
+__device__ inline bool finite(float x) { return __builtin_isfinite(x); }
+
+template <typename T> __device__ inline float ld(const T* p, int64_t i);
+template <> __device__ inline float ld<float>(const float* p, int64_t i) { return p[i]; }
+template <> __device__ inline float ld<uint16_t>(const uint16_t* p, int64_t i) {
+  return h2f(p[i]);
+}
+
+// scale of a group from its absmax m: one IEEE float32 division.
+__device__ inline float group_scale(float m, int qmax) {
+  float s = __fdiv_rn(m, (float)qmax);
+  return (m == 0.0f || s == 0.0f) ? 1.0f : s;
+}
+// offset-binary code of x under scale s.
+__device__ inline uint32_t encode(float x, float s, int qmax) {
+  float q = rintf(__fdiv_rn(x, s));
+  q = fminf(fmaxf(q, (float)-qmax), (float)qmax);
+  return (uint32_t)((int)q + qmax + 1);
+}
+
+__device__ inline uint16_t f32_to_bf16_rne(float x) {
+  uint32_t u = __builtin_bit_cast(uint32_t, x);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// ---------------------------------------------------------------------------
+// Stateless per-channel quantizer: one workgroup per (matrix, key group).
+// Pass 1 reduces the per-channel absmax over the group's tokens; pass 2
+// encodes kChunk-row chunks into LDS bytes and packs them into rows.
+// ---------------------------------------------------------------------------
+template <typename T>
+__global__ void __launch_bounds__(kThreads)
+quantize_k_kernel(const T* __restrict__ k, int64_t n_tok, int d, int bits,
+                  int G, uint32_t* __restrict__ codes,
+                  float* __restrict__ scales, uint32_t* err) {
+  __shared__ float red[kThreads];
+  __shared__ float sc[kMaxD];
+  __shared__ uint8_t u8[kChunk * kMaxD];
+  const int tid = threadIdx.x;
+  const int64_t mat = blockIdx.y;
+  const int64_t g = blockIdx.x;
+  const int64_t n_groups = (n_tok + G - 1) / G;
+  const int64_t t0 = g * G, t1 = min(n_tok, t0 + G);
+  const T* x = k + mat * n_tok * d;
+  const int qmax = qmax_of(bits);
+  const int slices = kThreads / d;
+  bool bad = false;
+  if (tid < slices * d) {
+    int c = tid % d, sl = tid / d;
+    float m = 0.0f;
+    for (int64_t t = t0 + sl; t < t1; t += slices) {
+      float v = ld(x, t * d + c);
+      bad |= !finite(v);
+      m = fmaxf(m, fabsf(v));
+    }
+    red[tid] = m;
+  }
+  __syncthreads();
+  if (tid < d) {
+    float m = red[tid];
+    for (int sl = 1; sl < slices; ++sl) m = fmaxf(m, red[sl * d + tid]);
+    float s = group_scale(m, qmax);
+    sc[tid] = s;
+    scales[(mat * n_groups + g) * d + tid] = s;
+  }
+  if (bad && err) atomicOr(err, 1u);
+  __syncthreads();
+  const int wk = words_of(d, bits), pw = fields_per_word(bits);
+  for (int64_t r0 = t0; r0 < t1; r0 += kChunk) {
+    const int rows = (int)min((int64_t)kChunk, t1 - r0);
+    for (int i = tid; i < rows * d; i += kThreads) {
+      int r = i / d, c = i % d;
+      u8[i] = (uint8_t)encode(ld(x, (r0 + r) * d + c), sc[c], qmax);
+    }
+    __syncthreads();
+    for (int i = tid; i < rows * wk; i += kThreads) {
+      int r = i / wk, w = i % wk;
+      uint32_t word = 0;
+      for (int j = 0; j < pw; ++j) {
+        int c = w * pw + j;
+        if (c < d) word |= (uint32_t)u8[r * d + c] << (j * bits);
+      }
+      codes[(mat * n_tok + r0 + r) * wk + w] = word;
+    }
+    __syncthreads();
+  }
+}
+
+// Stateless per-token quantizer: one workgroup per (matrix, kChunk tokens).
+template <typename T>
+__global__ void __launch_bounds__(kThreads)
+quantize_v_kernel(const T* __restrict__ v, int64_t n_tok, int d, int bits,
+                  int Gv, uint32_t* __restrict__ codes,
+                  float* __restrict__ scales, uint32_t* err) {
+  __shared__ float xs[kChunk * kMaxD];
+  __shared__ float sc[kChunk * kMaxD];  // worst case Gv = 1
+  __shared__ uint8_t u8[kChunk * kMaxD];
+  const int tid = threadIdx.x;
+  const int64_t mat = blockIdx.y;
+  const int64_t r0 = (int64_t)blockIdx.x * kChunk;
+  const int rows = (int)min((int64_t)kChunk, n_tok - r0);
+  const T* x = v + (mat * n_tok + r0) * d;
+  const int qmax = qmax_of(bits);
+  const int ng = d / Gv;
+  bool bad = false;
+  for (int i = tid; i < rows * d; i += kThreads) {
+    float val = ld(x, i);
+    bad |= !finite(val);
+    xs[i] = val;
+  }
+  if (bad && err) atomicOr(err, 1u);
+  __syncthreads();
+  for (int i = tid; i < rows * ng; i += kThreads) {
+    int r = i / ng, j = i % ng;
+    float m = 0.0f;
+    for (int c = 0; c < Gv; ++c) m = fmaxf(m, fabsf(xs[r * d + j * Gv + c]));
+    float s = group_scale(m, qmax);
+    sc[i] = s;
+    scales[(mat * n_tok + r0 + r) * ng + j] = s;
+  }
+  __syncthreads();
+  for (int i = tid; i < rows * d; i += kThreads) {
+    int r = i / d, c = i % d;
+    u8[i] = (uint8_t)encode(xs[i], sc[r * ng + c / Gv], qmax);
+  }
+  __syncthreads();
+  const int wk = words_of(d, bits), pw = fields_per_word(bits);
+  for (int i = tid; i < rows * wk; i += kThreads) {
+    int r = i / wk, w = i % wk;
+    uint32_t word = 0;
+    for (int j = 0; j < pw; ++j) {
+      int c = w * pw + j;
+      if (c < d) word |= (uint32_t)u8[r * d + c] << (j * bits);
+    }
+    codes[(mat * n_tok + r0 + r) * wk + w] = word;
+  }
+}
+
+__global__ void dequant_kernel(const uint32_t* __restrict__ codes,
+                               const float* __restrict__ scales,
+                               int64_t n_mats, int64_t n_tok, int d, int bits,
+                               int axis, int group, float* __restrict__ out) {
+  const int64_t total = n_mats * n_tok * d;
+  const int wk = words_of(d, bits), pw = fields_per_word(bits);
+  const int off = qmax_of(bits) + 1;
+  const int64_t n_groups = (n_tok + group - 1) / group;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    int64_t row = i / d;
+    int c = (int)(i % d);
+    int64_t mat = row / n_tok, t = row % n_tok;
+    uint32_t w = codes[row * wk + c / pw];
+    int u = (int)((w >> ((c % pw) * bits)) & ((1u << bits) - 1u));
+    float s = axis == KVQ_PER_CHANNEL
+                  ? scales[(mat * n_groups + t / group) * d + c]
+                  : scales[row * (d / group) + c / group];
+    out[i] = (float)(u - off) * s;
+  }
+}
+
+__global__ void fill_u32_kernel(uint32_t* dst, uint32_t v, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x)
+    dst[i] = v;
+}
+__global__ void fill_f64_kernel(double* dst, double v, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x)
+    dst[i] = v;
+}
+
+// ---------------------------------------------------------------------------
+// Append: fp16 rows to the sink and to ring rows of the tail.
+// grid.y = stream; grid.x covers the rows.
+// ---------------------------------------------------------------------------
+__global__ void append_rows_kernel(CacheDev c, const uint16_t* __restrict__ k_in,
+                                   const uint16_t* __restrict__ v_in,
+                                   int64_t n_new, int64_t ns_old, int64_t take,
+                                   int64_t in_lo, int64_t in_hi, int64_t p_lo) {
+  const int64_t st = blockIdx.y;
+  const int D = c.D;
+  const int64_t n_rows = take + (in_hi - in_lo);
+  const int64_t total = n_rows * D;
+  bool bad = false;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    int64_t r = i / D;
+    int d = (int)(i % D);
+    int64_t src, dst;
+    uint16_t *dk, *dv;
+    if (r < take) {
+      src = r;
+      dst = st * c.s_sink + (ns_old + r) * D + d;
+      dk = c.sink_k; dv = c.sink_v;
+    } else {
+      int64_t in = in_lo + (r - take);
+      src = in;
+      int64_t p = p_lo + (in - in_lo);
+      dst = st * c.s_tail + (p % c.R) * D + d;
+      dk = c.tail_k; dv = c.tail_v;
+    }
+    uint16_t kk = k_in[(st * n_new + src) * D + d];
+    uint16_t vv = v_in[(st * n_new + src) * D + d];
+    bad |= !finite(h2f(kk)) || !finite(h2f(vv));
+    dk[dst] = kk;
+    dv[dst] = vv;
+  }
+  if (bad) atomicOr(c.err, 1u);
+}
+
+// ---------------------------------------------------------------------------
+// Flush: one workgroup per (key group, KV head, batch).
+// ---------------------------------------------------------------------------
+struct FlushSrc {
+  const uint16_t* k_in;
+  const uint16_t* v_in;
+  int64_t n_new, take, nq_old, nt_old;
+};
+
+__device__ inline int64_t src_index(const CacheDev& c, const FlushSrc& f,
+                                    int64_t st, int64_t p, bool* from_ring) {
+  if (p < f.nq_old + f.nt_old) {
+    *from_ring = true;
+    return st * c.s_tail + (p % c.R) * c.D;
+  }
+  *from_ring = false;
+  return (st * f.n_new + f.take + (p - f.nq_old - f.nt_old)) * c.D;
+}
+
+__global__ void __launch_bounds__(kThreads)
+flush_kernel(CacheDev c, FlushSrc f) {
+  __shared__ float red[kThreads];
+  __shared__ float kmax[kMaxD];     // S_d (absmax per channel)
+  __shared__ float ksc[kMaxD];      // scale per channel (uniform or class)
+  __shared__ int kpos[kMaxD];       // position in class order (mixed)
+  __shared__ int kcls[kMaxD];
+  __shared__ double A[kMaxD];
+  __shared__ float xs[kChunk * kMaxD];
+  __shared__ float vsc[kChunk * kMaxD];
+  __shared__ uint8_t u8[kChunk * kMaxD];
+  __shared__ uint16_t b16[kChunk * kMaxD];
+  const int tid = threadIdx.x;
+  const int D = c.D, G = c.G;
+  const int64_t st = (int64_t)blockIdx.z * c.H + blockIdx.y;
+  const int64_t grp = f.nq_old / G + blockIdx.x;
+  const int64_t p0 = grp * G;
+  bool bad = false;
+
+  // ---- keys, pass 1: per-channel absmax over the G tokens.
+  const int slices = kThreads / D;
+  if (tid < slices * D) {
+    int ch = tid % D, sl = tid / D;
+    float m = 0.0f;
+    for (int r = sl; r < G; r += slices) {
+      bool ring;
+      int64_t base = src_index(c, f, st, p0 + r, &ring);
+      float v = h2f(ring ? c.tail_k[base + ch] : f.k_in[base + ch]);
+      bad |= !finite(v);
+      m = fmaxf(m, fabsf(v));
+    }
+    red[tid] = m;
+  }
+  __syncthreads();
+  if (tid < D) {
+    float m = red[tid];
+    for (int sl = 1; sl < slices; ++sl) m = fmaxf(m, red[sl * D + tid]);
+    kmax[tid] = m;
+  }
+  __syncthreads();
+
+  if (!c.mixed) {
+    if (tid < D) {
+      float s = group_scale(kmax[tid], qmax_of(c.k_bits));
+      ksc[tid] = s;
+      c.k_scales[st * c.s_k_scales + grp * D + tid] = s;
+    }
+  } else {
+    // MixKVQ classes: A_d = I_d * S_d (float64), rank by (-A, d).
+    if (tid < D) A[tid] = c.I[st * D + tid] * (double)kmax[tid];
+    __syncthreads();
+    if (tid < D) {
+      double a = A[tid];
+      int rank = 0;
+      for (int e = 0; e < D; ++e) {
+        double b = A[e];
+        rank += (b > a) || (b == a && e < tid);
+      }
+      kcls[tid] = rank < c.n_bf16 ? 0 : (rank < c.n_bf16 + c.n_int4 ? 1 : 2);
+    }
+    __syncthreads();
+    if (tid < D) {
+      int cl = kcls[tid], before = 0;
+      for (int e = 0; e < tid; ++e) before += (kcls[e] == cl);
+      int start = cl == 0 ? 0 : (cl == 1 ? c.n_bf16 : c.n_bf16 + c.n_int4);
+      int pos = start + before;
+      kpos[tid] = pos;
+      c.k_pos[st * c.s_k_pos + grp * D + tid] = (uint8_t)pos;
+      if (cl != 0) {
+        float s = group_scale(kmax[tid], qmax_of(cl == 1 ? 4 : 2));
+        ksc[tid] = s;
+        c.k_scales[st * c.s_k_scales + grp * (D - c.n_bf16) + (pos - c.n_bf16)] = s;
+      } else {
+        ksc[tid] = 1.0f;
+      }
+    }
+  }
+  if (tid == 0) {
+    float gm = 0.0f;
+    for (int e = 0; e < D; ++e) gm = fmaxf(gm, kmax[e]);
+    c.k_gmax[st * c.s_k_gmax + grp] = gm;
+  }
+  __syncthreads();
+
+  // ---- keys, pass 2 and values, chunk by chunk of kChunk tokens.
+  const int ngv = D / c.Gv;
+  const int qv = qmax_of(c.v_bits);
+  for (int r0 = 0; r0 < G; r0 += kChunk) {
+    const int rows = min(kChunk, G - r0);
+    // stage K chunk and encode
+    for (int i = tid; i < rows * D; i += kThreads) {
+      int r = i / D, ch = i % D;
+      bool ring;
+      int64_t base = src_index(c, f, st, p0 + r0 + r, &ring);
+      float v = h2f(ring ? c.tail_k[base + ch] : f.k_in[base + ch]);
+      if (!c.mixed) {
+        u8[i] = (uint8_t)encode(v, ksc[ch], qmax_of(c.k_bits));
+      } else {
+        int cl = kcls[ch];
+        if (cl == 0) {
+          b16[r * D + kpos[ch]] = f32_to_bf16_rne(v);
+        } else {
+          u8[r * D + kpos[ch]] = (uint8_t)encode(v, ksc[ch], qmax_of(cl == 1 ? 4 : 2));
+        }
+      }
+    }
+    __syncthreads();
+    const int64_t prow = p0 + r0;  // quantized index of the chunk's first row
+    if (!c.mixed) {
+      const int wk = words_of(D, c.k_bits), pw = fields_per_word(c.k_bits);
+      for (int i = tid; i < rows * wk; i += kThreads) {
+        int r = i / wk, w = i % wk;
+        uint32_t word = 0;
+        for (int j = 0; j < pw; ++j) {
+          int ch = w * pw + j;
+          if (ch < D) word |= (uint32_t)u8[r * D + ch] << (j * c.k_bits);
+        }
+        c.k_codes[st * c.s_k_codes + (prow + r) * wk + w] = word;
+      }
+    } else {
+      const int nb = c.n_bf16, n4 = c.n_int4, n2 = D - nb - n4;
+      for (int i = tid; i < rows * nb; i += kThreads) {
+        int r = i / nb, j = i % nb;
+        c.k_bf16[st * c.s_k_bf16 + (prow + r) * nb + j] = b16[r * D + j];
+      }
+      const int w4 = words_of(n4, 4), w2 = words_of(n2, 2);
+      for (int i = tid; i < rows * (w4 + w2); i += kThreads) {
+        int r = i / (w4 + w2), w = i % (w4 + w2);
+        uint32_t word = 0;
+        if (w < w4) {
+          for (int j = 0; j < 8; ++j) {
+            int k = w * 8 + j;
+            if (k < n4) word |= (uint32_t)u8[r * D + nb + k] << (4 * j);
+          }
+          c.k_int4[st * c.s_k_int4 + (prow + r) * w4 + w] = word;
+        } else {
+          w -= w4;
+          for (int j = 0; j < 16; ++j) {
+            int k = w * 16 + j;
+            if (k < n2) word |= (uint32_t)u8[r * D + nb + n4 + k] << (2 * j);
+          }
+          c.k_int2[st * c.s_k_int2 + (prow + r) * w2 + w] = word;
+        }
+      }
+    }
+    __syncthreads();
+    // values: stage, per-token group scales, encode, pack
+    for (int i = tid; i < rows * D; i += kThreads) {
+      int r = i / D, ch = i % D;
+      bool ring;
+      int64_t base = src_index(c, f, st, p0 + r0 + r, &ring);
+      float v = h2f(ring ? c.tail_v[base + ch] : f.v_in[base + ch]);
+      bad |= !finite(v);
+      xs[i] = v;
+    }
+    __syncthreads();
+    for (int i = tid; i < rows * ngv; i += kThreads) {
+      int r = i / ngv, j = i % ngv;
+      float m = 0.0f;
+      for (int e = 0; e < c.Gv; ++e) m = fmaxf(m, fabsf(xs[r * D + j * c.Gv + e]));
+      float s = group_scale(m, qv);
+      vsc[i] = s;
+      c.v_scales[st * c.s_v_scales + (prow + r) * ngv + j] = s;
+    }
+    __syncthreads();
+    for (int i = tid; i < rows * D; i += kThreads) {
+      int r = i / D, ch = i % D;
+      u8[i] = (uint8_t)encode(xs[i], vsc[r * ngv + ch / c.Gv], qv);
+    }
+    __syncthreads();
+    if (c.v_layout == KVQ_V_ROWS) {
+      const int wv = words_of(D, c.v_bits), pw = fields_per_word(c.v_bits);
+      for (int i = tid; i < rows * wv; i += kThreads) {
+        int r = i / wv, w = i % wv;
+        uint32_t word = 0;
+        for (int j = 0; j < pw; ++j) {
+          int ch = w * pw + j;
+          if (ch < D) word |= (uint32_t)u8[r * D + ch] << (j * c.v_bits);
+        }
+        c.v_codes[st * c.s_v_codes + (prow + r) * wv + w] = word;
+      }
+    } else {
+      // whole 32-token tile (G and the group start are multiples of 32)
+      const int vb = c.v_bits;
+      const int Wl = v_tile_lane_words(D, vb);
+      const int C = Wl < 4 ? Wl : 4;
+      const int n_words = D * vb;
+      const int nf = 32 / vb;
+      uint32_t* tile = c.v_codes + st * c.s_v_codes + (prow >> 5) * (int64_t)n_words;
+      for (int i = tid; i < n_words; i += kThreads) {
+        int chunk = i / (64 * C), rem = i % (64 * C);
+        int l = rem / C, w = chunk * C + rem % C;
+        uint32_t word = 0;
+        for (int p = 0; p < nf; ++p) {
+          int tau, ch;
+          v_tile_field(l, w, p, vb, &tau, &ch);
+          word |= (uint32_t)u8[tau * D + ch] << (p * vb);
+        }
+        tile[i] = word;
+      }
+    }
+    __syncthreads();
+  }
+  if (bad) atomicOr(c.err, 1u);
+}
+
+// I[b][kvh][d] = sum over rows r and grouped heads h of |q_win[b][r][h][d]|.
+__global__ void salience_kernel(CacheDev c, const uint16_t* __restrict__ q,
+                                int w_rows, int Hq) {
+  const int d = threadIdx.x;
+  const int h = blockIdx.x, b = blockIdx.y;
+  const int g = Hq / c.H;
+  if (d >= c.D) return;
+  double acc = 0.0;
+  bool bad = false;
+  for (int r = 0; r < w_rows; ++r)
+    for (int hh = h * g; hh < (h + 1) * g; ++hh) {
+      float v = h2f(q[(((int64_t)b * w_rows + r) * Hq + hh) * c.D + d]);
+      bad |= !finite(v);
+      acc += fabs((double)v);
+    }
+  c.I[((int64_t)b * c.H + h) * c.D + d] = acc;
+  if (bad) atomicOr(c.err, 1u);
+}
+
+// ---------------------------------------------------------------------------
+// Export: strided copies into dense per-stream arrays, tail ring -> token
+// order, value tiles -> rows, key positions -> classes.
+// ---------------------------------------------------------------------------
+__global__ void copy_streams_u16(const uint16_t* __restrict__ src,
+                                 int64_t src_stride, int64_t src_off,
+                                 uint16_t* __restrict__ dst, int64_t n_per,
+                                 int64_t n_streams) {
+  const int64_t total = n_per * n_streams;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    int64_t s = i / n_per, j = i % n_per;
+    dst[i] = src[s * src_stride + src_off + j];
+  }
+}
+__global__ void copy_streams_u32(const uint32_t* __restrict__ src,
+                                 int64_t src_stride, uint32_t* __restrict__ dst,
+                                 int64_t n_per, int64_t n_streams) {
+  const int64_t total = n_per * n_streams;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    int64_t s = i / n_per, j = i % n_per;
+    dst[i] = src[s * src_stride + j];
+  }
+}
+__global__ void export_tail(const uint16_t* __restrict__ ring, int64_t stride,
+                            int R, int D, int64_t nq, int64_t nt,
+                            uint16_t* __restrict__ dst, int64_t n_streams) {
+  const int64_t total = nt * D * n_streams;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    int64_t s = i / (nt * D), rem = i % (nt * D);
+    int64_t t = rem / D;
+    int d = (int)(rem % D);
+    dst[i] = ring[s * stride + ((nq + t) % R) * D + d];
+  }
+}
+__global__ void export_v_tiles(const uint32_t* __restrict__ tiles,
+                               int64_t stride, int D, int vb, int64_t nq,
+                               uint32_t* __restrict__ dst, int64_t n_streams) {
+  const int wv = words_of(D, vb), pw = fields_per_word(vb);
+  const int64_t total = nq * wv * n_streams;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    int64_t s = i / (nq * wv), rem = i % (nq * wv);
+    int64_t t = rem / wv;
+    int w = (int)(rem % wv);
+    uint32_t word = 0;
+    for (int j = 0; j < pw; ++j) {
+      int d = w * pw + j;
+      if (d >= D) break;
+      int64_t widx;
+      int bit;
+      v_tile_pos(t, d, D, vb, &widx, &bit);
+      uint32_t u = (tiles[s * stride + widx] >> bit) & ((1u << vb) - 1u);
+      word |= u << (j * vb);
+    }
+    dst[i] = word;
+  }
+}
+__global__ void export_classes(const uint8_t* __restrict__ pos, int64_t stride,
+                               int64_t n_per, int nb, int n4,
+                               uint8_t* __restrict__ dst, int64_t n_streams) {
+  const int64_t total = n_per * n_streams;
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    int64_t s = i / n_per, j = i % n_per;
+    int p = pos[s * stride + j];
+    dst[i] = (uint8_t)(p < nb ? 0 : (p < nb + n4 ? 1 : 2));
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Counter-based synthetic fp16 (SplitMix64 output function over
+// seed + (counter + 1) * golden gamma; Irwin-Hall sum of four 16-bit lanes).
+// ---------------------------------------------------------------------------
+// float32 -> float16 bits, round to nearest even, subnormal results kept
+// (integer arithmetic, so independent of the hardware denormal mode).
+// Finite |f| < 65520 only, which the generator guarantees.
+__device__ inline uint16_t f2h_rne_int(float f) {
+  const uint32_t x = __builtin_bit_cast(uint32_t, f);
+  const uint32_t sign = (x >> 16) & 0x8000u;
+  const uint32_t ax = x & 0x7FFFFFFFu;
+  uint32_t r;
+  if (ax < 0x38800000u) {  // below 2^-14: float16 subnormal (or zero)
+    const uint32_t e = ax >> 23;
+    const uint32_t mant = (ax & 0x7FFFFFu) | 0x800000u;
+    const uint32_t sh = 126u - e;  // value / 2^-24 = mant >> sh
+    if (e == 0 || sh > 24u) return (uint16_t)sign;
+    r = mant >> sh;
+    const uint32_t rem = mant & ((1u << sh) - 1u), half = 1u << (sh - 1u);
+    if (rem > half || (rem == half && (r & 1u))) ++r;
+  } else {
+    r = (ax >> 13) - (112u << 10);
+    const uint32_t rem = ax & 0x1FFFu;
+    if (rem > 0x1000u || (rem == 0x1000u && (r & 1u))) ++r;
+  }
+  return (uint16_t)(sign | r);
+}
+
+__device__ inline uint64_t splitmix_out(uint64_t z) {
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+__global__ void synth_kernel(uint16_t* __restrict__ out, uint64_t seed,
+                             int tensor, int layer, int head0, int n_heads,
+                             int64_t t0, int64_t n_tok, int d,
+                             int64_t head_stride) {
+  const int64_t per = n_tok * d;
+  const int64_t total = per * n_heads;
+  // float32 nearest to 1/sqrt((2^32 - 1)/3)
+  const float kScale = 0x1.bb67aep-16f;  // 2.642899744e-05
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < total;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    int64_t hh = i / per, rem = i % per;
+    int64_t t = t0 + rem / d;
+    uint64_t ch = (uint64_t)(rem % d);
+    uint64_t hi = (uint64_t)(((int64_t)tensor * 256 + layer) * 256 + head0 + hh);
+    uint64_t ctr = ((hi << 32) + (uint64_t)t) * 256ull + ch;
+    uint64_t h = splitmix_out(seed + (ctr + 1ull) * 0x9E3779B97F4A7C15ull);
+    int64_t s = (int64_t)(h & 0xFFFF) + (int64_t)((h >> 16) & 0xFFFF) +
+                (int64_t)((h >> 32) & 0xFFFF) + (int64_t)(h >> 48) - 131070;
+    float x = __fmul_rn((float)s, kScale);
+    out[hh * head_stride + rem] = f2h_rne_int(x);
+  }
+}
+
+inline dim3 grid_for(int64_t n, int threads) {
+  int64_t b = (n + threads - 1) / threads;
+  if (b < 1) b = 1;
+  if (b > 65536) b = 65536;
+  return dim3((unsigned)b);
+}
+
+}  // namespace
+
+hipError_t launch_quantize_k(const void* k, int f16, int64_t n_mats,
+                             int64_t n_tok, int d, int bits, int G,
+                             uint32_t* codes, float* scales, uint32_t* err,
+                             hipStream_t s) {
+  int64_t ng = (n_tok + G - 1) / G;
+  dim3 grid((unsigned)ng, (unsigned)n_mats);
+  if (f16)
+    quantize_k_kernel<uint16_t><<<grid, kThreads, 0, s>>>(
+        (const uint16_t*)k, n_tok, d, bits, G, codes, scales, err);
+  else
+    quantize_k_kernel<float><<<grid, kThreads, 0, s>>>(
+        (const float*)k, n_tok, d, bits, G, codes, scales, err);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_v(const void* v, int f16, int64_t n_mats,
+                             int64_t n_tok, int d, int bits, int Gv,
+                             uint32_t* codes, float* scales, uint32_t* err,
+                             hipStream_t s) {
+  dim3 grid((unsigned)((n_tok + kChunk - 1) / kChunk), (unsigned)n_mats);
+  if (f16)
+    quantize_v_kernel<uint16_t><<<grid, kThreads, 0, s>>>(
+        (const uint16_t*)v, n_tok, d, bits, Gv, codes, scales, err);
+  else
+    quantize_v_kernel<float><<<grid, kThreads, 0, s>>>(
+        (const float*)v, n_tok, d, bits, Gv, codes, scales, err);
+  return hipGetLastError();
+}
+
+hipError_t launch_dequant(const uint32_t* codes, const float* scales,
+                          int64_t n_mats, int64_t n_tok, int d, int bits,
+                          int axis, int group, float* out, hipStream_t s) {
+  dequant_kernel<<<grid_for(n_mats * n_tok * d, 256), 256, 0, s>>>(
+      codes, scales, n_mats, n_tok, d, bits, axis, group, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_fill_u32(uint32_t* dst, uint32_t v, int64_t n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  fill_u32_kernel<<<grid_for(n, 256), 256, 0, s>>>(dst, v, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_fill_f64(double* dst, double v, int64_t n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  fill_f64_kernel<<<grid_for(n, 256), 256, 0, s>>>(dst, v, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_append_rows(const CacheDev& c, const uint16_t* k_in,
+                              const uint16_t* v_in, int64_t n_new,
+                              int64_t ns_old, int64_t take, int64_t in_lo,
+                              int64_t in_hi, int64_t p_lo, hipStream_t s) {
+  int64_t rows = take + (in_hi - in_lo);
+  if (rows <= 0) return hipSuccess;
+  int64_t per = rows * c.D;
+  int64_t bx = (per + 255) / 256;
+  if (bx > 4096) bx = 4096;
+  dim3 grid((unsigned)bx, (unsigned)(c.B * c.H));
+  append_rows_kernel<<<grid, 256, 0, s>>>(c, k_in, v_in, n_new, ns_old, take,
+                                          in_lo, in_hi, p_lo);
+  return hipGetLastError();
+}
+
+hipError_t launch_flush(const CacheDev& c, const uint16_t* k_in,
+                        const uint16_t* v_in, int64_t n_new, int64_t take,
+                        int64_t nq_old, int64_t nt_old, int64_t n_groups,
+                        hipStream_t s) {
+  if (n_groups <= 0) return hipSuccess;
+  FlushSrc f{k_in, v_in, n_new, take, nq_old, nt_old};
+  dim3 grid((unsigned)n_groups, (unsigned)c.H, (unsigned)c.B);
+  flush_kernel<<<grid, kThreads, 0, s>>>(c, f);
+  return hipGetLastError();
+}
+
+hipError_t launch_salience(const CacheDev& c, const uint16_t* q_win, int w_rows,
+                           int n_q_heads, hipStream_t s) {
+  dim3 grid((unsigned)c.H, (unsigned)c.B);
+  salience_kernel<<<grid, kMaxD, 0, s>>>(c, q_win, w_rows, n_q_heads);
+  return hipGetLastError();
+}
+
+hipError_t launch_export(const kvq_kv_view& v, const kvq_export_bufs& o,
+                         hipStream_t s) {
+  const int64_t ns = (int64_t)v.batch * v.kv_heads;
+  const int D = v.head_dim;
+  const int64_t nq = v.n_quant, ng = v.group_tok > 0 ? nq / v.group_tok : 0;
+  auto g = [](int64_t n) { return grid_for(n, 256); };
+  if (v.n_sink > 0) {
+    int64_t n = v.n_sink * D;
+    if (o.sink_k) copy_streams_u16<<<g(n * ns), 256, 0, s>>>(v.sink_k, v.sink_stride, 0, (uint16_t*)o.sink_k, n, ns);
+    if (o.sink_v) copy_streams_u16<<<g(n * ns), 256, 0, s>>>(v.sink_v, v.sink_stride, 0, (uint16_t*)o.sink_v, n, ns);
+  }
+  if (v.n_tail > 0) {
+    int64_t n = v.n_tail * D * ns;
+    if (o.tail_k) export_tail<<<g(n), 256, 0, s>>>(v.tail_k, v.tail_stride, v.residual, D, nq, v.n_tail, (uint16_t*)o.tail_k, ns);
+    if (o.tail_v) export_tail<<<g(n), 256, 0, s>>>(v.tail_v, v.tail_stride, v.residual, D, nq, v.n_tail, (uint16_t*)o.tail_v, ns);
+  }
+  if (nq > 0) {
+    if (!v.k_mixed) {
+      int64_t n = nq * words_of(D, v.k_bits);
+      if (o.k_codes) copy_streams_u32<<<g(n * ns), 256, 0, s>>>(v.k_codes, v.k_codes_stride, o.k_codes, n, ns);
+      if (o.k_scales) copy_streams_u32<<<g(ng * D * ns), 256, 0, s>>>((const uint32_t*)v.k_scales, v.k_scales_stride, (uint32_t*)o.k_scales, ng * D, ns);
+    } else {
+      const int nb = v.n_bf16, n4 = v.n_int4, n2 = D - nb - n4;
+      if (o.k_class) export_classes<<<g(ng * D * ns), 256, 0, s>>>(v.k_pos, v.k_pos_stride, ng * D, nb, n4, o.k_class, ns);
+      if (o.k_bf16 && nb) copy_streams_u16<<<g(nq * nb * ns), 256, 0, s>>>(v.k_bf16, v.k_bf16_stride, 0, o.k_bf16, nq * nb, ns);
+      if (o.k_int4 && n4) copy_streams_u32<<<g(nq * words_of(n4, 4) * ns), 256, 0, s>>>(v.k_int4, v.k_int4_stride, o.k_int4, nq * words_of(n4, 4), ns);
+      if (o.k_int2 && n2) copy_streams_u32<<<g(nq * words_of(n2, 2) * ns), 256, 0, s>>>(v.k_int2, v.k_int2_stride, o.k_int2, nq * words_of(n2, 2), ns);
+      if (o.k_scales) copy_streams_u32<<<g(ng * (n4 + n2) * ns), 256, 0, s>>>((const uint32_t*)v.k_scales, v.k_scales_stride, (uint32_t*)o.k_scales, ng * (n4 + n2), ns);
+    }
+    if (o.v_codes) {
+      int64_t n = nq * words_of(D, v.v_bits);
+      if (v.v_layout == KVQ_V_ROWS)
+        copy_streams_u32<<<g(n * ns), 256, 0, s>>>(v.v_codes, v.v_codes_stride, o.v_codes, n, ns);
+      else
+        export_v_tiles<<<g(n * ns), 256, 0, s>>>(v.v_codes, v.v_codes_stride, D, v.v_bits, nq, o.v_codes, ns);
+    }
+    if (o.v_scales) {
+      int64_t n = nq * (D / v.group_ch);
+      copy_streams_u32<<<g(n * ns), 256, 0, s>>>((const uint32_t*)v.v_scales, v.v_scales_stride, (uint32_t*)o.v_scales, n, ns);
+    }
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_synth(uint16_t* out, uint64_t seed, int tensor, int layer,
+                        int head0, int n_heads, int64_t t0, int64_t n_tok,
+                        int d, int64_t head_stride, hipStream_t s) {
+  int64_t n = n_tok * d * n_heads;
+  if (n <= 0) return hipSuccess;
+  synth_kernel<<<grid_for(n, 256), 256, 0, s>>>(out, seed, tensor, layer,
+                                                head0, n_heads, t0, n_tok, d,
+                                                head_stride);
+  return hipGetLastError();
+}
+
+}  // namespace kvq

@@ -1,0 +1,363 @@
+"""Thin ctypes binding of libkvq.so (same names as the C ABI in include/kvq.h).
+
+Argument marshalling only: every step of the path runs in the HIP kernels of
+libkvq.so.  PyTorch supplies device memory (tensors) and the current HIP
+stream.  If the library is missing the import of this module still works,
+but every call raises -- there is no fallback.
+"""
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkvq.so")
+
+KVQ_OK, KVQ_E_ARG, KVQ_E_CAPACITY, KVQ_E_NONFINITE, KVQ_E_HIP, \
+    KVQ_E_POISONED, KVQ_E_UNSUPPORTED = range(7)
+KVQ_F32, KVQ_F16 = 0, 1
+KVQ_PER_CHANNEL, KVQ_PER_TOKEN = 0, 1
+KVQ_V_ROWS, KVQ_V_TILE32 = 0, 1
+KVQ_DECODE_AUTO, KVQ_DECODE_GENERIC = 0, 1
+
+EXPORTED = [
+    "kvq_words", "kvq_quantize_k", "kvq_quantize_v", "kvq_dequant",
+    "kvq_cache_bytes", "kvq_cache_init", "kvq_cache_free", "kvq_cache_tokens",
+    "kvq_append", "kvq_salience_select", "kvq_cache_check", "kvq_cache_view",
+    "kvq_export", "kvq_decode_workspace_bytes", "kvq_decode_attention",
+    "kvq_poll_error", "kvq_strerror", "kvq_fill_u32", "kvq_synth_normal_f16",
+]
+
+_c_i32, _c_i64, _c_u64, _c_p, _c_f = (ctypes.c_int32, ctypes.c_int64,
+                                      ctypes.c_uint64, ctypes.c_void_p,
+                                      ctypes.c_float)
+
+
+class CacheCfg(ctypes.Structure):
+    _fields_ = [("batch", _c_i32), ("kv_heads", _c_i32), ("head_dim", _c_i32),
+                ("k_bits", _c_i32), ("v_bits", _c_i32), ("group_tok", _c_i32),
+                ("group_ch", _c_i32), ("residual", _c_i32), ("sink", _c_i32),
+                ("k_mixed", _c_i32), ("n_bf16", _c_i32), ("n_int4", _c_i32),
+                ("max_tokens", _c_i64)]
+
+
+class KvView(ctypes.Structure):
+    _fields_ = [("batch", _c_i32), ("kv_heads", _c_i32), ("head_dim", _c_i32),
+                ("k_bits", _c_i32), ("v_bits", _c_i32), ("group_tok", _c_i32),
+                ("group_ch", _c_i32), ("k_mixed", _c_i32), ("n_bf16", _c_i32),
+                ("n_int4", _c_i32), ("v_layout", _c_i32), ("residual", _c_i32),
+                ("n_sink", _c_i64), ("n_quant", _c_i64), ("n_tail", _c_i64),
+                ("sink_k", _c_p), ("sink_v", _c_p), ("sink_stride", _c_i64),
+                ("tail_k", _c_p), ("tail_v", _c_p), ("tail_stride", _c_i64),
+                ("k_codes", _c_p), ("k_codes_stride", _c_i64),
+                ("k_scales", _c_p), ("k_scales_stride", _c_i64),
+                ("k_gmax", _c_p), ("k_gmax_stride", _c_i64),
+                ("k_pos", _c_p), ("k_pos_stride", _c_i64),
+                ("k_bf16", _c_p), ("k_bf16_stride", _c_i64),
+                ("k_int4", _c_p), ("k_int4_stride", _c_i64),
+                ("k_int2", _c_p), ("k_int2_stride", _c_i64),
+                ("v_codes", _c_p), ("v_codes_stride", _c_i64),
+                ("v_scales", _c_p), ("v_scales_stride", _c_i64),
+                ("err_flag", _c_p)]
+
+
+class ExportBufs(ctypes.Structure):
+    _fields_ = [(n, _c_p) for n in (
+        "sink_k", "sink_v", "tail_k", "tail_v", "k_codes", "k_scales",
+        "k_class", "k_bf16", "k_int4", "k_int2", "v_codes", "v_scales")]
+
+
+class KvqError(RuntimeError):
+    def __init__(self, status, where):
+        self.status = status
+        super().__init__(f"{where}: {strerror(status)} (status {status})")
+
+
+_lib = None
+
+
+def lib():
+    """The loaded libkvq.so; raises if it was not built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"{LIB_PATH} is missing: build it with "
+            "'python -m quantized_decode_attention_02_amd.build'")
+    L = ctypes.CDLL(LIB_PATH)
+    sig = {
+        "kvq_words": (_c_i32, [_c_i32, _c_i32]),
+        "kvq_quantize_k": (_c_i32, [_c_p, _c_i32, _c_i64, _c_i64, _c_i32,
+                                    _c_i32, _c_i32, _c_p, _c_p, _c_p, _c_p]),
+        "kvq_quantize_v": (_c_i32, [_c_p, _c_i32, _c_i64, _c_i64, _c_i32,
+                                    _c_i32, _c_i32, _c_p, _c_p, _c_p, _c_p]),
+        "kvq_dequant": (_c_i32, [_c_p, _c_p, _c_i64, _c_i64, _c_i32, _c_i32,
+                                 _c_i32, _c_i32, _c_p, _c_p]),
+        "kvq_cache_bytes": (ctypes.c_size_t, [ctypes.POINTER(CacheCfg)]),
+        "kvq_cache_init": (_c_i32, [ctypes.POINTER(CacheCfg), _c_p,
+                                    ctypes.c_size_t, _c_i64,
+                                    ctypes.POINTER(_c_p), _c_p]),
+        "kvq_cache_free": (None, [_c_p]),
+        "kvq_cache_tokens": (_c_i64, [_c_p]),
+        "kvq_append": (_c_i32, [_c_p, _c_p, _c_p, _c_i32, _c_i64, _c_p]),
+        "kvq_salience_select": (_c_i32, [_c_p, _c_p, _c_i32, _c_i32, _c_i32,
+                                         _c_p]),
+        "kvq_cache_check": (_c_i32, [_c_p, _c_p]),
+        "kvq_cache_view": (_c_i32, [_c_p, ctypes.POINTER(KvView)]),
+        "kvq_export": (_c_i32, [ctypes.POINTER(KvView),
+                                ctypes.POINTER(ExportBufs), _c_p]),
+        "kvq_decode_workspace_bytes": (ctypes.c_size_t, [
+            ctypes.POINTER(KvView), _c_i32, _c_i32]),
+        "kvq_decode_attention": (_c_i32, [
+            ctypes.POINTER(KvView), _c_p, _c_i32, _c_i32, _c_f, _c_p, _c_i32,
+            _c_i32, _c_p, ctypes.c_size_t, _c_p]),
+        "kvq_poll_error": (_c_i32, [_c_p, _c_p]),
+        "kvq_strerror": (ctypes.c_char_p, [_c_i32]),
+        "kvq_fill_u32": (_c_i32, [_c_p, ctypes.c_uint32, _c_i64, _c_p]),
+        "kvq_synth_normal_f16": (_c_i32, [_c_p, _c_u64, _c_i32, _c_i32,
+                                          _c_i32, _c_i32, _c_i64, _c_i64,
+                                          _c_i32, _c_i64, _c_p]),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(L, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = L
+    return L
+
+
+def strerror(status):
+    try:
+        return lib().kvq_strerror(status).decode()
+    except RuntimeError:
+        return f"status {status}"
+
+
+def _check(status, where):
+    if status != KVQ_OK:
+        raise KvqError(status, where)
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _ptr(t):
+    return ctypes.c_void_p(t.data_ptr()) if t is not None else None
+
+
+def _dtype(t):
+    if t.dtype == torch.float16:
+        return KVQ_F16
+    if t.dtype == torch.float32:
+        return KVQ_F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _need_cuda(*ts):
+    for t in ts:
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("device tensors must be contiguous CUDA tensors")
+
+
+def kvq_words(n_fields, bits):
+    return lib().kvq_words(n_fields, bits)
+
+
+def kvq_quantize_k(k, bits, group_tok, err=None):
+    """k: [n_mats][n_tok][d] -> (codes int32 [.., words], scales f32, err)."""
+    _need_cuda(k)
+    n_mats, n_tok, d = k.shape
+    w = kvq_words(d, bits)
+    ng = (n_tok + group_tok - 1) // group_tok if group_tok > 0 else 0
+    codes = torch.empty((n_mats, n_tok, max(w, 0)), dtype=torch.int32,
+                        device=k.device)
+    scales = torch.empty((n_mats, ng, d), dtype=torch.float32, device=k.device)
+    if err is None:
+        err = torch.zeros(1, dtype=torch.int32, device=k.device)
+    _check(lib().kvq_quantize_k(_ptr(k), _dtype(k), n_mats, n_tok, d, bits,
+                                group_tok, _ptr(codes), _ptr(scales),
+                                _ptr(err), _stream()), "kvq_quantize_k")
+    return codes, scales, err
+
+
+def kvq_quantize_v(v, bits, group_ch, err=None):
+    """v: [n_mats][n_tok][d] -> (codes, scales [.., d/Gv], err)."""
+    _need_cuda(v)
+    n_mats, n_tok, d = v.shape
+    w = kvq_words(d, bits)
+    ng = d // group_ch if group_ch > 0 else 0
+    codes = torch.empty((n_mats, n_tok, max(w, 0)), dtype=torch.int32,
+                        device=v.device)
+    scales = torch.empty((n_mats, n_tok, ng), dtype=torch.float32,
+                         device=v.device)
+    if err is None:
+        err = torch.zeros(1, dtype=torch.int32, device=v.device)
+    _check(lib().kvq_quantize_v(_ptr(v), _dtype(v), n_mats, n_tok, d, bits,
+                                group_ch, _ptr(codes), _ptr(scales),
+                                _ptr(err), _stream()), "kvq_quantize_v")
+    return codes, scales, err
+
+
+def kvq_dequant(codes, scales, n_tok, d, bits, axis, group):
+    _need_cuda(codes, scales)
+    n_mats = codes.shape[0]
+    out = torch.empty((n_mats, n_tok, d), dtype=torch.float32,
+                      device=codes.device)
+    _check(lib().kvq_dequant(_ptr(codes), _ptr(scales), n_mats, n_tok, d,
+                             bits, axis, group, _ptr(out), _stream()),
+           "kvq_dequant")
+    return out
+
+
+def kvq_poll_error(err):
+    return lib().kvq_poll_error(_ptr(err), _stream())
+
+
+def kvq_synth_normal_f16(out, seed, tensor, layer, head0, n_heads, t0, n_tok,
+                         d, head_stride=None):
+    _need_cuda(out)
+    if head_stride is None:
+        head_stride = n_tok * d
+    _check(lib().kvq_synth_normal_f16(_ptr(out), seed, tensor, layer, head0,
+                                      n_heads, t0, n_tok, d, head_stride,
+                                      _stream()), "kvq_synth_normal_f16")
+    return out
+
+
+class Cache:
+    """A kvq_cache bound to one torch-allocated device buffer."""
+
+    def __init__(self, B, Hkv, D, max_tokens, k_bits, v_bits, G, Gv, R, S=0,
+                 mixed=False, n_bf16=0, n_int4=0, device="cuda"):
+        self.cfg = CacheCfg(batch=B, kv_heads=Hkv, head_dim=D, k_bits=k_bits,
+                            v_bits=v_bits, group_tok=G, group_ch=Gv,
+                            residual=R, sink=S, k_mixed=int(mixed),
+                            n_bf16=n_bf16, n_int4=n_int4,
+                            max_tokens=max_tokens)
+        nbytes = lib().kvq_cache_bytes(ctypes.byref(self.cfg))
+        if nbytes == 0:
+            raise KvqError(KVQ_E_ARG, "kvq_cache_bytes")
+        self.buf = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        h = ctypes.c_void_p()
+        _check(lib().kvq_cache_init(ctypes.byref(self.cfg), _ptr(self.buf),
+                                    nbytes, 0, ctypes.byref(h), _stream()),
+               "kvq_cache_init")
+        self.handle = h
+        self.mixed = mixed
+
+    def __del__(self):
+        h = getattr(self, "handle", None)
+        if h and _lib is not None:
+            _lib.kvq_cache_free(h)
+            self.handle = None
+
+    @property
+    def n_tokens(self):
+        return lib().kvq_cache_tokens(self.handle)
+
+    def kvq_append(self, k_new, v_new):
+        _need_cuda(k_new, v_new)
+        n_new = k_new.shape[2]
+        _check(lib().kvq_append(self.handle, _ptr(k_new), _ptr(v_new),
+                                _dtype(k_new), n_new, _stream()),
+               "kvq_append")
+
+    def kvq_salience_select(self, q_win):
+        _need_cuda(q_win)
+        _, w, hq, _ = q_win.shape
+        _check(lib().kvq_salience_select(self.handle, _ptr(q_win),
+                                         _dtype(q_win), w, hq, _stream()),
+               "kvq_salience_select")
+
+    def kvq_cache_check(self):
+        return lib().kvq_cache_check(self.handle, _stream())
+
+    def kvq_cache_view(self):
+        v = KvView()
+        _check(lib().kvq_cache_view(self.handle, ctypes.byref(v)),
+               "kvq_cache_view")
+        return v
+
+
+def kvq_export(view):
+    """Canonical dense device copies of a view (dict of torch tensors)."""
+    B, H, D = view.batch, view.kv_heads, view.head_dim
+    ns, nq, nt = view.n_sink, view.n_quant, view.n_tail
+    dev = torch.device("cuda")
+    ng = nq // view.group_tok if view.group_tok > 0 else 0
+    t = {
+        "sink_k": torch.empty((B, H, ns, D), dtype=torch.float16, device=dev),
+        "sink_v": torch.empty((B, H, ns, D), dtype=torch.float16, device=dev),
+        "tail_k": torch.empty((B, H, nt, D), dtype=torch.float16, device=dev),
+        "tail_v": torch.empty((B, H, nt, D), dtype=torch.float16, device=dev),
+        "v_codes": torch.empty((B, H, nq, kvq_words(D, view.v_bits)),
+                               dtype=torch.int32, device=dev),
+        "v_scales": torch.empty((B, H, nq, D // view.group_ch),
+                                dtype=torch.float32, device=dev),
+    }
+    if view.k_mixed:
+        nb, n4 = view.n_bf16, view.n_int4
+        n2 = D - nb - n4
+        t["k_class"] = torch.empty((B, H, ng, D), dtype=torch.uint8,
+                                   device=dev)
+        t["k_bf16"] = torch.empty((B, H, nq, nb), dtype=torch.int16,
+                                  device=dev)
+        t["k_int4"] = torch.empty((B, H, nq, kvq_words(n4, 4)),
+                                  dtype=torch.int32, device=dev)
+        t["k_int2"] = torch.empty((B, H, nq, kvq_words(n2, 2)),
+                                  dtype=torch.int32, device=dev)
+        t["k_scales"] = torch.empty((B, H, ng, n4 + n2), dtype=torch.float32,
+                                    device=dev)
+    else:
+        t["k_codes"] = torch.empty((B, H, nq, kvq_words(D, view.k_bits)),
+                                   dtype=torch.int32, device=dev)
+        t["k_scales"] = torch.empty((B, H, ng, D), dtype=torch.float32,
+                                    device=dev)
+    bufs = ExportBufs(**{k: (v.data_ptr() if v.numel() else None)
+                         for k, v in t.items()})
+    _check(lib().kvq_export(ctypes.byref(view), ctypes.byref(bufs), _stream()),
+           "kvq_export")
+    return t
+
+
+def kvq_decode_workspace_bytes(view, n_q_heads, n_splits=0):
+    return lib().kvq_decode_workspace_bytes(ctypes.byref(view), n_q_heads,
+                                            n_splits)
+
+
+def kvq_decode_attention(view, q, sm_scale=None, n_splits=0,
+                         flags=KVQ_DECODE_AUTO, workspace=None, out=None):
+    """q: [B][Hq][D] f16/f32 -> out [B][Hq][D] float32."""
+    _need_cuda(q)
+    B, hq, D = q.shape
+    if sm_scale is None:
+        sm_scale = 1.0 / D ** 0.5
+    ws_bytes = kvq_decode_workspace_bytes(view, hq, n_splits)
+    if ws_bytes == 0:
+        raise KvqError(KVQ_E_ARG, "kvq_decode_workspace_bytes")
+    if workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty((B, hq, D), dtype=torch.float32, device=q.device)
+    _check(lib().kvq_decode_attention(
+        ctypes.byref(view), _ptr(q), _dtype(q), hq, sm_scale, _ptr(out),
+        n_splits, flags, _ptr(workspace), workspace.numel(), _stream()),
+        "kvq_decode_attention")
+    return out
+
+
+def stateless_view(k_codes, k_scales, v_codes, v_scales, B, Hkv, D, k_bits,
+                   v_bits, G, Gv, n_tok):
+    """A view over kvq_quantize_k/v outputs ([B*Hkv][n_tok][..] arrays)."""
+    v = KvView()
+    v.batch, v.kv_heads, v.head_dim = B, Hkv, D
+    v.k_bits, v.v_bits, v.group_tok, v.group_ch = k_bits, v_bits, G, Gv
+    v.v_layout = KVQ_V_ROWS
+    v.n_quant = n_tok
+    v.k_codes, v.k_codes_stride = k_codes.data_ptr(), k_codes[0].numel()
+    v.k_scales, v.k_scales_stride = k_scales.data_ptr(), k_scales[0].numel()
+    v.v_codes, v.v_codes_stride = v_codes.data_ptr(), v_codes[0].numel()
+    v.v_scales, v.v_scales_stride = v_scales.data_ptr(), v_scales[0].numel()
+    return v

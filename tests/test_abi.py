@@ -1,0 +1,106 @@
+"""The C-ABI library loads, exports every symbol include/kvq.h declares, and
+rejects bad arguments on the host before touching the GPU (CPU only)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from quantized_decode_attention_02_amd import kvq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvq.h")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(kvq_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_library_exports_every_declared_symbol():
+    L = kvq.lib()
+    names = declared_functions()
+    assert len(names) >= 18
+    for n in names:
+        assert hasattr(L, n), n
+    assert sorted(kvq.EXPORTED) == names
+
+
+def test_words_and_strerror():
+    assert kvq.kvq_words(128, 4) == 16
+    assert kvq.kvq_words(128, 2) == 8
+    assert kvq.kvq_words(128, 3) == 13
+    assert kvq.kvq_words(32, 8) == 8
+    assert kvq.kvq_words(5, 7) == -1
+    assert kvq.strerror(kvq.KVQ_E_NONFINITE) == "NaN/Inf input rejected"
+
+
+def _cfg(**kw):
+    base = dict(batch=1, kv_heads=32, head_dim=128, k_bits=4, v_bits=2,
+                group_tok=128, group_ch=32, residual=128, sink=0, k_mixed=0,
+                n_bf16=0, n_int4=0, max_tokens=4096)
+    base.update(kw)
+    return kvq.CacheCfg(**base)
+
+
+def test_cache_bytes_covers_the_payload():
+    L = kvq.lib()
+    c = _cfg()
+    nbytes = L.kvq_cache_bytes(ctypes.byref(c))
+    # payload of a full cache: 3968 quantized tokens + 128 tail per head
+    payload = 32 * (3968 * (64 + 32 + 16) + 31 * 128 * 4 + 128 * 512)
+    assert payload <= nbytes <= payload * 1.1
+
+
+@pytest.mark.parametrize("bad", [dict(k_bits=5), dict(residual=100),
+                                 dict(group_ch=48), dict(head_dim=300),
+                                 dict(k_mixed=1, n_bf16=100, n_int4=40),
+                                 dict(batch=0)])
+def test_cache_bytes_rejects_bad_config(bad):
+    c = _cfg(**bad)
+    assert kvq.lib().kvq_cache_bytes(ctypes.byref(c)) == 0
+
+
+def test_host_argument_errors_enqueue_nothing():
+    L = kvq.lib()
+    p = ctypes.c_void_p(256)
+    # bad bit width / group / dtype: rejected before any HIP call
+    assert L.kvq_quantize_k(p, 1, 1, 4, 8, 5, 2, p, p, None, None) == \
+        kvq.KVQ_E_ARG
+    assert L.kvq_quantize_v(p, 1, 1, 4, 8, 4, 3, p, p, None, None) == \
+        kvq.KVQ_E_ARG
+    assert L.kvq_quantize_k(p, 7, 1, 4, 8, 4, 2, p, p, None, None) == \
+        kvq.KVQ_E_ARG
+    # empty input is a successful no-op
+    assert L.kvq_quantize_k(p, 1, 0, 4, 8, 4, 2, p, p, None, None) == \
+        kvq.KVQ_OK
+    assert L.kvq_dequant(p, p, 1, 4, 8, 4, 9, 2, p, None) == kvq.KVQ_E_ARG
+    c = _cfg()
+    h = ctypes.c_void_p()
+    # misaligned buffer
+    assert L.kvq_cache_init(ctypes.byref(c), ctypes.c_void_p(100), 1 << 30,
+                            0, ctypes.byref(h), None) == kvq.KVQ_E_ARG
+    # too small
+    assert L.kvq_cache_init(ctypes.byref(c), ctypes.c_void_p(256), 16, 0,
+                            ctypes.byref(h), None) == kvq.KVQ_E_ARG
+    assert L.kvq_synth_normal_f16(p, 1, 9, 0, 0, 1, 0, 1, 8, 8, None) == \
+        kvq.KVQ_E_ARG
+
+
+def test_view_validation_and_empty_decode():
+    L = kvq.lib()
+    v = kvq.KvView()
+    v.batch, v.kv_heads, v.head_dim = 1, 1, 32
+    # an empty view: decode is an argument error, workspace query too for a
+    # head count that does not divide
+    assert L.kvq_decode_workspace_bytes(ctypes.byref(v), 3, 0) > 0
+    p = ctypes.c_void_p(256)
+    assert L.kvq_decode_attention(ctypes.byref(v), p, 1, 3, 0.1, p, 0, 0, p,
+                                  1 << 20, None) == kvq.KVQ_E_ARG
+    v2 = kvq.KvView()
+    v2.batch, v2.kv_heads, v2.head_dim = 1, 2, 32
+    assert L.kvq_decode_workspace_bytes(ctypes.byref(v2), 3, 0) == 0
+    # quantized tokens but no code arrays
+    v.n_quant, v.group_tok, v.group_ch, v.k_bits, v.v_bits = 64, 64, 32, 4, 2
+    assert L.kvq_decode_workspace_bytes(ctypes.byref(v), 1, 0) == 0
