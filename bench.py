@@ -1,0 +1,328 @@
+"""Benchmark of quantized-KV decode attention on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--gpus 1]
+
+A step is one decode step of the whole hot path: for every layer, append the
+new token's K and V (fp16 tail, a key-group flush every G steps) and run
+decode attention over the packed cache.  Default workload: 32 layers x 32
+heads x head_dim 128 at 1,048,576 tokens of context, K and V at 2 bits (K per
+channel in 128-token groups, V per token in 32-channel groups), an fp16 sink
+token and a 128-token fp16 tail; the cache (90 GB) is built on the device
+from the counter-based synthetic generator.  The 4096-token prefill append
+into every layer is timed separately.
+
+Prints one JSON line.  `value` is whole-job algorithmic HBM throughput in
+GB/s: the bytes one step must read (packed codes, float32 scales, fp16 sink
+and tail rows, queries) over the step time; `roofline` relates the decode
+call's bytes to its HIP-event time; `cpu_baseline` times the CPU oracle's
+decode (dequant to float64 + float64 attention) on a bounded sample.
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+import synth
+
+PEAK_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="1m_32layer",
+                    choices=["1m_32layer", "gqa_128k", "mixkvq_32k",
+                             "7b_layer_4k"])
+    ap.add_argument("--layers", type=int, default=None,
+                    help="layers of the 1m_32layer workload (default 32)")
+    ap.add_argument("--seed", type=int, default=7)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--splits", type=int, default=0)
+    return ap.parse_args()
+
+
+def stream_bytes(view, hq):
+    """Algorithmic bytes one decode call reads (all streams of the view)."""
+    D = view.head_dim
+    nq, ns, nt = view.n_quant, view.n_sink, view.n_tail
+    G, Gv = view.group_tok, view.group_ch
+    if view.k_mixed:
+        nb, n4 = view.n_bf16, view.n_int4
+        n2 = D - nb - n4
+        k = nq * (2 * nb + 4 * math.ceil(n4 / 8) + 4 * math.ceil(n2 / 16))
+        k += (nq // G) * (4 * (n4 + n2) + D)
+    else:
+        k = nq * 4 * math.ceil(D / (32 // view.k_bits)) + (nq // G) * D * 4
+    v = nq * 4 * math.ceil(D / (32 // view.v_bits)) + nq * (D // Gv) * 4
+    fp16 = (ns + nt) * D * 2 * 2
+    per_stream = k + v + fp16
+    return view.batch * view.kv_heads * per_stream + view.batch * hq * D * 2
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from quantized_decode_attention_02_amd import kvq
+
+    kvq.lib()  # fail loudly if the library is missing
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream()
+    w = dict(synth.WORKLOADS[args.workload])
+    extra = {}
+
+    if args.workload == "1m_32layer":
+        layers = args.layers or w["layers"]
+        B, Hq, Hkv, N, D = w["B"], w["Hq"], w["Hkv"], w["N"], w["D"]
+        chunk = w["chunk"]
+        cap = N + args.warmup + args.steps + 8
+        caches = []
+        build_chunk = 65536
+        kbuf = torch.empty(Hkv * build_chunk * D, dtype=torch.float16,
+                           device=dev)
+        vbuf = torch.empty_like(kbuf)
+        t_build = time.time()
+        for L in range(layers):
+            c = kvq.Cache(B, Hkv, D, cap, w["k_bits"], w["v_bits"], w["G"],
+                          w["Gv"], w["R"], S=w["S"])
+            t = 0
+            while t < N - chunk:
+                n = min(build_chunk, N - chunk - t)
+                kv = kbuf[:Hkv * n * D].view(1, Hkv, n, D)
+                vv = vbuf[:Hkv * n * D].view(1, Hkv, n, D)
+                kvq.kvq_synth_normal_f16(kv, args.seed, synth.TENSOR_K, L, 0,
+                                         Hkv, t, n, D, n * D)
+                kvq.kvq_synth_normal_f16(vv, args.seed, synth.TENSOR_V, L, 0,
+                                         Hkv, t, n, D, n * D)
+                c.kvq_append(kv, vv)
+                t += n
+            caches.append(c)
+            if L % 8 == 7 or L == layers - 1:
+                torch.cuda.synchronize()
+                print(f"# built {L + 1}/{layers} layers "
+                      f"({time.time() - t_build:.1f}s)", file=sys.stderr,
+                      flush=True)
+        del kbuf, vbuf
+        # the last 4096-token prefill chunk of every layer: timed append
+        kc = torch.empty((layers, 1, Hkv, chunk, D), dtype=torch.float16,
+                         device=dev)
+        vc = torch.empty_like(kc)
+        for L in range(layers):
+            kvq.kvq_synth_normal_f16(kc[L, 0], args.seed, synth.TENSOR_K, L,
+                                     0, Hkv, N - chunk, chunk, D, chunk * D)
+            kvq.kvq_synth_normal_f16(vc[L, 0], args.seed, synth.TENSOR_V, L,
+                                     0, Hkv, N - chunk, chunk, D, chunk * D)
+        torch.cuda.synchronize()
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record(stream)
+        for L in range(layers):
+            caches[L].kvq_append(kc[L], vc[L])
+        ev[1].record(stream)
+        torch.cuda.synchronize()
+        append_ms = ev[0].elapsed_time(ev[1])
+        extra["append_4096_us_per_layer"] = round(1000 * append_ms / layers,
+                                                  2)
+        del kc, vc
+        for c in caches:
+            assert c.kvq_cache_check() == kvq.KVQ_OK
+        # per-step inputs: queries and the new token of every layer
+        n_steps_total = args.warmup + args.steps
+        q = torch.empty((layers, B, Hq, D), dtype=torch.float16, device=dev)
+        knew = torch.empty((n_steps_total, layers, B, Hkv, 1, D),
+                           dtype=torch.float16, device=dev)
+        vnew = torch.empty_like(knew)
+        for L in range(layers):
+            kvq.kvq_synth_normal_f16(q[L, 0], args.seed, synth.TENSOR_Q, L, 0,
+                                     Hq, 0, 1, D, D)
+            for st in range(n_steps_total):
+                kvq.kvq_synth_normal_f16(knew[st, L, 0], args.seed,
+                                         synth.TENSOR_K, L, 0, Hkv, N + st, 1,
+                                         D, D)
+                kvq.kvq_synth_normal_f16(vnew[st, L, 0], args.seed,
+                                         synth.TENSOR_V, L, 0, Hkv, N + st, 1,
+                                         D, D)
+        config = {"workload": "1m_32layer", "layers": layers, "batch": B,
+                  "q_heads": Hq, "kv_heads": Hkv, "head_dim": D,
+                  "context": N, "k_bits": w["k_bits"], "v_bits": w["v_bits"],
+                  "k_group_tokens": w["G"], "v_group_channels": w["Gv"],
+                  "residual": w["R"], "sink": w["S"]}
+    else:
+        layers = 1
+        B, Hq, Hkv, N, D = w["B"], w["Hq"], w["Hkv"], w["N"], w["D"]
+        ikw = {k: w[k] for k in ("outliers", "n_out", "out_factor", "frac",
+                                 "fmin", "fmax", "sink_factor") if k in w}
+        qn, kn, vn = synth.kv_inputs(args.seed, B, Hq, Hkv,
+                                     N + args.warmup + args.steps, D, **ikw)
+        c = kvq.Cache(B, Hkv, D, N + args.warmup + args.steps + 8,
+                      w["k_bits"], w["v_bits"], w["G"], w["Gv"], w["R"],
+                      S=w["S"], mixed=w.get("mixed", False),
+                      n_bf16=w.get("n_bf16", 0), n_int4=w.get("n_int4", 0))
+        if w.get("mixed"):
+            qw = synth.query_window(args.seed, B, w["W"], Hq, D)
+            c.kvq_salience_select(torch.from_numpy(qw).to(dev))
+        c.kvq_append(torch.from_numpy(np.ascontiguousarray(kn[:, :, :N])).to(dev),
+                     torch.from_numpy(np.ascontiguousarray(vn[:, :, :N])).to(dev))
+        assert c.kvq_cache_check() == kvq.KVQ_OK
+        caches = [c]
+        q = torch.from_numpy(qn).to(dev)[None]
+        knew = torch.from_numpy(np.ascontiguousarray(
+            kn[:, :, N:].transpose(2, 0, 1, 3)[:, None, :, :, None, :])).to(dev)
+        vnew = torch.from_numpy(np.ascontiguousarray(
+            vn[:, :, N:].transpose(2, 0, 1, 3)[:, None, :, :, None, :])).to(dev)
+        config = {"workload": args.workload, "batch": B, "q_heads": Hq,
+                  "kv_heads": Hkv, "head_dim": D, "context": N,
+                  "k_bits": "mixed bf16/int4/int2" if w.get("mixed")
+                  else w["k_bits"], "v_bits": w["v_bits"],
+                  "k_group_tokens": w["G"], "v_group_channels": w["Gv"],
+                  "residual": w["R"], "sink": w["S"]}
+
+    # decode workspaces and outputs (allocated before timing)
+    views = [c.kvq_cache_view() for c in caches]
+    ws_bytes = max(kvq.kvq_decode_workspace_bytes(v, Hq, args.splits)
+                   for v in views) + 4096
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+    out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
+    flush_buf = None
+    if args.workload != "1m_32layer":
+        flush_buf = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+
+    def step(i, events=None):
+        for L, c in enumerate(caches):
+            c.kvq_append(knew[i, L], vnew[i, L])
+            view = c.kvq_cache_view()
+            if events is not None:
+                events[L][0].record(stream)
+            kvq.kvq_decode_attention(view, q[L], n_splits=args.splits,
+                                     workspace=ws, out=out)
+            if events is not None:
+                events[L][1].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    for c in caches:
+        assert c.kvq_cache_check() == kvq.KVQ_OK
+
+    dec_events = [[[torch.cuda.Event(enable_timing=True) for _ in range(2)]
+                   for _ in caches] for _ in range(args.steps)]
+    step_events = [[torch.cuda.Event(enable_timing=True) for _ in range(2)]
+                   for _ in range(args.steps)]
+    bytes_step = 0
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        if flush_buf is not None:
+            flush_buf.fill_(s & 0xFF)   # evict the 256 MB Infinity Cache
+        step_events[s][0].record(stream)
+        step(args.warmup + s, dec_events[s])
+        step_events[s][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    for c in caches:
+        assert c.kvq_cache_check() == kvq.KVQ_OK
+    views = [c.kvq_cache_view() for c in caches]
+    bytes_step = sum(stream_bytes(v, Hq) for v in views)
+    step_ms = [e[0].elapsed_time(e[1]) for e in step_events]
+    ms_per_step = float(np.mean(step_ms)) if flush_buf is not None else \
+        1000.0 * wall / args.steps
+    dec_ms = [e[0].elapsed_time(e[1]) for st in dec_events for e in st]
+    dec_avg_ms = float(np.mean(dec_ms))
+    bytes_launch = bytes_step / len(caches)
+    achieved = bytes_launch / (dec_avg_ms * 1e-3) / 1e9
+    value = bytes_step / (ms_per_step * 1e-3) / 1e9
+
+    res = {
+        "metric": "quantized-KV decode attention: µs/step + achieved "
+                  "HBM GB/s (% of peak)",
+        "value": round(value, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "us_per_step": round(1000 * ms_per_step, 1),
+        "pct_of_hbm_peak": round(100 * value / PEAK_GBS, 1),
+        "tokens_per_s": round(B * 1000.0 / ms_per_step, 2),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "int2/int4 codes, fp16 MFMA, fp32 accumulate",
+        "data": "synthetic (seeded; N(0,1)-like bodies, no weights)",
+        "config": config,
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(achieved, 1),
+            "peak": PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(achieved / PEAK_GBS, 4),
+            "traffic": None,
+            "kernel": "kvq_decode_attention (decode_mfma_kernel + fp16 "
+                      "sink/tail partials + merge)",
+            "bytes_per_launch": int(bytes_launch),
+            "avg_launch_us": round(1000 * dec_avg_ms, 2),
+        },
+        "bytes_per_step": int(bytes_step),
+    }
+    res.update(extra)
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(args, w, layers)
+    print(json.dumps(res), flush=True)
+
+
+def cpu_baseline(args, w, layers):
+    """The oracle's decode on one (batch, KV head) stream, scaled."""
+    from threadpoolctl import threadpool_limits
+    from oracle import attention, cache as ocache
+
+    D = w["D"]
+    if args.workload == "1m_32layer":
+        n_sample = 262144
+        k, v = synth.counter_kv(args.seed, 0, w["Hkv"], 0, n_sample, D,
+                                heads=[0])
+        q = synth.counter_query(args.seed, 0, w["Hq"], D)[:1]
+        scale = (w["N"] / n_sample) * w["Hkv"] * layers * w["B"]
+        sample = (f"1 of {w['Hkv']} KV heads of 1 of {layers} layers at "
+                  f"{n_sample} of {w['N']} tokens; scaled x{scale:g}")
+        g = 1
+    else:
+        n_sample = min(w["N"], 131072)
+        qn, kn, vn = synth.kv_inputs(args.seed, 1, w["Hq"] // w["Hkv"], 1,
+                                     n_sample, D)
+        k, v, q = kn[0], vn[0], qn[0]
+        g = w["Hq"] // w["Hkv"]
+        scale = (w["N"] / n_sample) * w["Hkv"] * w["B"]
+        sample = (f"1 of {w['B'] * w['Hkv']} (batch, KV head) streams at "
+                  f"{n_sample} of {w['N']} tokens; scaled x{scale:g}")
+    cfg = ocache.CacheConfig(B=1, Hkv=1, D=D, S=w["S"], R=w["R"], G=w["G"],
+                             Gv=w["Gv"], k_bits=w.get("k_bits", 2),
+                             v_bits=w["v_bits"], mixed=w.get("mixed", False),
+                             n_bf16=w.get("n_bf16", 0),
+                             n_int4=w.get("n_int4", 0))
+    oc = ocache.Cache(cfg)
+    oc.append(k[None], v[None])
+    times = []
+    with threadpool_limits(limits=1):
+        for i in range(4):
+            t0 = time.perf_counter()
+            kh, vh = oc.dequantized(0, 0)
+            attention.attention(q[:g].astype(np.float64), kh[None], vh[None])
+            times.append(time.perf_counter() - t0)
+    t = float(np.median(times[1:]))
+    us_step = t * scale * 1e6
+    return {"value": round(us_step, 1), "unit": "us/step", "cores": 1,
+            "kind": "oracle", "sample": sample,
+            "sample_seconds": round(t, 3)}
+
+
+if __name__ == "__main__":
+    main()

@@ -94,7 +94,9 @@ template <> __device__ inline float ldq<uint16_t>(const uint16_t* p, int64_t i) 
 template <typename QT>
 __global__ void __launch_bounds__(kThreads)
 decode_generic_kernel(kvq_kv_view v, const QT* __restrict__ q, int Hq,
-                      float qscale, float* __restrict__ partials, int n_parts) {
+                      float qscale, float* __restrict__ partials,
+                      int64_t range_lo, int64_t range_hi, int n_parts,
+                      int part_offset, int part_stride) {
   extern __shared__ float smem[];
   const int D = v.head_dim;
   const int g = Hq / v.kv_heads;
@@ -107,9 +109,10 @@ decode_generic_kernel(kvq_kv_view v, const QT* __restrict__ q, int Hq,
   const int tid = threadIdx.x;
   const int part = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int64_t s = (int64_t)b * v.kv_heads + kvh;
-  const int64_t N = v.n_sink + v.n_quant + v.n_tail;
+  const int64_t N = range_hi - range_lo;
   const int64_t per = (N + n_parts - 1) / n_parts;
-  const int64_t t_lo = min(N, (int64_t)part * per), t_hi = min(N, t_lo + per);
+  const int64_t t_lo = range_lo + min(N, (int64_t)part * per);
+  const int64_t t_hi = min(range_hi, t_lo + per);
 
   for (int i = tid; i < g * D; i += kThreads) {
     const int h = i / D, d = i % D;
@@ -160,7 +163,8 @@ decode_generic_kernel(kvq_kv_view v, const QT* __restrict__ q, int Hq,
   for (int i = tid; i < g * (D + 2); i += kThreads) {
     const int h = i / (D + 2), j = i % (D + 2);
     float val = j == 0 ? ms[h] : (j == 1 ? ls[h] : os[h * D + j - 2]);
-    partials[(((int64_t)b * Hq + kvh * g + h) * n_parts + part) * (D + 2) + j] = val;
+    partials[(((int64_t)b * Hq + kvh * g + h) * part_stride + part_offset + part) * (D + 2) + j] =
+        val;
   }
 }
 
@@ -189,9 +193,10 @@ __global__ void merge_kernel(const float* __restrict__ partials, int D,
 
 }  // namespace
 
-hipError_t launch_decode_generic(const kvq_kv_view& v, const void* q, int f16,
-                                 int Hq, float sm_scale, float* partials,
-                                 int n_parts, hipStream_t s) {
+hipError_t launch_decode_generic_range(const kvq_kv_view& v, const void* q, int f16,
+                                       int Hq, float sm_scale, float* partials,
+                                       int64_t range_lo, int64_t range_hi, int n_parts,
+                                       int part_offset, int part_stride, hipStream_t s) {
   const int g = Hq / v.kv_heads;
   const size_t lds = sizeof(float) * ((size_t)g * v.head_dim * 2 +
                                       (size_t)g * kChunkTok + 3 * (size_t)g);
@@ -206,11 +211,21 @@ hipError_t launch_decode_generic(const kvq_kv_view& v, const void* q, int f16,
   }
   if (f16)
     decode_generic_kernel<uint16_t><<<grid, kThreads, lds, s>>>(
-        v, (const uint16_t*)q, Hq, qscale, partials, n_parts);
+        v, (const uint16_t*)q, Hq, qscale, partials, range_lo, range_hi, n_parts, part_offset,
+        part_stride);
   else
     decode_generic_kernel<float><<<grid, kThreads, lds, s>>>(
-        v, (const float*)q, Hq, qscale, partials, n_parts);
+        v, (const float*)q, Hq, qscale, partials, range_lo, range_hi, n_parts, part_offset,
+        part_stride);
   return hipGetLastError();
+}
+
+hipError_t launch_decode_generic(const kvq_kv_view& v, const void* q, int f16,
+                                 int Hq, float sm_scale, float* partials,
+                                 int n_parts, hipStream_t s) {
+  const int64_t N = v.n_sink + v.n_quant + v.n_tail;
+  return launch_decode_generic_range(v, q, f16, Hq, sm_scale, partials, 0, N, n_parts, 0,
+                                     n_parts, s);
 }
 
 hipError_t launch_merge(const float* partials, int B, int Hq, int D,

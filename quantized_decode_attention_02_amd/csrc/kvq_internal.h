@@ -146,6 +146,12 @@ hipError_t launch_synth(uint16_t* out, uint64_t seed, int tensor, int layer,
 hipError_t launch_decode_generic(const kvq_kv_view& v, const void* q, int f16,
                                  int Hq, float sm_scale, float* partials,
                                  int n_parts, hipStream_t s);
+// Tokens [range_lo, range_hi) of the cache order split into n_parts
+// partials written at slots part_offset .. of part_stride per head.
+hipError_t launch_decode_generic_range(const kvq_kv_view& v, const void* q, int f16,
+                                       int Hq, float sm_scale, float* partials,
+                                       int64_t range_lo, int64_t range_hi, int n_parts,
+                                       int part_offset, int part_stride, hipStream_t s);
 bool mfma_decode_eligible(const kvq_kv_view& v, int Hq);
 int mfma_decode_parts(const kvq_kv_view& v, int Hq, int n_splits);
 hipError_t launch_decode_mfma(const kvq_kv_view& v, const void* q, int f16,

@@ -274,12 +274,16 @@ def test_cache_parity(name):
             say(f"  flags={flags} splits={splits} err={err:.3e}")
             assert err <= TOL
             outs[(flags, splits)] = out
-    # the split count changes only the float32 summation order
-    for flags in (kvq.KVQ_DECODE_AUTO, kvq.KVQ_DECODE_GENERIC):
+    # The split count changes the summation order, and on the matrix-core
+    # path also the running max against which P' = p * v_scale is rounded to
+    # fp16 (relative 2^-11 per element): bounds 1e-4 (general, float32) and
+    # 1e-3 (matrix core).
+    for flags, bound in ((kvq.KVQ_DECODE_AUTO, 1e-3),
+                         (kvq.KVQ_DECODE_GENERIC, 1e-4)):
         a = outs[(flags, 1)]
         for s in (0, 3):
             rel = np.max(np.abs(outs[(flags, s)] - a)) / np.max(np.abs(a))
-            assert rel <= 1e-4
+            assert rel <= bound
     # fp32 query gives the same result as its fp16 values
     out32 = kvq.kvq_decode_attention(view, qt.float()).cpu().numpy()
     assert attention.max_row_relative_error(out32, ref) <= TOL
