@@ -44,7 +44,21 @@ def parse():
     ap.add_argument("--seed", type=int, default=7)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--splits", type=int, default=0)
+    ap.add_argument("--calibrate-copy", type=int, default=0, metavar="MIB",
+                    help="only copy a MIB-MiB device buffer 3 times (a "
+                         "known-size kernel to scale FETCH_SIZE/WRITE_SIZE)")
     return ap.parse_args()
+
+
+def calibrate_copy(mib):
+    import torch
+    n = mib << 20
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_per_launch": n, "launches": 3}), flush=True)
 
 
 def stream_bytes(view, hq):
@@ -71,6 +85,9 @@ def main():
         print("bench.py measures one GPU: this build has no multi-GPU path "
               "(run with --gpus 1)", file=sys.stderr)
         sys.exit(2)
+    if args.calibrate_copy:
+        calibrate_copy(args.calibrate_copy)
+        return
     import torch
     from quantized_decode_attention_02_amd import kvq
 
@@ -188,8 +205,10 @@ def main():
 
     # decode workspaces and outputs (allocated before timing)
     views = [c.kvq_cache_view() for c in caches]
-    ws_bytes = max(kvq.kvq_decode_workspace_bytes(v, Hq, args.splits)
-                   for v in views) + 4096
+    # room for a few more partials than the first step needs: the automatic
+    # split count can grow by one as flushes add key groups
+    ws_bytes = 2 * max(kvq.kvq_decode_workspace_bytes(v, Hq, args.splits)
+                       for v in views) + 65536
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
     flush_buf = None

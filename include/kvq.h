@@ -203,7 +203,9 @@ typedef struct {
   /* uniform keys: codes [n_quant][kvq_words(D, k_bits)], scales [groups][D] */
   const uint32_t* k_codes; int64_t k_codes_stride;
   const float* k_scales; int64_t k_scales_stride;
-  /* largest |K| of each key group (float32), nullable */
+  /* per key group: the largest channel scale (for bf16 channels of mixed
+     keys, the largest |K|), a bound used to keep matrix-core operands in
+     range; nullable (the matrix-core path then is not used) */
   const float* k_gmax; int64_t k_gmax_stride;
   /* mixed keys: per group, k_pos[d] = position of channel d in the order
      [bf16 channels | int4 channels | int2 channels], each ascending;

@@ -339,7 +339,9 @@ kvq_status kvq_export(const kvq_kv_view* v, const kvq_export_bufs* out, void* st
 }
 
 size_t kvq_decode_workspace_bytes(const kvq_kv_view* v, int n_q_heads, int n_splits) {
-  if (!view_ok(v) || n_q_heads < 1 || n_q_heads % v->kv_heads || n_splits < 0) return 0;
+  if (!view_ok(v) || n_q_heads < 1 || n_q_heads % v->kv_heads || n_splits < 0 ||
+      n_splits > 16384)
+    return 0;
   int parts = generic_parts(v, n_splits);
   if (mfma_decode_eligible(*v, n_q_heads)) {
     int pm = mfma_decode_parts(*v, n_q_heads, n_splits);
@@ -353,7 +355,8 @@ kvq_status kvq_decode_attention(const kvq_kv_view* v, const void* q, int dtype,
                                 int flags, void* workspace, size_t ws_bytes, void* stream) {
   if (!view_ok(v) || !q || !out || !workspace) return KVQ_E_ARG;
   if (dtype != KVQ_F16 && dtype != KVQ_F32) return KVQ_E_ARG;
-  if (n_q_heads < 1 || n_q_heads % v->kv_heads || n_splits < 0) return KVQ_E_ARG;
+  if (n_q_heads < 1 || n_q_heads % v->kv_heads || n_splits < 0 || n_splits > 16384)
+    return KVQ_E_ARG;
   if (flags != KVQ_DECODE_AUTO && flags != KVQ_DECODE_GENERIC) return KVQ_E_ARG;
   if (!aligned(q, dtype == KVQ_F32 ? 4 : 2) || !aligned(out, 4) || !aligned(workspace, 4))
     return KVQ_E_ARG;

@@ -168,26 +168,62 @@ decode_generic_kernel(kvq_kv_view v, const QT* __restrict__ q, int Hq,
   }
 }
 
-// out[b][h][:] = sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) l_p.
-__global__ void merge_kernel(const float* __restrict__ partials, int D,
-                             int n_parts, float* __restrict__ out) {
+// out[b][h][:] = sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) l_p, one
+// workgroup per (batch, query head): the partial weights are reduced in LDS,
+// then two thread halves sum the weighted o vectors over alternate partials.
+constexpr int kMergeThreads = 256;
+__global__ void __launch_bounds__(kMergeThreads)
+merge_kernel(const float* __restrict__ partials, int D, int n_parts,
+             float* __restrict__ out) {
+  __shared__ float red[kMergeThreads];
+  __shared__ float acc2[kMergeThreads];
+  extern __shared__ float wts[];  // [n_parts]
+  const int tid = threadIdx.x;
   const int64_t bh = blockIdx.x;
   const float* p = partials + bh * n_parts * (int64_t)(D + 2);
   float M = -INFINITY;
-  for (int i = 0; i < n_parts; ++i)
-    if (p[i * (D + 2) + 1] > 0.0f) M = fmaxf(M, p[i * (D + 2)]);
-  float L = 0.0f;
-  for (int i = 0; i < n_parts; ++i) {
-    const float l = p[i * (D + 2) + 1];
-    if (l > 0.0f) L += l * exp2f(p[i * (D + 2)] - M);
+  for (int i = tid; i < n_parts; i += kMergeThreads)
+    if (p[(int64_t)i * (D + 2) + 1] > 0.0f) M = fmaxf(M, p[(int64_t)i * (D + 2)]);
+  red[tid] = M;
+  __syncthreads();
+  for (int st = kMergeThreads / 2; st > 0; st >>= 1) {
+    if (tid < st) red[tid] = fmaxf(red[tid], red[tid + st]);
+    __syncthreads();
   }
-  for (int d = threadIdx.x; d < D; d += blockDim.x) {
+  M = red[0];
+  __syncthreads();
+  float L = 0.0f;
+  for (int i = tid; i < n_parts; i += kMergeThreads) {
+    const float l = p[(int64_t)i * (D + 2) + 1];
+    const float w = l > 0.0f ? exp2f(p[(int64_t)i * (D + 2)] - M) : 0.0f;
+    wts[i] = w;
+    L += l * w;
+  }
+  red[tid] = L;
+  __syncthreads();
+  for (int st = kMergeThreads / 2; st > 0; st >>= 1) {
+    if (tid < st) red[tid] += red[tid + st];
+    __syncthreads();
+  }
+  L = red[0];
+  const int half = tid / 128, d = tid % 128;
+  for (int d0 = 0; d0 < D; d0 += 128) {
     float acc = 0.0f;
-    for (int i = 0; i < n_parts; ++i) {
-      const float l = p[i * (D + 2) + 1];
-      if (l > 0.0f) acc += p[i * (D + 2) + 2 + d] * exp2f(p[i * (D + 2)] - M);
+    if (d0 + d < D) {
+      int i = half;
+      for (; i + 6 < n_parts; i += 8) {
+        const float a0 = p[(int64_t)i * (D + 2) + 2 + d0 + d];
+        const float a1 = p[(int64_t)(i + 2) * (D + 2) + 2 + d0 + d];
+        const float a2 = p[(int64_t)(i + 4) * (D + 2) + 2 + d0 + d];
+        const float a3 = p[(int64_t)(i + 6) * (D + 2) + 2 + d0 + d];
+        acc += a0 * wts[i] + a1 * wts[i + 2] + a2 * wts[i + 4] + a3 * wts[i + 6];
+      }
+      for (; i < n_parts; i += 2) acc += p[(int64_t)i * (D + 2) + 2 + d0 + d] * wts[i];
     }
-    out[bh * D + d] = acc / L;
+    acc2[tid] = acc;
+    __syncthreads();
+    if (half == 0 && d0 + d < D) out[bh * D + d0 + d] = (acc2[tid] + acc2[tid + 128]) / L;
+    __syncthreads();
   }
 }
 
@@ -230,7 +266,13 @@ hipError_t launch_decode_generic(const kvq_kv_view& v, const void* q, int f16,
 
 hipError_t launch_merge(const float* partials, int B, int Hq, int D,
                         int n_parts, float* out, hipStream_t s) {
-  merge_kernel<<<dim3((unsigned)(B * Hq)), 128, 0, s>>>(partials, D, n_parts, out);
+  const size_t lds = sizeof(float) * (size_t)n_parts;
+  if (lds + 2 * 1024 > 64 * 1024) {
+    hipError_t e = hipFuncSetAttribute((const void*)merge_kernel,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  merge_kernel<<<dim3((unsigned)(B * Hq)), kMergeThreads, lds, s>>>(partials, D, n_parts, out);
   return hipGetLastError();
 }
 

@@ -19,9 +19,11 @@
 // per key group by a power of two chosen from the group's largest |K| so it
 // stays inside the fp16 range.
 //
-// One workgroup = 4 wavefronts = one (batch, KV head, split).  Each wave
-// walks 32-token tiles i = wave, wave+4, ... of the split with its own
-// online-softmax state; the four states are merged in LDS at the end.  Lane
+// One workgroup = 4 wavefronts = one (batch, KV head, split).  A split is
+// cut into units of up to four 32-token tiles inside one key group; wave w
+// takes units w, w+4, ... with its own online-softmax state (Q' is rebuilt
+// only when the key group changes), and the four states are merged in LDS
+// at the end.  The output is rescaled only when a running max grows.  Lane
 // l = 16*q + n works on query head n (the B operand column) and on the
 // MFMA k-slots 8q..8q+7.  fp16 sink and tail rows go through the general
 // kernel as extra partials.
@@ -44,16 +46,25 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 __device__ inline float h2f(uint16_t u) { return (float)__builtin_bit_cast(_Float16, u); }
 
+// v_and_or_b32: (a & mask) | magic in one instruction (the mask travels in
+// an SGPR, the magic in a VGPR: gfx9 VOP3 takes no literal and at most one
+// scalar operand).
+__device__ inline uint32_t and_or(uint32_t a, uint32_t mask, uint32_t magic) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "s"(mask), "v"(magic));
+  return r;
+}
+
 // Four fp16 pairs (one MFMA operand) from one 32-bit word of int4 codes:
 // pair i holds nibbles (i, 4 + i) of the word times f_i = (1, 16, 1, 16),
 // minus the offset 8: the exact values f_i * code.
-__device__ inline half8 int4_operand(uint32_t w) {
+__device__ inline half8 int4_operand(uint32_t w, uint32_t magic) {
   const uint32_t w8 = w >> 8;
   u32x4 r;
-  r[0] = (w & 0x000F000Fu) | 0x64006400u;
-  r[1] = (w & 0x00F000F0u) | 0x64006400u;
-  r[2] = (w8 & 0x000F000Fu) | 0x64006400u;
-  r[3] = (w8 & 0x00F000F0u) | 0x64006400u;
+  r[0] = and_or(w, 0x000F000Fu, magic);
+  r[1] = and_or(w, 0x00F000F0u, magic);
+  r[2] = and_or(w8, 0x000F000Fu, magic);
+  r[3] = and_or(w8, 0x00F000F0u, magic);
   half8 h = __builtin_bit_cast(half8, r);
   const half8 off = {(_Float16)1032.0f, (_Float16)1032.0f, (_Float16)1152.0f,
                      (_Float16)1152.0f, (_Float16)1032.0f, (_Float16)1032.0f,
@@ -64,12 +75,12 @@ __device__ inline half8 int4_operand(uint32_t w) {
 // Four fp16 pairs from 16 bits of int2 codes (the low or high byte pair of
 // a word, selected by shifting by 8 first): pair i holds fields (i, 8 + i)
 // times 4^i, minus the offset 2.
-__device__ inline half8 int2_operand(uint32_t ws) {
+__device__ inline half8 int2_operand(uint32_t ws, uint32_t magic) {
   u32x4 r;
-  r[0] = (ws & 0x00030003u) | 0x64006400u;
-  r[1] = (ws & 0x000C000Cu) | 0x64006400u;
-  r[2] = (ws & 0x00300030u) | 0x64006400u;
-  r[3] = (ws & 0x00C000C0u) | 0x64006400u;
+  r[0] = and_or(ws, 0x00030003u, magic);
+  r[1] = and_or(ws, 0x000C000Cu, magic);
+  r[2] = and_or(ws, 0x00300030u, magic);
+  r[3] = and_or(ws, 0x00C000C0u, magic);
   half8 h = __builtin_bit_cast(half8, r);
   const half8 off = {(_Float16)1026.0f, (_Float16)1026.0f, (_Float16)1032.0f,
                      (_Float16)1032.0f, (_Float16)1056.0f, (_Float16)1056.0f,
@@ -78,16 +89,16 @@ __device__ inline half8 int2_operand(uint32_t ws) {
 }
 
 // Local channel (0..31 within the lane group's 32 channels) of k-slot
-// pair i, element e, of key MFMA kb, and the factor that slot carries.
+// pair i, element e, of key MFMA kb.
 template <int KB>
 __device__ inline int k_slot_channel(int kb, int i, int e) {
   if (KB == 4) return 8 * kb + i + 4 * e;
   return 16 * (kb >> 1) + 4 * (kb & 1) + i + 8 * e;
 }
+// log2 of the factor carried by slot pair i of an operand of BITS-bit codes.
 template <int BITS>
-__device__ inline float slot_factor_inv(int i) {
-  if (BITS == 4) return (i & 1) ? 0.0625f : 1.0f;
-  return i == 0 ? 1.0f : (i == 1 ? 0.25f : (i == 2 ? 0.0625f : 0.015625f));
+__host__ __device__ constexpr int slot_log2f(int i) {
+  return BITS == 4 ? ((i & 1) ? 4 : 0) : 2 * i;
 }
 
 struct MfmaArgs {
@@ -101,192 +112,407 @@ struct MfmaArgs {
   int n_splits;
 };
 
-template <int KB, int VB, int NC>
-__global__ void __launch_bounds__(kThreads)
+// A work unit of one wave: up to 4 tiles (128 tokens) of one key group.
+constexpr int kUnitTiles = 4;
+constexpr int kRowsPerChunk = 64;  // fp16 sink/tail rows per extra workgroup
+
+// LDS of the matrix-core path and of the fp16-rows path (one buffer).
+template <int NC>
+struct MainLds {
+  float vs[kWaves][kUnitTiles * 32 * NC];
+  float4v qf[8][64];   // lane l's 32 query values, 4 per entry
+  float m[kWaves][16];
+  float l[kWaves][16];
+  float o[kWaves][16][kD + 1];
+  float red[kThreads];
+};
+struct RowsLds {
+  float k[kRowsPerChunk][kD + 1];
+  uint16_t v[kRowsPerChunk][kD];
+  float q[16][kD];
+  float p[16][kRowsPerChunk];
+};
+template <int NC>
+constexpr size_t lds_bytes() {
+  return sizeof(MainLds<NC>) > sizeof(RowsLds) ? sizeof(MainLds<NC>) : sizeof(RowsLds);
+}
+
+// fp16 rows (sink rows, then tail rows in token order) chunk `chunk` of one
+// (batch, KV head): plain fp32 dot products from LDS; writes one partial.
+__device__ void fp16_rows_partial(const MfmaArgs& a, int chunk, int part, int kvh, int b,
+                                  RowsLds& L) {
+  const kvq_kv_view& v = a.v;
+  const int tid = threadIdx.x;
+  const int g = a.Hq / v.kv_heads;
+  const int64_t s = (int64_t)b * v.kv_heads + kvh;
+  const int64_t nr = v.n_sink + v.n_tail;
+  const int r0 = chunk * kRowsPerChunk;
+  const int n = (int)min((int64_t)kRowsPerChunk, nr - r0);
+  for (int i = tid; i < n * kD; i += kThreads) {
+    const int r = i / kD, d = i % kD;
+    const int64_t j = r0 + r;
+    int64_t off;
+    const uint16_t *kp, *vp;
+    if (j < v.n_sink) {
+      off = s * v.sink_stride + j * kD + d;
+      kp = v.sink_k; vp = v.sink_v;
+    } else {
+      off = s * v.tail_stride + ((v.n_quant + j - v.n_sink) % v.residual) * kD + d;
+      kp = v.tail_k; vp = v.tail_v;
+    }
+    L.k[r][d] = h2f(kp[off]);
+    L.v[r][d] = vp[off];
+  }
+  for (int i = tid; i < g * kD; i += kThreads) {
+    const int h = i / kD, d = i % kD;
+    const int64_t qi = ((int64_t)b * a.Hq + kvh * g + h) * kD + d;
+    L.q[h][d] = (a.q_f16 ? h2f(((const uint16_t*)a.q)[qi]) : ((const float*)a.q)[qi]) * a.qscale;
+  }
+  __syncthreads();
+  for (int i = tid; i < g * n; i += kThreads) {
+    const int h = i / n, r = i % n;
+    float acc = 0.0f;
+#pragma unroll 8
+    for (int d = 0; d < kD; ++d) acc += L.q[h][d] * L.k[r][d];
+    L.p[h][r] = acc;
+  }
+  __syncthreads();
+  float* out = a.partials + (((int64_t)b * a.Hq + kvh * g) * a.n_parts + part) * (kD + 2);
+  const int64_t hstride = (int64_t)a.n_parts * (kD + 2);
+  if (tid < g) {
+    float m = -INFINITY;
+    for (int r = 0; r < n; ++r) m = fmaxf(m, L.p[tid][r]);
+    float l = 0.0f;
+    for (int r = 0; r < n; ++r) {
+      const float e = exp2f(L.p[tid][r] - m);
+      L.p[tid][r] = e;
+      l += e;
+    }
+    out[tid * hstride] = m;
+    out[tid * hstride + 1] = l;
+  }
+  __syncthreads();
+  for (int i = tid; i < g * kD; i += kThreads) {
+    const int h = i / kD, d = i % kD;
+    float acc = 0.0f;
+    for (int r = 0; r < n; ++r) acc += L.p[h][r] * h2f(L.v[r][d]);
+    out[h * hstride + 2 + d] = acc;
+  }
+}
+
+// Value of the next lane of the 16-lane row (DPP row_shl:1); lane 15 gets 0.
+__device__ inline float from_next_lane(float x) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x101, 0xF, 0xF, false));
+}
+
+// PACKED (2 * g * NC <= 16): MFMA column n = 2 * (h * NC + c) + part.  On the
+// key side column n carries the high (part 0) or low (part 1) fp16 limb of
+// Q'_h, so one MFMA gives both limbs and a row shift adds them; on the value
+// side the even columns carry P'_h for value-channel group c.  Otherwise
+// column n is query head n, with separate high/low MFMAs and every value
+// group's P' built in every lane.
+template <int KB, int VB, int NC, bool PACKED>
+__global__ void __launch_bounds__(kThreads, 2)
 decode_mfma_kernel(MfmaArgs a) {
-  __shared__ float sm_m[kWaves][16];
-  __shared__ float sm_l[kWaves][16];
-  __shared__ float sm_o[kWaves][16][kD + 1];
+  __shared__ __align__(16) unsigned char lds_raw[lds_bytes<NC>()];
+  const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  if (split >= a.n_splits) {
+    fp16_rows_partial(a, split - a.n_splits, split, kvh, b, *(RowsLds*)lds_raw);
+    return;
+  }
+  MainLds<NC>& S = *(MainLds<NC>*)lds_raw;
+  auto& sm_vs = S.vs;
+  auto& sm_qf = S.qf;
+  auto& sm_m = S.m;
+  auto& sm_l = S.l;
+  auto& sm_o = S.o;
 
   const kvq_kv_view& v = a.v;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int lq = lane >> 4, ln = lane & 15;
-  const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int g = a.Hq / v.kv_heads;
   const int64_t s = (int64_t)b * v.kv_heads + kvh;
-  const bool head_ok = ln < g;
-  const int G = v.group_tok;
-  const int qmax_k = (1 << (KB - 1)) - 1;
+  // this lane's column: query head hh, value group cc, limb part
+  const int hh = PACKED ? (ln >> 1) / NC : ln;
+  const int cc = PACKED ? (ln >> 1) % NC : 0;
+  const int part = PACKED ? (ln & 1) : 0;
+  const bool head_ok = hh < g;
+  const bool col_valid = head_ok && part == 0;  // value-side column in use
+  uint32_t magic = 0x64006400u;
+  asm volatile("" : "+v"(magic));  // keep the fp16 magic in a VGPR
 
-  // this lane's 32 query channels 32*lq .. 32*lq + 31 of head ln
-  float qv[32];
-  float qabs = 0.0f;
+  const int tpg = v.group_tok / 32;                 // tiles per key group
+  const int ut = tpg < kUnitTiles ? tpg : kUnitTiles;  // tiles per unit
+  const int upg = tpg / ut;                         // units per group
+  const int n_units = (int)(v.n_quant / (32 * ut));
+  const int per = (n_units + a.n_splits - 1) / a.n_splits;
+  const int u_lo = min(n_units, split * per);
+  const int u_hi = min(n_units, u_lo + per);
+  const float* kg = v.k_gmax + s * v.k_gmax_stride;
+  // largest key scale over the split's key groups
   {
-    const int64_t base = ((int64_t)b * a.Hq + kvh * g + (head_ok ? ln : 0)) * kD + 32 * lq;
+    float gm = 0.0f;
+    const int g_lo = u_lo / upg, g_hi = (u_hi + upg - 1) / upg;
+    for (int gi = g_lo + threadIdx.x; gi < g_hi; gi += kThreads) gm = fmaxf(gm, kg[gi]);
+    S.red[threadIdx.x] = gm;
+  }
+  __syncthreads();
+  for (int st = kThreads / 2; st > 0; st >>= 1) {
+    if (threadIdx.x < st) S.red[threadIdx.x] = fmaxf(S.red[threadIdx.x], S.red[threadIdx.x + st]);
+    __syncthreads();
+  }
+  const float gmax = S.red[0];
+
+  // This lane's query values on its key MFMA k-slots, times the inverse of
+  // each slot's factor, sm_scale * log2(e) and the split's power-of-two
+  // prescale sigma: qf[kb][2i + e], kept in LDS (every wave uses the same
+  // values; wave 0 writes them).
+  float qabs = 0.0f;
+  float inv_sigma;
+  {
+    float qf[4][8];
+    const int64_t base = ((int64_t)b * a.Hq + kvh * g + (head_ok ? hh : 0)) * kD + 32 * lq;
 #pragma unroll
-    for (int c = 0; c < 32; ++c) {
-      float x = 0.0f;
-      if (head_ok)
-        x = a.q_f16 ? h2f(((const uint16_t*)a.q)[base + c]) : ((const float*)a.q)[base + c];
-      qv[c] = x * a.qscale;
-      qabs = fmaxf(qabs, fabsf(qv[c]));
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+          const int c = k_slot_channel<KB>(kb, i, e);
+          float x = 0.0f;
+          if (head_ok)
+            x = a.q_f16 ? h2f(((const uint16_t*)a.q)[base + c]) : ((const float*)a.q)[base + c];
+          x *= a.qscale;
+          qabs = fmaxf(qabs, fabsf(x));
+          qf[kb][2 * i + e] = x * (1.0f / (float)(1 << slot_log2f<KB>(i)));
+        }
+    qabs = fmaxf(qabs, __shfl_xor(qabs, 16));
+    qabs = fmaxf(qabs, __shfl_xor(qabs, 32));
+    // power-of-two prescale keeping |Q'| = |q k_scale| below 2^14 (gmax is
+    // the largest key scale of the split)
+    const float bound = qabs * gmax;
+    int ex = (int)((__builtin_bit_cast(uint32_t, bound) >> 23) & 0xFF) - 127;
+    ex = ex < -100 ? -100 : (ex > 100 ? 100 : ex);
+    const float sigma = __builtin_bit_cast(float, (uint32_t)(127 + 13 - ex) << 23);
+    inv_sigma = __builtin_bit_cast(float, (uint32_t)(127 - 13 + ex) << 23);
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) qf[kb][j] *= sigma;
+    if (wave == 0) {
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        sm_qf[2 * kb][lane] = (float4v){qf[kb][0], qf[kb][1], qf[kb][2], qf[kb][3]};
+        sm_qf[2 * kb + 1][lane] = (float4v){qf[kb][4], qf[kb][5], qf[kb][6], qf[kb][7]};
+      }
     }
   }
-  qabs = fmaxf(qabs, __shfl_xor(qabs, 16));
-  qabs = fmaxf(qabs, __shfl_xor(qabs, 32));
-
-  const int64_t n_tiles = v.n_quant / 32;
-  const int64_t per = (n_tiles + a.n_splits - 1) / a.n_splits;
-  const int64_t t_lo = min(n_tiles, (int64_t)split * per);
-  const int64_t t_hi = min(n_tiles, t_lo + per);
+  __syncthreads();
 
   const uint32_t* kc = v.k_codes + s * v.k_codes_stride;
   const float* ks = v.k_scales + s * v.k_scales_stride;
-  const float* kg = v.k_gmax + s * v.k_gmax_stride;
   const uint32_t* vc = v.v_codes + s * v.v_codes_stride;
   const float* vs = v.v_scales + s * v.v_scales_stride;
+  float* my_vs = sm_vs[wave];
 
-  half8 qhi[4], qlo[4];
-  float inv_sigma = 1.0f;
-  int64_t cur_group = -1;
+  half8 qhi[4], qlo[PACKED ? 1 : 4];
+  int cur_group = -1;
 
   float m_run = -INFINITY, l_run = 0.0f;
   float4v o[8];
 #pragma unroll
   for (int jb = 0; jb < 8; ++jb) o[jb] = (float4v){0.0f, 0.0f, 0.0f, 0.0f};
 
-  for (int64_t tile = t_lo + wave; tile < t_hi; tile += kWaves) {
-    const int64_t tok0 = tile * 32;
-    const int64_t grp = tok0 / G;
+  for (int u = u_lo + wave; u < u_hi; u += kWaves) {
+    const int tile0 = u * ut;
+    const int grp = u / upg;
+    // ---- issue the unit's loads
+    u32x4 kw[kUnitTiles][2];
+    u32x4 vw[kUnitTiles][VB == 4 ? 2 : 1];
+#pragma unroll
+    for (int i = 0; i < kUnitTiles; ++i) {
+      if (i < ut) {
+        const int64_t t32 = (int64_t)(tile0 + i) * 32;
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int64_t tok = t32 + 16 * h + ln;
+          if (KB == 4) {
+            kw[i][h] = *(const u32x4*)(kc + tok * 16 + 4 * lq);
+          } else {
+            const u32x2 w2 = *(const u32x2*)(kc + tok * 8 + 2 * lq);
+            kw[i][h] = (u32x4){w2[0], w2[1], 0u, 0u};
+          }
+        }
+        const int64_t tw = (int64_t)(tile0 + i) * (32 * VB * kD / 32);
+        vw[i][0] = *(const u32x4*)(vc + tw + lane * 4);
+        if (VB == 4) vw[i][VB == 4 ? 1 : 0] = *(const u32x4*)(vc + tw + 256 + lane * 4);
+      }
+    }
+    {
+      // value scales of the unit's tokens -> this wave's LDS slice
+      const int n4 = ut * 32 * NC / 4;
+      const float4v* src = (const float4v*)(vs + (int64_t)tile0 * 32 * NC);
+      for (int j = lane; j < n4; j += 64) ((float4v*)my_vs)[j] = src[j];
+    }
     if (grp != cur_group) {
       cur_group = grp;
-      // power-of-two prescale keeping |Q'| below 2^14
-      const float bound = qabs * kg[grp] / (float)qmax_k;
-      int ex = (int)((__builtin_bit_cast(uint32_t, bound) >> 23) & 0xFF) - 127;
-      ex = ex < -100 ? -100 : (ex > 100 ? 100 : ex);
-      const float sigma = __builtin_bit_cast(float, (uint32_t)(127 + 13 - ex) << 23);
-      inv_sigma = __builtin_bit_cast(float, (uint32_t)(127 - 13 + ex) << 23);
-      const float* kss = ks + grp * kD + 32 * lq;
+      const float* kss = ks + (int64_t)grp * kD + 32 * lq;
       float ksv[32];
 #pragma unroll
       for (int c = 0; c < 32; c += 4) {
-        float4v t4 = *(const float4v*)(kss + c);
+        const float4v t4 = *(const float4v*)(kss + c);
         ksv[c] = t4[0]; ksv[c + 1] = t4[1]; ksv[c + 2] = t4[2]; ksv[c + 3] = t4[3];
       }
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
+        const float4v q0 = sm_qf[2 * kb][lane], q1 = sm_qf[2 * kb + 1][lane];
+        const float qk[8] = {q0[0], q0[1], q0[2], q0[3], q1[0], q1[1], q1[2], q1[3]};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
           for (int e = 0; e < 2; ++e) {
-            const int c = k_slot_channel<KB>(kb, i, e);
-            const float x = qv[c] * ksv[c] * sigma * slot_factor_inv<KB>(i);
+            const float x = qk[2 * i + e] * ksv[k_slot_channel<KB>(kb, i, e)];
             const _Float16 hi = (_Float16)x;
-            qhi[kb][2 * i + e] = hi;
-            qlo[kb][2 * i + e] = (_Float16)(x - (float)hi);
+            const _Float16 lo = (_Float16)(x - (float)hi);
+            if (PACKED) {
+              qhi[kb][2 * i + e] = part ? lo : hi;
+            } else {
+              qhi[kb][2 * i + e] = hi;
+              qlo[PACKED ? 0 : kb][2 * i + e] = lo;
+            }
           }
-        }
       }
     }
+    __builtin_amdgcn_wave_barrier();
 
-    // ---- scores for the 32 tokens: two 16-token halves
-    float sc[8];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int64_t tok = tok0 + 16 * h + ln;
-      float4v acc = {0.0f, 0.0f, 0.0f, 0.0f};
-      if (KB == 4) {
-        const u32x4 w = *(const u32x4*)(kc + tok * 16 + 4 * lq);
+    for (int i = 0; i < kUnitTiles; ++i) {
+      if (i >= ut) break;
+      // ---- scores of the tile's 32 tokens (two 16-token halves)
+      float4v acc[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        float4v acc_lo = (float4v){0.0f, 0.0f, 0.0f, 0.0f};
+        acc[h] = (float4v){0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
-          const half8 A = int4_operand(w[kb]);
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, qhi[kb], acc, 0, 0, 0);
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, qlo[kb], acc, 0, 0, 0);
+          half8 A;
+          if (KB == 4) {
+            A = int4_operand(kw[i][h][kb], magic);
+          } else {
+            const uint32_t word = kw[i][h][kb >> 1];
+            A = int2_operand((kb & 1) ? (word >> 8) : word, magic);
+          }
+          acc[h] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, qhi[kb], acc[h], 0, 0, 0);
+          if (!PACKED)
+            acc_lo = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, qlo[PACKED ? 0 : kb], acc_lo, 0, 0, 0);
+        }
+        if (PACKED) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) acc[h][j] += from_next_lane(acc[h][j]);
+        } else {
+          acc[h] += acc_lo;
+        }
+      }
+      // ---- online softmax; slot sl = 4h + j of this lane is token
+      //      j + 4*lq + 16*h of the tile, query head hh
+      float amax = fmaxf(fmaxf(fmaxf(acc[0][0], acc[0][1]), fmaxf(acc[0][2], acc[0][3])),
+                         fmaxf(fmaxf(acc[1][0], acc[1][1]), fmaxf(acc[1][2], acc[1][3])));
+      float tmax = amax * inv_sigma;
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
+      if (__any(tmax > m_run)) {
+        const float m_new = fmaxf(m_run, tmax);
+        const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
+        m_run = m_new;
+        l_run *= alpha;
+#pragma unroll
+        for (int jb = 0; jb < 8; ++jb) o[jb] *= alpha;
+      }
+      // p / f(slot pair) for the value operand (0 in unused columns); psum of
+      // the unscaled p
+      const float neg_m = (PACKED && !col_valid) ? -INFINITY : -m_run;
+      float p[8];
+      float psum = 0.0f;
+#pragma unroll
+      for (int sl = 0; sl < 8; ++sl) {
+        const int lf = slot_log2f<VB>(sl >> 1);
+        p[sl] = __builtin_amdgcn_exp2f(
+            __builtin_fmaf(acc[sl >> 2][sl & 3], inv_sigma, neg_m - (float)lf));
+        psum = __builtin_fmaf(p[sl], (float)(1 << lf), psum);
+      }
+      l_run += psum;
+      // ---- P' operands and the value MFMAs
+      if (PACKED) {
+        half8 pb;
+#pragma unroll
+        for (int sl = 0; sl < 8; ++sl) {
+          const int tau = (sl & 3) + 4 * lq + 16 * (sl >> 2);
+          pb[sl] = (_Float16)(p[sl] * my_vs[(i * 32 + tau) * NC + cc]);
+        }
+#pragma unroll
+        for (int jb = 0; jb < 8; ++jb) {
+          half8 A;
+          if (VB == 2) {
+            const uint32_t word = vw[i][0][jb >> 1];
+            A = int2_operand((jb & 1) ? (word >> 8) : word, magic);
+          } else {
+            A = int4_operand(vw[i][jb >> 2][jb & 3], magic);
+          }
+          o[jb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, pb, o[jb], 0, 0, 0);
         }
       } else {
-        const u32x2 w = *(const u32x2*)(kc + tok * 8 + 2 * lq);
+        half8 pb[NC];
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-          const uint32_t word = w[kb >> 1];
-          const half8 A = int2_operand((kb & 1) ? (word >> 8) : word);
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, qhi[kb], acc, 0, 0, 0);
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, qlo[kb], acc, 0, 0, 0);
+        for (int sl = 0; sl < 8; ++sl) {
+          const int tau = (sl & 3) + 4 * lq + 16 * (sl >> 2);
+          const float* row = my_vs + (i * 32 + tau) * NC;
+#pragma unroll
+          for (int c = 0; c < NC; ++c) pb[c][sl] = (_Float16)(p[sl] * row[c]);
+        }
+#pragma unroll
+        for (int jb = 0; jb < 8; ++jb) {
+          half8 A;
+          if (VB == 2) {
+            const uint32_t word = vw[i][0][jb >> 1];
+            A = int2_operand((jb & 1) ? (word >> 8) : word, magic);
+          } else {
+            A = int4_operand(vw[i][jb >> 2][jb & 3], magic);
+          }
+          o[jb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, pb[(jb * 16 * NC) / kD], o[jb], 0,
+                                                         0, 0);
         }
       }
-#pragma unroll
-      for (int j = 0; j < 4; ++j) sc[4 * h + j] = acc[j] * inv_sigma;
     }
-
-    // ---- online softmax; slot sigma of this lane is token
-    //      (sigma % 4) + 4*lq + 16*(sigma / 4) of the tile, head ln
-    float tmax = sc[0];
-#pragma unroll
-    for (int i = 1; i < 8; ++i) tmax = fmaxf(tmax, sc[i]);
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-    const float m_new = fmaxf(m_run, tmax);
-    const float alpha = exp2f(m_run - m_new);
-    m_run = m_new;
-    float p[8];
-    float psum = 0.0f;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      p[i] = exp2f(sc[i] - m_new);
-      psum += p[i];
-    }
-    l_run = l_run * alpha + psum;
-#pragma unroll
-    for (int jb = 0; jb < 8; ++jb) o[jb] *= alpha;
-
-    // ---- values
-    float vsc[8][NC];
-#pragma unroll
-    for (int r = 0; r < 2; ++r) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const float* row = vs + (tok0 + 16 * r + 4 * lq + j) * NC;
-#pragma unroll
-        for (int c = 0; c < NC; ++c) vsc[4 * r + j][c] = row[c];
-      }
-    }
-    half8 pb[NC];
-#pragma unroll
-    for (int c = 0; c < NC; ++c) {
-#pragma unroll
-      for (int sl = 0; sl < 8; ++sl)
-        pb[c][sl] = (_Float16)(p[sl] * vsc[sl][c] * slot_factor_inv<VB>(sl >> 1));
-    }
-    if (VB == 2) {
-      const u32x4 w = *(const u32x4*)(vc + tile * 256 + lane * 4);
-#pragma unroll
-      for (int jb = 0; jb < 8; ++jb) {
-        const uint32_t word = w[jb >> 1];
-        const half8 A = int2_operand((jb & 1) ? (word >> 8) : word);
-        o[jb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, pb[(jb * 16 * NC) / kD], o[jb], 0, 0, 0);
-      }
-    } else {
-      const u32x4 w0 = *(const u32x4*)(vc + tile * 512 + lane * 4);
-      const u32x4 w1 = *(const u32x4*)(vc + tile * 512 + 256 + lane * 4);
-#pragma unroll
-      for (int jb = 0; jb < 8; ++jb) {
-        const uint32_t word = jb < 4 ? w0[jb] : w1[jb - 4];
-        const half8 A = int4_operand(word);
-        o[jb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, pb[(jb * 16 * NC) / kD], o[jb], 0, 0, 0);
-      }
-    }
+    __builtin_amdgcn_wave_barrier();
   }
 
   // ---- per-wave state to LDS: m, l (summed over the 4 lane groups), O
   l_run += __shfl_xor(l_run, 16);
   l_run += __shfl_xor(l_run, 32);
-  if (lq == 0) {
-    sm_m[wave][ln] = m_run;
-    sm_l[wave][ln] = l_run;
+  if (PACKED) {
+    if (lq == 0 && col_valid && cc == 0) {
+      sm_m[wave][hh] = m_run;
+      sm_l[wave][hh] = l_run;
+    }
+    if (col_valid) {
+#pragma unroll
+      for (int jb = 0; jb < 8; ++jb)
+        if ((jb * 16 * NC) / kD == cc)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) sm_o[wave][hh][16 * jb + 4 * lq + j] = o[jb][j];
+    }
+  } else {
+    if (lq == 0) {
+      sm_m[wave][ln] = m_run;
+      sm_l[wave][ln] = l_run;
+    }
+#pragma unroll
+    for (int jb = 0; jb < 8; ++jb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) sm_o[wave][ln][16 * jb + 4 * lq + j] = o[jb][j];
   }
-#pragma unroll
-  for (int jb = 0; jb < 8; ++jb)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) sm_o[wave][ln][16 * jb + 4 * lq + j] = o[jb][j];
   __syncthreads();
 
   // ---- merge the four waves into this split's partial
@@ -313,10 +539,12 @@ decode_mfma_kernel(MfmaArgs a) {
 }
 
 int auto_splits(const kvq_kv_view& v) {
-  const int64_t n_tiles = v.n_quant / 32;
+  const int tpg = v.group_tok / 32;
+  const int ut = tpg < kUnitTiles ? tpg : kUnitTiles;
+  const int64_t n_units = v.n_quant / (32 * ut);
   const int64_t streams = (int64_t)v.batch * v.kv_heads;
   int64_t sp = (2048 + streams - 1) / streams;
-  int64_t by_len = n_tiles / 8;  // at least two tiles per wave
+  int64_t by_len = n_units / 8;  // at least two units per wave
   if (sp > by_len) sp = by_len;
   if (sp < 1) sp = 1;
   if (sp > 65535) sp = 65535;
@@ -324,13 +552,17 @@ int auto_splits(const kvq_kv_view& v) {
 }
 
 int fp16_parts(const kvq_kv_view& v) {
-  return (v.n_sink > 0 ? 1 : 0) + (int)((v.n_tail + 63) / 64);
+  return (int)((v.n_sink + v.n_tail + kRowsPerChunk - 1) / kRowsPerChunk);
 }
 
 template <int KB, int VB, int NC>
 hipError_t launch_t(const MfmaArgs& a, hipStream_t s) {
-  dim3 grid((unsigned)a.n_splits, (unsigned)a.v.kv_heads, (unsigned)a.v.batch);
-  decode_mfma_kernel<KB, VB, NC><<<grid, kThreads, 0, s>>>(a);
+  dim3 grid((unsigned)a.n_parts, (unsigned)a.v.kv_heads, (unsigned)a.v.batch);
+  const int g = a.Hq / a.v.kv_heads;
+  if (2 * g * NC <= 16)
+    decode_mfma_kernel<KB, VB, NC, true><<<grid, kThreads, 0, s>>>(a);
+  else
+    decode_mfma_kernel<KB, VB, NC, false><<<grid, kThreads, 0, s>>>(a);
   return hipGetLastError();
 }
 
@@ -352,7 +584,8 @@ bool mfma_decode_eligible(const kvq_kv_view& v, int Hq) {
   if (v.k_bits != 4 && v.k_bits != 2) return false;
   if (v.v_bits != 4 && v.v_bits != 2) return false;
   if (v.v_layout != KVQ_V_TILE32 || v.group_tok % 32 || v.n_quant % 32) return false;
-  if (v.n_quant < 32 || !v.k_gmax) return false;
+  if (v.group_tok > 32 * kUnitTiles && v.group_tok % (32 * kUnitTiles)) return false;
+  if (v.n_quant < 32 || !v.k_gmax || v.n_quant / 32 > 0x7FFFFFFF) return false;
   const int nc = kD / v.group_ch;
   if (nc != 1 && nc != 2 && nc != 4 && nc != 8) return false;
   const int g = Hq / v.kv_heads;
@@ -377,21 +610,6 @@ hipError_t launch_decode_mfma(const kvq_kv_view& v, const void* q, int f16, int 
   else if (v.k_bits == 4 && v.v_bits == 4) e = launch_nc<4, 4>(a, nc, s);
   else if (v.k_bits == 2 && v.v_bits == 2) e = launch_nc<2, 2>(a, nc, s);
   else e = launch_nc<2, 4>(a, nc, s);
-  if (e != hipSuccess) return e;
-  // fp16 rows: the sink as one partial, the tail in 64-token partials
-  int part = n_splits;
-  if (v.n_sink > 0) {
-    e = launch_decode_generic_range(v, q, f16, Hq, sm_scale, partials, 0, v.n_sink, 1, part,
-                                    n_parts, s);
-    if (e != hipSuccess) return e;
-    part += 1;
-  }
-  if (v.n_tail > 0) {
-    const int tp = (int)((v.n_tail + 63) / 64);
-    const int64_t lo = v.n_sink + v.n_quant;
-    e = launch_decode_generic_range(v, q, f16, Hq, sm_scale, partials, lo, lo + v.n_tail, tp,
-                                    part, n_parts, s);
-  }
   return e;
 }
 

@@ -327,9 +327,11 @@ flush_kernel(CacheDev c, FlushSrc f) {
       }
     }
   }
+  // bound on |k_hat| / code of the group: the largest channel scale (the
+  // absmax itself for bf16 channels)
   if (tid == 0) {
     float gm = 0.0f;
-    for (int e = 0; e < D; ++e) gm = fmaxf(gm, kmax[e]);
+    for (int e = 0; e < D; ++e) gm = fmaxf(gm, (c.mixed && kcls[e] == 0) ? kmax[e] : ksc[e]);
     c.k_gmax[st * c.s_k_gmax + grp] = gm;
   }
   __syncthreads();
