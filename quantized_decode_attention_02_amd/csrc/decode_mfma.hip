@@ -88,6 +88,41 @@ __device__ inline half8 int2_operand(uint32_t ws, uint32_t magic) {
   return h - off;
 }
 
+// Key operands as fp16 denormals: a field masked in place is the exact fp16
+// value f * u * 2^-24 (no implicit leading one, so nothing to subtract per
+// code); the code offset is removed once per key group through the MFMA
+// accumulator (see k_offset_operand).  The MFMA keeps fp16 denormal inputs
+// exact.
+__device__ inline half8 int4_key_operand(uint32_t w) {
+  const uint32_t w8 = w >> 8;
+  u32x4 r;
+  r[0] = w & 0x000F000Fu;
+  r[1] = w & 0x00F000F0u;
+  r[2] = w8 & 0x000F000Fu;
+  r[3] = w8 & 0x00F000F0u;
+  return __builtin_bit_cast(half8, r);
+}
+__device__ inline half8 int2_key_operand(uint32_t ws) {
+  u32x4 r;
+  r[0] = ws & 0x00030003u;
+  r[1] = ws & 0x000C000Cu;
+  r[2] = ws & 0x00300030u;
+  r[3] = ws & 0x00C000C0u;
+  return __builtin_bit_cast(half8, r);
+}
+// The denormal operand of the code offsets (8 for int4, 2 for int2) with
+// each slot pair's factor: sum_k off_k * B_k is the group's offset term.
+template <int KB>
+__device__ inline half8 k_offset_operand() {
+  u32x4 r;
+  if (KB == 4) {
+    r[0] = 0x00080008u; r[1] = 0x00800080u; r[2] = 0x00080008u; r[3] = 0x00800080u;
+  } else {
+    r[0] = 0x00020002u; r[1] = 0x00080008u; r[2] = 0x00200020u; r[3] = 0x00800080u;
+  }
+  return __builtin_bit_cast(half8, r);
+}
+
 // Local channel (0..31 within the lane group's 32 channels) of k-slot
 // pair i, element e, of key MFMA kb.
 template <int KB>
@@ -127,7 +162,7 @@ struct MainLds {
   float red[kThreads];
 };
 struct RowsLds {
-  float k[kRowsPerChunk][kD + 1];
+  uint16_t k[kRowsPerChunk][kD + 2];  // fp16 rows, padded against bank conflicts
   uint16_t v[kRowsPerChunk][kD];
   float q[16][kD];
   float p[16][kRowsPerChunk];
@@ -160,7 +195,7 @@ __device__ void fp16_rows_partial(const MfmaArgs& a, int chunk, int part, int kv
       off = s * v.tail_stride + ((v.n_quant + j - v.n_sink) % v.residual) * kD + d;
       kp = v.tail_k; vp = v.tail_v;
     }
-    L.k[r][d] = h2f(kp[off]);
+    L.k[r][d] = kp[off];
     L.v[r][d] = vp[off];
   }
   for (int i = tid; i < g * kD; i += kThreads) {
@@ -173,7 +208,7 @@ __device__ void fp16_rows_partial(const MfmaArgs& a, int chunk, int part, int kv
     const int h = i / n, r = i % n;
     float acc = 0.0f;
 #pragma unroll 8
-    for (int d = 0; d < kD; ++d) acc += L.q[h][d] * L.k[r][d];
+    for (int d = 0; d < kD; ++d) acc += L.q[h][d] * h2f(L.k[r][d]);
     L.p[h][r] = acc;
   }
   __syncthreads();
@@ -213,7 +248,7 @@ __device__ inline float from_next_lane(float x) {
 // column n is query head n, with separate high/low MFMAs and every value
 // group's P' built in every lane.
 template <int KB, int VB, int NC, bool PACKED>
-__global__ void __launch_bounds__(kThreads, 2)
+__global__ void __launch_bounds__(kThreads, (PACKED && NC <= 4) ? 3 : 2)
 decode_mfma_kernel(MfmaArgs a) {
   __shared__ __align__(16) unsigned char lds_raw[lds_bytes<NC>()];
   const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
@@ -317,7 +352,9 @@ decode_mfma_kernel(MfmaArgs a) {
   float* my_vs = sm_vs[wave];
 
   half8 qhi[4], qlo[PACKED ? 1 : 4];
+  float4v negcorr_hi, negcorr_lo;  // minus the group's offset terms
   int cur_group = -1;
+  const float inv_sigma_k = inv_sigma * 16777216.0f;  // undo sigma and 2^-24
 
   float m_run = -INFINITY, l_run = 0.0f;
   float4v o[8];
@@ -383,6 +420,16 @@ decode_mfma_kernel(MfmaArgs a) {
             }
           }
       }
+      const half8 aoff = k_offset_operand<KB>();
+      float4v c_hi = (float4v){0.0f, 0.0f, 0.0f, 0.0f}, c_lo = c_hi;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        c_hi = __builtin_amdgcn_mfma_f32_16x16x32_f16(aoff, qhi[kb], c_hi, 0, 0, 0);
+        if (!PACKED)
+          c_lo = __builtin_amdgcn_mfma_f32_16x16x32_f16(aoff, qlo[PACKED ? 0 : kb], c_lo, 0, 0, 0);
+      }
+      negcorr_hi = -c_hi;
+      negcorr_lo = -c_lo;
     }
     __builtin_amdgcn_wave_barrier();
 
@@ -393,16 +440,16 @@ decode_mfma_kernel(MfmaArgs a) {
       float4v acc[2];
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
-        float4v acc_lo = (float4v){0.0f, 0.0f, 0.0f, 0.0f};
-        acc[h] = (float4v){0.0f, 0.0f, 0.0f, 0.0f};
+        float4v acc_lo = negcorr_lo;
+        acc[h] = negcorr_hi;
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
           half8 A;
           if (KB == 4) {
-            A = int4_operand(kw[i][h][kb], magic);
+            A = int4_key_operand(kw[i][h][kb]);
           } else {
             const uint32_t word = kw[i][h][kb >> 1];
-            A = int2_operand((kb & 1) ? (word >> 8) : word, magic);
+            A = int2_key_operand((kb & 1) ? (word >> 8) : word);
           }
           acc[h] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, qhi[kb], acc[h], 0, 0, 0);
           if (!PACKED)
@@ -419,7 +466,7 @@ decode_mfma_kernel(MfmaArgs a) {
       //      j + 4*lq + 16*h of the tile, query head hh
       float amax = fmaxf(fmaxf(fmaxf(acc[0][0], acc[0][1]), fmaxf(acc[0][2], acc[0][3])),
                          fmaxf(fmaxf(acc[1][0], acc[1][1]), fmaxf(acc[1][2], acc[1][3])));
-      float tmax = amax * inv_sigma;
+      float tmax = amax * inv_sigma_k;
       tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
       tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
       if (__any(tmax > m_run)) {
@@ -439,7 +486,7 @@ decode_mfma_kernel(MfmaArgs a) {
       for (int sl = 0; sl < 8; ++sl) {
         const int lf = slot_log2f<VB>(sl >> 1);
         p[sl] = __builtin_amdgcn_exp2f(
-            __builtin_fmaf(acc[sl >> 2][sl & 3], inv_sigma, neg_m - (float)lf));
+            __builtin_fmaf(acc[sl >> 2][sl & 3], inv_sigma_k, neg_m - (float)lf));
         psum = __builtin_fmaf(p[sl], (float)(1 << lf), psum);
       }
       l_run += psum;
@@ -538,16 +585,19 @@ decode_mfma_kernel(MfmaArgs a) {
   }
 }
 
+// Splits per (batch, KV head): about four workgroups per compute unit
+// (two resident, two rounds -- measured faster than one round of two), and
+// at least eight units per wave.
 int auto_splits(const kvq_kv_view& v) {
   const int tpg = v.group_tok / 32;
   const int ut = tpg < kUnitTiles ? tpg : kUnitTiles;
   const int64_t n_units = v.n_quant / (32 * ut);
   const int64_t streams = (int64_t)v.batch * v.kv_heads;
-  int64_t sp = (2048 + streams - 1) / streams;
-  int64_t by_len = n_units / 8;  // at least two units per wave
+  int64_t sp = (1024 + streams - 1) / streams;
+  int64_t by_len = n_units / (8 * kWaves);
   if (sp > by_len) sp = by_len;
   if (sp < 1) sp = 1;
-  if (sp > 65535) sp = 65535;
+  if (sp > 16000) sp = 16000;
   return (int)sp;
 }
 
