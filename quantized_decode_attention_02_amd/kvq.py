@@ -361,3 +361,27 @@ def stateless_view(k_codes, k_scales, v_codes, v_scales, B, Hkv, D, k_bits,
     v.v_codes, v.v_codes_stride = v_codes.data_ptr(), v_codes[0].numel()
     v.v_scales, v.v_scales_stride = v_scales.data_ptr(), v_scales[0].numel()
     return v
+
+
+_STREAM_ARRAYS = [
+    ("sink_k", "sink_stride", 2), ("sink_v", "sink_stride", 2),
+    ("tail_k", "tail_stride", 2), ("tail_v", "tail_stride", 2),
+    ("k_codes", "k_codes_stride", 4), ("k_scales", "k_scales_stride", 4),
+    ("k_gmax", "k_gmax_stride", 4), ("k_pos", "k_pos_stride", 1),
+    ("k_bf16", "k_bf16_stride", 2), ("k_int4", "k_int4_stride", 4),
+    ("k_int2", "k_int2_stride", 4), ("v_codes", "v_codes_stride", 4),
+    ("v_scales", "v_scales_stride", 4),
+]
+
+
+def stream_view(view, b, kvh):
+    """A one-stream (batch 1, one KV head) view of stream (b, kvh)."""
+    v = KvView()
+    ctypes.memmove(ctypes.byref(v), ctypes.byref(view), ctypes.sizeof(KvView))
+    s = b * view.kv_heads + kvh
+    v.batch, v.kv_heads = 1, 1
+    for name, stride, size in _STREAM_ARRAYS:
+        p = getattr(view, name)
+        if p:
+            setattr(v, name, p + s * getattr(view, stride) * size)
+    return v
