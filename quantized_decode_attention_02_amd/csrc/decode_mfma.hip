@@ -155,6 +155,7 @@ constexpr int kRowsPerChunk = 64;  // fp16 sink/tail rows per extra workgroup
 template <int NC>
 struct MainLds {
   float vs[kWaves][kUnitTiles * 32 * NC];
+  float ks[kWaves][kD];
   float4v qf[8][64];   // lane l's 32 query values, 4 per entry
   float m[kWaves][16];
   float l[kWaves][16];
@@ -248,7 +249,7 @@ __device__ inline float from_next_lane(float x) {
 // column n is query head n, with separate high/low MFMAs and every value
 // group's P' built in every lane.
 template <int KB, int VB, int NC, bool PACKED>
-__global__ void __launch_bounds__(kThreads, (PACKED && NC <= 4) ? 3 : 2)
+__global__ void __launch_bounds__(kThreads, (PACKED && NC <= 4 && !(KB == 4 && VB == 4)) ? 3 : 2)
 decode_mfma_kernel(MfmaArgs a) {
   __shared__ __align__(16) unsigned char lds_raw[lds_bytes<NC>()];
   const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
@@ -361,40 +362,66 @@ decode_mfma_kernel(MfmaArgs a) {
 #pragma unroll
   for (int jb = 0; jb < 8; ++jb) o[jb] = (float4v){0.0f, 0.0f, 0.0f, 0.0f};
 
-  for (int u = u_lo + wave; u < u_hi; u += kWaves) {
-    const int tile0 = u * ut;
-    const int grp = u / upg;
-    // ---- issue the unit's loads
-    u32x4 kw[kUnitTiles][2];
-    u32x4 vw[kUnitTiles][VB == 4 ? 2 : 1];
+  // Rolling prefetch: the codes of tile i of the wave's next unit are loaded
+  // into tile i's registers as soon as tile i of the current unit is done;
+  // the next unit's value scales and key-scale row wait in registers and are
+  // committed to this wave's LDS slice at the unit boundary.
+  constexpr int kVs4 = (kUnitTiles * 32 * NC / 4 + 63) / 64;  // float4 per lane
+  const int n_vs4 = ut * 32 * NC / 4;
+  u32x4 kw[kUnitTiles][2];
+  u32x4 vw[kUnitTiles][VB == 4 ? 2 : 1];
+  float4v vsn[kVs4];
+  float4v ksn = (float4v){0.0f, 0.0f, 0.0f, 0.0f};
+  auto load_tile = [&](int unit, int i) {
+    const int64_t t32 = (int64_t)(unit * ut + i) * 32;
 #pragma unroll
-    for (int i = 0; i < kUnitTiles; ++i) {
-      if (i < ut) {
-        const int64_t t32 = (int64_t)(tile0 + i) * 32;
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          const int64_t tok = t32 + 16 * h + ln;
-          if (KB == 4) {
-            kw[i][h] = *(const u32x4*)(kc + tok * 16 + 4 * lq);
-          } else {
-            const u32x2 w2 = *(const u32x2*)(kc + tok * 8 + 2 * lq);
-            kw[i][h] = (u32x4){w2[0], w2[1], 0u, 0u};
-          }
-        }
-        const int64_t tw = (int64_t)(tile0 + i) * (32 * VB * kD / 32);
-        vw[i][0] = *(const u32x4*)(vc + tw + lane * 4);
-        if (VB == 4) vw[i][VB == 4 ? 1 : 0] = *(const u32x4*)(vc + tw + 256 + lane * 4);
+    for (int h = 0; h < 2; ++h) {
+      const int64_t tok = t32 + 16 * h + ln;
+      if (KB == 4) {
+        kw[i][h] = *(const u32x4*)(kc + tok * 16 + 4 * lq);
+      } else {
+        const u32x2 w2 = *(const u32x2*)(kc + tok * 8 + 2 * lq);
+        kw[i][h] = (u32x4){w2[0], w2[1], 0u, 0u};
       }
     }
-    {
-      // value scales of the unit's tokens -> this wave's LDS slice
-      const int n4 = ut * 32 * NC / 4;
-      const float4v* src = (const float4v*)(vs + (int64_t)tile0 * 32 * NC);
-      for (int j = lane; j < n4; j += 64) ((float4v*)my_vs)[j] = src[j];
+    const int64_t tw = (int64_t)(unit * ut + i) * (32 * VB * kD / 32);
+    vw[i][0] = *(const u32x4*)(vc + tw + lane * 4);
+    if (VB == 4) vw[i][VB == 4 ? 1 : 0] = *(const u32x4*)(vc + tw + 256 + lane * 4);
+  };
+  auto load_scales = [&](int unit) {
+    const float4v* src = (const float4v*)(vs + (int64_t)unit * ut * 32 * NC);
+#pragma unroll
+    for (int j = 0; j < kVs4; ++j) {
+      const int idx = lane + 64 * j;
+      if (idx < n_vs4) vsn[j] = src[idx];
     }
+    if (lane < kD / 4) ksn = ((const float4v*)(ks + (int64_t)(unit / upg) * kD))[lane];
+  };
+  float* my_ks = S.ks[wave];
+  const int u_first = u_lo + wave;
+  if (u_first < u_hi) {
+#pragma unroll
+    for (int i = 0; i < kUnitTiles; ++i)
+      if (i < ut) load_tile(u_first, i);
+    load_scales(u_first);
+  }
+
+  for (int u = u_first; u < u_hi; u += kWaves) {
+    const int grp = u / upg;
+    // ---- commit this unit's scales to LDS, then fetch the next unit's
+#pragma unroll
+    for (int j = 0; j < kVs4; ++j) {
+      const int idx = lane + 64 * j;
+      if (idx < n_vs4) ((float4v*)my_vs)[idx] = vsn[j];
+    }
+    if (lane < kD / 4) ((float4v*)my_ks)[lane] = ksn;
+    __builtin_amdgcn_wave_barrier();
+    const int un = u + kWaves;
+    const bool has_next = un < u_hi;
+    if (has_next) load_scales(un);
     if (grp != cur_group) {
       cur_group = grp;
-      const float* kss = ks + (int64_t)grp * kD + 32 * lq;
+      const float* kss = my_ks + 32 * lq;
       float ksv[32];
 #pragma unroll
       for (int c = 0; c < 32; c += 4) {
@@ -531,6 +558,7 @@ decode_mfma_kernel(MfmaArgs a) {
                                                          0, 0);
         }
       }
+      if (has_next) load_tile(un, i);
     }
     __builtin_amdgcn_wave_barrier();
   }
