@@ -265,6 +265,8 @@ size_t kvq_decode_workspace_bytes(const kvq_kv_view* v, int n_q_heads,
  * Query head h reads KV head h / (n_q_heads / Hkv).  The context is split
  * into n_splits ranges (0 = automatic) whose softmax partials are merged
  * with the log-sum-exp rule.  workspace >= kvq_decode_workspace_bytes.
+ * The matrix-core kernel also needs q 16-byte aligned; otherwise, and for
+ * views it does not cover, KVQ_DECODE_AUTO runs the general kernel.
  * An empty view (no tokens) is KVQ_E_ARG.                               */
 kvq_status kvq_decode_attention(const kvq_kv_view* v, const void* q,
                                 int dtype, int n_q_heads, float sm_scale,

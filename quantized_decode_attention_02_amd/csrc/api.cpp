@@ -370,7 +370,7 @@ kvq_status kvq_decode_attention(const kvq_kv_view* v, const void* q, int dtype,
   const int g = n_q_heads / v->kv_heads;
   hipError_t e;
   int parts;
-  if (flags == KVQ_DECODE_AUTO && mfma_decode_eligible(*v, n_q_heads)) {
+  if (flags == KVQ_DECODE_AUTO && aligned(q, 16) && mfma_decode_eligible(*v, n_q_heads)) {
     parts = mfma_decode_parts(*v, n_q_heads, n_splits);
     e = launch_decode_mfma(*v, q, dtype == KVQ_F16, n_q_heads, sm_scale, partials, parts, s);
   } else {

@@ -160,7 +160,6 @@ struct MainLds {
   float m[kWaves][16];
   float l[kWaves][16];
   float o[kWaves][16][kD + 1];
-  float red[kThreads];
 };
 struct RowsLds {
   uint16_t k[kRowsPerChunk][kD + 2];  // fp16 rows, padded against bank conflicts
@@ -286,61 +285,56 @@ decode_mfma_kernel(MfmaArgs a) {
   const int u_lo = min(n_units, split * per);
   const int u_hi = min(n_units, u_lo + per);
   const float* kg = v.k_gmax + s * v.k_gmax_stride;
-  // largest key scale over the split's key groups
-  {
-    float gm = 0.0f;
-    const int g_lo = u_lo / upg, g_hi = (u_hi + upg - 1) / upg;
-    for (int gi = g_lo + threadIdx.x; gi < g_hi; gi += kThreads) gm = fmaxf(gm, kg[gi]);
-    S.red[threadIdx.x] = gm;
-  }
-  __syncthreads();
-  for (int st = kThreads / 2; st > 0; st >>= 1) {
-    if (threadIdx.x < st) S.red[threadIdx.x] = fmaxf(S.red[threadIdx.x], S.red[threadIdx.x + st]);
-    __syncthreads();
-  }
-  const float gmax = S.red[0];
 
   // This lane's query values on its key MFMA k-slots, times the inverse of
-  // each slot's factor, sm_scale * log2(e) and the split's power-of-two
-  // prescale sigma: qf[kb][2i + e], kept in LDS (every wave uses the same
-  // values; wave 0 writes them).
-  float qabs = 0.0f;
-  float inv_sigma;
+  // each slot's factor, sm_scale * log2(e) and a power of two sigma_q that
+  // brings them below 2 in magnitude: qf[kb][2i + e], kept in LDS (every
+  // wave uses the same values; wave 0 writes them).  Each key group's scale
+  // row is multiplied by its own power of two sigma_g (largest scale below
+  // 2^13) when it is committed to LDS, so |Q'| < 2^14 stays in fp16 range.
+  float inv_sigma_q;
   {
-    float qf[4][8];
+    float qv[32];
     const int64_t base = ((int64_t)b * a.Hq + kvh * g + (head_ok ? hh : 0)) * kD + 32 * lq;
+    if (a.q_f16) {
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
+      for (int c = 0; c < 32; c += 8) {
+        const half8 h8 = *(const half8*)((const uint16_t*)a.q + base + c);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+        for (int j = 0; j < 8; ++j) qv[c + j] = (float)h8[j];
+      }
+    } else {
 #pragma unroll
-        for (int e = 0; e < 2; ++e) {
-          const int c = k_slot_channel<KB>(kb, i, e);
-          float x = 0.0f;
-          if (head_ok)
-            x = a.q_f16 ? h2f(((const uint16_t*)a.q)[base + c]) : ((const float*)a.q)[base + c];
-          x *= a.qscale;
-          qabs = fmaxf(qabs, fabsf(x));
-          qf[kb][2 * i + e] = x * (1.0f / (float)(1 << slot_log2f<KB>(i)));
-        }
+      for (int c = 0; c < 32; c += 4) {
+        const float4v f4 = *(const float4v*)((const float*)a.q + base + c);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) qv[c + j] = f4[j];
+      }
+    }
+    float qabs = 0.0f;
+#pragma unroll
+    for (int c = 0; c < 32; ++c) {
+      qv[c] = head_ok ? qv[c] * a.qscale : 0.0f;
+      qabs = fmaxf(qabs, fabsf(qv[c]));
+    }
     qabs = fmaxf(qabs, __shfl_xor(qabs, 16));
     qabs = fmaxf(qabs, __shfl_xor(qabs, 32));
-    // power-of-two prescale keeping |Q'| = |q k_scale| below 2^14 (gmax is
-    // the largest key scale of the split)
-    const float bound = qabs * gmax;
-    int ex = (int)((__builtin_bit_cast(uint32_t, bound) >> 23) & 0xFF) - 127;
-    ex = ex < -100 ? -100 : (ex > 100 ? 100 : ex);
-    const float sigma = __builtin_bit_cast(float, (uint32_t)(127 + 13 - ex) << 23);
-    inv_sigma = __builtin_bit_cast(float, (uint32_t)(127 - 13 + ex) << 23);
-#pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
-#pragma unroll
-      for (int j = 0; j < 8; ++j) qf[kb][j] *= sigma;
+    int ex = (int)((__builtin_bit_cast(uint32_t, qabs) >> 23) & 0xFF) - 127;
+    ex = ex < -100 ? -100 : ex;
+    const float sigma_q = __builtin_bit_cast(float, (uint32_t)(127 - ex) << 23);
+    inv_sigma_q = __builtin_bit_cast(float, (uint32_t)(127 + ex) << 23);
     if (wave == 0) {
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
-        sm_qf[2 * kb][lane] = (float4v){qf[kb][0], qf[kb][1], qf[kb][2], qf[kb][3]};
-        sm_qf[2 * kb + 1][lane] = (float4v){qf[kb][4], qf[kb][5], qf[kb][6], qf[kb][7]};
+        float qf[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int e = 0; e < 2; ++e)
+            qf[2 * i + e] = qv[k_slot_channel<KB>(kb, i, e)] * sigma_q *
+                            (1.0f / (float)(1 << slot_log2f<KB>(i)));
+        sm_qf[2 * kb][lane] = (float4v){qf[0], qf[1], qf[2], qf[3]};
+        sm_qf[2 * kb + 1][lane] = (float4v){qf[4], qf[5], qf[6], qf[7]};
       }
     }
   }
@@ -355,7 +349,7 @@ decode_mfma_kernel(MfmaArgs a) {
   half8 qhi[4], qlo[PACKED ? 1 : 4];
   float4v negcorr_hi, negcorr_lo;  // minus the group's offset terms
   int cur_group = -1;
-  const float inv_sigma_k = inv_sigma * 16777216.0f;  // undo sigma and 2^-24
+  float inv_sigma_k = 0.0f;  // undoes sigma_q * sigma_g and the 2^-24
 
   float m_run = -INFINITY, l_run = 0.0f;
   float4v o[8];
@@ -372,6 +366,7 @@ decode_mfma_kernel(MfmaArgs a) {
   u32x4 vw[kUnitTiles][VB == 4 ? 2 : 1];
   float4v vsn[kVs4];
   float4v ksn = (float4v){0.0f, 0.0f, 0.0f, 0.0f};
+  float kgn = 0.0f;
   auto load_tile = [&](int unit, int i) {
     const int64_t t32 = (int64_t)(unit * ut + i) * 32;
 #pragma unroll
@@ -396,6 +391,7 @@ decode_mfma_kernel(MfmaArgs a) {
       if (idx < n_vs4) vsn[j] = src[idx];
     }
     if (lane < kD / 4) ksn = ((const float4v*)(ks + (int64_t)(unit / upg) * kD))[lane];
+    kgn = kg[unit / upg];
   };
   float* my_ks = S.ks[wave];
   const int u_first = u_lo + wave;
@@ -414,13 +410,19 @@ decode_mfma_kernel(MfmaArgs a) {
       const int idx = lane + 64 * j;
       if (idx < n_vs4) ((float4v*)my_vs)[idx] = vsn[j];
     }
-    if (lane < kD / 4) ((float4v*)my_ks)[lane] = ksn;
+    // sigma_g: power of two bringing the group's largest scale below 2^13
+    int exg = (int)((__builtin_bit_cast(uint32_t, kgn) >> 23) & 0xFF) - 127;
+    exg = exg < -100 ? -100 : exg;
+    const float sigma_g = __builtin_bit_cast(float, (uint32_t)(127 + 12 - exg) << 23);
+    const float inv_sigma_g = __builtin_bit_cast(float, (uint32_t)(127 - 12 + exg) << 23);
+    if (lane < kD / 4) ((float4v*)my_ks)[lane] = ksn * sigma_g;
     __builtin_amdgcn_wave_barrier();
     const int un = u + kWaves;
     const bool has_next = un < u_hi;
     if (has_next) load_scales(un);
     if (grp != cur_group) {
       cur_group = grp;
+      inv_sigma_k = inv_sigma_q * inv_sigma_g * 16777216.0f;
       const float* kss = my_ks + 32 * lq;
       float ksv[32];
 #pragma unroll

@@ -287,6 +287,37 @@ def test_cache_parity(name):
     # fp32 query gives the same result as its fp16 values
     out32 = kvq.kvq_decode_attention(view, qt.float()).cpu().numpy()
     assert attention.max_row_relative_error(out32, ref) <= TOL
+    # a query that is only 2-byte aligned (general kernel on AUTO)
+    flat = torch.empty(qt.numel() + 1, dtype=qt.dtype, device=DEV)
+    qm = flat[1:].view(qt.shape)
+    qm.copy_(qt)
+    outm = kvq.kvq_decode_attention(view, qm).cpu().numpy()
+    assert attention.max_row_relative_error(outm, ref) <= TOL
+
+
+@pytest.mark.parametrize("qmul,sm", [(2.0 ** 12, 1e-4), (2.0 ** -12, 40.0),
+                                     (1.0, 3.0), (64.0, 0.02)])
+def test_decode_query_and_scale_range(qmul, sm):
+    """Query magnitudes and softmax scales far from 1 (the matrix-core path
+    rescales the query and each key group by powers of two)."""
+    say("query range", qmul, sm)
+    q, oc, gc, Hkv = build_both("k4v2_gqa_sink", CACHE_CASES)
+    view = gc.kvq_cache_view()
+    qs = (q.astype(np.float32) * qmul).astype(np.float16)
+    B = q.shape[0]
+    ref = []
+    for b in range(B):
+        kh = np.stack([oc.dequantized(b, h)[0] for h in range(Hkv)])
+        vh = np.stack([oc.dequantized(b, h)[1] for h in range(Hkv)])
+        ref.append(attention.attention(qs[b].astype(np.float64), kh, vh,
+                                       sm_scale=sm))
+    ref = np.stack(ref)
+    for flags in (kvq.KVQ_DECODE_AUTO, kvq.KVQ_DECODE_GENERIC):
+        out = kvq.kvq_decode_attention(view, torch.from_numpy(qs).to(DEV),
+                                       sm_scale=sm, flags=flags).cpu().numpy()
+        err = attention.max_row_relative_error(out, ref)
+        say(f"  flags={flags} err={err:.3e}")
+        assert err <= TOL
 
 
 def test_append_determinism_and_capacity():
