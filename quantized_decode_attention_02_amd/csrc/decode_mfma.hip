@@ -615,16 +615,481 @@ decode_mfma_kernel(MfmaArgs a) {
   }
 }
 
-// Splits per (batch, KV head): about four workgroups per compute unit
-// (two resident, two rounds -- measured faster than one round of two), and
-// at least eight units per wave.
-int auto_splits(const kvq_kv_view& v) {
+// ---------------------------------------------------------------------------
+// Row-score kernel: up to 8 query heads per KV head and g * NC <= 16.
+//
+// The scores are computed transposed, S[row][token] = Q'[row] . code[token],
+// with the rows of Q' (head, limb) as the MFMA A operand and the key codes
+// as B.  Lane 16r + t then holds, for token t of each 16-token half, the
+// high and low limb sums of the two heads of row group r, so every lane
+// owns whole scores of distinct tokens and the softmax costs one exp per
+// (head, token) and lane group instead of one per MFMA output column.  Row
+// groups that would hold the same heads (g <= 4) split the value groups
+// between them.  The fp16 P' values go through a per-wave LDS buffer into
+// the value MFMA's B layout, whose columns are (head, value group).
+//
+// Value operands are exact centred fp16 codes (AND-OR with the pattern of
+// 1024, packed subtract).  Removing the value offset through an extra MFMA
+// against a constant operand, as on the key side, is not used here: the
+// offset term has the same sign for every token and the MFMA accumulation
+// does not round it away without bias over thousands of tiles.
+constexpr int kPlStride = 40;  // halves per P' row: 32 + 8 against bank conflicts
+
+template <int NC>
+struct RsLds {
+  float vs[kWaves][kUnitTiles * 32 * NC];
+  float ks[kWaves][kD];
+  float4v qf[8][64];
+  float m[kWaves][8];
+  float l[kWaves][8];
+  union alignas(16) {
+    float o[kWaves][8][kD + 1];
+    _Float16 pl[kWaves][16][kPlStride];
+  } u;
+};
+template <int NC>
+constexpr size_t rs_lds_bytes() {
+  return sizeof(RsLds<NC>) > sizeof(RowsLds) ? sizeof(RsLds<NC>) : sizeof(RowsLds);
+}
+
+template <int CTRL>
+__device__ inline float dpp_f(float x) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+// Max / sum over the 16 lanes of a row (row_ror 8, 4, 2, 1).  The max is
+// one v_max_f32 with a DPP source per step (the builtin form adds a copy
+// and a canonicalizing max); the s_nop covers the VALU-write-to-DPP-read
+// wait states.
+template <int ROR>
+__device__ inline float max_ror(float x) {
+  float r;
+  asm("s_nop 1\n\tv_max_f32_dpp %0, %1, %1 row_ror:%2 row_mask:0xf bank_mask:0xf"
+      : "=v"(r)
+      : "v"(x), "i"(ROR));
+  return r;
+}
+__device__ inline float row_max16(float x) {
+  return max_ror<1>(max_ror<2>(max_ror<4>(max_ror<8>(x))));
+}
+__device__ inline float row_sum16(float x) {
+  x += dpp_f<0x128>(x);
+  x += dpp_f<0x124>(x);
+  x += dpp_f<0x122>(x);
+  x += dpp_f<0x121>(x);
+  return x;
+}
+
+// HS: head slots per score lane (1 when g == 1, else 2).  Three waves per
+// SIMD (168 registers) where the variant fits without spilling, else two.
+template <int KB, int VB, int NC, int HS>
+constexpr int rs_waves() {
+  return ((KB == 4 && VB == 4) || NC == 8 || (NC == 4 && (KB == 4 || VB == 4) && !(KB == 2 && HS == 1)))
+             ? 2
+             : 3;
+}
+template <int KB, int VB, int NC, int HS>
+__global__ void __launch_bounds__(kThreads, (rs_waves<KB, VB, NC, HS>())) decode_rs_kernel(MfmaArgs a) {
+  __shared__ __align__(16) unsigned char lds_raw[rs_lds_bytes<NC>()];
+  const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  if (split >= a.n_splits) {
+    fp16_rows_partial(a, split - a.n_splits, split, kvh, b, *(RowsLds*)lds_raw);
+    return;
+  }
+  RsLds<NC>& S = *(RsLds<NC>*)lds_raw;
+  const kvq_kv_view& v = a.v;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+  const int lq = lane >> 4, ln = lane & 15;
+  const int g = a.Hq / v.kv_heads;
+  const int64_t s = (int64_t)b * v.kv_heads + kvh;
+  // row groups with distinct heads; each is repeated rep times
+  const int rgd = HS == 1 ? 1 : (g <= 2 ? 1 : (g <= 4 ? 2 : 4));
+  const int rep = HS == 1 ? 4 : 4 / rgd;
+  // A layout: Q' row ln = 4r + 2hl + limb is head 2(r mod rgd) + hl
+  const int a_head = HS == 1 ? 0 : 2 * ((ln >> 2) % rgd) + ((ln >> 1) & 1);
+  const int limb = ln & 1;
+  // score layout: lane holds rows 4lq .. 4lq + 3 of token ln of each half
+  int s_head[HS];
+#pragma unroll
+  for (int hl = 0; hl < HS; ++hl) s_head[hl] = HS == 1 ? 0 : 2 * (lq % rgd) + hl;
+  const int rep_idx = lq / rgd;
+  // value layout: column ln = head * NC + value group
+  const int v_head = ln / NC, v_cc = ln % NC;
+  const bool v_valid = v_head < g;
+
+  const int tpg = v.group_tok / 32;                    // tiles per key group
+  const int ut = tpg < kUnitTiles ? tpg : kUnitTiles;  // tiles per unit
+  const int upg = tpg / ut;                            // units per group
+  const int n_units = (int)(v.n_quant / (32 * ut));
+  const int per = (n_units + a.n_splits - 1) / a.n_splits;
+  const int u_lo = min(n_units, split * per);
+  const int u_hi = min(n_units, u_lo + per);
+  const float* kg = v.k_gmax + s * v.k_gmax_stride;
+
+  const uint32_t* kc = v.k_codes + s * v.k_codes_stride;
+  const float* ks = v.k_scales + s * v.k_scales_stride;
+  const uint32_t* vc = v.v_codes + s * v.v_codes_stride;
+  const float* vs = v.v_scales + s * v.v_scales_stride;
+  float* my_vs = S.vs[wave];
+  float* my_ks = S.ks[wave];
+  _Float16(*my_pl)[kPlStride] = S.u.pl[wave];
+
+  half8 qa[4];              // Q' rows (A operand), one limb per lane
+  float4v negc;             // minus the group's offset terms, per row
+  int cur_group = -1;
+  float isk = 0.0f;         // undoes sigma_q * sigma_g and the 2^-24
+
+  // online softmax state per head slot (score layout)
+  float m_run[HS], l_part[HS], cm[2][HS];
+  // value-operand slot factor of token 16 h16 + ln: k-slot pair
+  // ((ln & 3) >> 1) + 2 h16
+  const int lf0 = slot_log2f<VB>((ln & 3) >> 1), lf1 = slot_log2f<VB>(((ln & 3) >> 1) + 2);
+  const float f0 = (float)(1 << lf0), f1 = (float)(1 << lf1);
+#pragma unroll
+  for (int hl = 0; hl < HS; ++hl) {
+    m_run[hl] = -INFINITY;
+    l_part[hl] = 0.0f;
+    cm[0][hl] = -INFINITY;
+    cm[1][hl] = -INFINITY;
+  }
+  // P' buffer position of token 16 h16 + ln in its column (+ 4 h16)
+  const int kpos = 8 * (ln >> 2) + (ln & 3);
+  const int niter = (NC + rep - 1) / rep;  // value groups per score lane
+
+  float4v o[8];
+#pragma unroll
+  for (int jb = 0; jb < 8; ++jb) o[jb] = (float4v){0.0f, 0.0f, 0.0f, 0.0f};
+  uint32_t magic = 0x64006400u;
+  asm volatile("" : "+v"(magic));  // keep the fp16 magic in a VGPR
+
+  // Rolling prefetch (as in the column kernel above).  The first unit is
+  // requested before the query prologue so the two latencies overlap.
+  constexpr int kVs4 = (kUnitTiles * 32 * NC / 4 + 63) / 64;
+  const int n_vs4 = ut * 32 * NC / 4;
+  u32x4 kw[kUnitTiles][2];
+  u32x4 vw[kUnitTiles][VB == 4 ? 2 : 1];
+  float4v vsn[kVs4];
+  float4v ksn = (float4v){0.0f, 0.0f, 0.0f, 0.0f};
+  float kgn = 0.0f;
+  auto load_tile = [&](int unit, int i) {
+    const int64_t t32 = (int64_t)(unit * ut + i) * 32;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int64_t tok = t32 + 16 * h + ln;
+      if (KB == 4) {
+        kw[i][h] = *(const u32x4*)(kc + tok * 16 + 4 * lq);
+      } else {
+        const u32x2 w2 = *(const u32x2*)(kc + tok * 8 + 2 * lq);
+        kw[i][h] = (u32x4){w2[0], w2[1], 0u, 0u};
+      }
+    }
+    const int64_t tw = (int64_t)(unit * ut + i) * (32 * VB * kD / 32);
+    vw[i][0] = *(const u32x4*)(vc + tw + lane * 4);
+    if (VB == 4) vw[i][VB == 4 ? 1 : 0] = *(const u32x4*)(vc + tw + 256 + lane * 4);
+  };
+  auto load_scales = [&](int unit) {
+    const float4v* src = (const float4v*)(vs + (int64_t)unit * ut * 32 * NC);
+#pragma unroll
+    for (int j = 0; j < kVs4; ++j) {
+      const int idx = lane + 64 * j;
+      if (idx < n_vs4) vsn[j] = src[idx];
+    }
+    if (lane < kD / 4) ksn = ((const float4v*)(ks + (int64_t)(unit / upg) * kD))[lane];
+    kgn = kg[unit / upg];
+  };
+  const int u_first = u_lo + wave;
+  if (u_first < u_hi) {
+#pragma unroll
+    for (int i = 0; i < kUnitTiles; ++i)
+      if (i < ut) load_tile(u_first, i);
+    load_scales(u_first);
+  }
+
+  // This lane's query values (head a_head, channels of lane group lq) on
+  // its key k-slots, times the inverse slot factor, sm_scale * log2(e) and
+  // a power of two sigma_q (one for all heads) that brings them below 2 in
+  // magnitude; wave 0 keeps them in LDS for all waves.  Each key group's
+  // scale row is multiplied by its own power of two sigma_g (largest scale
+  // below 2^13) when it is committed to LDS, so |Q'| < 2^14.
+  float inv_sigma_q;
+  {
+    const bool ok = a_head < g;
+    float qv[32];
+    const int64_t base = ((int64_t)b * a.Hq + kvh * g + (ok ? a_head : 0)) * kD + 32 * lq;
+    if (a.q_f16) {
+#pragma unroll
+      for (int c = 0; c < 32; c += 8) {
+        const half8 h8 = *(const half8*)((const uint16_t*)a.q + base + c);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) qv[c + j] = (float)h8[j];
+      }
+    } else {
+#pragma unroll
+      for (int c = 0; c < 32; c += 4) {
+        const float4v f4 = *(const float4v*)((const float*)a.q + base + c);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) qv[c + j] = f4[j];
+      }
+    }
+    float qabs = 0.0f;
+#pragma unroll
+    for (int c = 0; c < 32; ++c) {
+      qv[c] = ok ? qv[c] * a.qscale : 0.0f;
+      qabs = fmaxf(qabs, fabsf(qv[c]));
+    }
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) qabs = fmaxf(qabs, __shfl_xor(qabs, o));
+    int ex = (int)((__builtin_bit_cast(uint32_t, qabs) >> 23) & 0xFF) - 127;
+    ex = ex < -100 ? -100 : ex;
+    const float sigma_q = __builtin_bit_cast(float, (uint32_t)(127 - ex) << 23);
+    inv_sigma_q = __builtin_bit_cast(float, (uint32_t)(127 + ex) << 23);
+    if (wave == 0) {
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        float qf[8];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int e = 0; e < 2; ++e)
+            qf[2 * i + e] = qv[k_slot_channel<KB>(kb, i, e)] * sigma_q *
+                            (1.0f / (float)(1 << slot_log2f<KB>(i)));
+        S.qf[2 * kb][lane] = (float4v){qf[0], qf[1], qf[2], qf[3]};
+        S.qf[2 * kb + 1][lane] = (float4v){qf[4], qf[5], qf[6], qf[7]};
+      }
+    }
+  }
+  __syncthreads();
+
+  for (int u = u_first; u < u_hi; u += kWaves) {
+    const int grp = u / upg;
+#pragma unroll
+    for (int j = 0; j < kVs4; ++j) {
+      const int idx = lane + 64 * j;
+      if (idx < n_vs4) ((float4v*)my_vs)[idx] = vsn[j];
+    }
+    int exg = (int)((__builtin_bit_cast(uint32_t, kgn) >> 23) & 0xFF) - 127;
+    exg = exg < -100 ? -100 : exg;
+    const float sigma_g = __builtin_bit_cast(float, (uint32_t)(127 + 12 - exg) << 23);
+    const float inv_sigma_g = __builtin_bit_cast(float, (uint32_t)(127 - 12 + exg) << 23);
+    if (lane < kD / 4) ((float4v*)my_ks)[lane] = ksn * sigma_g;
+    __builtin_amdgcn_wave_barrier();
+    const int un = u + kWaves;
+    const bool has_next = un < u_hi;
+    if (has_next) load_scales(un);
+    if (grp != cur_group) {
+      cur_group = grp;
+      isk = inv_sigma_q * inv_sigma_g * 16777216.0f;
+      const float* kss = my_ks + 32 * lq;
+      float ksv[32];
+#pragma unroll
+      for (int c = 0; c < 32; c += 4) {
+        const float4v t4 = *(const float4v*)(kss + c);
+        ksv[c] = t4[0]; ksv[c + 1] = t4[1]; ksv[c + 2] = t4[2]; ksv[c + 3] = t4[3];
+      }
+      // one limb per lane: the high part, or the rounding residual
+      const uint32_t lmask = limb ? 0xFFFFFFFFu : 0u;
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) {
+        const float4v q0 = S.qf[2 * kb][lane], q1 = S.qf[2 * kb + 1][lane];
+        const float qk[8] = {q0[0], q0[1], q0[2], q0[3], q1[0], q1[1], q1[2], q1[3]};
+        u32x4 r;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float x0 = qk[2 * i] * ksv[k_slot_channel<KB>(kb, i, 0)];
+          const float x1 = qk[2 * i + 1] * ksv[k_slot_channel<KB>(kb, i, 1)];
+          typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+          const half2v hi = {(_Float16)x0, (_Float16)x1};
+          const half2v hsel = __builtin_bit_cast(half2v, __builtin_bit_cast(uint32_t, hi) & lmask);
+          const half2v res = {(_Float16)(x0 - (float)hsel[0]), (_Float16)(x1 - (float)hsel[1])};
+          r[i] = __builtin_bit_cast(uint32_t, res);
+        }
+        qa[kb] = __builtin_bit_cast(half8, r);
+      }
+      const half8 aoff = k_offset_operand<KB>();
+      float4v c = (float4v){0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb) c = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[kb], aoff, c, 0, 0, 0);
+      negc = -c;
+    }
+    __builtin_amdgcn_wave_barrier();
+
+#pragma unroll
+    for (int i = 0; i < kUnitTiles; ++i) {
+      if (i >= ut) break;
+      // ---- scores: rows 4lq..4lq+3 (head slots x limbs) of token ln of
+      //      each 16-token half
+      float4v acc[2];
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        acc[h] = negc;
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+          half8 B;
+          if (KB == 4) {
+            B = int4_key_operand(kw[i][h][kb]);
+          } else {
+            const uint32_t word = kw[i][h][kb >> 1];
+            B = int2_key_operand((kb & 1) ? (word >> 8) : word);
+          }
+          acc[h] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[kb], B, acc[h], 0, 0, 0);
+        }
+      }
+      float sc[2][HS];
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int hl = 0; hl < HS; ++hl) sc[h][hl] = acc[h][2 * hl] + acc[h][2 * hl + 1];
+      // ---- tile max per head slot, online softmax
+      float tmx[HS];
+      bool grow = false;
+#pragma unroll
+      for (int hl = 0; hl < HS; ++hl) {
+        tmx[hl] = row_max16(fmaxf(sc[0][hl], sc[1][hl])) * isk;
+        grow = grow || tmx[hl] > m_run[hl];
+      }
+      if (__any(grow)) {
+        float alpha[HS];
+#pragma unroll
+        for (int hl = 0; hl < HS; ++hl) {
+          const float mn = fmaxf(m_run[hl], tmx[hl]);
+          alpha[hl] = __builtin_amdgcn_exp2f(m_run[hl] - mn);
+          m_run[hl] = mn;
+          l_part[hl] *= alpha[hl];
+          cm[0][hl] = -mn - (float)lf0;
+          cm[1][hl] = -mn - (float)lf1;
+        }
+        float av;
+        if (HS == 1) {
+          av = alpha[0];
+        } else {
+          const int src = 16 * ((v_head >> 1) % rgd);
+          const float a0 = __shfl(alpha[0], src), a1 = __shfl(alpha[HS - 1], src);
+          av = (v_head & 1) ? a1 : a0;
+        }
+#pragma unroll
+        for (int jb = 0; jb < 8; ++jb) o[jb] *= av;
+      }
+      // p / f(slot pair) for the value operand, sums of the unscaled p
+      float p[2][HS];
+#pragma unroll
+      for (int hl = 0; hl < HS; ++hl) {
+        p[0][hl] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[0][hl], isk, cm[0][hl]));
+        p[1][hl] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[1][hl], isk, cm[1][hl]));
+        l_part[hl] = __builtin_fmaf(p[0][hl], f0, __builtin_fmaf(p[1][hl], f1, l_part[hl]));
+      }
+      // ---- P' = p * v_scale into the value B layout
+      const float* vrow = my_vs + (i * 32 + ln) * NC;
+#pragma unroll
+      for (int j = 0; j < NC; ++j) {
+        if (j >= niter) break;
+        const int c = rep_idx + j * rep;
+        if (c < NC) {
+          const float vs0 = vrow[c], vs1 = vrow[16 * NC + c];
+#pragma unroll
+          for (int hl = 0; hl < HS; ++hl) {
+            if (s_head[hl] < g) {
+              _Float16* row = my_pl[s_head[hl] * NC + c];
+              row[kpos] = (_Float16)(p[0][hl] * vs0);
+              row[kpos + 4] = (_Float16)(p[1][hl] * vs1);
+            }
+          }
+        }
+      }
+      __builtin_amdgcn_wave_barrier();
+      const half8 pb = *(const half8*)&my_pl[ln][8 * lq];
+      // ---- value MFMAs
+#pragma unroll
+      for (int jb = 0; jb < 8; ++jb) {
+        half8 A;
+        if (VB == 2) {
+          const uint32_t word = vw[i][0][jb >> 1];
+          A = int2_operand((jb & 1) ? (word >> 8) : word, magic);
+        } else {
+          A = int4_operand(vw[i][jb >> 2][jb & 3], magic);
+        }
+        o[jb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, pb, o[jb], 0, 0, 0);
+      }
+      __builtin_amdgcn_wave_barrier();
+      if (has_next) load_tile(un, i);
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+
+  // ---- per-wave state to LDS (after every wave is done with its P' buffer)
+#pragma unroll
+  for (int hl = 0; hl < HS; ++hl) l_part[hl] = row_sum16(l_part[hl]);
+  __syncthreads();
+  if (ln == 0 && lq < rgd) {
+#pragma unroll
+    for (int hl = 0; hl < HS; ++hl) {
+      if (s_head[hl] < g) {
+        S.m[wave][s_head[hl]] = m_run[hl];
+        S.l[wave][s_head[hl]] = l_part[hl];
+      }
+    }
+  }
+  if (v_valid) {
+#pragma unroll
+    for (int jb = 0; jb < 8; ++jb)
+      if ((jb * NC) / 8 == v_cc)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          S.u.o[wave][v_head][16 * jb + 4 * lq + j] = o[jb][j];
+  }
+  __syncthreads();
+
+  // ---- merge the four waves into this split's partial
+  for (int i = threadIdx.x; i < g * (kD + 2); i += kThreads) {
+    const int h = i / (kD + 2), jx = i % (kD + 2);
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w)
+      if (S.l[w][h] > 0.0f) M = fmaxf(M, S.m[w][h]);
+    float val = 0.0f;
+    if (jx == 0) {
+      val = M;
+    } else {
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        if (S.l[w][h] > 0.0f) {
+          const float sc_w = exp2f(S.m[w][h] - M);
+          val += (jx == 1 ? S.l[w][h] : S.u.o[w][h][jx - 2]) * sc_w;
+        }
+      }
+    }
+    a.partials[(((int64_t)b * a.Hq + kvh * g + h) * a.n_parts + split) * (kD + 2) + jx] = val;
+  }
+}
+
+
+// Whether the row-score kernel runs for this view (else the column kernel).
+bool rows_kernel(const kvq_kv_view& v, int Hq) {
+  const int g = Hq / v.kv_heads, nc = kD / v.group_ch;
+  return g <= 8 && g * nc <= 16;
+}
+
+// Splits per (batch, KV head).  Column kernel: about four workgroups per
+// compute unit (two resident, two rounds) and at least eight units per
+// wave.  Row-score kernel (three resident per compute unit): one full
+// round of 768 workgroups, or four rounds when that would leave more than
+// 48 tiles per wave (smaller workgroups balance better over the 256
+// compute units: at 1M tokens 3072 beat 768, 1024 and 6144), and at least
+// one unit per wave.
+int auto_splits(const kvq_kv_view& v, int Hq) {
+  const int64_t streams = (int64_t)v.batch * v.kv_heads;
+  int64_t sp, by_len;
   const int tpg = v.group_tok / 32;
   const int ut = tpg < kUnitTiles ? tpg : kUnitTiles;
   const int64_t n_units = v.n_quant / (32 * ut);
-  const int64_t streams = (int64_t)v.batch * v.kv_heads;
-  int64_t sp = (1024 + streams - 1) / streams;
-  int64_t by_len = n_units / (8 * kWaves);
+  if (rows_kernel(v, Hq)) {
+    sp = (768 + streams - 1) / streams;
+    if (v.n_quant / 32 > sp * kWaves * 48) sp = (3072 + streams - 1) / streams;
+    by_len = n_units / kWaves;
+  } else {
+    sp = (1024 + streams - 1) / streams;
+    by_len = n_units / (8 * kWaves);
+  }
   if (sp > by_len) sp = by_len;
   if (sp < 1) sp = 1;
   if (sp > 16000) sp = 16000;
@@ -639,8 +1104,10 @@ template <int KB, int VB, int NC>
 hipError_t launch_t(const MfmaArgs& a, hipStream_t s) {
   dim3 grid((unsigned)a.n_parts, (unsigned)a.v.kv_heads, (unsigned)a.v.batch);
   const int g = a.Hq / a.v.kv_heads;
-  if (2 * g * NC <= 16)
-    decode_mfma_kernel<KB, VB, NC, true><<<grid, kThreads, 0, s>>>(a);
+  if (g == 1)
+    decode_rs_kernel<KB, VB, NC, 1><<<grid, kThreads, 0, s>>>(a);
+  else if (rows_kernel(a.v, a.Hq))
+    decode_rs_kernel<KB, VB, NC, 2><<<grid, kThreads, 0, s>>>(a);
   else
     decode_mfma_kernel<KB, VB, NC, false><<<grid, kThreads, 0, s>>>(a);
   return hipGetLastError();
@@ -673,8 +1140,7 @@ bool mfma_decode_eligible(const kvq_kv_view& v, int Hq) {
 }
 
 int mfma_decode_parts(const kvq_kv_view& v, int Hq, int n_splits) {
-  (void)Hq;
-  const int sp = n_splits > 0 ? n_splits : auto_splits(v);
+  const int sp = n_splits > 0 ? n_splits : auto_splits(v, Hq);
   return sp + fp16_parts(v);
 }
 

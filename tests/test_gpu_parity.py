@@ -185,6 +185,25 @@ CACHE_CASES = {
               61, [1, 1, 1, 58], dict(outliers="none")),
     "tail_only": (dict(D=128, S=1, G=64, Gv=32, R=128, k_bits=4, v_bits=2),
                   1, 4, 2, 90, [90], dict(outliers="none")),
+    # head-group shapes of the matrix-core kernels: g = 3, 5 (padded row
+    # groups), 8 with two value groups, 2 with eight, and the wide-column
+    # kernel (g * NC > 16, g = 16); key groups of 1, 2 and 8 tiles
+    "k4v4_g3": (dict(D=128, S=0, G=64, Gv=32, R=64, k_bits=4, v_bits=4),
+                1, 6, 2, 1100, [1100], dict(outliers="per_head", n_out=3)),
+    "k4v2_g5_g256": (dict(D=128, S=1, G=256, Gv=64, R=256, k_bits=4,
+                          v_bits=2), 1, 10, 2, 1700, [1700],
+                     dict(outliers="fraction", frac=0.02, sink_factor=20.0)),
+    "k2v2_g8": (dict(D=128, S=0, G=32, Gv=64, R=32, k_bits=2, v_bits=2),
+                1, 16, 2, 900, [900], dict(outliers="none")),
+    "k2v4_g2_nc8": (dict(D=128, S=0, G=128, Gv=16, R=128, k_bits=2,
+                         v_bits=4), 2, 4, 2, 1200, [1200],
+                    dict(outliers="per_head", n_out=4, out_factor=15.0)),
+    "k2v4_g8_wide": (dict(D=128, S=1, G=64, Gv=32, R=64, k_bits=2,
+                          v_bits=4), 1, 16, 2, 1000, [1000],
+                     dict(outliers="none")),
+    "k4v2_g16_wide": (dict(D=128, S=0, G=128, Gv=128, R=128, k_bits=4,
+                           v_bits=2), 1, 16, 1, 1300, [1300],
+                      dict(outliers="per_head", n_out=2)),
 }
 MIXED_CASES = {
     "mixkvq_small": (dict(D=128, S=0, G=128, Gv=64, R=128, k_bits=2,
