@@ -635,11 +635,13 @@ decode_mfma_kernel(MfmaArgs a) {
 // does not round it away without bias over thousands of tiles.
 constexpr int kPlStride = 40;  // halves per P' row: 32 + 8 against bank conflicts
 
-template <int NC>
+template <int NC, bool KM>
 struct RsLds {
   float vs[kWaves][kUnitTiles * 32 * NC];
   float ks[kWaves][kD];
   float4v qf[8][64];
+  float qs[KM ? 8 : 1][kD];           // mixed keys: q * sm_scale * log2(e) * sigma_q
+  uint16_t inv[kWaves][KM ? kD + 8 : 8];  // mixed keys: 4 x channel of each slot, then bf16 ones
   float m[kWaves][8];
   float l[kWaves][8];
   union alignas(16) {
@@ -647,9 +649,9 @@ struct RsLds {
     _Float16 pl[kWaves][16][kPlStride];
   } u;
 };
-template <int NC>
+template <int NC, bool KM>
 constexpr size_t rs_lds_bytes() {
-  return sizeof(RsLds<NC>) > sizeof(RowsLds) ? sizeof(RsLds<NC>) : sizeof(RowsLds);
+  return sizeof(RsLds<NC, KM>) > sizeof(RowsLds) ? sizeof(RsLds<NC, KM>) : sizeof(RowsLds);
 }
 
 template <int CTRL>
@@ -680,23 +682,27 @@ __device__ inline float row_sum16(float x) {
   return x;
 }
 
-// HS: head slots per score lane (1 when g == 1, else 2).  Three waves per
-// SIMD (168 registers) where the variant fits without spilling, else two.
+// KB: uniform key bits (4 or 2), or 0 for mixed keys (bf16 / int4 / int2
+// channels per group, the MixKVQ layout).  HS: head slots per score lane
+// (1 when g == 1, else 2).  Three waves per SIMD (168 registers) where the
+// variant fits without spilling, else two.
 template <int KB, int VB, int NC, int HS>
 constexpr int rs_waves() {
-  return ((KB == 4 && VB == 4) || NC == 8 || (NC == 4 && (KB == 4 || VB == 4) && !(KB == 2 && HS == 1)))
+  return (KB == 0 || (KB == 4 && VB == 4) || NC == 8 ||
+          (NC == 4 && (KB == 4 || VB == 4) && !(KB == 2 && HS == 1)))
              ? 2
              : 3;
 }
 template <int KB, int VB, int NC, int HS>
 __global__ void __launch_bounds__(kThreads, (rs_waves<KB, VB, NC, HS>())) decode_rs_kernel(MfmaArgs a) {
-  __shared__ __align__(16) unsigned char lds_raw[rs_lds_bytes<NC>()];
+  constexpr bool KM = KB == 0;  // mixed-precision keys
+  __shared__ __align__(16) unsigned char lds_raw[rs_lds_bytes<NC, KM>()];
   const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   if (split >= a.n_splits) {
     fp16_rows_partial(a, split - a.n_splits, split, kvh, b, *(RowsLds*)lds_raw);
     return;
   }
-  RsLds<NC>& S = *(RsLds<NC>*)lds_raw;
+  RsLds<NC, KM>& S = *(RsLds<NC, KM>*)lds_raw;
   const kvq_kv_view& v = a.v;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
@@ -734,6 +740,40 @@ __global__ void __launch_bounds__(kThreads, (rs_waves<KB, VB, NC, HS>())) decode
   float* my_vs = S.vs[wave];
   float* my_ks = S.ks[wave];
   _Float16(*my_pl)[kPlStride] = S.u.pl[wave];
+  // mixed keys: class sizes, packed row words, and the MFMA blocks (the
+  // first n4b take int4 positions, the rest int2 positions, 32 each)
+  const int NB = KM ? v.n_bf16 : 0, N4 = KM ? v.n_int4 : 0, N2 = kD - NB - N4;
+  const int w4 = (N4 + 7) / 8, w2 = (N2 + 15) / 16;
+  const int n4b = (N4 + 31) / 32;
+  const int ksrow = KM ? kD - NB : kD;  // key scales per group
+  const uint32_t* k4p = KM ? v.k_int4 + s * v.k_int4_stride : nullptr;
+  const uint32_t* k2p = KM ? v.k_int2 + s * v.k_int2_stride : nullptr;
+  const uint16_t* kbp = KM ? v.k_bf16 + s * v.k_bf16_stride : nullptr;
+  const uint8_t* kpp = KM ? v.k_pos + s * v.k_pos_stride : nullptr;
+  uint16_t* my_inv = S.inv[wave];
+  // mixed keys, per MFMA block kb: row array, row words and this lane's
+  // word (clamped into the row: a padding slot's code is never used, its
+  // scale is zero); int2 words are shifted so the lane's 8 fields sit in
+  // the low bytes
+  const uint32_t* kbase[4];
+  int kstride[4], kwi[4], kshift[4];
+#pragma unroll
+  for (int kb = 0; kb < 4; ++kb) {
+    const bool b4 = kb < n4b;
+    kbase[kb] = b4 ? k4p : k2p;
+    kstride[kb] = b4 ? w4 : w2;
+    const int wi = b4 ? 4 * kb + lq : 2 * (kb - n4b) + (lq >> 1);
+    const int wmax = (b4 ? w4 : w2) - 1;
+    kwi[kb] = wi < wmax ? wi : (wmax > 0 ? wmax : 0);
+    kshift[kb] = b4 ? 0 : 8 * (lq & 1);
+  }
+  if (KM) {
+    // padding slots of the scale row stay zero; unused map entries name
+    // channel 0
+    const bool pad = (lane >= N4 / 4 && lane < 8 * n4b) || lane >= 8 * n4b + N2 / 4;
+    if (lane < kD / 4 && pad) ((float4v*)my_ks)[lane] = (float4v){0.0f, 0.0f, 0.0f, 0.0f};
+    for (int j = lane; j < kD + 8; j += 64) my_inv[j] = 0;  // channel 0
+  }
 
   half8 qa[4];              // Q' rows (A operand), one limb per lane
   float4v negc;             // minus the group's offset terms, per row
@@ -767,26 +807,44 @@ __global__ void __launch_bounds__(kThreads, (rs_waves<KB, VB, NC, HS>())) decode
   // requested before the query prologue so the two latencies overlap.
   constexpr int kVs4 = (kUnitTiles * 32 * NC / 4 + 63) / 64;
   const int n_vs4 = ut * 32 * NC / 4;
-  u32x4 kw[kUnitTiles][2];
-  u32x4 vw[kUnitTiles][VB == 4 ? 2 : 1];
+  // code slots: a whole unit (tile i in slot i), or for mixed keys two
+  // (tile i in slot i % 2, refilled with the tile two places later)
+  constexpr int kSlots = KM ? 2 : kUnitTiles;
+  u32x4 kw[kSlots][2];
+  u32x4 vw[kSlots][VB == 4 ? 2 : 1];
+  u32x4 kb16[KM ? kSlots : 1][2];  // mixed keys: the token's bf16 channels
   float4v vsn[kVs4];
   float4v ksn = (float4v){0.0f, 0.0f, 0.0f, 0.0f};
   float kgn = 0.0f;
-  auto load_tile = [&](int unit, int i) {
+  uint32_t kpn = 0;  // mixed keys: class positions of channels 2 lane, 2 lane + 1
+  auto load_tile = [&](int unit, int i, int slot) {
     const int64_t t32 = (int64_t)(unit * ut + i) * 32;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
       const int64_t tok = t32 + 16 * h + ln;
-      if (KB == 4) {
-        kw[i][h] = *(const u32x4*)(kc + tok * 16 + 4 * lq);
+      if (KM) {
+        // word of MFMA block kb: int4 word 4 kb + lq, or int2 word
+        // 2 (kb - n4b) + lq / 2
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) kw[slot][h][kb] = kbase[kb][tok * kstride[kb] + kwi[kb]];
+        if (NB == 8) {
+          kb16[KM ? slot : 0][h] = *(const u32x4*)(kbp + tok * 8);
+        } else if (NB == 4) {
+          const u32x2 b2 = *(const u32x2*)(kbp + tok * 4);
+          kb16[KM ? slot : 0][h] = (u32x4){b2[0], b2[1], 0u, 0u};
+        } else {
+          kb16[KM ? slot : 0][h] = (u32x4){0u, 0u, 0u, 0u};
+        }
+      } else if (KB == 4) {
+        kw[slot][h] = *(const u32x4*)(kc + tok * 16 + 4 * lq);
       } else {
         const u32x2 w2 = *(const u32x2*)(kc + tok * 8 + 2 * lq);
-        kw[i][h] = (u32x4){w2[0], w2[1], 0u, 0u};
+        kw[slot][h] = (u32x4){w2[0], w2[1], 0u, 0u};
       }
     }
     const int64_t tw = (int64_t)(unit * ut + i) * (32 * VB * kD / 32);
-    vw[i][0] = *(const u32x4*)(vc + tw + lane * 4);
-    if (VB == 4) vw[i][VB == 4 ? 1 : 0] = *(const u32x4*)(vc + tw + 256 + lane * 4);
+    vw[slot][0] = *(const u32x4*)(vc + tw + lane * 4);
+    if (VB == 4) vw[slot][VB == 4 ? 1 : 0] = *(const u32x4*)(vc + tw + 256 + lane * 4);
   };
   auto load_scales = [&](int unit) {
     const float4v* src = (const float4v*)(vs + (int64_t)unit * ut * 32 * NC);
@@ -795,14 +853,15 @@ __global__ void __launch_bounds__(kThreads, (rs_waves<KB, VB, NC, HS>())) decode
       const int idx = lane + 64 * j;
       if (idx < n_vs4) vsn[j] = src[idx];
     }
-    if (lane < kD / 4) ksn = ((const float4v*)(ks + (int64_t)(unit / upg) * kD))[lane];
+    if (lane < ksrow / 4) ksn = ((const float4v*)(ks + (int64_t)(unit / upg) * ksrow))[lane];
     kgn = kg[unit / upg];
+    if (KM) kpn = ((const uint16_t*)(kpp + (int64_t)(unit / upg) * kD))[lane];
   };
   const int u_first = u_lo + wave;
   if (u_first < u_hi) {
 #pragma unroll
-    for (int i = 0; i < kUnitTiles; ++i)
-      if (i < ut) load_tile(u_first, i);
+    for (int i = 0; i < kSlots; ++i)
+      if (i < ut) load_tile(u_first, i, i);
     load_scales(u_first);
   }
 
@@ -844,7 +903,21 @@ __global__ void __launch_bounds__(kThreads, (rs_waves<KB, VB, NC, HS>())) decode
     ex = ex < -100 ? -100 : ex;
     const float sigma_q = __builtin_bit_cast(float, (uint32_t)(127 - ex) << 23);
     inv_sigma_q = __builtin_bit_cast(float, (uint32_t)(127 + ex) << 23);
-    if (wave == 0) {
+    if (KM) {
+      // mixed keys: the class order differs per group, so keep q by
+      // channel (lanes of one row and lane group write the same values;
+      // rows of heads past g are zero)
+      if (wave == 0) {
+        for (int j = lane; j < 8 * kD; j += 64)
+          if (j / kD >= g) S.qs[j / kD][j % kD] = 0.0f;
+        if (ok) {
+#pragma unroll
+          for (int c = 0; c < 32; c += 4)
+            *(float4v*)&S.qs[a_head][32 * lq + c] =
+                (float4v){qv[c], qv[c + 1], qv[c + 2], qv[c + 3]} * sigma_q;
+        }
+      }
+    } else if (wave == 0) {
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
         float qf[8];
@@ -852,14 +925,16 @@ __global__ void __launch_bounds__(kThreads, (rs_waves<KB, VB, NC, HS>())) decode
         for (int i = 0; i < 4; ++i)
 #pragma unroll
           for (int e = 0; e < 2; ++e)
-            qf[2 * i + e] = qv[k_slot_channel<KB>(kb, i, e)] * sigma_q *
-                            (1.0f / (float)(1 << slot_log2f<KB>(i)));
+            qf[2 * i + e] = qv[k_slot_channel<KB == 0 ? 4 : KB>(kb, i, e)] * sigma_q *
+                            (1.0f / (float)(1 << slot_log2f<KB == 0 ? 4 : KB>(i)));
         S.qf[2 * kb][lane] = (float4v){qf[0], qf[1], qf[2], qf[3]};
         S.qf[2 * kb + 1][lane] = (float4v){qf[4], qf[5], qf[6], qf[7]};
       }
     }
   }
   __syncthreads();
+  // mixed keys: the query on the bf16 channels (true units), per head slot
+  float qb[KM ? HS : 1][8];
 
   for (int u = u_first; u < u_hi; u += kWaves) {
     const int grp = u / upg;
@@ -872,7 +947,27 @@ __global__ void __launch_bounds__(kThreads, (rs_waves<KB, VB, NC, HS>())) decode
     exg = exg < -100 ? -100 : exg;
     const float sigma_g = __builtin_bit_cast(float, (uint32_t)(127 + 12 - exg) << 23);
     const float inv_sigma_g = __builtin_bit_cast(float, (uint32_t)(127 - 12 + exg) << 23);
-    if (lane < kD / 4) ((float4v*)my_ks)[lane] = ksn * sigma_g;
+    if (!KM) {
+      if (lane < kD / 4) ((float4v*)my_ks)[lane] = ksn * sigma_g;
+    } else {
+      // padded slot layout: int4 positions at slots 0 .. 32 n4b - 1, int2
+      // positions from slot 32 n4b on; padding slots keep scale 0
+      if (lane < ksrow / 4) {
+        // times the inverse slot factors: int4 (1, 1/16, 1, 1/16), int2
+        // (1, 1/4, 1, 1/4) (a float4 of slots is one slot pair pattern)
+        const bool i4 = 4 * lane < N4;
+        const int dst = i4 ? lane : 8 * n4b + lane - N4 / 4;
+        const float fo = i4 ? 0.0625f : 0.25f;
+        ((float4v*)my_ks)[dst] = ksn * sigma_g * (float4v){1.0f, fo, 1.0f, fo};
+      }
+      // slot (or bf16 index) -> channel, for channels 2 lane and 2 lane + 1
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const int pos = (kpn >> (8 * e)) & 0xFF;
+        const int slot = pos < NB ? kD + pos : (pos < NB + N4 ? pos - NB : 32 * n4b + pos - NB - N4);
+        my_inv[slot] = (uint16_t)(4 * (2 * lane + e));
+      }
+    }
     __builtin_amdgcn_wave_barrier();
     const int un = u + kWaves;
     const bool has_next = un < u_hi;
@@ -880,6 +975,56 @@ __global__ void __launch_bounds__(kThreads, (rs_waves<KB, VB, NC, HS>())) decode
     if (grp != cur_group) {
       cur_group = grp;
       isk = inv_sigma_q * inv_sigma_g * 16777216.0f;
+      // one limb per lane: the high part, or the rounding residual
+      const uint32_t lmask = limb ? 0xFFFFFFFFu : 0u;
+      typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+      if (KM) {
+        // Q' by padded slot: block kb < n4b holds int4 slots 32 kb + 8 lq +
+        // nibble (slot pair i: nibbles i and i + 4, factor 1 or 16); the
+        // others int2 slots 32 kb + 16 (lq / 2) + 4 (lq & 1) + field (fields
+        // i and i + 8, factor 1 or 4: fields 2 and 3 are read from the word
+        // shifted right by 4).  Padding slots have scale 0.
+        const char* qrow = (const char*)S.qs[a_head < g ? a_head : 7];
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+          const bool b4 = kb < n4b;
+          const int base = b4 ? 32 * kb + 8 * lq : 32 * kb + 16 * (lq >> 1) + 4 * (lq & 1);
+          const int step = b4 ? 4 : 8;  // slot distance of element 1
+          const float4v k0 = *(const float4v*)(my_ks + base);
+          const float4v k1 = *(const float4v*)(my_ks + base + step);
+          u32x4 r;
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            // slot factors are already in the scale row; unused slots have
+            // scale 0, rows of heads past g are zero
+            const float x0 = *(const float*)(qrow + my_inv[base + i]) * k0[i];
+            const float x1 = *(const float*)(qrow + my_inv[base + step + i]) * k1[i];
+            const half2v hi = {(_Float16)x0, (_Float16)x1};
+            const half2v hsel = __builtin_bit_cast(half2v, __builtin_bit_cast(uint32_t, hi) & lmask);
+            const half2v res = {(_Float16)(x0 - (float)hsel[0]), (_Float16)(x1 - (float)hsel[1])};
+            r[i] = __builtin_bit_cast(uint32_t, res);
+          }
+          qa[kb] = __builtin_bit_cast(half8, r);
+        }
+        float4v c = (float4v){0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+          // offsets 8 (int4) or 2 (int2) times the slot pair factors
+          const u32x4 o4 = {0x00080008u, 0x00800080u, 0x00080008u, 0x00800080u};
+          const u32x4 o2 = {0x00020002u, 0x00080008u, 0x00020002u, 0x00080008u};
+          const half8 aoff = __builtin_bit_cast(half8, kb < n4b ? o4 : o2);
+          c = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[kb], aoff, c, 0, 0, 0);
+        }
+        negc = -c;
+        // the bf16 channels' query values in true units, per head slot
+#pragma unroll
+        for (int hl = 0; hl < (KM ? HS : 1); ++hl) {
+          const char* hrow = (const char*)S.qs[s_head[hl] < g ? s_head[hl] : 7];
+#pragma unroll
+          for (int j = 0; j < 8; ++j)
+            qb[hl][j] = j < NB ? *(const float*)(hrow + my_inv[kD + j]) * inv_sigma_q : 0.0f;
+        }
+      } else {
       const float* kss = my_ks + 32 * lq;
       float ksv[32];
 #pragma unroll
@@ -887,8 +1032,6 @@ __global__ void __launch_bounds__(kThreads, (rs_waves<KB, VB, NC, HS>())) decode
         const float4v t4 = *(const float4v*)(kss + c);
         ksv[c] = t4[0]; ksv[c + 1] = t4[1]; ksv[c + 2] = t4[2]; ksv[c + 3] = t4[3];
       }
-      // one limb per lane: the high part, or the rounding residual
-      const uint32_t lmask = limb ? 0xFFFFFFFFu : 0u;
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) {
         const float4v q0 = S.qf[2 * kb][lane], q1 = S.qf[2 * kb + 1][lane];
@@ -896,9 +1039,8 @@ __global__ void __launch_bounds__(kThreads, (rs_waves<KB, VB, NC, HS>())) decode
         u32x4 r;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float x0 = qk[2 * i] * ksv[k_slot_channel<KB>(kb, i, 0)];
-          const float x1 = qk[2 * i + 1] * ksv[k_slot_channel<KB>(kb, i, 1)];
-          typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+          const float x0 = qk[2 * i] * ksv[k_slot_channel<KB == 0 ? 4 : KB>(kb, i, 0)];
+          const float x1 = qk[2 * i + 1] * ksv[k_slot_channel<KB == 0 ? 4 : KB>(kb, i, 1)];
           const half2v hi = {(_Float16)x0, (_Float16)x1};
           const half2v hsel = __builtin_bit_cast(half2v, __builtin_bit_cast(uint32_t, hi) & lmask);
           const half2v res = {(_Float16)(x0 - (float)hsel[0]), (_Float16)(x1 - (float)hsel[1])};
@@ -906,11 +1048,12 @@ __global__ void __launch_bounds__(kThreads, (rs_waves<KB, VB, NC, HS>())) decode
         }
         qa[kb] = __builtin_bit_cast(half8, r);
       }
-      const half8 aoff = k_offset_operand<KB>();
+      const half8 aoff = k_offset_operand<KB == 0 ? 4 : KB>();
       float4v c = (float4v){0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int kb = 0; kb < 4; ++kb) c = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[kb], aoff, c, 0, 0, 0);
       negc = -c;
+      }
     }
     __builtin_amdgcn_wave_barrier();
 
@@ -926,26 +1069,62 @@ __global__ void __launch_bounds__(kThreads, (rs_waves<KB, VB, NC, HS>())) decode
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
           half8 B;
-          if (KB == 4) {
-            B = int4_key_operand(kw[i][h][kb]);
+          if (KM) {
+            // one form for both classes: int4 masks nibble pairs of the word
+            // and of the word >> 8; int2 masks 2-bit pairs of the lane's 16
+            // bits (the word >> kshift)
+            const bool b4 = kb < n4b;
+            const uint32_t w = kw[i % kSlots][h][kb] >> kshift[kb];
+            const uint32_t w8 = w >> (b4 ? 8 : 4);
+            u32x4 r;
+            r[0] = w & (b4 ? 0x000F000Fu : 0x00030003u);
+            r[1] = w & (b4 ? 0x00F000F0u : 0x000C000Cu);
+            r[2] = w8 & (b4 ? 0x000F000Fu : 0x00030003u);
+            r[3] = w8 & (b4 ? 0x00F000F0u : 0x000C000Cu);
+            B = __builtin_bit_cast(half8, r);
+          } else if (KB == 4) {
+            B = int4_key_operand(kw[i % kSlots][h][kb]);
           } else {
-            const uint32_t word = kw[i][h][kb >> 1];
+            const uint32_t word = kw[i % kSlots][h][kb >> 1];
             B = int2_key_operand((kb & 1) ? (word >> 8) : word);
           }
           acc[h] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[kb], B, acc[h], 0, 0, 0);
         }
       }
+      // whole scores; mixed keys add the bf16 channels in true units and
+      // carry the scale already (sk = 1)
       float sc[2][HS];
 #pragma unroll
       for (int h = 0; h < 2; ++h)
 #pragma unroll
         for (int hl = 0; hl < HS; ++hl) sc[h][hl] = acc[h][2 * hl] + acc[h][2 * hl + 1];
+      float sk = isk;
+      if (KM) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          float kf[8];
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const uint32_t w = kb16[KM ? i % kSlots : 0][h][j];
+            kf[2 * j] = __builtin_bit_cast(float, w << 16);
+            kf[2 * j + 1] = __builtin_bit_cast(float, w & 0xFFFF0000u);
+          }
+#pragma unroll
+          for (int hl = 0; hl < HS; ++hl) {
+            float d = sc[h][hl] * isk;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) d = __builtin_fmaf(qb[KM ? hl : 0][j], kf[j], d);
+            sc[h][hl] = d;
+          }
+        }
+        sk = 1.0f;
+      }
       // ---- tile max per head slot, online softmax
       float tmx[HS];
       bool grow = false;
 #pragma unroll
       for (int hl = 0; hl < HS; ++hl) {
-        tmx[hl] = row_max16(fmaxf(sc[0][hl], sc[1][hl])) * isk;
+        tmx[hl] = row_max16(fmaxf(sc[0][hl], sc[1][hl])) * sk;
         grow = grow || tmx[hl] > m_run[hl];
       }
       if (__any(grow)) {
@@ -974,8 +1153,8 @@ __global__ void __launch_bounds__(kThreads, (rs_waves<KB, VB, NC, HS>())) decode
       float p[2][HS];
 #pragma unroll
       for (int hl = 0; hl < HS; ++hl) {
-        p[0][hl] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[0][hl], isk, cm[0][hl]));
-        p[1][hl] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[1][hl], isk, cm[1][hl]));
+        p[0][hl] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[0][hl], sk, cm[0][hl]));
+        p[1][hl] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[1][hl], sk, cm[1][hl]));
         l_part[hl] = __builtin_fmaf(p[0][hl], f0, __builtin_fmaf(p[1][hl], f1, l_part[hl]));
       }
       // ---- P' = p * v_scale into the value B layout
@@ -1003,15 +1182,23 @@ __global__ void __launch_bounds__(kThreads, (rs_waves<KB, VB, NC, HS>())) decode
       for (int jb = 0; jb < 8; ++jb) {
         half8 A;
         if (VB == 2) {
-          const uint32_t word = vw[i][0][jb >> 1];
+          const uint32_t word = vw[i % kSlots][0][jb >> 1];
           A = int2_operand((jb & 1) ? (word >> 8) : word, magic);
         } else {
-          A = int4_operand(vw[i][jb >> 2][jb & 3], magic);
+          A = int4_operand(vw[i % kSlots][jb >> 2][jb & 3], magic);
         }
         o[jb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, pb, o[jb], 0, 0, 0);
       }
       __builtin_amdgcn_wave_barrier();
-      if (has_next) load_tile(un, i);
+      if (kSlots == kUnitTiles) {
+        if (has_next) load_tile(un, i, i);
+      } else if (i + kSlots < ut) {
+        load_tile(u, i + kSlots, i % kSlots);
+      } else if (has_next) {
+        // ut is even here (2 or 4), so the next unit's tile lands in the
+        // same slot parity
+        load_tile(un, i + kSlots - ut, i % kSlots);
+      }
     }
     __builtin_amdgcn_wave_barrier();
   }
@@ -1069,11 +1256,54 @@ bool rows_kernel(const kvq_kv_view& v, int Hq) {
   return g <= 8 && g * nc <= 16;
 }
 
+// Resident workgroups per compute unit of a row-score variant (the
+// occupancy the compiler's register and LDS use allows), cached.
+template <int KB, int VB, int NC>
+int rs_wgs_per_cu(int g) {
+  static int cached[2] = {0, 0};
+  int& c = cached[g == 1 ? 0 : 1];
+  if (c == 0) {
+    int n = 0;
+    const hipError_t e =
+        g == 1 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_rs_kernel<KB, VB, NC, 1>, kThreads, 0)
+               : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_rs_kernel<KB, VB, NC, 2>, kThreads, 0);
+    c = (e == hipSuccess && n > 0) ? n : 2;
+  }
+  return c;
+}
+template <int KB, int VB>
+int rs_wgs_nc(int nc, int g) {
+  switch (nc) {
+    case 1: return rs_wgs_per_cu<KB, VB, 1>(g);
+    case 2: return rs_wgs_per_cu<KB, VB, 2>(g);
+    case 4: return rs_wgs_per_cu<KB, VB, 4>(g);
+    default: return rs_wgs_per_cu<KB, VB, 8>(g);
+  }
+}
+int rs_wgs(const kvq_kv_view& v, int Hq) {
+  const int nc = kD / v.group_ch, g = Hq / v.kv_heads;
+  if (v.k_mixed) return v.v_bits == 2 ? rs_wgs_nc<0, 2>(nc, g) : rs_wgs_nc<0, 4>(nc, g);
+  if (v.k_bits == 4) return v.v_bits == 2 ? rs_wgs_nc<4, 2>(nc, g) : rs_wgs_nc<4, 4>(nc, g);
+  return v.v_bits == 2 ? rs_wgs_nc<2, 2>(nc, g) : rs_wgs_nc<2, 4>(nc, g);
+}
+int n_cus() {
+  static int cached = 0;
+  if (cached == 0) {
+    int dev = 0, n = 0;
+    if (hipGetDevice(&dev) == hipSuccess &&
+        hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && n > 0)
+      cached = n;
+    else
+      cached = 256;
+  }
+  return cached;
+}
+
 // Splits per (batch, KV head).  Column kernel: about four workgroups per
 // compute unit (two resident, two rounds) and at least eight units per
-// wave.  Row-score kernel (three resident per compute unit): one full
-// round of 768 workgroups, or four rounds when that would leave more than
-// 48 tiles per wave (smaller workgroups balance better over the 256
+// wave.  Row-score kernel: one full round of resident workgroups (compute
+// units x resident per unit), or four rounds when that would leave more
+// than 48 tiles per wave (smaller workgroups balance better over the
 // compute units: at 1M tokens 3072 beat 768, 1024 and 6144), and at least
 // one unit per wave.
 int auto_splits(const kvq_kv_view& v, int Hq) {
@@ -1083,8 +1313,9 @@ int auto_splits(const kvq_kv_view& v, int Hq) {
   const int ut = tpg < kUnitTiles ? tpg : kUnitTiles;
   const int64_t n_units = v.n_quant / (32 * ut);
   if (rows_kernel(v, Hq)) {
-    sp = (768 + streams - 1) / streams;
-    if (v.n_quant / 32 > sp * kWaves * 48) sp = (3072 + streams - 1) / streams;
+    const int64_t round = (int64_t)n_cus() * rs_wgs(v, Hq);
+    sp = (round + streams - 1) / streams;
+    if (v.n_quant / 32 > sp * kWaves * 48) sp = (4 * round + streams - 1) / streams;
     by_len = n_units / kWaves;
   } else {
     sp = (1024 + streams - 1) / streams;
@@ -1108,7 +1339,7 @@ hipError_t launch_t(const MfmaArgs& a, hipStream_t s) {
     decode_rs_kernel<KB, VB, NC, 1><<<grid, kThreads, 0, s>>>(a);
   else if (rows_kernel(a.v, a.Hq))
     decode_rs_kernel<KB, VB, NC, 2><<<grid, kThreads, 0, s>>>(a);
-  else
+  else if constexpr (KB != 0)  // mixed keys run only in the row-score kernel
     decode_mfma_kernel<KB, VB, NC, false><<<grid, kThreads, 0, s>>>(a);
   return hipGetLastError();
 }
@@ -1127,8 +1358,19 @@ hipError_t launch_nc(const MfmaArgs& a, int nc, hipStream_t s) {
 }  // namespace
 
 bool mfma_decode_eligible(const kvq_kv_view& v, int Hq) {
-  if (v.head_dim != kD || v.k_mixed) return false;
-  if (v.k_bits != 4 && v.k_bits != 2) return false;
+  if (v.head_dim != kD || Hq < v.kv_heads || Hq % v.kv_heads) return false;
+  if (v.k_mixed) {
+    // row-score kernel only, groups of at least two tiles; 0, 4 or 8 bf16
+    // channels, whole int4 words, and the int4 and int2 positions in at
+    // most four 32-position blocks
+    if (!rows_kernel(v, Hq) || v.group_tok < 64) return false;
+    if (v.n_bf16 != 0 && v.n_bf16 != 4 && v.n_bf16 != 8) return false;
+    const int n2 = kD - v.n_bf16 - v.n_int4;
+    if (v.n_int4 < 0 || v.n_int4 % 8 || n2 < 0) return false;
+    if ((v.n_int4 + 31) / 32 + (n2 + 31) / 32 > 4) return false;
+  } else if (v.k_bits != 4 && v.k_bits != 2) {
+    return false;
+  }
   if (v.v_bits != 4 && v.v_bits != 2) return false;
   if (v.v_layout != KVQ_V_TILE32 || v.group_tok % 32 || v.n_quant % 32) return false;
   if (v.group_tok > 32 * kUnitTiles && v.group_tok % (32 * kUnitTiles)) return false;
@@ -1152,7 +1394,8 @@ hipError_t launch_decode_mfma(const kvq_kv_view& v, const void* q, int f16, int 
   MfmaArgs a{v, q, f16, Hq, sm_scale * kLog2e, partials, n_parts, n_splits};
   const int nc = kD / v.group_ch;
   hipError_t e;
-  if (v.k_bits == 4 && v.v_bits == 2) e = launch_nc<4, 2>(a, nc, s);
+  if (v.k_mixed) e = v.v_bits == 2 ? launch_nc<0, 2>(a, nc, s) : launch_nc<0, 4>(a, nc, s);
+  else if (v.k_bits == 4 && v.v_bits == 2) e = launch_nc<4, 2>(a, nc, s);
   else if (v.k_bits == 4 && v.v_bits == 4) e = launch_nc<4, 4>(a, nc, s);
   else if (v.k_bits == 2 && v.v_bits == 2) e = launch_nc<2, 2>(a, nc, s);
   else e = launch_nc<2, 4>(a, nc, s);

@@ -213,6 +213,19 @@ MIXED_CASES = {
     "mixed_odd_counts": (dict(D=64, S=1, G=32, Gv=16, R=64, k_bits=2,
                               v_bits=4, mixed=True, n_bf16=3, n_int4=13),
                          1, 4, 2, 333, [100, 233], dict(outliers="per_head")),
+    # class-size shapes of the matrix-core mixed-key path: 4 bf16 channels
+    # and a padded last int2 word, no bf16 and half int4, all int2
+    "mixed_nb4_v4": (dict(D=128, S=1, G=64, Gv=32, R=64, k_bits=2, v_bits=4,
+                          mixed=True, n_bf16=4, n_int4=32),
+                     1, 2, 2, 1000, [1000],
+                     dict(outliers="per_head", n_out=4, out_factor=15.0)),
+    "mixed_int4_half_g8": (dict(D=128, S=0, G=128, Gv=128, R=128, k_bits=2,
+                                v_bits=2, mixed=True, n_bf16=0, n_int4=64),
+                           1, 16, 2, 900, [900], dict(outliers="none")),
+    "mixed_all_int2": (dict(D=128, S=0, G=64, Gv=64, R=64, k_bits=2,
+                            v_bits=2, mixed=True, n_bf16=8, n_int4=0),
+                       2, 4, 2, 700, [300, 400],
+                       dict(outliers="per_head", n_out=8, out_factor=20.0)),
 }
 
 
