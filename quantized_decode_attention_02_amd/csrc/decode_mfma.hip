@@ -162,8 +162,8 @@ struct MainLds {
   float o[kWaves][16][kD + 1];
 };
 struct RowsLds {
-  uint16_t k[kRowsPerChunk][kD + 2];  // fp16 rows, padded against bank conflicts
-  uint16_t v[kRowsPerChunk][kD];
+  uint16_t k[kRowsPerChunk][kD + 8];  // fp16 rows (padded: 16-byte rows, fewer conflicts)
+  uint16_t v[kRowsPerChunk][kD + 8];
   float q[16][kD];
   float p[16][kRowsPerChunk];
 };
@@ -173,30 +173,34 @@ constexpr size_t lds_bytes() {
 }
 
 // fp16 rows (sink rows, then tail rows in token order) chunk `chunk` of one
-// (batch, KV head): plain fp32 dot products from LDS; writes one partial.
+// (batch, KV head): exact fp32 attention over up to 64 rows; writes one
+// partial.  Rows arrive with 16-byte loads; each wave takes 16 rows, a lane
+// one row and a quarter of the channels; softmax and the weighted sum of
+// the values are spread over the workgroup.
 __device__ void fp16_rows_partial(const MfmaArgs& a, int chunk, int part, int kvh, int b,
                                   RowsLds& L) {
   const kvq_kv_view& v = a.v;
-  const int tid = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int g = a.Hq / v.kv_heads;
   const int64_t s = (int64_t)b * v.kv_heads + kvh;
   const int64_t nr = v.n_sink + v.n_tail;
   const int r0 = chunk * kRowsPerChunk;
   const int n = (int)min((int64_t)kRowsPerChunk, nr - r0);
-  for (int i = tid; i < n * kD; i += kThreads) {
-    const int r = i / kD, d = i % kD;
+  // rows: 16 threads per row, 16 bytes each
+  for (int i = tid; i < n * 16; i += kThreads) {
+    const int r = i >> 4, c8 = (i & 15) * 8;
     const int64_t j = r0 + r;
     int64_t off;
     const uint16_t *kp, *vp;
     if (j < v.n_sink) {
-      off = s * v.sink_stride + j * kD + d;
+      off = s * v.sink_stride + j * kD;
       kp = v.sink_k; vp = v.sink_v;
     } else {
-      off = s * v.tail_stride + ((v.n_quant + j - v.n_sink) % v.residual) * kD + d;
+      off = s * v.tail_stride + ((v.n_quant + j - v.n_sink) % v.residual) * kD;
       kp = v.tail_k; vp = v.tail_v;
     }
-    L.k[r][d] = kp[off];
-    L.v[r][d] = vp[off];
+    *(u32x4*)&L.k[r][c8] = *(const u32x4*)(kp + off + c8);
+    *(u32x4*)&L.v[r][c8] = *(const u32x4*)(vp + off + c8);
   }
   for (int i = tid; i < g * kD; i += kThreads) {
     const int h = i / kD, d = i % kD;
@@ -204,34 +208,68 @@ __device__ void fp16_rows_partial(const MfmaArgs& a, int chunk, int part, int kv
     L.q[h][d] = (a.q_f16 ? h2f(((const uint16_t*)a.q)[qi]) : ((const float*)a.q)[qi]) * a.qscale;
   }
   __syncthreads();
-  for (int i = tid; i < g * n; i += kThreads) {
-    const int h = i / n, r = i % n;
-    float acc = 0.0f;
-#pragma unroll 8
-    for (int d = 0; d < kD; ++d) acc += L.q[h][d] * h2f(L.k[r][d]);
-    L.p[h][r] = acc;
+  // scores: wave w takes rows 16 w .. 16 w + 15; lane (row ln, channel
+  // quarter lq) sums 32 channels, then the quarters are added
+  {
+    const int ln = lane & 15, lq = lane >> 4, r = 16 * wave + ln;
+    float kf[32];
+    if (r < n) {
+#pragma unroll
+      for (int c = 0; c < 32; c += 8) {
+        const half8 h8 = *(const half8*)&L.k[r][32 * lq + c];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) kf[c + j] = (float)h8[j];
+      }
+    }
+    for (int h = 0; h < g; ++h) {
+      float acc = 0.0f;
+      if (r < n) {
+#pragma unroll
+        for (int c = 0; c < 32; c += 4) {
+          const float4v q4 = *(const float4v*)&L.q[h][32 * lq + c];
+          acc = __builtin_fmaf(q4[0], kf[c], acc);
+          acc = __builtin_fmaf(q4[1], kf[c + 1], acc);
+          acc = __builtin_fmaf(q4[2], kf[c + 2], acc);
+          acc = __builtin_fmaf(q4[3], kf[c + 3], acc);
+        }
+      }
+      acc += __shfl_xor(acc, 16);
+      acc += __shfl_xor(acc, 32);
+      if (lq == 0 && r < n) L.p[h][r] = acc;
+    }
   }
   __syncthreads();
   float* out = a.partials + (((int64_t)b * a.Hq + kvh * g) * a.n_parts + part) * (kD + 2);
   const int64_t hstride = (int64_t)a.n_parts * (kD + 2);
-  if (tid < g) {
-    float m = -INFINITY;
-    for (int r = 0; r < n; ++r) m = fmaxf(m, L.p[tid][r]);
-    float l = 0.0f;
-    for (int r = 0; r < n; ++r) {
-      const float e = exp2f(L.p[tid][r] - m);
-      L.p[tid][r] = e;
-      l += e;
+  // softmax per head: wave w takes heads w, w + 4, ...; lane = row
+  for (int h = wave; h < g; h += kWaves) {
+    const float x = lane < n ? L.p[h][lane] : -INFINITY;
+    float m = x;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) m = fmaxf(m, __shfl_xor(m, o));
+    const float e = lane < n ? exp2f(x - m) : 0.0f;
+    float l = e;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) l += __shfl_xor(l, o);
+    if (lane < n) L.p[h][lane] = e;
+    if (lane == 0) {
+      out[h * hstride] = m;
+      out[h * hstride + 1] = l;
     }
-    out[tid * hstride] = m;
-    out[tid * hstride + 1] = l;
   }
   __syncthreads();
-  for (int i = tid; i < g * kD; i += kThreads) {
-    const int h = i / kD, d = i % kD;
-    float acc = 0.0f;
-    for (int r = 0; r < n; ++r) acc += L.p[h][r] * h2f(L.v[r][d]);
-    out[h * hstride + 2 + d] = acc;
+  // weighted sum of the value rows: thread (head, channel pair)
+  for (int i = tid; i < g * (kD / 2); i += kThreads) {
+    const int h = i / (kD / 2), d2 = 2 * (i % (kD / 2));
+    float o0 = 0.0f, o1 = 0.0f;
+    for (int r = 0; r < n; ++r) {
+      const float pr = L.p[h][r];
+      const uint32_t w = *(const uint32_t*)&L.v[r][d2];
+      o0 = __builtin_fmaf(pr, h2f((uint16_t)(w & 0xFFFF)), o0);
+      o1 = __builtin_fmaf(pr, h2f((uint16_t)(w >> 16)), o1);
+    }
+    out[h * hstride + 2 + d2] = o0;
+    out[h * hstride + 3 + d2] = o1;
   }
 }
 
