@@ -250,44 +250,89 @@ __device__ inline int64_t src_index(const CacheDev& c, const FlushSrc& f,
   return (st * f.n_new + f.take + (p - f.nq_old - f.nt_old)) * c.D;
 }
 
+// MAXD: largest head dimension the LDS rows hold (128 or 256; the smaller
+// one fits four workgroups per compute unit).
+template <int MAXD>
 __global__ void __launch_bounds__(kThreads)
 flush_kernel(CacheDev c, FlushSrc f) {
-  __shared__ float red[kThreads];
-  __shared__ float kmax[kMaxD];     // S_d (absmax per channel)
-  __shared__ float ksc[kMaxD];      // scale per channel (uniform or class)
-  __shared__ int kpos[kMaxD];       // position in class order (mixed)
-  __shared__ int kcls[kMaxD];
-  __shared__ double A[kMaxD];
-  __shared__ float xs[kChunk * kMaxD];
-  __shared__ float vsc[kChunk * kMaxD];
-  __shared__ uint8_t u8[kChunk * kMaxD];
-  __shared__ uint16_t b16[kChunk * kMaxD];
+  // pass 1 reduction scratch shares storage with the staged fp16 rows
+  __shared__ __align__(16) union {
+    float red[kThreads * 8];
+    struct {
+      uint16_t xk[kChunk * MAXD];
+      uint16_t xv[kChunk * MAXD];
+    } rows;
+  } U;
+  float* red = U.red;
+  uint16_t* xk = U.rows.xk;
+  uint16_t* xv = U.rows.xv;
+  __shared__ float kmax[MAXD];     // S_d (absmax per channel)
+  __shared__ float ksc[MAXD];      // scale per channel (uniform or class)
+  __shared__ int kpos[MAXD];       // position in class order (mixed)
+  __shared__ int kcls[MAXD];
+  __shared__ double A[MAXD];
+  __shared__ float vsc[kChunk * (MAXD / 2)];  // value scales (D / Gv <= MAXD / 2)
+  __shared__ uint8_t u8[kChunk * MAXD];
+  __shared__ uint16_t b16[kChunk * MAXD];
   const int tid = threadIdx.x;
   const int D = c.D, G = c.G;
   const int64_t st = (int64_t)blockIdx.z * c.H + blockIdx.y;
   const int64_t grp = f.nq_old / G + blockIdx.x;
   const int64_t p0 = grp * G;
   bool bad = false;
+  // 16-byte row chunks when rows allow it (else element by element)
+  const bool vec = (D % 8 == 0) && (((uintptr_t)f.k_in | (uintptr_t)f.v_in) % 16 == 0);
+  const int cpr = D / 8;  // 16-byte chunks per row
 
   // ---- keys, pass 1: per-channel absmax over the G tokens.
-  const int slices = kThreads / D;
-  if (tid < slices * D) {
-    int ch = tid % D, sl = tid / D;
-    float m = 0.0f;
-    for (int r = sl; r < G; r += slices) {
-      bool ring;
-      int64_t base = src_index(c, f, st, p0 + r, &ring);
-      float v = h2f(ring ? c.tail_k[base + ch] : f.k_in[base + ch]);
-      bad |= !finite(v);
-      m = fmaxf(m, fabsf(v));
+  if (vec) {
+    // thread = (row slice, 8-channel chunk); rows stride by the slice count
+    const int slices = kThreads / cpr;
+    const int c8 = tid % cpr, sl = tid / cpr;
+    float m[8] = {0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f, 0.0f};
+    if (sl < slices) {
+#pragma unroll 4
+      for (int r = sl; r < G; r += slices) {
+        bool ring;
+        const int64_t base = src_index(c, f, st, p0 + r, &ring) + 8 * c8;
+        const uint4 w = *(const uint4*)((ring ? c.tail_k : f.k_in) + base);
+        const uint32_t wv[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float x = h2f((uint16_t)(wv[j >> 1] >> (16 * (j & 1))));
+          bad |= !finite(x);
+          m[j] = fmaxf(m[j], fabsf(x));
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) red[sl * D + 8 * c8 + j] = m[j];
     }
-    red[tid] = m;
-  }
-  __syncthreads();
-  if (tid < D) {
-    float m = red[tid];
-    for (int sl = 1; sl < slices; ++sl) m = fmaxf(m, red[sl * D + tid]);
-    kmax[tid] = m;
+    __syncthreads();
+    if (tid < D) {
+      float mm = red[tid];
+      for (int q = 1; q < slices; ++q) mm = fmaxf(mm, red[q * D + tid]);
+      kmax[tid] = mm;
+    }
+  } else {
+    const int slices = kThreads / D;
+    if (tid < slices * D) {
+      int ch = tid % D, sl = tid / D;
+      float m = 0.0f;
+      for (int r = sl; r < G; r += slices) {
+        bool ring;
+        int64_t base = src_index(c, f, st, p0 + r, &ring);
+        float v = h2f(ring ? c.tail_k[base + ch] : f.k_in[base + ch]);
+        bad |= !finite(v);
+        m = fmaxf(m, fabsf(v));
+      }
+      red[tid] = m;
+    }
+    __syncthreads();
+    if (tid < D) {
+      float m = red[tid];
+      for (int sl = 1; sl < slices; ++sl) m = fmaxf(m, red[sl * D + tid]);
+      kmax[tid] = m;
+    }
   }
   __syncthreads();
 
@@ -341,12 +386,29 @@ flush_kernel(CacheDev c, FlushSrc f) {
   const int qv = qmax_of(c.v_bits);
   for (int r0 = 0; r0 < G; r0 += kChunk) {
     const int rows = min(kChunk, G - r0);
-    // stage K chunk and encode
+    // stage the chunk's K and V rows (fp16) in LDS
+    if (vec) {
+      for (int i = tid; i < rows * cpr; i += kThreads) {
+        const int r = i / cpr, c8 = i % cpr;
+        bool ring;
+        const int64_t base = src_index(c, f, st, p0 + r0 + r, &ring) + 8 * c8;
+        *(uint4*)&xk[r * D + 8 * c8] = *(const uint4*)((ring ? c.tail_k : f.k_in) + base);
+        *(uint4*)&xv[r * D + 8 * c8] = *(const uint4*)((ring ? c.tail_v : f.v_in) + base);
+      }
+    } else {
+      for (int i = tid; i < rows * D; i += kThreads) {
+        const int r = i / D, ch = i % D;
+        bool ring;
+        const int64_t base = src_index(c, f, st, p0 + r0 + r, &ring);
+        xk[i] = ring ? c.tail_k[base + ch] : f.k_in[base + ch];
+        xv[i] = ring ? c.tail_v[base + ch] : f.v_in[base + ch];
+      }
+    }
+    __syncthreads();
+    // encode K
     for (int i = tid; i < rows * D; i += kThreads) {
       int r = i / D, ch = i % D;
-      bool ring;
-      int64_t base = src_index(c, f, st, p0 + r0 + r, &ring);
-      float v = h2f(ring ? c.tail_k[base + ch] : f.k_in[base + ch]);
+      float v = h2f(xk[i]);
       if (!c.mixed) {
         u8[i] = (uint8_t)encode(v, ksc[ch], qmax_of(c.k_bits));
       } else {
@@ -398,28 +460,27 @@ flush_kernel(CacheDev c, FlushSrc f) {
       }
     }
     __syncthreads();
-    // values: stage, per-token group scales, encode, pack
-    for (int i = tid; i < rows * D; i += kThreads) {
-      int r = i / D, ch = i % D;
-      bool ring;
-      int64_t base = src_index(c, f, st, p0 + r0 + r, &ring);
-      float v = h2f(ring ? c.tail_v[base + ch] : f.v_in[base + ch]);
-      bad |= !finite(v);
-      xs[i] = v;
-    }
-    __syncthreads();
+    // values: per-token group scales, encode, pack
     for (int i = tid; i < rows * ngv; i += kThreads) {
       int r = i / ngv, j = i % ngv;
       float m = 0.0f;
-      for (int e = 0; e < c.Gv; ++e) m = fmaxf(m, fabsf(xs[r * D + j * c.Gv + e]));
+      for (int e = 0; e < c.Gv; ++e) {
+        const float x = h2f(xv[r * D + j * c.Gv + e]);
+        bad |= !finite(x);
+        m = fmaxf(m, fabsf(x));
+      }
       float s = group_scale(m, qv);
-      vsc[i] = s;
+      if (ngv <= MAXD / 2) vsc[i] = s;
       c.v_scales[st * c.s_v_scales + (prow + r) * ngv + j] = s;
     }
     __syncthreads();
     for (int i = tid; i < rows * D; i += kThreads) {
       int r = i / D, ch = i % D;
-      u8[i] = (uint8_t)encode(xs[i], vsc[r * ngv + ch / c.Gv], qv);
+      const float x = h2f(xv[i]);
+      // more groups than the LDS row holds only with Gv = 1: the scale of a
+      // one-element group is |x| / qmax
+      const float sv = ngv <= MAXD / 2 ? vsc[r * ngv + ch / c.Gv] : group_scale(fabsf(x), qv);
+      u8[i] = (uint8_t)encode(x, sv, qv);
     }
     __syncthreads();
     if (c.v_layout == KVQ_V_ROWS) {
@@ -686,7 +747,10 @@ hipError_t launch_flush(const CacheDev& c, const uint16_t* k_in,
   if (n_groups <= 0) return hipSuccess;
   FlushSrc f{k_in, v_in, n_new, take, nq_old, nt_old};
   dim3 grid((unsigned)n_groups, (unsigned)c.H, (unsigned)c.B);
-  flush_kernel<<<grid, kThreads, 0, s>>>(c, f);
+  if (c.D <= 128)
+    flush_kernel<128><<<grid, kThreads, 0, s>>>(c, f);
+  else
+    flush_kernel<kMaxD><<<grid, kThreads, 0, s>>>(c, f);
   return hipGetLastError();
 }
 
