@@ -169,60 +169,84 @@ decode_generic_kernel(kvq_kv_view v, const QT* __restrict__ q, int Hq,
 }
 
 // out[b][h][:] = sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) l_p, one
-// workgroup per (batch, query head): the partial weights are reduced in LDS,
-// then two thread halves sum the weighted o vectors over alternate partials.
+// workgroup per (batch, query head).  One pass reads every (m, l) pair into
+// LDS; M and the weights follow from LDS; then wave w sums partials w, w + 4,
+// ... with lane l on channels 2l and 2l + 1 (eight partials in flight per
+// lane), and the four wave sums are added in LDS.
 constexpr int kMergeThreads = 256;
+__device__ inline float wave_max(float x) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) x = fmaxf(x, __shfl_xor(x, o));
+  return x;
+}
+__device__ inline float wave_sum(float x) {
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) x += __shfl_xor(x, o);
+  return x;
+}
 __global__ void __launch_bounds__(kMergeThreads)
 merge_kernel(const float* __restrict__ partials, int D, int n_parts,
              float* __restrict__ out) {
-  __shared__ float red[kMergeThreads];
-  __shared__ float acc2[kMergeThreads];
-  extern __shared__ float wts[];  // [n_parts]
-  const int tid = threadIdx.x;
+  __shared__ float red[kMergeThreads / 64];
+  __shared__ float osum[kMergeThreads / 64][2 * 64];
+  extern __shared__ float ml[];  // [2][n_parts]: m, then weight; l in between
+  float* mm = ml;
+  float* ww = ml + n_parts;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t bh = blockIdx.x;
-  const float* p = partials + bh * n_parts * (int64_t)(D + 2);
+  const int64_t stride = D + 2;
+  const float* p = partials + bh * n_parts * stride;
   float M = -INFINITY;
-  for (int i = tid; i < n_parts; i += kMergeThreads)
-    if (p[(int64_t)i * (D + 2) + 1] > 0.0f) M = fmaxf(M, p[(int64_t)i * (D + 2)]);
-  red[tid] = M;
-  __syncthreads();
-  for (int st = kMergeThreads / 2; st > 0; st >>= 1) {
-    if (tid < st) red[tid] = fmaxf(red[tid], red[tid + st]);
-    __syncthreads();
+  for (int i = tid; i < n_parts; i += kMergeThreads) {
+    const float m = p[i * stride], l = p[i * stride + 1];
+    mm[i] = m;
+    ww[i] = l;
+    if (l > 0.0f) M = fmaxf(M, m);
   }
-  M = red[0];
+  M = wave_max(M);
+  if (lane == 0) red[wave] = M;
   __syncthreads();
+  M = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
   float L = 0.0f;
   for (int i = tid; i < n_parts; i += kMergeThreads) {
-    const float l = p[(int64_t)i * (D + 2) + 1];
-    const float w = l > 0.0f ? exp2f(p[(int64_t)i * (D + 2)] - M) : 0.0f;
-    wts[i] = w;
+    const float l = ww[i];
+    const float w = l > 0.0f ? exp2f(mm[i] - M) : 0.0f;
+    ww[i] = w;
     L += l * w;
   }
-  red[tid] = L;
+  L = wave_sum(L);
   __syncthreads();
-  for (int st = kMergeThreads / 2; st > 0; st >>= 1) {
-    if (tid < st) red[tid] += red[tid + st];
-    __syncthreads();
-  }
-  L = red[0];
-  const int half = tid / 128, d = tid % 128;
+  if (lane == 0) red[wave] = L;
+  __syncthreads();
+  L = red[0] + red[1] + red[2] + red[3];
   for (int d0 = 0; d0 < D; d0 += 128) {
-    float acc = 0.0f;
-    if (d0 + d < D) {
-      int i = half;
-      for (; i + 6 < n_parts; i += 8) {
-        const float a0 = p[(int64_t)i * (D + 2) + 2 + d0 + d];
-        const float a1 = p[(int64_t)(i + 2) * (D + 2) + 2 + d0 + d];
-        const float a2 = p[(int64_t)(i + 4) * (D + 2) + 2 + d0 + d];
-        const float a3 = p[(int64_t)(i + 6) * (D + 2) + 2 + d0 + d];
-        acc += a0 * wts[i] + a1 * wts[i + 2] + a2 * wts[i + 4] + a3 * wts[i + 6];
+    const int d = d0 + 2 * lane;
+    float a0 = 0.0f, a1 = 0.0f;
+    if (d < D) {
+      int i = wave;
+      for (; i + 28 < n_parts; i += 32) {
+        float x[8][2];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          x[k][0] = p[(i + 4 * k) * stride + 2 + d];
+          x[k][1] = d + 1 < D ? p[(i + 4 * k) * stride + 3 + d] : 0.0f;
+        }
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          a0 = __builtin_fmaf(x[k][0], ww[i + 4 * k], a0);
+          a1 = __builtin_fmaf(x[k][1], ww[i + 4 * k], a1);
+        }
       }
-      for (; i < n_parts; i += 2) acc += p[(int64_t)i * (D + 2) + 2 + d0 + d] * wts[i];
+      for (; i < n_parts; i += 4) {
+        a0 = __builtin_fmaf(p[i * stride + 2 + d], ww[i], a0);
+        if (d + 1 < D) a1 = __builtin_fmaf(p[i * stride + 3 + d], ww[i], a1);
+      }
     }
-    acc2[tid] = acc;
+    osum[wave][2 * lane] = a0;
+    osum[wave][2 * lane + 1] = a1;
     __syncthreads();
-    if (half == 0 && d0 + d < D) out[bh * D + d0 + d] = (acc2[tid] + acc2[tid + 128]) / L;
+    if (tid < 128 && d0 + tid < D)
+      out[bh * D + d0 + tid] = (osum[0][tid] + osum[1][tid] + osum[2][tid] + osum[3][tid]) / L;
     __syncthreads();
   }
 }
@@ -266,8 +290,8 @@ hipError_t launch_decode_generic(const kvq_kv_view& v, const void* q, int f16,
 
 hipError_t launch_merge(const float* partials, int B, int Hq, int D,
                         int n_parts, float* out, hipStream_t s) {
-  const size_t lds = sizeof(float) * (size_t)n_parts;
-  if (lds + 2 * 1024 > 64 * 1024) {
+  const size_t lds = 2 * sizeof(float) * (size_t)n_parts;
+  if (lds + 3 * 1024 > 64 * 1024) {
     hipError_t e = hipFuncSetAttribute((const void*)merge_kernel,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
