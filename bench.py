@@ -233,7 +233,7 @@ def main():
     out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
     flush_buf = None
     if args.workload != "1m_32layer":
-        flush_buf = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        flush_buf = torch.zeros(1 << 30, dtype=torch.uint8, device=dev)
 
     def step(i, events=None):
         for L, c in enumerate(caches):
@@ -261,7 +261,12 @@ def main():
     t0 = time.perf_counter()
     for s in range(args.steps):
         if flush_buf is not None:
-            flush_buf.fill_(s & 0xFF)   # evict the 256 MB Infinity Cache
+            # evict the 256 MB Infinity Cache by reading 1 GiB: the lines
+            # left behind are clean, as after the other reads of a model
+            # step (a buffer rewritten instead leaves dirty lines whose
+            # write-back competes with the timed reads and halves the
+            # read rate even of a plain copy kernel at these sizes)
+            flush_buf.view(torch.float32).sum()
         step_events[s][0].record(stream)
         step(args.warmup + s, dec_events[s])
         step_events[s][1].record(stream)

@@ -37,6 +37,7 @@ namespace {
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float float4v __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int kWaves = 4;
@@ -731,7 +732,7 @@ constexpr int rs_waves() {
              ? 2
              : 3;
 }
-template <int KB, int VB, int NC, int HS>
+template <int KB, int VB, int NC, int HS, int UT>
 __global__ void __launch_bounds__(kThreads, (rs_waves<KB, VB, NC, HS>())) decode_rs_kernel(MfmaArgs a) {
   constexpr bool KM = KB == 0;  // mixed-precision keys
   __shared__ __align__(16) unsigned char lds_raw[rs_lds_bytes<NC, KM>()];
@@ -763,7 +764,7 @@ __global__ void __launch_bounds__(kThreads, (rs_waves<KB, VB, NC, HS>())) decode
   const bool v_valid = v_head < g;
 
   const int tpg = v.group_tok / 32;                    // tiles per key group
-  const int ut = tpg < kUnitTiles ? tpg : kUnitTiles;  // tiles per unit
+  constexpr int ut = UT;                               // tiles per unit
   const int upg = tpg / ut;                            // units per group
   const int n_units = (int)(v.n_quant / (32 * ut));
   const int per = (n_units + a.n_splits - 1) / a.n_splits;
@@ -815,7 +816,6 @@ __global__ void __launch_bounds__(kThreads, (rs_waves<KB, VB, NC, HS>())) decode
 
   half8 qa[4];              // Q' rows (A operand), one limb per lane
   float4v negc;             // minus the group's offset terms, per row
-  int cur_group = -1;
   float isk = 0.0f;         // undoes sigma_q * sigma_g and the 2^-24
 
   // online softmax state per head slot (score layout)
@@ -843,8 +843,8 @@ __global__ void __launch_bounds__(kThreads, (rs_waves<KB, VB, NC, HS>())) decode
 
   // Rolling prefetch (as in the column kernel above).  The first unit is
   // requested before the query prologue so the two latencies overlap.
-  constexpr int kVs4 = (kUnitTiles * 32 * NC / 4 + 63) / 64;
-  const int n_vs4 = ut * 32 * NC / 4;
+  constexpr int kVs4 = (UT * 32 * NC / 4 + 63) / 64;
+  constexpr int n_vs4 = UT * 32 * NC / 4;
   // code slots: a whole unit (tile i in slot i), or for mixed keys two
   // (tile i in slot i % 2, refilled with the tile two places later)
   constexpr int kSlots = KM ? 2 : kUnitTiles;
@@ -895,12 +895,36 @@ __global__ void __launch_bounds__(kThreads, (rs_waves<KB, VB, NC, HS>())) decode
     kgn = kg[unit / upg];
     if (KM) kpn = ((const uint16_t*)(kpp + (int64_t)(unit / upg) * kD))[lane];
   };
+  // A step of the wave covers kStep tiles: one unit, or kStep / ut units
+  // (u, u + 4, ...) when units are shorter than the slot ring, so the code
+  // prefetch always runs kSlots tiles ahead; tile i of a step is tile
+  // i % ut of unit u + 4 (i / ut) and lives in slot i % kSlots.
+  constexpr int kStep = kSlots > ut ? kSlots : ut;
+  constexpr int ups = kStep / ut;  // units per step
   const int u_first = u_lo + wave;
-  if (u_first < u_hi) {
+  // Request order: the query, the first unit's scales, then its codes.
+  // Loads complete in order, so the query prologue waits only for the
+  // query and the first tile only for the scales and itself, not for the
+  // whole prefetch burst.
+  const bool q_ok = a_head < g;
+  u32x4 qraw[8];
+  {
+    const int64_t base = ((int64_t)b * a.Hq + kvh * g + (q_ok ? a_head : 0)) * kD + 32 * lq;
+    if (a.q_f16) {
 #pragma unroll
-    for (int i = 0; i < kSlots; ++i)
-      if (i < ut) load_tile(u_first, i, i);
+      for (int c = 0; c < 4; ++c) qraw[c] = *(const u32x4*)((const uint16_t*)a.q + base + 8 * c);
+    } else {
+#pragma unroll
+      for (int c = 0; c < 8; ++c) qraw[c] = *(const u32x4*)((const float*)a.q + base + 4 * c);
+    }
+  }
+  if (u_first < u_hi) {
     load_scales(u_first);
+#pragma unroll
+    for (int i = 0; i < kSlots; ++i) {
+      const int uu = u_first + kWaves * (i / ut);
+      if (uu < u_hi) load_tile(uu, i % ut, i);
+    }
   }
 
   // This lane's query values (head a_head, channels of lane group lq) on
@@ -911,22 +935,21 @@ __global__ void __launch_bounds__(kThreads, (rs_waves<KB, VB, NC, HS>())) decode
   // below 2^13) when it is committed to LDS, so |Q'| < 2^14.
   float inv_sigma_q;
   {
-    const bool ok = a_head < g;
+    const bool ok = q_ok;
     float qv[32];
-    const int64_t base = ((int64_t)b * a.Hq + kvh * g + (ok ? a_head : 0)) * kD + 32 * lq;
     if (a.q_f16) {
 #pragma unroll
-      for (int c = 0; c < 32; c += 8) {
-        const half8 h8 = *(const half8*)((const uint16_t*)a.q + base + c);
+      for (int c = 0; c < 4; ++c) {
+        const half8 h8 = __builtin_bit_cast(half8, qraw[c]);
 #pragma unroll
-        for (int j = 0; j < 8; ++j) qv[c + j] = (float)h8[j];
+        for (int j = 0; j < 8; ++j) qv[8 * c + j] = (float)h8[j];
       }
     } else {
 #pragma unroll
-      for (int c = 0; c < 32; c += 4) {
-        const float4v f4 = *(const float4v*)((const float*)a.q + base + c);
+      for (int c = 0; c < 8; ++c) {
+        const float4v f4 = __builtin_bit_cast(float4v, qraw[c]);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) qv[c + j] = f4[j];
+        for (int j = 0; j < 4; ++j) qv[4 * c + j] = f4[j];
       }
     }
     float qabs = 0.0f;
@@ -971,133 +994,150 @@ __global__ void __launch_bounds__(kThreads, (rs_waves<KB, VB, NC, HS>())) decode
     }
   }
   __syncthreads();
-  // mixed keys: the query on the bf16 channels (true units), per head slot
-  float qb[KM ? HS : 1][8];
+  // mixed keys: A operands of the bf16-channel MFMAs (three bf16 limbs of
+  // the query on the bf16 channels)
+  bf16x8 qbA = {}, qbB = {};
 
-  for (int u = u_first; u < u_hi; u += kWaves) {
-    const int grp = u / upg;
+  for (int u = u_first; u < u_hi; u += kWaves * ups) {
+    const int un = u + kWaves * ups;  // first unit of the next step
 #pragma unroll
-    for (int j = 0; j < kVs4; ++j) {
-      const int idx = lane + 64 * j;
-      if (idx < n_vs4) ((float4v*)my_vs)[idx] = vsn[j];
-    }
-    int exg = (int)((__builtin_bit_cast(uint32_t, kgn) >> 23) & 0xFF) - 127;
-    exg = exg < -100 ? -100 : exg;
-    const float sigma_g = __builtin_bit_cast(float, (uint32_t)(127 + 12 - exg) << 23);
-    const float inv_sigma_g = __builtin_bit_cast(float, (uint32_t)(127 - 12 + exg) << 23);
-    if (!KM) {
-      if (lane < kD / 4) ((float4v*)my_ks)[lane] = ksn * sigma_g;
-    } else {
-      // padded slot layout: int4 positions at slots 0 .. 32 n4b - 1, int2
-      // positions from slot 32 n4b on; padding slots keep scale 0
-      if (lane < ksrow / 4) {
-        // times the inverse slot factors: int4 (1, 1/16, 1, 1/16), int2
-        // (1, 1/4, 1, 1/4) (a float4 of slots is one slot pair pattern)
-        const bool i4 = 4 * lane < N4;
-        const int dst = i4 ? lane : 8 * n4b + lane - N4 / 4;
-        const float fo = i4 ? 0.0625f : 0.25f;
-        ((float4v*)my_ks)[dst] = ksn * sigma_g * (float4v){1.0f, fo, 1.0f, fo};
-      }
-      // slot (or bf16 index) -> channel, for channels 2 lane and 2 lane + 1
+    for (int i = 0; i < kStep; ++i) {
+      const int uc = u + kWaves * (i / ut);  // this tile's unit
+      if (i % ut == 0) {
+        if (i > 0 && uc >= u_hi) break;
+        // ---- unit start: commit the unit's scales, request the next
+        //      unit's, and build Q' for the unit's key group (every unit,
+        //      so that Q' is not carried from one unit to the next, which
+        //      costs registers)
 #pragma unroll
-      for (int e = 0; e < 2; ++e) {
-        const int pos = (kpn >> (8 * e)) & 0xFF;
-        const int slot = pos < NB ? kD + pos : (pos < NB + N4 ? pos - NB : 32 * n4b + pos - NB - N4);
-        my_inv[slot] = (uint16_t)(4 * (2 * lane + e));
-      }
-    }
-    __builtin_amdgcn_wave_barrier();
-    const int un = u + kWaves;
-    const bool has_next = un < u_hi;
-    if (has_next) load_scales(un);
-    if (grp != cur_group) {
-      cur_group = grp;
-      isk = inv_sigma_q * inv_sigma_g * 16777216.0f;
-      // one limb per lane: the high part, or the rounding residual
-      const uint32_t lmask = limb ? 0xFFFFFFFFu : 0u;
-      typedef _Float16 half2v __attribute__((ext_vector_type(2)));
-      if (KM) {
-        // Q' by padded slot: block kb < n4b holds int4 slots 32 kb + 8 lq +
-        // nibble (slot pair i: nibbles i and i + 4, factor 1 or 16); the
-        // others int2 slots 32 kb + 16 (lq / 2) + 4 (lq & 1) + field (fields
-        // i and i + 8, factor 1 or 4: fields 2 and 3 are read from the word
-        // shifted right by 4).  Padding slots have scale 0.
-        const char* qrow = (const char*)S.qs[a_head < g ? a_head : 7];
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-          const bool b4 = kb < n4b;
-          const int base = b4 ? 32 * kb + 8 * lq : 32 * kb + 16 * (lq >> 1) + 4 * (lq & 1);
-          const int step = b4 ? 4 : 8;  // slot distance of element 1
-          const float4v k0 = *(const float4v*)(my_ks + base);
-          const float4v k1 = *(const float4v*)(my_ks + base + step);
-          u32x4 r;
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            // slot factors are already in the scale row; unused slots have
-            // scale 0, rows of heads past g are zero
-            const float x0 = *(const float*)(qrow + my_inv[base + i]) * k0[i];
-            const float x1 = *(const float*)(qrow + my_inv[base + step + i]) * k1[i];
-            const half2v hi = {(_Float16)x0, (_Float16)x1};
-            const half2v hsel = __builtin_bit_cast(half2v, __builtin_bit_cast(uint32_t, hi) & lmask);
-            const half2v res = {(_Float16)(x0 - (float)hsel[0]), (_Float16)(x1 - (float)hsel[1])};
-            r[i] = __builtin_bit_cast(uint32_t, res);
+        for (int j = 0; j < kVs4; ++j) {
+          const int idx = lane + 64 * j;
+          if (idx < n_vs4) ((float4v*)my_vs)[idx] = vsn[j];
+        }
+        int exg = (int)((__builtin_bit_cast(uint32_t, kgn) >> 23) & 0xFF) - 127;
+        exg = exg < -100 ? -100 : exg;
+        const float sigma_g = __builtin_bit_cast(float, (uint32_t)(127 + 12 - exg) << 23);
+        const float inv_sigma_g = __builtin_bit_cast(float, (uint32_t)(127 - 12 + exg) << 23);
+        if (!KM) {
+          if (lane < kD / 4) ((float4v*)my_ks)[lane] = ksn * sigma_g;
+        } else {
+          // padded slot layout: int4 positions at slots 0 .. 32 n4b - 1, int2
+          // positions from slot 32 n4b on; padding slots keep scale 0
+          if (lane < ksrow / 4) {
+            // times the inverse slot factors: int4 (1, 1/16, 1, 1/16), int2
+            // (1, 1/4, 1, 1/4) (a float4 of slots is one slot pair pattern)
+            const bool i4 = 4 * lane < N4;
+            const int dst = i4 ? lane : 8 * n4b + lane - N4 / 4;
+            const float fo = i4 ? 0.0625f : 0.25f;
+            ((float4v*)my_ks)[dst] = ksn * sigma_g * (float4v){1.0f, fo, 1.0f, fo};
           }
-          qa[kb] = __builtin_bit_cast(half8, r);
+          // slot (or bf16 index) -> channel, for channels 2 lane and 2 lane + 1
+#pragma unroll
+          for (int e = 0; e < 2; ++e) {
+            const int pos = (kpn >> (8 * e)) & 0xFF;
+            const int slot = pos < NB ? kD + pos : (pos < NB + N4 ? pos - NB : 32 * n4b + pos - NB - N4);
+            my_inv[slot] = (uint16_t)(4 * (2 * lane + e));
+          }
         }
-        float4v c = (float4v){0.0f, 0.0f, 0.0f, 0.0f};
+        __builtin_amdgcn_wave_barrier();
+        // scales of the wave's next unit
+        if (uc + kWaves < u_hi) load_scales(uc + kWaves);
+        {
+          isk = inv_sigma_q * inv_sigma_g * 16777216.0f;
+          // one limb per lane: the high part, or the rounding residual
+          const uint32_t lmask = limb ? 0xFFFFFFFFu : 0u;
+          typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+          if (KM) {
+            // Q' by padded slot: block kb < n4b holds int4 slots 32 kb + 8 lq +
+            // nibble (slot pair i: nibbles i and i + 4, factor 1 or 16); the
+            // others int2 slots 32 kb + 16 (lq / 2) + 4 (lq & 1) + field (fields
+            // i and i + 8, factor 1 or 4: fields 2 and 3 are read from the word
+            // shifted right by 4).  Padding slots have scale 0.
+            const char* qrow = (const char*)S.qs[a_head < g ? a_head : 7];
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-          // offsets 8 (int4) or 2 (int2) times the slot pair factors
-          const u32x4 o4 = {0x00080008u, 0x00800080u, 0x00080008u, 0x00800080u};
-          const u32x4 o2 = {0x00020002u, 0x00080008u, 0x00020002u, 0x00080008u};
-          const half8 aoff = __builtin_bit_cast(half8, kb < n4b ? o4 : o2);
-          c = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[kb], aoff, c, 0, 0, 0);
+            for (int kb = 0; kb < 4; ++kb) {
+              const bool b4 = kb < n4b;
+              const int base = b4 ? 32 * kb + 8 * lq : 32 * kb + 16 * (lq >> 1) + 4 * (lq & 1);
+              const int step = b4 ? 4 : 8;  // slot distance of element 1
+              const float4v k0 = *(const float4v*)(my_ks + base);
+              const float4v k1 = *(const float4v*)(my_ks + base + step);
+              u32x4 r;
+#pragma unroll
+              for (int i = 0; i < 4; ++i) {
+                // slot factors are already in the scale row; unused slots have
+                // scale 0, rows of heads past g are zero
+                const float x0 = *(const float*)(qrow + my_inv[base + i]) * k0[i];
+                const float x1 = *(const float*)(qrow + my_inv[base + step + i]) * k1[i];
+                const half2v hi = {(_Float16)x0, (_Float16)x1};
+                const half2v hsel = __builtin_bit_cast(half2v, __builtin_bit_cast(uint32_t, hi) & lmask);
+                const half2v res = {(_Float16)(x0 - (float)hsel[0]), (_Float16)(x1 - (float)hsel[1])};
+                r[i] = __builtin_bit_cast(uint32_t, res);
+              }
+              qa[kb] = __builtin_bit_cast(half8, r);
+            }
+            float4v c = (float4v){0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) {
+              // offsets 8 (int4) or 2 (int2) times the slot pair factors
+              const u32x4 o4 = {0x00080008u, 0x00800080u, 0x00080008u, 0x00800080u};
+              const u32x4 o2 = {0x00020002u, 0x00080008u, 0x00020002u, 0x00080008u};
+              const half8 aoff = __builtin_bit_cast(half8, kb < n4b ? o4 : o2);
+              c = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[kb], aoff, c, 0, 0, 0);
+            }
+            negc = -c;
+            // bf16 channels: lane group 0 holds row ln's query on bf16
+            // index j (k-slot j of a bf16 MFMA whose key operand is the
+            // token's bf16 row), in the integer part's units (times
+            // sigma_g 2^-24, which isk undoes) and split into three bf16
+            // limbs: limb-0 rows take the first and third, limb-1 rows the
+            // second, so the row pair's sum carries the fp32 product
+            if (NB > 0) {
+              const float fg = sigma_g * __builtin_bit_cast(float, 0x33800000u);  // 2^-24
+#pragma unroll
+              for (int j = 0; j < 8; ++j) {
+                const float x = (lq == 0 && j < NB) ? *(const float*)(qrow + my_inv[kD + j]) * fg : 0.0f;
+                const __bf16 h1 = (__bf16)x;
+                const float r1 = x - (float)h1;
+                const __bf16 h2 = (__bf16)r1;
+                const __bf16 h3 = (__bf16)(r1 - (float)h2);
+                qbA[j] = limb ? h2 : h1;
+                qbB[j] = limb ? (__bf16)0.0f : h3;
+              }
+            }
+          } else {
+          const float* kss = my_ks + 32 * lq;
+          float ksv[32];
+#pragma unroll
+          for (int c = 0; c < 32; c += 4) {
+            const float4v t4 = *(const float4v*)(kss + c);
+            ksv[c] = t4[0]; ksv[c + 1] = t4[1]; ksv[c + 2] = t4[2]; ksv[c + 3] = t4[3];
+          }
+#pragma unroll
+          for (int kb = 0; kb < 4; ++kb) {
+            const float4v q0 = S.qf[2 * kb][lane], q1 = S.qf[2 * kb + 1][lane];
+            const float qk[8] = {q0[0], q0[1], q0[2], q0[3], q1[0], q1[1], q1[2], q1[3]};
+            u32x4 r;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const float x0 = qk[2 * i] * ksv[k_slot_channel<KB == 0 ? 4 : KB>(kb, i, 0)];
+              const float x1 = qk[2 * i + 1] * ksv[k_slot_channel<KB == 0 ? 4 : KB>(kb, i, 1)];
+              const half2v hi = {(_Float16)x0, (_Float16)x1};
+              const half2v hsel = __builtin_bit_cast(half2v, __builtin_bit_cast(uint32_t, hi) & lmask);
+              const half2v res = {(_Float16)(x0 - (float)hsel[0]), (_Float16)(x1 - (float)hsel[1])};
+              r[i] = __builtin_bit_cast(uint32_t, res);
+            }
+            qa[kb] = __builtin_bit_cast(half8, r);
+          }
+          const half8 aoff = k_offset_operand<KB == 0 ? 4 : KB>();
+          float4v c = (float4v){0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+          for (int kb = 0; kb < 4; ++kb) c = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[kb], aoff, c, 0, 0, 0);
+          negc = -c;
+          }
         }
-        negc = -c;
-        // the bf16 channels' query values in true units, per head slot
-#pragma unroll
-        for (int hl = 0; hl < (KM ? HS : 1); ++hl) {
-          const char* hrow = (const char*)S.qs[s_head[hl] < g ? s_head[hl] : 7];
-#pragma unroll
-          for (int j = 0; j < 8; ++j)
-            qb[hl][j] = j < NB ? *(const float*)(hrow + my_inv[kD + j]) * inv_sigma_q : 0.0f;
-        }
-      } else {
-      const float* kss = my_ks + 32 * lq;
-      float ksv[32];
-#pragma unroll
-      for (int c = 0; c < 32; c += 4) {
-        const float4v t4 = *(const float4v*)(kss + c);
-        ksv[c] = t4[0]; ksv[c + 1] = t4[1]; ksv[c + 2] = t4[2]; ksv[c + 3] = t4[3];
+        __builtin_amdgcn_wave_barrier();
       }
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb) {
-        const float4v q0 = S.qf[2 * kb][lane], q1 = S.qf[2 * kb + 1][lane];
-        const float qk[8] = {q0[0], q0[1], q0[2], q0[3], q1[0], q1[1], q1[2], q1[3]};
-        u32x4 r;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float x0 = qk[2 * i] * ksv[k_slot_channel<KB == 0 ? 4 : KB>(kb, i, 0)];
-          const float x1 = qk[2 * i + 1] * ksv[k_slot_channel<KB == 0 ? 4 : KB>(kb, i, 1)];
-          const half2v hi = {(_Float16)x0, (_Float16)x1};
-          const half2v hsel = __builtin_bit_cast(half2v, __builtin_bit_cast(uint32_t, hi) & lmask);
-          const half2v res = {(_Float16)(x0 - (float)hsel[0]), (_Float16)(x1 - (float)hsel[1])};
-          r[i] = __builtin_bit_cast(uint32_t, res);
-        }
-        qa[kb] = __builtin_bit_cast(half8, r);
-      }
-      const half8 aoff = k_offset_operand<KB == 0 ? 4 : KB>();
-      float4v c = (float4v){0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-      for (int kb = 0; kb < 4; ++kb) c = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[kb], aoff, c, 0, 0, 0);
-      negc = -c;
-      }
-    }
-    __builtin_amdgcn_wave_barrier();
 
-#pragma unroll
-    for (int i = 0; i < kUnitTiles; ++i) {
-      if (i >= ut) break;
       // ---- scores: rows 4lq..4lq+3 (head slots x limbs) of token ln of
       //      each 16-token half
       float4v acc[2];
@@ -1128,35 +1168,22 @@ __global__ void __launch_bounds__(kThreads, (rs_waves<KB, VB, NC, HS>())) decode
           }
           acc[h] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[kb], B, acc[h], 0, 0, 0);
         }
+        if (KM && NB > 0) {
+          // the bf16 channels: the token's bf16 row is the key operand
+          // (k-slots past NB, and every slot of lane groups 1-3, meet zero
+          // query limbs)
+          const bf16x8 kbf = __builtin_bit_cast(bf16x8, kb16[KM ? i % kSlots : 0][h]);
+          acc[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qbA, kbf, acc[h], 0, 0, 0);
+          acc[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qbB, kbf, acc[h], 0, 0, 0);
+        }
       }
-      // whole scores; mixed keys add the bf16 channels in true units and
-      // carry the scale already (sk = 1)
+      // whole scores (head slot hl: rows 2 hl and 2 hl + 1, the limbs)
       float sc[2][HS];
 #pragma unroll
       for (int h = 0; h < 2; ++h)
 #pragma unroll
         for (int hl = 0; hl < HS; ++hl) sc[h][hl] = acc[h][2 * hl] + acc[h][2 * hl + 1];
-      float sk = isk;
-      if (KM) {
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-          float kf[8];
-#pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            const uint32_t w = kb16[KM ? i % kSlots : 0][h][j];
-            kf[2 * j] = __builtin_bit_cast(float, w << 16);
-            kf[2 * j + 1] = __builtin_bit_cast(float, w & 0xFFFF0000u);
-          }
-#pragma unroll
-          for (int hl = 0; hl < HS; ++hl) {
-            float d = sc[h][hl] * isk;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) d = __builtin_fmaf(qb[KM ? hl : 0][j], kf[j], d);
-            sc[h][hl] = d;
-          }
-        }
-        sk = 1.0f;
-      }
+      const float sk = isk;
       // ---- tile max per head slot, online softmax
       float tmx[HS];
       bool grow = false;
@@ -1196,7 +1223,7 @@ __global__ void __launch_bounds__(kThreads, (rs_waves<KB, VB, NC, HS>())) decode
         l_part[hl] = __builtin_fmaf(p[0][hl], f0, __builtin_fmaf(p[1][hl], f1, l_part[hl]));
       }
       // ---- P' = p * v_scale into the value B layout
-      const float* vrow = my_vs + (i * 32 + ln) * NC;
+      const float* vrow = my_vs + ((i % ut) * 32 + ln) * NC;
 #pragma unroll
       for (int j = 0; j < NC; ++j) {
         if (j >= niter) break;
@@ -1228,14 +1255,13 @@ __global__ void __launch_bounds__(kThreads, (rs_waves<KB, VB, NC, HS>())) decode
         o[jb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, pb, o[jb], 0, 0, 0);
       }
       __builtin_amdgcn_wave_barrier();
-      if (kSlots == kUnitTiles) {
-        if (has_next) load_tile(un, i, i);
-      } else if (i + kSlots < ut) {
-        load_tile(u, i + kSlots, i % kSlots);
-      } else if (has_next) {
-        // ut is even here (2 or 4), so the next unit's tile lands in the
-        // same slot parity
-        load_tile(un, i + kSlots - ut, i % kSlots);
+      // refill the slot with the wave's tile kSlots places later
+      if (i + kSlots < kStep) {
+        const int uf = u + kWaves * ((i + kSlots) / ut);
+        if (uf < u_hi) load_tile(uf, (i + kSlots) % ut, i % kSlots);
+      } else {
+        const int uf = un + kWaves * ((i + kSlots - kStep) / ut);
+        if (uf < u_hi) load_tile(uf, (i + kSlots - kStep) % ut, i % kSlots);
       }
     }
     __builtin_amdgcn_wave_barrier();
@@ -1296,33 +1322,45 @@ bool rows_kernel(const kvq_kv_view& v, int Hq) {
 
 // Resident workgroups per compute unit of a row-score variant (the
 // occupancy the compiler's register and LDS use allows), cached.
-template <int KB, int VB, int NC>
-int rs_wgs_per_cu(int g) {
-  static int cached[2] = {0, 0};
-  int& c = cached[g == 1 ? 0 : 1];
+// Tiles per unit of the row-score kernel: four, or two or one when the key
+// group is shorter or not a multiple of four tiles.
+int rs_unit_tiles(const kvq_kv_view& v) {
+  const int tpg = v.group_tok / 32;
+  return tpg % 4 == 0 ? 4 : (tpg % 2 == 0 ? 2 : 1);
+}
+
+template <int KB, int VB, int NC, int HS>
+int rs_wgs_ut(int ut) {
+  static int cached[3] = {0, 0, 0};
+  int& c = cached[ut == 4 ? 2 : ut - 1];
   if (c == 0) {
     int n = 0;
     const hipError_t e =
-        g == 1 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_rs_kernel<KB, VB, NC, 1>, kThreads, 0)
-               : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_rs_kernel<KB, VB, NC, 2>, kThreads, 0);
+        ut == 4 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_rs_kernel<KB, VB, NC, HS, 4>, kThreads, 0)
+        : ut == 2 ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_rs_kernel<KB, VB, NC, HS, 2>, kThreads, 0)
+                  : hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_rs_kernel<KB, VB, NC, HS, 1>, kThreads, 0);
     c = (e == hipSuccess && n > 0) ? n : 2;
   }
   return c;
 }
+template <int KB, int VB, int NC>
+int rs_wgs_per_cu(int g, int ut) {
+  return g == 1 ? rs_wgs_ut<KB, VB, NC, 1>(ut) : rs_wgs_ut<KB, VB, NC, 2>(ut);
+}
 template <int KB, int VB>
-int rs_wgs_nc(int nc, int g) {
+int rs_wgs_nc(int nc, int g, int ut) {
   switch (nc) {
-    case 1: return rs_wgs_per_cu<KB, VB, 1>(g);
-    case 2: return rs_wgs_per_cu<KB, VB, 2>(g);
-    case 4: return rs_wgs_per_cu<KB, VB, 4>(g);
-    default: return rs_wgs_per_cu<KB, VB, 8>(g);
+    case 1: return rs_wgs_per_cu<KB, VB, 1>(g, ut);
+    case 2: return rs_wgs_per_cu<KB, VB, 2>(g, ut);
+    case 4: return rs_wgs_per_cu<KB, VB, 4>(g, ut);
+    default: return rs_wgs_per_cu<KB, VB, 8>(g, ut);
   }
 }
 int rs_wgs(const kvq_kv_view& v, int Hq) {
-  const int nc = kD / v.group_ch, g = Hq / v.kv_heads;
-  if (v.k_mixed) return v.v_bits == 2 ? rs_wgs_nc<0, 2>(nc, g) : rs_wgs_nc<0, 4>(nc, g);
-  if (v.k_bits == 4) return v.v_bits == 2 ? rs_wgs_nc<4, 2>(nc, g) : rs_wgs_nc<4, 4>(nc, g);
-  return v.v_bits == 2 ? rs_wgs_nc<2, 2>(nc, g) : rs_wgs_nc<2, 4>(nc, g);
+  const int nc = kD / v.group_ch, g = Hq / v.kv_heads, ut = rs_unit_tiles(v);
+  if (v.k_mixed) return v.v_bits == 2 ? rs_wgs_nc<0, 2>(nc, g, ut) : rs_wgs_nc<0, 4>(nc, g, ut);
+  if (v.k_bits == 4) return v.v_bits == 2 ? rs_wgs_nc<4, 2>(nc, g, ut) : rs_wgs_nc<4, 4>(nc, g, ut);
+  return v.v_bits == 2 ? rs_wgs_nc<2, 2>(nc, g, ut) : rs_wgs_nc<2, 4>(nc, g, ut);
 }
 int n_cus() {
   static int cached = 0;
@@ -1348,7 +1386,7 @@ int auto_splits(const kvq_kv_view& v, int Hq) {
   const int64_t streams = (int64_t)v.batch * v.kv_heads;
   int64_t sp, by_len;
   const int tpg = v.group_tok / 32;
-  const int ut = tpg < kUnitTiles ? tpg : kUnitTiles;
+  const int ut = rows_kernel(v, Hq) ? rs_unit_tiles(v) : (tpg < kUnitTiles ? tpg : kUnitTiles);
   const int64_t n_units = v.n_quant / (32 * ut);
   if (rows_kernel(v, Hq)) {
     const int64_t round = (int64_t)n_cus() * rs_wgs(v, Hq);
@@ -1369,15 +1407,27 @@ int fp16_parts(const kvq_kv_view& v) {
   return (int)((v.n_sink + v.n_tail + kRowsPerChunk - 1) / kRowsPerChunk);
 }
 
+template <int KB, int VB, int NC, int HS>
+void launch_rs(const MfmaArgs& a, int ut, dim3 grid, hipStream_t s) {
+  if (ut == 4)
+    decode_rs_kernel<KB, VB, NC, HS, 4><<<grid, kThreads, 0, s>>>(a);
+  else if (ut == 2)
+    decode_rs_kernel<KB, VB, NC, HS, 2><<<grid, kThreads, 0, s>>>(a);
+  else
+    decode_rs_kernel<KB, VB, NC, HS, 1><<<grid, kThreads, 0, s>>>(a);
+}
+
 template <int KB, int VB, int NC>
 hipError_t launch_t(const MfmaArgs& a, hipStream_t s) {
   dim3 grid((unsigned)a.n_parts, (unsigned)a.v.kv_heads, (unsigned)a.v.batch);
   const int g = a.Hq / a.v.kv_heads;
-  if (g == 1)
-    decode_rs_kernel<KB, VB, NC, 1><<<grid, kThreads, 0, s>>>(a);
-  else if (rows_kernel(a.v, a.Hq))
-    decode_rs_kernel<KB, VB, NC, 2><<<grid, kThreads, 0, s>>>(a);
-  else if constexpr (KB != 0)  // mixed keys run only in the row-score kernel
+  if (rows_kernel(a.v, a.Hq)) {
+    const int ut = rs_unit_tiles(a.v);
+    if (g == 1)
+      launch_rs<KB, VB, NC, 1>(a, ut, grid, s);
+    else
+      launch_rs<KB, VB, NC, 2>(a, ut, grid, s);
+  } else if constexpr (KB != 0)  // mixed keys run only in the row-score kernel
     decode_mfma_kernel<KB, VB, NC, false><<<grid, kThreads, 0, s>>>(a);
   return hipGetLastError();
 }
@@ -1411,7 +1461,10 @@ bool mfma_decode_eligible(const kvq_kv_view& v, int Hq) {
   }
   if (v.v_bits != 4 && v.v_bits != 2) return false;
   if (v.v_layout != KVQ_V_TILE32 || v.group_tok % 32 || v.n_quant % 32) return false;
-  if (v.group_tok > 32 * kUnitTiles && v.group_tok % (32 * kUnitTiles)) return false;
+  // the column kernel's units need groups of at most four tiles or whole
+  // multiples of four (the row-score kernel takes any multiple of a tile)
+  if (!rows_kernel(v, Hq) && v.group_tok > 32 * kUnitTiles && v.group_tok % (32 * kUnitTiles))
+    return false;
   if (v.n_quant < 32 || !v.k_gmax || v.n_quant / 32 > 0x7FFFFFFF) return false;
   const int nc = kD / v.group_ch;
   if (nc != 1 && nc != 2 && nc != 4 && nc != 8) return false;

@@ -204,6 +204,17 @@ CACHE_CASES = {
     "k4v2_g16_wide": (dict(D=128, S=0, G=128, Gv=128, R=128, k_bits=4,
                            v_bits=2), 1, 16, 1, 1300, [1300],
                       dict(outliers="per_head", n_out=2)),
+    # key groups that are not a multiple of four tiles: 3 tiles (one-tile
+    # units, three per group) and 6 tiles (two-tile units, three per group),
+    # and one-tile groups with a single query head per KV head
+    "k4v2_g96": (dict(D=128, S=1, G=96, Gv=32, R=96, k_bits=4, v_bits=2),
+                 1, 8, 2, 1500, [700, 800],
+                 dict(outliers="per_head", n_out=4, out_factor=15.0)),
+    "k2v4_g192": (dict(D=128, S=0, G=192, Gv=64, R=192, k_bits=2, v_bits=4),
+                  1, 4, 2, 2100, [2100], dict(outliers="none")),
+    "k2v2_g32_mha": (dict(D=128, S=1, G=32, Gv=128, R=32, k_bits=2,
+                          v_bits=2), 1, 2, 2, 1000, [1000],
+                     dict(outliers="fraction", frac=0.02, sink_factor=20.0)),
 }
 MIXED_CASES = {
     "mixkvq_small": (dict(D=128, S=0, G=128, Gv=64, R=128, k_bits=2,
