@@ -290,11 +290,15 @@ template <int KB, int VB, int NC, bool PACKED>
 __global__ void __launch_bounds__(kThreads, (PACKED && NC <= 4 && !(KB == 4 && VB == 4)) ? 3 : 2)
 decode_mfma_kernel(MfmaArgs a) {
   __shared__ __align__(16) unsigned char lds_raw[lds_bytes<NC>()];
-  const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
-  if (split >= a.n_splits) {
-    fp16_rows_partial(a, split - a.n_splits, split, kvh, b, *(RowsLds*)lds_raw);
+  // partial slots: the short fp16-row parts first (dispatched first, so they
+  // do not trail the long quantized splits), then the splits
+  const int slot = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  const int n_fp = a.n_parts - a.n_splits;
+  if (slot < n_fp) {
+    fp16_rows_partial(a, slot, slot, kvh, b, *(RowsLds*)lds_raw);
     return;
   }
+  const int split = slot - n_fp;
   MainLds<NC>& S = *(MainLds<NC>*)lds_raw;
   auto& sm_vs = S.vs;
   auto& sm_qf = S.qf;
@@ -320,9 +324,9 @@ decode_mfma_kernel(MfmaArgs a) {
   const int ut = tpg < kUnitTiles ? tpg : kUnitTiles;  // tiles per unit
   const int upg = tpg / ut;                         // units per group
   const int n_units = (int)(v.n_quant / (32 * ut));
-  const int per = (n_units + a.n_splits - 1) / a.n_splits;
-  const int u_lo = min(n_units, split * per);
-  const int u_hi = min(n_units, u_lo + per);
+  // units split as evenly as possible over the splits
+  const int u_lo = (int)((int64_t)split * n_units / a.n_splits);
+  const int u_hi = (int)((int64_t)(split + 1) * n_units / a.n_splits);
   const float* kg = v.k_gmax + s * v.k_gmax_stride;
 
   // This lane's query values on its key MFMA k-slots, times the inverse of
@@ -650,7 +654,7 @@ decode_mfma_kernel(MfmaArgs a) {
         }
       }
     }
-    a.partials[(((int64_t)b * a.Hq + kvh * g + h) * a.n_parts + split) * (kD + 2) + jx] = val;
+    a.partials[(((int64_t)b * a.Hq + kvh * g + h) * a.n_parts + slot) * (kD + 2) + jx] = val;
   }
 }
 
@@ -736,11 +740,15 @@ template <int KB, int VB, int NC, int HS, int UT>
 __global__ void __launch_bounds__(kThreads, (rs_waves<KB, VB, NC, HS>())) decode_rs_kernel(MfmaArgs a) {
   constexpr bool KM = KB == 0;  // mixed-precision keys
   __shared__ __align__(16) unsigned char lds_raw[rs_lds_bytes<NC, KM>()];
-  const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
-  if (split >= a.n_splits) {
-    fp16_rows_partial(a, split - a.n_splits, split, kvh, b, *(RowsLds*)lds_raw);
+  // partial slots: the short fp16-row parts first (dispatched first, so they
+  // do not trail the long quantized splits), then the splits
+  const int part = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  const int n_fp = a.n_parts - a.n_splits;
+  if (part < n_fp) {
+    fp16_rows_partial(a, part, part, kvh, b, *(RowsLds*)lds_raw);
     return;
   }
+  const int split = part - n_fp;
   RsLds<NC, KM>& S = *(RsLds<NC, KM>*)lds_raw;
   const kvq_kv_view& v = a.v;
   const int lane = threadIdx.x & 63;
@@ -767,9 +775,9 @@ __global__ void __launch_bounds__(kThreads, (rs_waves<KB, VB, NC, HS>())) decode
   constexpr int ut = UT;                               // tiles per unit
   const int upg = tpg / ut;                            // units per group
   const int n_units = (int)(v.n_quant / (32 * ut));
-  const int per = (n_units + a.n_splits - 1) / a.n_splits;
-  const int u_lo = min(n_units, split * per);
-  const int u_hi = min(n_units, u_lo + per);
+  // units split as evenly as possible over the splits
+  const int u_lo = (int)((int64_t)split * n_units / a.n_splits);
+  const int u_hi = (int)((int64_t)(split + 1) * n_units / a.n_splits);
   const float* kg = v.k_gmax + s * v.k_gmax_stride;
 
   const uint32_t* kc = v.k_codes + s * v.k_codes_stride;
@@ -1309,7 +1317,7 @@ __global__ void __launch_bounds__(kThreads, (rs_waves<KB, VB, NC, HS>())) decode
         }
       }
     }
-    a.partials[(((int64_t)b * a.Hq + kvh * g + h) * a.n_parts + split) * (kD + 2) + jx] = val;
+    a.partials[(((int64_t)b * a.Hq + kvh * g + h) * a.n_parts + part) * (kD + 2) + jx] = val;
   }
 }
 
@@ -1375,13 +1383,20 @@ int n_cus() {
   return cached;
 }
 
+int fp16_parts(const kvq_kv_view& v);
+
 // Splits per (batch, KV head).  Column kernel: about four workgroups per
 // compute unit (two resident, two rounds) and at least eight units per
-// wave.  Row-score kernel: one full round of resident workgroups (compute
-// units x resident per unit), or four rounds when that would leave more
-// than 48 tiles per wave (smaller workgroups balance better over the
-// compute units: at 1M tokens 3072 beat 768, 1024 and 6144), and at least
-// one unit per wave.
+// wave.  Row-score kernel: the resident workgroups (compute units x
+// resident per unit, fp16-row parts included) in one round, or in four
+// rounds when one round would leave more than 48 tiles per wave (smaller
+// workgroups balance better over the compute units: at 1M tokens 3072 beat
+// 768, 1024 and 6144), and at least one unit per wave.  In one round the
+// fp16-row parts either take slots of their own, so that every workgroup is
+// resident at once, or keep none: they are dispatched first and the last
+// splits start when they end.  The second is taken when the shorter splits
+// save more than one fp16-row part takes (estimates: 2 us per tile per
+// wave, 10 us per fp16-row part).
 int auto_splits(const kvq_kv_view& v, int Hq) {
   const int64_t streams = (int64_t)v.batch * v.kv_heads;
   int64_t sp, by_len;
@@ -1390,8 +1405,16 @@ int auto_splits(const kvq_kv_view& v, int Hq) {
   const int64_t n_units = v.n_quant / (32 * ut);
   if (rows_kernel(v, Hq)) {
     const int64_t round = (int64_t)n_cus() * rs_wgs(v, Hq);
-    sp = (round + streams - 1) / streams;
-    if (v.n_quant / 32 > sp * kWaves * 48) sp = (4 * round + streams - 1) / streams;
+    const int64_t fp = fp16_parts(v);
+    const double tiles = (double)(v.n_quant / 32);
+    auto wave_tiles = [&](int64_t n) { return tiles / (double)(n * kWaves); };
+    const int64_t slots = round / streams > 1 ? round / streams : 1;
+    sp = slots - fp;
+    if (sp < 1 || (fp > 0 && 2.0 * (wave_tiles(sp) - wave_tiles(slots)) > 10.0)) sp = slots;
+    if (wave_tiles(sp) > 48.0) {
+      sp = 4 * round / streams - fp;
+      if (sp < 1) sp = 1;
+    }
     by_len = n_units / kWaves;
   } else {
     sp = (1024 + streams - 1) / streams;
