@@ -148,6 +148,28 @@ struct MfmaArgs {
   int n_splits;
 };
 
+// One-dimensional grid: the short fp16-row parts of every stream first
+// (dispatched first, so that none of them trails the long quantized
+// splits), then the splits; partial slot = fp16 chunk, or n_fp + split.
+struct PartIndex {
+  int part, kvh, b;
+};
+__device__ inline PartIndex part_index(const MfmaArgs& a) {
+  const int64_t L = blockIdx.x;
+  const int n_fp = a.n_parts - a.n_splits;
+  const int64_t n_fp_all = (int64_t)a.v.batch * a.v.kv_heads * n_fp;
+  int64_t s;
+  int part;
+  if (L < n_fp_all) {
+    s = L / n_fp;
+    part = (int)(L % n_fp);
+  } else {
+    s = (L - n_fp_all) / a.n_splits;
+    part = n_fp + (int)((L - n_fp_all) % a.n_splits);
+  }
+  return PartIndex{part, (int)(s % a.v.kv_heads), (int)(s / a.v.kv_heads)};
+}
+
 // A work unit of one wave: up to 4 tiles (128 tokens) of one key group.
 constexpr int kUnitTiles = 4;
 constexpr int kRowsPerChunk = 64;  // fp16 sink/tail rows per extra workgroup
@@ -290,9 +312,8 @@ template <int KB, int VB, int NC, bool PACKED>
 __global__ void __launch_bounds__(kThreads, (PACKED && NC <= 4 && !(KB == 4 && VB == 4)) ? 3 : 2)
 decode_mfma_kernel(MfmaArgs a) {
   __shared__ __align__(16) unsigned char lds_raw[lds_bytes<NC>()];
-  // partial slots: the short fp16-row parts first (dispatched first, so they
-  // do not trail the long quantized splits), then the splits
-  const int slot = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  const PartIndex pi = part_index(a);
+  const int slot = pi.part, kvh = pi.kvh, b = pi.b;
   const int n_fp = a.n_parts - a.n_splits;
   if (slot < n_fp) {
     fp16_rows_partial(a, slot, slot, kvh, b, *(RowsLds*)lds_raw);
@@ -740,9 +761,8 @@ template <int KB, int VB, int NC, int HS, int UT>
 __global__ void __launch_bounds__(kThreads, (rs_waves<KB, VB, NC, HS>())) decode_rs_kernel(MfmaArgs a) {
   constexpr bool KM = KB == 0;  // mixed-precision keys
   __shared__ __align__(16) unsigned char lds_raw[rs_lds_bytes<NC, KM>()];
-  // partial slots: the short fp16-row parts first (dispatched first, so they
-  // do not trail the long quantized splits), then the splits
-  const int part = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  const PartIndex pi = part_index(a);
+  const int part = pi.part, kvh = pi.kvh, b = pi.b;
   const int n_fp = a.n_parts - a.n_splits;
   if (part < n_fp) {
     fp16_rows_partial(a, part, part, kvh, b, *(RowsLds*)lds_raw);
@@ -1442,7 +1462,7 @@ void launch_rs(const MfmaArgs& a, int ut, dim3 grid, hipStream_t s) {
 
 template <int KB, int VB, int NC>
 hipError_t launch_t(const MfmaArgs& a, hipStream_t s) {
-  dim3 grid((unsigned)a.n_parts, (unsigned)a.v.kv_heads, (unsigned)a.v.batch);
+  dim3 grid((unsigned)((int64_t)a.n_parts * a.v.kv_heads * a.v.batch));
   const int g = a.Hq / a.v.kv_heads;
   if (rows_kernel(a.v, a.Hq)) {
     const int ut = rs_unit_tiles(a.v);
@@ -1505,6 +1525,7 @@ hipError_t launch_decode_mfma(const kvq_kv_view& v, const void* q, int f16, int 
                               hipStream_t s) {
   const int fp = fp16_parts(v);
   const int n_splits = n_parts - fp;
+  if ((int64_t)n_parts * v.kv_heads * v.batch > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
   MfmaArgs a{v, q, f16, Hq, sm_scale * kLog2e, partials, n_parts, n_splits};
   const int nc = kD / v.group_ch;
   hipError_t e;
