@@ -99,6 +99,27 @@ def stream_bytes(view, hq):
     return view.batch * view.kv_heads * per_stream + view.batch * hq * D * 2
 
 
+def read_ceiling(torch, kvq, dev, stream, gib=4, reps=5):
+    """GB/s of the library's plain streaming-read kernel over `gib` GiB
+    (median of `reps` event-timed launches after two untimed ones)."""
+    buf = torch.empty(gib << 30, dtype=torch.uint8, device=dev)
+    sink = torch.empty(2048, dtype=torch.int32, device=dev)
+    for _ in range(2):
+        kvq.kvq_stream_read(buf, sink)
+    ts = []
+    for _ in range(reps):
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        kvq.kvq_stream_read(buf, sink)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1))
+    del buf, sink
+    torch.cuda.empty_cache()
+    return (gib << 30) / (float(np.median(ts)) * 1e-3) / 1e9
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -281,6 +302,7 @@ def main():
         1000.0 * wall / args.steps
     dec_ms = [e[0].elapsed_time(e[1]) for st in dec_events for e in st]
     dec_avg_ms = float(np.mean(dec_ms))
+    ceiling = read_ceiling(torch, kvq, dev, stream)
     bytes_launch = bytes_step / len(caches)
     achieved = bytes_launch / (dec_avg_ms * 1e-3) / 1e9
     value = bytes_step / (ms_per_step * 1e-3) / 1e9
@@ -297,6 +319,18 @@ def main():
         "us_per_step": round(1000 * ms_per_step, 1),
         "pct_of_hbm_peak": round(100 * value / PEAK_GBS, 1),
         "tokens_per_s": round(B * 1000.0 / ms_per_step, 2),
+        "context_tokens_per_s": round(
+            sum(v.batch * (v.n_sink + v.n_quant + v.n_tail) for v in views)
+            * 1000.0 / ms_per_step, 1),
+        "decode_call_us": {
+            "mean": round(1000 * dec_avg_ms, 2),
+            "median": round(1000 * float(np.median(dec_ms)), 2),
+            "p10": round(1000 * float(np.percentile(dec_ms, 10)), 2),
+            "p90": round(1000 * float(np.percentile(dec_ms, 90)), 2),
+            "calls": len(dec_ms)},
+        "read_ceiling": {"value": round(ceiling, 1), "unit": "GB/s",
+                         "bytes": 4 << 30, "kernel": "kvq_stream_read"},
+        "pct_of_read_ceiling": round(100 * value / ceiling, 1),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -310,10 +344,11 @@ def main():
             "unit": "GB/s",
             "frac": round(achieved / PEAK_GBS, 4),
             "traffic": measured_traffic(args.workload),
-            "kernel": "kvq_decode_attention (decode_mfma_kernel + fp16 "
-                      "sink/tail partials + merge)",
+            "kernel": "kvq_decode_attention (decode_rs_kernel: quantized "
+                      "splits + fp16 sink/tail parts; then merge_kernel)",
             "bytes_per_launch": int(bytes_launch),
             "avg_launch_us": round(1000 * dec_avg_ms, 2),
+            "frac_of_read_ceiling": round(achieved / ceiling, 4),
         },
         "bytes_per_step": int(bytes_step),
     }

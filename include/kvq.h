@@ -288,6 +288,14 @@ const char* kvq_strerror(kvq_status s);
 kvq_status kvq_fill_u32(uint32_t* dst, uint32_t value, int64_t n,
                         void* stream);
 
+/* Measured streaming-read ceiling: one launch of a plain read kernel over
+ * `bytes` (a multiple of 16) of device memory at src (16-byte aligned);
+ * each of the 2048 workgroups reads a contiguous share with 16-byte loads
+ * and writes one word to sink (2048 uint32, device).  Time it with events
+ * to compare the decode kernel with what a bare read reaches.          */
+kvq_status kvq_stream_read(const void* src, int64_t bytes, uint32_t* sink,
+                           void* stream);
+
 /* Seeded synthetic fp16 data for benchmarks too large to draw on the host:
  * element (head, token, channel) of `tensor` (0 K, 1 V, 2 q) in `layer` is
  * the counter-th output of a SplitMix64 stream (Steele, Lea and Flood,

@@ -397,6 +397,12 @@ kvq_status kvq_fill_u32(uint32_t* dst, uint32_t value, int64_t n, void* stream) 
   return hip_status(launch_fill_u32(dst, value, n, (hipStream_t)stream));
 }
 
+kvq_status kvq_stream_read(const void* src, int64_t bytes, uint32_t* sink, void* stream) {
+  if (bytes < 0 || bytes % 16 || (bytes > 0 && (!src || !aligned(src, 16) || !sink || !aligned(sink, 4))))
+    return KVQ_E_ARG;
+  return hip_status(launch_stream_read(src, bytes, sink, (hipStream_t)stream));
+}
+
 kvq_status kvq_synth_normal_f16(void* out, uint64_t seed, int tensor, int layer, int head0,
                                 int n_heads, int64_t t0, int64_t n_tok, int d,
                                 int64_t head_stride, void* stream) {

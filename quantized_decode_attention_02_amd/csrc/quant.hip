@@ -186,6 +186,28 @@ __global__ void fill_u32_kernel(uint32_t* dst, uint32_t v, int64_t n) {
        i += (int64_t)gridDim.x * blockDim.x)
     dst[i] = v;
 }
+// Streaming read: block b reads its contiguous share of src with 16-byte
+// loads, four in flight per thread, and stores the XOR of what it read to
+// sink[b] (so the loads cannot be dropped).
+__global__ void __launch_bounds__(256) stream_read_kernel(const uint4* __restrict__ src, int64_t n16,
+                                                          uint32_t* sink) {
+  const int64_t per = (n16 + gridDim.x - 1) / gridDim.x;
+  const int64_t lo = (int64_t)blockIdx.x * per;
+  const int64_t hi = lo + per < n16 ? lo + per : n16;
+  uint32_t x = 0;
+  for (int64_t i = lo + threadIdx.x; i < hi; i += 4 * 256) {
+    uint4 a = src[i];
+    uint4 b = i + 256 < hi ? src[i + 256] : make_uint4(0, 0, 0, 0);
+    uint4 c = i + 512 < hi ? src[i + 512] : make_uint4(0, 0, 0, 0);
+    uint4 d = i + 768 < hi ? src[i + 768] : make_uint4(0, 0, 0, 0);
+    x ^= a.x ^ a.y ^ a.z ^ a.w ^ b.x ^ b.y ^ b.z ^ b.w ^ c.x ^ c.y ^ c.z ^ c.w ^ d.x ^ d.y ^ d.z ^ d.w;
+  }
+  for (int o = 1; o < 64; o <<= 1) x ^= __shfl_xor(x, o);
+  __shared__ uint32_t red[4];
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
+  __syncthreads();
+  if (threadIdx.x == 0) sink[blockIdx.x] = red[0] ^ red[1] ^ red[2] ^ red[3];
+}
 __global__ void fill_f64_kernel(double* dst, double v, int64_t n) {
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
        i += (int64_t)gridDim.x * blockDim.x)
@@ -716,6 +738,12 @@ hipError_t launch_dequant(const uint32_t* codes, const float* scales,
 hipError_t launch_fill_u32(uint32_t* dst, uint32_t v, int64_t n, hipStream_t s) {
   if (n <= 0) return hipSuccess;
   fill_u32_kernel<<<grid_for(n, 256), 256, 0, s>>>(dst, v, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_stream_read(const void* src, int64_t bytes, uint32_t* sink, hipStream_t s) {
+  if (bytes <= 0) return hipSuccess;
+  stream_read_kernel<<<kStreamReadBlocks, 256, 0, s>>>((const uint4*)src, bytes / 16, sink);
   return hipGetLastError();
 }
 

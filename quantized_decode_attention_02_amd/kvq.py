@@ -25,7 +25,7 @@ EXPORTED = [
     "kvq_cache_bytes", "kvq_cache_init", "kvq_cache_free", "kvq_cache_tokens",
     "kvq_append", "kvq_salience_select", "kvq_cache_check", "kvq_cache_view",
     "kvq_export", "kvq_decode_workspace_bytes", "kvq_decode_attention",
-    "kvq_poll_error", "kvq_strerror", "kvq_fill_u32", "kvq_synth_normal_f16",
+    "kvq_poll_error", "kvq_strerror", "kvq_fill_u32", "kvq_synth_normal_f16", "kvq_stream_read",
 ]
 
 _c_i32, _c_i64, _c_u64, _c_p, _c_f = (ctypes.c_int32, ctypes.c_int64,
@@ -115,6 +115,7 @@ def lib():
         "kvq_poll_error": (_c_i32, [_c_p, _c_p]),
         "kvq_strerror": (ctypes.c_char_p, [_c_i32]),
         "kvq_fill_u32": (_c_i32, [_c_p, ctypes.c_uint32, _c_i64, _c_p]),
+        "kvq_stream_read": (_c_i32, [_c_p, _c_i64, _c_p, _c_p]),
         "kvq_synth_normal_f16": (_c_i32, [_c_p, _c_u64, _c_i32, _c_i32,
                                           _c_i32, _c_i32, _c_i64, _c_i64,
                                           _c_i32, _c_i64, _c_p]),
@@ -224,6 +225,18 @@ def kvq_synth_normal_f16(out, seed, tensor, layer, head0, n_heads, t0, n_tok,
                                       n_heads, t0, n_tok, d, head_stride,
                                       _stream()), "kvq_synth_normal_f16")
     return out
+
+
+def kvq_stream_read(buf, sink):
+    """One launch of the plain streaming-read kernel over the bytes of buf
+    (a device tensor); sink: device tensor of at least 2048 int32."""
+    _need_cuda(buf)
+    _need_cuda(sink)
+    n = buf.numel() * buf.element_size()
+    if sink.numel() * sink.element_size() < 2048 * 4:
+        raise ValueError("sink needs 2048 words")
+    _check(lib().kvq_stream_read(_ptr(buf), n - n % 16, _ptr(sink), _stream()),
+           "kvq_stream_read")
 
 
 class Cache:
