@@ -704,7 +704,10 @@ struct RsLds {
   float vs[kWaves][kUnitTiles * 32 * NC];
   float ks[kWaves][kD];
   float4v qf[8][64];
-  float qs[KM ? 8 : 1][kD];           // mixed keys: q * sm_scale * log2(e) * sigma_q
+  // mixed keys: q * sm_scale * log2(e) * sigma_q by channel; rows padded
+  // to 132 floats so that the heads of one channel fall in distinct banks
+  // (the Q' gather reads one channel of up to eight heads per instruction)
+  float qs[KM ? 8 : 1][kD + 4];
   uint16_t inv[kWaves][KM ? kD + 8 : 8];  // mixed keys: 4 x channel of each slot, then bf16 ones
   float m[kWaves][8];
   float l[kWaves][8];
