@@ -541,6 +541,207 @@ flush_kernel(CacheDev c, FlushSrc f) {
   if (bad) atomicOr(c.err, 1u);
 }
 
+// ---------------------------------------------------------------------------
+// Register-resident flush for the common layouts: uniform keys and values of
+// 2, 4 or 8 bits, D a power of two in [8, 256], value groups of at least 8
+// channels, and at most kRegRows rows of the key group per thread.  Thread
+// (slice sl, 8-channel chunk c8) loads rows sl, sl + slices, ... of the group
+// (keys and values, fp16) into registers in one round of requests; the
+// absmax reductions work on fp16 magnitudes (max is exact in any format).
+//
+// Codes: rint(x / s) is taken as rint(x * rcp(s)) unless that product lies
+// within 2^-13 of a rounding boundary, where the IEEE quotient decides.
+// Here |x / s| <= qmax * (1 + 2^-23) < 128 (s is the rounded absmax / qmax of
+// x's own group), v_rcp_f32 is within 1 ulp and the multiply rounds once, so
+// the product differs from the rounded quotient by less than 128 * 2^-22 =
+// 2^-15: outside the band both lie strictly between the same two
+// half-integers and round to the same integer.  A NaN product takes the
+// division too, so every code equals the division's.
+// ---------------------------------------------------------------------------
+constexpr int kRegRows = 8;
+constexpr float kNearTie = 0.5f - 0x1p-13f;
+
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+
+__device__ inline uint32_t max_u16x2(uint32_t a, uint32_t b) {
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(__builtin_bit_cast(u16x2, a),
+                                                                __builtin_bit_cast(u16x2, b)));
+}
+// per-lane max of |x| over the eight fp16 values of w (fp16 bits)
+__device__ inline uint32_t absmax8(uint4 w) {
+  const uint32_t m = max_u16x2(max_u16x2(w.x & 0x7FFF7FFFu, w.y & 0x7FFF7FFFu),
+                               max_u16x2(w.z & 0x7FFF7FFFu, w.w & 0x7FFF7FFFu));
+  return max(m & 0xFFFFu, m >> 16);
+}
+
+// Offset-binary codes of the eight fp16 values of w at BITS bits, field j at
+// bit FW * j of the 64-bit result (x: fields 0..31, y: 32..63).
+template <int BITS, int FW>
+__device__ inline uint2 encode8(uint4 w, const float* s, const float* rc) {
+  constexpr int qmax = (1 << (BITS - 1)) - 1;
+  const uint32_t wv[4] = {w.x, w.y, w.z, w.w};
+  float x[8], q[8];
+  bool slow = false;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    x[j] = h2f((uint16_t)(wv[j >> 1] >> (16 * (j & 1))));
+    const float y = x[j] * rc[j];
+    q[j] = rintf(y);
+    slow |= !(fabsf(y - q[j]) < kNearTie);
+  }
+  if (slow) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) q[j] = rintf(__fdiv_rn(x[j], s[j]));
+  }
+  uint2 out = {0u, 0u};
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const float cq = fminf(fmaxf(q[j], (float)-qmax), (float)qmax);
+    const uint32_t code = (uint32_t)((int)cq + qmax + 1);
+    if (FW * j < 32) out.x |= code << (FW * j);
+    else out.y |= code << (FW * j - 32);
+  }
+  return out;
+}
+
+// stores the eight codes of one row chunk (packed at BITS bits) at chunk c8
+template <int BITS>
+__device__ inline void store_codes8(uint32_t* row, int c8, uint2 code) {
+  if (BITS == 2) ((uint16_t*)row)[c8] = (uint16_t)code.x;
+  else if (BITS == 4) row[c8] = code.x;
+  else ((uint2*)row)[c8] = code;
+}
+
+template <int KB, int VB>
+__global__ void __launch_bounds__(kThreads)
+__attribute__((amdgpu_waves_per_eu(4)))
+flush_reg_kernel(CacheDev c, FlushSrc f, int lg_cpr, int lg_gv8) {
+  __shared__ __align__(16) uint16_t kmag[kThreads * 8];         // [slice][channel] |k| maxima
+  __shared__ __align__(16) float ksc[kMaxD];                    // key scale per channel
+  __shared__ __align__(16) uint8_t vst[kRegRows * kThreads * 8];  // value codes [row][channel]
+  constexpr int qk = (1 << (KB - 1)) - 1, qv = (1 << (VB - 1)) - 1;
+  const int tid = threadIdx.x;
+  const int D = c.D, G = c.G;
+  const int slices = kThreads >> lg_cpr;
+  const int c8 = tid & ((1 << lg_cpr) - 1), sl = tid >> lg_cpr;
+  const int64_t st = (int64_t)blockIdx.z * c.H + blockIdx.y;
+  const int64_t grp = f.nq_old / G + blockIdx.x;
+  const int64_t p0 = grp * G;
+  // rows p < ring_end sit in the tail ring (R is a multiple of G, so the
+  // group's ring rows are contiguous from slot p0 % R); later ones in the input
+  const int64_t ring_end = f.nq_old + f.nt_old;
+  const int64_t ring0 = st * c.s_tail + (p0 % c.R) * D + 8 * c8;
+  const int64_t in0 = (st * f.n_new + f.take + (p0 - ring_end)) * D + 8 * c8;
+  // rows past the group's end load its last row again: a repeated row leaves
+  // every maximum unchanged, and its codes are not stored
+  uint4 kr[kRegRows], vr[kRegRows];
+#pragma unroll
+  for (int k = 0; k < kRegRows; ++k) {
+    const int r = min(sl + k * slices, G - 1);
+    const bool ring = p0 + r < ring_end;
+    const int64_t at = (ring ? ring0 : in0) + (int64_t)r * D;
+    kr[k] = *(const uint4*)((ring ? c.tail_k : f.k_in) + at);
+    vr[k] = *(const uint4*)((ring ? c.tail_v : f.v_in) + at);
+  }
+  // ---- keys, pass 1: per-channel absmax over the group
+  {
+    uint32_t m[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int k = 0; k < kRegRows; ++k) {
+      m[0] = max_u16x2(m[0], kr[k].x & 0x7FFF7FFFu);
+      m[1] = max_u16x2(m[1], kr[k].y & 0x7FFF7FFFu);
+      m[2] = max_u16x2(m[2], kr[k].z & 0x7FFF7FFFu);
+      m[3] = max_u16x2(m[3], kr[k].w & 0x7FFF7FFFu);
+    }
+    *(uint4*)&kmag[sl * D + 8 * c8] = make_uint4(m[0], m[1], m[2], m[3]);
+  }
+  __syncthreads();
+  bool bad = false;
+  if (tid < D) {
+    uint32_t m = 0;
+    for (int q = 0; q < slices; ++q) m = max(m, (uint32_t)kmag[q * D + tid]);
+    bad = m >= 0x7C00u;
+    const float s = group_scale(h2f((uint16_t)m), qk);
+    ksc[tid] = s;
+    c.k_scales[st * c.s_k_scales + grp * D + tid] = s;
+  }
+  __syncthreads();
+  // bound on |k_hat| / code of the group: the largest channel scale
+  if (tid < 64) {
+    float g = 0.0f;
+    for (int ch = tid; ch < D; ch += 64) g = fmaxf(g, ksc[ch]);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) g = fmaxf(g, __shfl_xor(g, o));
+    if (tid == 0) c.k_gmax[st * c.s_k_gmax + grp] = g;
+  }
+  // ---- keys, pass 2
+  {
+    float s[8], rc[8];
+    const float4 a = *(const float4*)&ksc[8 * c8], b = *(const float4*)&ksc[8 * c8 + 4];
+    s[0] = a.x; s[1] = a.y; s[2] = a.z; s[3] = a.w;
+    s[4] = b.x; s[5] = b.y; s[6] = b.z; s[7] = b.w;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) rc[j] = __builtin_amdgcn_rcpf(s[j]);
+    const int wk = D * KB / 32;
+    uint32_t* krow = c.k_codes + st * c.s_k_codes + p0 * wk;
+#pragma unroll
+    for (int k = 0; k < kRegRows; ++k) {
+      const int r = sl + k * slices;
+      if (r < G) store_codes8<KB>(krow + (int64_t)r * wk, c8, encode8<KB, KB>(kr[k], s, rc));
+    }
+  }
+  // ---- values: per-token group scales over 2^lg_gv8 adjacent lanes
+  const bool tiles = c.v_layout == KVQ_V_TILE32;
+  const int ngv = D / c.Gv, wv = D * VB / 32;
+  const int gmask = (1 << lg_gv8) - 1;
+  uint32_t vbad = 0;
+#pragma unroll
+  for (int k = 0; k < kRegRows; ++k) {
+    const int r = sl + k * slices;
+    uint32_t m = absmax8(vr[k]);
+    if (r < G) vbad = max(vbad, m);
+    for (int o = 1; o <= gmask; o <<= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o));
+    if (r < G) {
+      const float sv = group_scale(h2f((uint16_t)m), qv);
+      const float rv = __builtin_amdgcn_rcpf(sv);
+      const float s[8] = {sv, sv, sv, sv, sv, sv, sv, sv};
+      const float rc[8] = {rv, rv, rv, rv, rv, rv, rv, rv};
+      const int64_t p = p0 + r;
+      if ((c8 & gmask) == 0) c.v_scales[st * c.s_v_scales + p * ngv + (c8 >> lg_gv8)] = sv;
+      if (tiles)
+        *(uint2*)&vst[r * D + 8 * c8] = encode8<VB, 8>(vr[k], s, rc);
+      else
+        store_codes8<VB>(c.v_codes + st * c.s_v_codes + p * wv, c8, encode8<VB, VB>(vr[k], s, rc));
+    }
+  }
+  bad |= vbad >= 0x7C00u;
+  if (tiles) {
+    // 32-token tiles of the group (G and p0 are multiples of 32): word w of
+    // lane l holds the fields that v_tile_field places there
+    __syncthreads();
+    const int lg_nw = lg_cpr + 3 + (VB == 4 ? 2 : 1);  // log2(D * VB)
+    const int Wl = D * VB / 64;
+    const int lg_c = Wl >= 4 ? 2 : (Wl == 2 ? 1 : 0);  // C = min(Wl, 4)
+    const int n = (G >> 5) << lg_nw;
+    uint32_t* tile0 = c.v_codes + st * c.s_v_codes + (p0 >> 5) * (int64_t)(D * VB);
+    for (int i = tid; i < n; i += kThreads) {
+      const int T = i >> lg_nw, rem = i & ((1 << lg_nw) - 1);
+      const int chunk = rem >> (6 + lg_c), rr = rem & ((64 << lg_c) - 1);
+      const int l = rr >> lg_c, w = (chunk << lg_c) + (rr & ((1 << lg_c) - 1));
+      const uint8_t* base = vst + T * 32 * D;
+      uint32_t word = 0;
+#pragma unroll
+      for (int p = 0; p < 32 / VB; ++p) {
+        int tau, ch;
+        v_tile_field(l, w, p, VB, &tau, &ch);
+        word |= (uint32_t)base[tau * D + ch] << (p * VB);
+      }
+      tile0[i] = word;
+    }
+  }
+  if (bad) atomicOr(c.err, 1u);
+}
+
 // I[b][kvh][d] = sum over rows r and grouped heads h of |q_win[b][r][h][d]|.
 __global__ void salience_kernel(CacheDev c, const uint16_t* __restrict__ q,
                                 int w_rows, int Hq) {
@@ -775,6 +976,22 @@ hipError_t launch_flush(const CacheDev& c, const uint16_t* k_in,
   if (n_groups <= 0) return hipSuccess;
   FlushSrc f{k_in, v_in, n_new, take, nq_old, nt_old};
   dim3 grid((unsigned)n_groups, (unsigned)c.H, (unsigned)c.B);
+  auto b248 = [](int b) { return b == 2 || b == 4 || b == 8; };
+  const int D = c.D;
+  if (!c.mixed && b248(c.k_bits) && b248(c.v_bits) && D >= 8 && (D & (D - 1)) == 0 &&
+      c.Gv >= 8 && c.G <= kRegRows * (kThreads / (D / 8)) &&
+      (((uintptr_t)k_in | (uintptr_t)v_in) % 16) == 0) {
+    const int lg_cpr = __builtin_ctz(D / 8), lg_gv8 = __builtin_ctz(c.Gv / 8);
+#define KVQ_FLUSH_REG(KB, VB)                                                   \
+  if (c.k_bits == KB && c.v_bits == VB) {                                       \
+    flush_reg_kernel<KB, VB><<<grid, kThreads, 0, s>>>(c, f, lg_cpr, lg_gv8);   \
+    return hipGetLastError();                                                   \
+  }
+    KVQ_FLUSH_REG(2, 2) KVQ_FLUSH_REG(2, 4) KVQ_FLUSH_REG(2, 8)
+    KVQ_FLUSH_REG(4, 2) KVQ_FLUSH_REG(4, 4) KVQ_FLUSH_REG(4, 8)
+    KVQ_FLUSH_REG(8, 2) KVQ_FLUSH_REG(8, 4) KVQ_FLUSH_REG(8, 8)
+#undef KVQ_FLUSH_REG
+  }
   if (c.D <= 128)
     flush_kernel<128><<<grid, kThreads, 0, s>>>(c, f);
   else

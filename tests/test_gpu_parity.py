@@ -380,6 +380,63 @@ def test_append_determinism_and_capacity():
     assert e.value.status == kvq.KVQ_E_CAPACITY
 
 
+# Rounding ties: each key channel's absmax (first row of every key group)
+# and each value group's absmax (its first channel) is qmax * 2^e, so the
+# scales are exactly 2^e, and every other value is a multiple of 2^(e-1): many
+# quotients land exactly on k + 1/2, where round-half-even decides, and the
+# rest one fp16 ulp either side of a tie.  (D, G, Gv, R, k_bits, v_bits, S,
+# append chunks); the first three take the register-resident flush kernel,
+# the last the general one.
+TIE_CASES = {
+    "k4v2_d128_g128": (128, 128, 32, 128, 4, 2, 1, [300, 1, 400, 63]),
+    "k2v4_d64_g32": (64, 32, 16, 64, 2, 4, 0, [100, 157]),
+    "k8v8_d128_g64": (128, 64, 8, 64, 8, 8, 2, [260]),
+    "k3v3_d64_g32": (64, 32, 16, 32, 3, 3, 1, [129, 64]),
+}
+
+
+def tie_inputs(seed, B, H, N, D, G, Gv, kb, vb, S):
+    rng = np.random.default_rng(seed)
+    qk, qv = (1 << (kb - 1)) - 1, (1 << (vb - 1)) - 1
+    e = 2.0 ** rng.integers(-6, 3, size=(B, H, 1, 1))
+    k = rng.integers(-2 * qk, 2 * qk + 1, size=(B, H, N, D)) / 2 * e
+    v = rng.integers(-2 * qv, 2 * qv + 1, size=(B, H, N, D)) / 2 * e
+    k[:, :, S::G, :] = qk * e
+    v[..., ::Gv] = qv * e
+    k, v = k.astype(np.float16), v.astype(np.float16)
+    for x in (k, v):  # a quarter of the other values one ulp off
+        bits = x.view(np.uint16)
+        near = rng.random(x.shape) < 0.25
+        near[:, :, S::G, :] = False
+        near[..., ::Gv] = False
+        near &= (bits & 0x7FFF) != 0
+        bits[near] += rng.choice(np.array([1, -1], dtype=np.int16),
+                                 size=int(near.sum())).astype(np.uint16)
+    return k, v
+
+
+@pytest.mark.parametrize("name", list(TIE_CASES))
+def test_cache_parity_ties(name):
+    D, G, Gv, R, kb, vb, S, chunks = TIE_CASES[name]
+    B, H = 2, 2
+    N = sum(chunks)
+    say("tie case", name)
+    k, v = tie_inputs(11, B, H, N, D, G, Gv, kb, vb, S)
+    oc = ocache.Cache(ocache.CacheConfig(B=B, Hkv=H, D=D, S=S, R=R, G=G,
+                                         Gv=Gv, k_bits=kb, v_bits=vb))
+    gc = kvq.Cache(B, H, D, N + 64, kb, vb, G, Gv, R, S=S)
+    t = 0
+    for n in chunks:
+        oc.append(k[:, :, t:t + n], v[:, :, t:t + n])
+        gc.kvq_append(torch.from_numpy(np.ascontiguousarray(
+            k[:, :, t:t + n])).to(DEV), torch.from_numpy(
+            np.ascontiguousarray(v[:, :, t:t + n])).to(DEV))
+        t += n
+    assert gc.kvq_cache_check() == kvq.KVQ_OK
+    view = compare_exports(oc, gc)
+    assert view.n_quant >= 2 * G
+
+
 def test_cache_nonfinite_poisons():
     c = kvq.Cache(1, 1, 32, 100, 4, 2, 8, 16, 8)
     k = torch.ones((1, 1, 20, 32), dtype=torch.float16, device=DEV)
