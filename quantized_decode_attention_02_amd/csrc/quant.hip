@@ -576,32 +576,52 @@ __device__ inline uint32_t absmax8(uint4 w) {
 
 // Offset-binary codes of the eight fp16 values of w at BITS bits, field j at
 // bit FW * j of the 64-bit result (x: fields 0..31, y: 32..63).
+//
+// fma(x, rc, M) with M = 1.5 * 2^23 + qmax + 1 rounds the exact product
+// x * rc to an integer n (ties to even, M being even) and leaves n + qmax + 1,
+// the code, in the low mantissa bits; the second fma gives x * rc - n to
+// within 2^-25.  No clamp is needed: |x * rc| <= qmax * (1 + 2^-22) rounds to
+// at most qmax.  v_alignbit shifts each code in from the top and drops the
+// exponent bits above it.
 template <int BITS, int FW>
 __device__ inline uint2 encode8(uint4 w, const float* s, const float* rc) {
   constexpr int qmax = (1 << (BITS - 1)) - 1;
+  constexpr float M = 12582912.0f + (float)(qmax + 1);
   const uint32_t wv[4] = {w.x, w.y, w.z, w.w};
-  float x[8], q[8];
-  bool slow = false;
+  float t[8];
+  float dmax = 0.0f;
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    x[j] = h2f((uint16_t)(wv[j >> 1] >> (16 * (j & 1))));
-    const float y = x[j] * rc[j];
-    q[j] = rintf(y);
-    slow |= !(fabsf(y - q[j]) < kNearTie);
+    const float x = h2f((uint16_t)(wv[j >> 1] >> (16 * (j & 1))));
+    t[j] = __builtin_fmaf(x, rc[j], M);
+    dmax = fmaxf(dmax, fabsf(__builtin_fmaf(x, rc[j], -(t[j] - M))));
   }
-  if (slow) {
+  if (!(dmax < kNearTie)) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) q[j] = rintf(__fdiv_rn(x[j], s[j]));
+    for (int j = 0; j < 8; ++j) {
+      const float x = h2f((uint16_t)(wv[j >> 1] >> (16 * (j & 1))));
+      t[j] = rintf(__fdiv_rn(x, s[j])) + M;
+    }
   }
-  uint2 out = {0u, 0u};
+  uint32_t acc[2] = {0u, 0u};
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
-    const float cq = fminf(fmaxf(q[j], (float)-qmax), (float)qmax);
-    const uint32_t code = (uint32_t)((int)cq + qmax + 1);
-    if (FW * j < 32) out.x |= code << (FW * j);
-    else out.y |= code << (FW * j - 32);
+    const int word = FW * j / 32;
+    acc[word] = __builtin_amdgcn_alignbit(__builtin_bit_cast(uint32_t, t[j]), acc[word], FW);
   }
-  return out;
+  // eight 2-bit fields fill only the top half of the word
+  if (FW * 8 < 32) acc[0] >>= 32 - FW * 8;
+  return make_uint2(acc[0], acc[1]);
+}
+
+// max of m over aligned groups of 2^lg lanes (lg <= 5), every lane active
+__device__ inline uint32_t group_max_lanes(uint32_t m, int lg) {
+  if (lg > 0) m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0xB1, 0xF, 0xF, false));
+  if (lg > 1) m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x4E, 0xF, 0xF, false));
+  if (lg > 2) m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x141, 0xF, 0xF, false));
+  if (lg > 3) m = max(m, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)m, 0x140, 0xF, 0xF, false));
+  if (lg > 4) m = max(m, (uint32_t)__shfl_xor((int)m, 16));
+  return m;
 }
 
 // stores the eight codes of one row chunk (packed at BITS bits) at chunk c8
@@ -700,9 +720,10 @@ flush_reg_kernel(CacheDev c, FlushSrc f, int lg_cpr, int lg_gv8) {
     const int r = sl + k * slices;
     uint32_t m = absmax8(vr[k]);
     if (r < G) vbad = max(vbad, m);
-    for (int o = 1; o <= gmask; o <<= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o));
+    m = group_max_lanes(m, lg_gv8);
     if (r < G) {
-      const float sv = group_scale(h2f((uint16_t)m), qv);
+      const float mf = h2f((uint16_t)m);
+      const float sv = qv == 1 ? (mf == 0.0f ? 1.0f : mf) : group_scale(mf, qv);
       const float rv = __builtin_amdgcn_rcpf(sv);
       const float s[8] = {sv, sv, sv, sv, sv, sv, sv, sv};
       const float rc[8] = {rv, rv, rv, rv, rv, rv, rv, rv};
