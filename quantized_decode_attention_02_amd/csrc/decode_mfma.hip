@@ -46,6 +46,11 @@ constexpr int kD = 128;
 constexpr float kLog2e = 1.4426950408889634f;
 
 __device__ inline float h2f(uint16_t u) { return (float)__builtin_bit_cast(_Float16, u); }
+// The packed cache is read once per call: its loads carry the nontemporal
+// hint, which streams them past the caches instead of filling them (a plain
+// read of several GiB runs about 13% faster that way on gfx950).
+template <typename T>
+__device__ inline T ldnt(const T* p) { return __builtin_nontemporal_load(p); }
 
 // v_and_or_b32: (a & mask) | magic in one instruction (the mask travels in
 // an SGPR, the magic in a VGPR: gfx9 VOP3 takes no literal and at most one
@@ -437,22 +442,22 @@ decode_mfma_kernel(MfmaArgs a) {
     for (int h = 0; h < 2; ++h) {
       const int64_t tok = t32 + 16 * h + ln;
       if (KB == 4) {
-        kw[i][h] = *(const u32x4*)(kc + tok * 16 + 4 * lq);
+        kw[i][h] = ldnt((const u32x4*)(kc + tok * 16 + 4 * lq));
       } else {
-        const u32x2 w2 = *(const u32x2*)(kc + tok * 8 + 2 * lq);
+        const u32x2 w2 = ldnt((const u32x2*)(kc + tok * 8 + 2 * lq));
         kw[i][h] = (u32x4){w2[0], w2[1], 0u, 0u};
       }
     }
     const int64_t tw = (int64_t)(unit * ut + i) * (32 * VB * kD / 32);
-    vw[i][0] = *(const u32x4*)(vc + tw + lane * 4);
-    if (VB == 4) vw[i][VB == 4 ? 1 : 0] = *(const u32x4*)(vc + tw + 256 + lane * 4);
+    vw[i][0] = ldnt((const u32x4*)(vc + tw + lane * 4));
+    if (VB == 4) vw[i][VB == 4 ? 1 : 0] = ldnt((const u32x4*)(vc + tw + 256 + lane * 4));
   };
   auto load_scales = [&](int unit) {
     const float4v* src = (const float4v*)(vs + (int64_t)unit * ut * 32 * NC);
 #pragma unroll
     for (int j = 0; j < kVs4; ++j) {
       const int idx = lane + 64 * j;
-      if (idx < n_vs4) vsn[j] = src[idx];
+      if (idx < n_vs4) vsn[j] = ldnt(src + idx);
     }
     if (lane < kD / 4) ksn = ((const float4v*)(ks + (int64_t)(unit / upg) * kD))[lane];
     kgn = kg[unit / upg];
@@ -895,32 +900,32 @@ __global__ void __launch_bounds__(kThreads, (rs_waves<KB, VB, NC, HS>())) decode
         // word of MFMA block kb: int4 word 4 kb + lq, or int2 word
         // 2 (kb - n4b) + lq / 2
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) kw[slot][h][kb] = kbase[kb][tok * kstride[kb] + kwi[kb]];
+        for (int kb = 0; kb < 4; ++kb) kw[slot][h][kb] = ldnt(&kbase[kb][tok * kstride[kb] + kwi[kb]]);
         if (NB == 8) {
-          kb16[KM ? slot : 0][h] = *(const u32x4*)(kbp + tok * 8);
+          kb16[KM ? slot : 0][h] = ldnt((const u32x4*)(kbp + tok * 8));
         } else if (NB == 4) {
-          const u32x2 b2 = *(const u32x2*)(kbp + tok * 4);
+          const u32x2 b2 = ldnt((const u32x2*)(kbp + tok * 4));
           kb16[KM ? slot : 0][h] = (u32x4){b2[0], b2[1], 0u, 0u};
         } else {
           kb16[KM ? slot : 0][h] = (u32x4){0u, 0u, 0u, 0u};
         }
       } else if (KB == 4) {
-        kw[slot][h] = *(const u32x4*)(kc + tok * 16 + 4 * lq);
+        kw[slot][h] = ldnt((const u32x4*)(kc + tok * 16 + 4 * lq));
       } else {
-        const u32x2 w2 = *(const u32x2*)(kc + tok * 8 + 2 * lq);
+        const u32x2 w2 = ldnt((const u32x2*)(kc + tok * 8 + 2 * lq));
         kw[slot][h] = (u32x4){w2[0], w2[1], 0u, 0u};
       }
     }
     const int64_t tw = (int64_t)(unit * ut + i) * (32 * VB * kD / 32);
-    vw[slot][0] = *(const u32x4*)(vc + tw + lane * 4);
-    if (VB == 4) vw[slot][VB == 4 ? 1 : 0] = *(const u32x4*)(vc + tw + 256 + lane * 4);
+    vw[slot][0] = ldnt((const u32x4*)(vc + tw + lane * 4));
+    if (VB == 4) vw[slot][VB == 4 ? 1 : 0] = ldnt((const u32x4*)(vc + tw + 256 + lane * 4));
   };
   auto load_scales = [&](int unit) {
     const float4v* src = (const float4v*)(vs + (int64_t)unit * ut * 32 * NC);
 #pragma unroll
     for (int j = 0; j < kVs4; ++j) {
       const int idx = lane + 64 * j;
-      if (idx < n_vs4) vsn[j] = src[idx];
+      if (idx < n_vs4) vsn[j] = ldnt(src + idx);
     }
     if (lane < ksrow / 4) ksn = ((const float4v*)(ks + (int64_t)(unit / upg) * ksrow))[lane];
     kgn = kg[unit / upg];
