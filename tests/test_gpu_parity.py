@@ -385,13 +385,17 @@ def test_append_determinism_and_capacity():
 # scales are exactly 2^e, and every other value is a multiple of 2^(e-1): many
 # quotients land exactly on k + 1/2, where round-half-even decides, and the
 # rest one fp16 ulp either side of a tie.  (D, G, Gv, R, k_bits, v_bits, S,
-# append chunks); the first three take the register-resident flush kernel,
-# the last the general one.
+# append chunks); all but the 3-bit case take the register-resident flush
+# kernel, which the 3-bit case leaves to the general one.
 TIE_CASES = {
     "k4v2_d128_g128": (128, 128, 32, 128, 4, 2, 1, [300, 1, 400, 63]),
     "k2v4_d64_g32": (64, 32, 16, 64, 2, 4, 0, [100, 157]),
     "k8v8_d128_g64": (128, 64, 8, 64, 8, 8, 2, [260]),
     "k3v3_d64_g32": (64, 32, 16, 32, 3, 3, 1, [129, 64]),
+    # value groups of 16 and 32 lanes (row mirror, then a cross-row shuffle)
+    "k2v2_d128_gv128": (128, 128, 128, 128, 2, 2, 0, [300, 229]),
+    "k4v4_d256_gv256": (256, 64, 256, 64, 4, 4, 1, [200, 77]),
+    "k8v2_d32_gv32": (32, 32, 32, 64, 8, 2, 0, [150]),
 }
 
 
