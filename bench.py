@@ -103,7 +103,7 @@ def read_ceiling(torch, kvq, dev, stream, gib=4, reps=5):
     """GB/s of the library's plain streaming-read kernel over `gib` GiB
     (median of `reps` event-timed launches after two untimed ones)."""
     buf = torch.empty(gib << 30, dtype=torch.uint8, device=dev)
-    sink = torch.empty(2048, dtype=torch.int32, device=dev)
+    sink = torch.empty(kvq.STREAM_READ_BLOCKS, dtype=torch.int32, device=dev)
     for _ in range(2):
         kvq.kvq_stream_read(buf, sink)
     ts = []

@@ -290,9 +290,10 @@ kvq_status kvq_fill_u32(uint32_t* dst, uint32_t value, int64_t n,
 
 /* Measured streaming-read ceiling: one launch of a plain read kernel over
  * `bytes` (a multiple of 16) of device memory at src (16-byte aligned);
- * each of the 2048 workgroups reads a contiguous share with 16-byte loads
- * and writes one word to sink (2048 uint32, device).  Time it with events
- * to compare the decode kernel with what a bare read reaches.          */
+ * each of the 8192 workgroups reads a contiguous share with nontemporal
+ * 16-byte loads and writes the XOR of its words to sink (8192 uint32,
+ * device).  Time it with events to compare the decode kernel with what a
+ * bare read reaches.                                                   */
 kvq_status kvq_stream_read(const void* src, int64_t bytes, uint32_t* sink,
                            void* stream);
 

@@ -189,19 +189,24 @@ __global__ void fill_u32_kernel(uint32_t* dst, uint32_t v, int64_t n) {
 // Streaming read: block b reads its contiguous share of src with 16-byte
 // loads, four in flight per thread, and stores the XOR of what it read to
 // sink[b] (so the loads cannot be dropped).
-__global__ void __launch_bounds__(256) stream_read_kernel(const uint4* __restrict__ src, int64_t n16,
+typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
+// Plain streaming read: workgroup b XORs the words of its contiguous share
+// into sink[b], eight nontemporal 16-byte loads in flight per thread.
+__global__ void __launch_bounds__(256) stream_read_kernel(const u32x4v* __restrict__ src, int64_t n16,
                                                           uint32_t* sink) {
   const int64_t per = (n16 + gridDim.x - 1) / gridDim.x;
   const int64_t lo = (int64_t)blockIdx.x * per;
   const int64_t hi = lo + per < n16 ? lo + per : n16;
-  uint32_t x = 0;
-  for (int64_t i = lo + threadIdx.x; i < hi; i += 4 * 256) {
-    uint4 a = src[i];
-    uint4 b = i + 256 < hi ? src[i + 256] : make_uint4(0, 0, 0, 0);
-    uint4 c = i + 512 < hi ? src[i + 512] : make_uint4(0, 0, 0, 0);
-    uint4 d = i + 768 < hi ? src[i + 768] : make_uint4(0, 0, 0, 0);
-    x ^= a.x ^ a.y ^ a.z ^ a.w ^ b.x ^ b.y ^ b.z ^ b.w ^ c.x ^ c.y ^ c.z ^ c.w ^ d.x ^ d.y ^ d.z ^ d.w;
+  u32x4v acc = {0u, 0u, 0u, 0u};
+  for (int64_t i = lo + threadIdx.x; i < hi; i += 8 * 256) {
+    u32x4v v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u)
+      v[u] = i + 256 * u < hi ? __builtin_nontemporal_load(src + i + 256 * u) : (u32x4v){0u, 0u, 0u, 0u};
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc ^= v[u];
   }
+  uint32_t x = acc[0] ^ acc[1] ^ acc[2] ^ acc[3];
   for (int o = 1; o < 64; o <<= 1) x ^= __shfl_xor(x, o);
   __shared__ uint32_t red[4];
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = x;
@@ -965,7 +970,7 @@ hipError_t launch_fill_u32(uint32_t* dst, uint32_t v, int64_t n, hipStream_t s) 
 
 hipError_t launch_stream_read(const void* src, int64_t bytes, uint32_t* sink, hipStream_t s) {
   if (bytes <= 0) return hipSuccess;
-  stream_read_kernel<<<kStreamReadBlocks, 256, 0, s>>>((const uint4*)src, bytes / 16, sink);
+  stream_read_kernel<<<kStreamReadBlocks, 256, 0, s>>>((const u32x4v*)src, bytes / 16, sink);
   return hipGetLastError();
 }
 

@@ -227,14 +227,18 @@ def kvq_synth_normal_f16(out, seed, tensor, layer, head0, n_heads, t0, n_tok,
     return out
 
 
+STREAM_READ_BLOCKS = 8192  # workgroups of kvq_stream_read
+
+
 def kvq_stream_read(buf, sink):
     """One launch of the plain streaming-read kernel over the bytes of buf
-    (a device tensor); sink: device tensor of at least 2048 int32."""
+    (a device tensor); sink: device tensor of at least STREAM_READ_BLOCKS
+    int32 (one XOR word per workgroup)."""
     _need_cuda(buf)
     _need_cuda(sink)
     n = buf.numel() * buf.element_size()
-    if sink.numel() * sink.element_size() < 2048 * 4:
-        raise ValueError("sink needs 2048 words")
+    if sink.numel() * sink.element_size() < STREAM_READ_BLOCKS * 4:
+        raise ValueError(f"sink needs {STREAM_READ_BLOCKS} words")
     _check(lib().kvq_stream_read(_ptr(buf), n - n % 16, _ptr(sink), _stream()),
            "kvq_stream_read")
 
