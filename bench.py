@@ -37,8 +37,8 @@ def parse():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="1m_32layer",
-                    choices=["1m_32layer", "gqa_128k", "mixkvq_32k",
-                             "7b_layer_4k"])
+                    choices=["1m_32layer", "gqa_128k", "gqa_128k_k2v4",
+                             "mixkvq_32k", "7b_layer_4k"])
     ap.add_argument("--layers", type=int, default=None,
                     help="layers of the 1m_32layer workload (default 32)")
     ap.add_argument("--seed", type=int, default=7)
@@ -226,8 +226,25 @@ def main():
                       S=w["S"], mixed=w.get("mixed", False),
                       n_bf16=w.get("n_bf16", 0), n_int4=w.get("n_int4", 0))
         if w.get("mixed"):
-            qw = synth.query_window(args.seed, B, w["W"], Hq, D)
-            c.kvq_salience_select(torch.from_numpy(qw).to(dev))
+            qw = torch.from_numpy(
+                synth.query_window(args.seed, B, w["W"], Hq, D)).to(dev)
+            c.kvq_salience_select(qw)
+            # the salience select (I over the last W query rows), timed on
+            # its own: it is summed with the decode call in the output.  A
+            # GPU spin ahead of each call keeps the host's launch latency
+            # out of the event interval.
+            sal = []
+            for r in range(12):
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                torch.cuda._sleep(1 << 18)
+                e0.record(stream)
+                c.kvq_salience_select(qw)
+                e1.record(stream)
+                torch.cuda.synchronize()
+                if r >= 2:
+                    sal.append(1000 * e0.elapsed_time(e1))
+            extra["salience_select_us"] = round(float(np.median(sal)), 2)
         c.kvq_append(torch.from_numpy(np.ascontiguousarray(kn[:, :, :N])).to(dev),
                      torch.from_numpy(np.ascontiguousarray(vn[:, :, :N])).to(dev))
         assert c.kvq_cache_check() == kvq.KVQ_OK
@@ -352,6 +369,9 @@ def main():
         },
         "bytes_per_step": int(bytes_step),
     }
+    if "salience_select_us" in extra:
+        extra["decode_plus_salience_us"] = round(
+            res["decode_call_us"]["median"] + extra["salience_select_us"], 2)
     res.update(extra)
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(args, w, layers)

@@ -175,7 +175,8 @@ kvq_status kvq_append(kvq_cache* c, const void* k_new, const void* v_new,
  *   q_win  [B][w_rows][n_q_heads][D] float16, the last w_rows query rows.
  * I[b][kvh][d] = sum over the rows and the query heads kvh*g .. kvh*g+g-1
  * (g = n_q_heads / Hkv) of |q|, in float64 (exact).  Applies to every later
- * key-group flush.  Requires k_mixed.                                   */
+ * key-group flush.  Requires k_mixed; n_q_heads / Hkv <= 1024
+ * (else KVQ_E_UNSUPPORTED).                                            */
 kvq_status kvq_salience_select(kvq_cache* c, const void* q_win, int dtype,
                                int w_rows, int n_q_heads, void* stream);
 

@@ -296,6 +296,9 @@ kvq_status kvq_salience_select(kvq_cache* c, const void* q_win, int dtype, int w
       n_q_heads % c->cfg.kv_heads)
     return KVQ_E_ARG;
   if (w_rows > 0 && (!q_win || !aligned(q_win, 2))) return KVQ_E_ARG;
+  // a window row of 32 channels of a KV head's query heads is staged in
+  // 64 KB of LDS
+  if ((int64_t)(n_q_heads / c->cfg.kv_heads) * 32 * 2 > 65536) return KVQ_E_UNSUPPORTED;
   return hip_status(launch_salience(c->dev, (const uint16_t*)q_win, w_rows, n_q_heads,
                                     (hipStream_t)stream));
 }

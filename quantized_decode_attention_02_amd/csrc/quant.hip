@@ -768,22 +768,102 @@ flush_reg_kernel(CacheDev c, FlushSrc f, int lg_cpr, int lg_gv8) {
   if (bad) atomicOr(c.err, 1u);
 }
 
-// I[b][kvh][d] = sum over rows r and grouped heads h of |q_win[b][r][h][d]|.
-__global__ void salience_kernel(CacheDev c, const uint16_t* __restrict__ q,
-                                int w_rows, int Hq) {
-  const int d = threadIdx.x;
-  const int h = blockIdx.x, b = blockIdx.y;
+// I[b][kvh][d] = sum over rows r and grouped heads h of |q_win[b][r][h][d]|,
+// in float64.  One workgroup per (kvh, b, block of kSalCh channels): the
+// block's columns of the window rows of the group's g heads are staged in
+// LDS (as many rows as fit 64 KB at a time) with coalesced loads, 16-byte
+// ones when the rows allow.
+//
+// Each |q| is a multiple of 2^-24 (the fp16 grain) below 2^16, so with at
+// most 8192 terms every partial sum is a multiple of 2^-24 below 2^29 and
+// exact in float64: the result does not depend on the order of the
+// additions.  The terms of a channel are then spread over eight threads and
+// four accumulators each.  Longer windows keep the sequential order (rows
+// ascending, heads ascending within a row) on one thread per channel.
+constexpr int kSalCh = 32;          // channels per workgroup
+constexpr int kSalLds = 65536;      // bytes of staged window columns
+constexpr int kSalExactTerms = 8192;
+__global__ void __launch_bounds__(256) salience_kernel(CacheDev c, const uint16_t* __restrict__ q,
+                                                       int w_rows, int Hq) {
+  __shared__ __align__(16) uint16_t st[kSalLds / 2];
+  const int tid = threadIdx.x, D = c.D;
+  const int h = blockIdx.x, b = blockIdx.y, d0 = blockIdx.z * kSalCh;
+  const int nc = min(kSalCh, D - d0);          // channels of this block
   const int g = Hq / c.H;
-  if (d >= c.D) return;
-  double acc = 0.0;
+  const int seg = g * kSalCh;                  // staged halves per window row
+  const int rows = kSalLds / 2 / seg;          // rows per chunk (>= 1: checked on the host)
+  const uint16_t* base = q + ((int64_t)b * w_rows * Hq + (int64_t)h * g) * D + d0;
+  const int64_t rstride = (int64_t)Hq * D;     // halves between window rows
+  const bool vec = nc == kSalCh && D % 8 == 0 && ((uintptr_t)base % 16) == 0;
+  const int P = (int64_t)w_rows * g <= kSalExactTerms ? 256 / kSalCh : 1;
+  const int cl = tid % kSalCh, part = tid / kSalCh;
+  const bool active = part < P && cl < nc;
+  double acc[4] = {0.0, 0.0, 0.0, 0.0};
   bool bad = false;
-  for (int r = 0; r < w_rows; ++r)
-    for (int hh = h * g; hh < (h + 1) * g; ++hh) {
-      float v = h2f(q[(((int64_t)b * w_rows + r) * Hq + hh) * c.D + d]);
-      bad |= !finite(v);
-      acc += fabs((double)v);
+  for (int r0 = 0; r0 < w_rows; r0 += rows) {
+    const int n = min(rows, w_rows - r0);
+    // item (r, hh, piece) of the chunk: window row r0 + r, head hh
+    if (vec) {
+      const int total = n * g * (kSalCh / 8);
+      for (int i0 = tid; i0 < total; i0 += 8 * 256) {
+        uint4 x[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const int i = i0 + k * 256;
+          if (i < total) {
+            const int p8 = i % (kSalCh / 8), t = i / (kSalCh / 8);  // t = r * g + hh
+            x[k] = *(const uint4*)(base + (int64_t)(r0 + t / g) * rstride + (t % g) * D + 8 * p8);
+          }
+        }
+#pragma unroll
+        for (int k = 0; k < 8; ++k) {
+          const int i = i0 + k * 256;
+          if (i < total) *(uint4*)&st[8 * i] = x[k];
+        }
+      }
+    } else {
+      const int total = n * g * kSalCh;
+      for (int i = tid; i < total; i += 256) {
+        const int e = i % kSalCh, t = i / kSalCh;
+        st[i] = e < nc ? base[(int64_t)(r0 + t / g) * rstride + (t % g) * D + e] : (uint16_t)0;
+      }
     }
-  c.I[((int64_t)b * c.H + h) * c.D + d] = acc;
+    __syncthreads();
+    // term t = r * g + hh of the chunk sits at st[t * kSalCh + cl]
+    const int nt = n * g;
+    if (active && P == 1) {
+      for (int t = 0; t < nt; ++t) {
+        const float v = h2f(st[t * kSalCh + cl]);
+        bad |= !finite(v);
+        acc[0] += fabs((double)v);
+      }
+    } else if (active) {
+      int t = part;
+      for (; t + 3 * P < nt; t += 4 * P) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          const float v = h2f(st[(t + k * P) * kSalCh + cl]);
+          bad |= !finite(v);
+          acc[k] += fabs((double)v);
+        }
+      }
+      for (; t < nt; t += P) {
+        const float v = h2f(st[t * kSalCh + cl]);
+        bad |= !finite(v);
+        acc[0] += fabs((double)v);
+      }
+    }
+    __syncthreads();
+  }
+  // combine the parts of each channel (exact when P > 1)
+  double* red = (double*)st;
+  red[tid] = active ? (acc[0] + acc[1]) + (acc[2] + acc[3]) : 0.0;
+  __syncthreads();
+  if (tid < nc) {
+    double t = red[tid];
+    for (int p = 1; p < P; ++p) t += red[p * kSalCh + tid];
+    c.I[((int64_t)b * c.H + h) * D + d0 + tid] = t;
+  }
   if (bad) atomicOr(c.err, 1u);
 }
 
@@ -1027,8 +1107,11 @@ hipError_t launch_flush(const CacheDev& c, const uint16_t* k_in,
 
 hipError_t launch_salience(const CacheDev& c, const uint16_t* q_win, int w_rows,
                            int n_q_heads, hipStream_t s) {
-  dim3 grid((unsigned)c.H, (unsigned)c.B);
-  salience_kernel<<<grid, kMaxD, 0, s>>>(c, q_win, w_rows, n_q_heads);
+  // one window row of a channel block of a KV head's query heads must fit
+  // the staging buffer
+  if ((int64_t)(n_q_heads / c.H) * kSalCh * 2 > kSalLds) return hipErrorInvalidValue;
+  dim3 grid((unsigned)c.H, (unsigned)c.B, (unsigned)((c.D + kSalCh - 1) / kSalCh));
+  salience_kernel<<<grid, 256, 0, s>>>(c, q_win, w_rows, n_q_heads);
   return hipGetLastError();
 }
 

@@ -171,6 +171,10 @@ WORKLOADS = {
     "gqa_128k": dict(B=1, Hq=32, Hkv=8, N=131072, D=128, S=1, G=64, Gv=64,
                      R=64, k_bits=4, v_bits=2, outliers="fraction",
                      frac=0.02, fmin=10.0, fmax=30.0, sink_factor=20.0),
+    # the same GQA layer with the bit widths swapped (the comparison run)
+    "gqa_128k_k2v4": dict(B=1, Hq=32, Hkv=8, N=131072, D=128, S=1, G=64,
+                          Gv=64, R=64, k_bits=2, v_bits=4, outliers="fraction",
+                          frac=0.02, fmin=10.0, fmax=30.0, sink_factor=20.0),
     "mixkvq_32k": dict(B=8, Hq=40, Hkv=8, N=32768, D=128, S=0, G=128, Gv=64,
                        R=128, k_bits=2, v_bits=2, mixed=True, n_bf16=8,
                        n_int4=32, W=64, outliers="per_head", n_out=4,

@@ -455,12 +455,24 @@ def test_cache_nonfinite_poisons():
     assert e.value.status == kvq.KVQ_E_POISONED
 
 
-def test_salience_intensity_exact():
-    B, W, Hq, Hkv, D = 2, 64, 10, 2, 128
+# (B, W, Hq, Hkv, D, element offset of the window): 16-byte staging over
+# two chunks; 2-byte staging (rows of 108 halves, seven threads a channel);
+# a window that is only 2-byte aligned, 19 chunks of 16 rows; an empty
+# window; more than 8192 terms a channel (the sequential sum)
+SALIENCE_CASES = [(2, 64, 10, 2, 128, 0), (1, 37, 6, 2, 36, 0),
+                  (1, 300, 16, 1, 128, 1), (1, 0, 4, 2, 64, 0),
+                  (1, 1100, 8, 1, 64, 0)]
+
+
+@pytest.mark.parametrize("B,W,Hq,Hkv,D,off", SALIENCE_CASES)
+def test_salience_intensity_exact(B, W, Hq, Hkv, D, off):
+    say("salience", B, W, Hq, Hkv, D, off)
     qw = synth.query_window(5, B, W, Hq, D)
-    c = kvq.Cache(B, Hkv, D, 256, 2, 2, 128, 64, 128, mixed=True, n_bf16=8,
-                  n_int4=32)
-    c.kvq_salience_select(torch.from_numpy(qw).to(DEV))
+    c = kvq.Cache(B, Hkv, D, 256, 2, 2, 32, D // 4, 64, mixed=True, n_bf16=4,
+                  n_int4=8)
+    flat = torch.zeros(qw.size + off, dtype=torch.float16, device=DEV)
+    flat[off:] = torch.from_numpy(qw.reshape(-1)).to(DEV)
+    c.kvq_salience_select(flat[off:].view(qw.shape))
     torch.cuda.synchronize()
     # I lives in the cache buffer after the 256-byte header
     I = c.buf[256:256 + B * Hkv * D * 8].cpu().numpy().view(np.float64)
