@@ -151,28 +151,33 @@ struct MfmaArgs {
   float* partials;     // [B][Hq][n_parts][D + 2]
   int n_parts;
   int n_splits;
+  int fp_last;         // grid order: the fp16-row parts after the splits
 };
 
 // One-dimensional grid: the short fp16-row parts of every stream first
 // (dispatched first, so that none of them trails the long quantized
-// splits), then the splits; partial slot = fp16 chunk, or n_fp + split.
+// splits), then the splits; or, when the workgroups overflow one resident
+// round by no more than the fp16-row parts (fp_last), the splits first, so
+// that every split starts at once and the short parts take the slots of
+// the first splits to finish.  Partial slot = fp16 chunk, or n_fp + split.
 struct PartIndex {
   int part, kvh, b;
 };
 __device__ inline PartIndex part_index(const MfmaArgs& a) {
-  const int64_t L = blockIdx.x;
-  const int n_fp = a.n_parts - a.n_splits;
-  const int64_t n_fp_all = (int64_t)a.v.batch * a.v.kv_heads * n_fp;
-  int64_t s;
-  int part;
-  if (L < n_fp_all) {
-    s = L / n_fp;
-    part = (int)(L % n_fp);
-  } else {
-    s = (L - n_fp_all) / a.n_splits;
-    part = n_fp + (int)((L - n_fp_all) % a.n_splits);
-  }
-  return PartIndex{part, (int)(s % a.v.kv_heads), (int)(s / a.v.kv_heads)};
+  // 32-bit arithmetic: the launcher keeps the grid below 2^31 blocks
+  const uint32_t L = blockIdx.x;
+  const uint32_t n_sp = (uint32_t)a.n_splits, n_fp = (uint32_t)a.n_parts - n_sp;
+  const uint32_t streams = (uint32_t)a.v.batch * (uint32_t)a.v.kv_heads;
+  const uint32_t first = a.fp_last ? streams * n_sp : streams * n_fp;  // blocks of the first region
+  const bool in_first = L < first;
+  const bool is_fp = in_first != (bool)a.fp_last;
+  const uint32_t idx = in_first ? L : L - first;
+  const uint32_t per = is_fp ? n_fp : n_sp;
+  const uint32_t s = idx / per;
+  const uint32_t r = idx - s * per;
+  const uint32_t H = (uint32_t)a.v.kv_heads;
+  const uint32_t bb = s / H;
+  return PartIndex{(int)(is_fp ? r : n_fp + r), (int)(s - bb * H), (int)bb};
 }
 
 // A work unit of one wave: up to 4 tiles (128 tokens) of one key group.
@@ -1421,10 +1426,13 @@ int fp16_parts(const kvq_kv_view& v);
 // workgroups balance better over the compute units: at 1M tokens 3072 beat
 // 768, 1024 and 6144), and at least one unit per wave.  In one round the
 // fp16-row parts either take slots of their own, so that every workgroup is
-// resident at once, or keep none: they are dispatched first and the last
-// splits start when they end.  The second is taken when the shorter splits
-// save more than one fp16-row part takes (estimates: 2 us per tile per
-// wave, 10 us per fp16-row part).
+// resident at once, or keep none: the splits are then dispatched first and
+// the fp16-row parts take the slots of the first splits to finish (see
+// part_index).  The second is taken when the shorter splits save more than
+// a trailing fp16-row part adds (estimates: 2 us per tile per wave, 5 us per
+// trailing part, which mostly overlaps the spread of the split ends; at
+// MixKVQ 32K x 8 with one part per stream, 8 splits and a trailing part
+// take 87 us, 7 splits and a slot of its own 100 us).
 int auto_splits(const kvq_kv_view& v, int Hq) {
   const int64_t streams = (int64_t)v.batch * v.kv_heads;
   int64_t sp, by_len;
@@ -1438,7 +1446,7 @@ int auto_splits(const kvq_kv_view& v, int Hq) {
     auto wave_tiles = [&](int64_t n) { return tiles / (double)(n * kWaves); };
     const int64_t slots = round / streams > 1 ? round / streams : 1;
     sp = slots - fp;
-    if (sp < 1 || (fp > 0 && 2.0 * (wave_tiles(sp) - wave_tiles(slots)) > 10.0)) sp = slots;
+    if (sp < 1 || (fp > 0 && 2.0 * (wave_tiles(sp) - wave_tiles(slots)) > 5.0)) sp = slots;
     if (wave_tiles(sp) > 48.0) {
       sp = 4 * round / streams - fp;
       if (sp < 1) sp = 1;
@@ -1534,7 +1542,12 @@ hipError_t launch_decode_mfma(const kvq_kv_view& v, const void* q, int f16, int 
   const int fp = fp16_parts(v);
   const int n_splits = n_parts - fp;
   if ((int64_t)n_parts * v.kv_heads * v.batch > 0x7FFFFFFF) return hipErrorInvalidConfiguration;
-  MfmaArgs a{v, q, f16, Hq, sm_scale * kLog2e, partials, n_parts, n_splits};
+  // resident workgroups of one round (row-score kernel)
+  const int64_t streams = (int64_t)v.batch * v.kv_heads;
+  const int64_t total = (int64_t)n_parts * streams;
+  const int64_t round = rows_kernel(v, Hq) ? (int64_t)n_cus() * rs_wgs(v, Hq) : 0;
+  const int fp_last = fp > 0 && round > 0 && total > round && total - round <= streams * fp;
+  MfmaArgs a{v, q, f16, Hq, sm_scale * kLog2e, partials, n_parts, n_splits, fp_last};
   const int nc = kD / v.group_ch;
   hipError_t e;
   if (v.k_mixed) e = v.v_bits == 2 ? launch_nc<0, 2>(a, nc, s) : launch_nc<0, 4>(a, nc, s);
