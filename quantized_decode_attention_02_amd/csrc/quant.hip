@@ -637,14 +637,19 @@ __device__ inline void store_codes8(uint32_t* row, int c8, uint2 code) {
   else ((uint2*)row)[c8] = code;
 }
 
+// KB = 0: mixed keys (MixKVQ): per group, the salience classes of the
+// channels, bf16 rows of the class-0 channels, int4 and int2 codes of the
+// others in ascending-channel order within each class; codes are staged in
+// LDS by class position and packed from there.
+constexpr int kMixBf16Stage = 4096;  // halves: G * n_bf16 bf16 keys of a group
 template <int KB, int VB>
 __global__ void __launch_bounds__(kThreads)
 __attribute__((amdgpu_waves_per_eu(4)))
 flush_reg_kernel(CacheDev c, FlushSrc f, int lg_cpr, int lg_gv8) {
   __shared__ __align__(16) uint16_t kmag[kThreads * 8];         // [slice][channel] |k| maxima
   __shared__ __align__(16) float ksc[kMaxD];                    // key scale per channel
-  __shared__ __align__(16) uint8_t vst[kRegRows * kThreads * 8];  // value codes [row][channel]
-  constexpr int qk = (1 << (KB - 1)) - 1, qv = (1 << (VB - 1)) - 1;
+  __shared__ __align__(16) uint8_t vst[kRegRows * kThreads * 8];  // codes [row][channel or position]
+  constexpr int qk = KB > 0 ? (1 << (KB - 1)) - 1 : 0, qv = (1 << (VB - 1)) - 1;
   const int tid = threadIdx.x;
   const int D = c.D, G = c.G;
   const int slices = kThreads >> lg_cpr;
@@ -682,25 +687,27 @@ flush_reg_kernel(CacheDev c, FlushSrc f, int lg_cpr, int lg_gv8) {
   }
   __syncthreads();
   bool bad = false;
+  uint32_t kmbits = 0;  // this channel's |k| maximum (fp16 bits), tid < D
   if (tid < D) {
-    uint32_t m = 0;
-    for (int q = 0; q < slices; ++q) m = max(m, (uint32_t)kmag[q * D + tid]);
-    bad = m >= 0x7C00u;
-    const float s = group_scale(h2f((uint16_t)m), qk);
-    ksc[tid] = s;
-    c.k_scales[st * c.s_k_scales + grp * D + tid] = s;
+    for (int q = 0; q < slices; ++q) kmbits = max(kmbits, (uint32_t)kmag[q * D + tid]);
+    bad = kmbits >= 0x7C00u;
   }
-  __syncthreads();
-  // bound on |k_hat| / code of the group: the largest channel scale
-  if (tid < 64) {
-    float g = 0.0f;
-    for (int ch = tid; ch < D; ch += 64) g = fmaxf(g, ksc[ch]);
+  if constexpr (KB > 0) {
+    if (tid < D) {
+      const float s = group_scale(h2f((uint16_t)kmbits), qk);
+      ksc[tid] = s;
+      c.k_scales[st * c.s_k_scales + grp * D + tid] = s;
+    }
+    __syncthreads();
+    // bound on |k_hat| / code of the group: the largest channel scale
+    if (tid < 64) {
+      float g = 0.0f;
+      for (int ch = tid; ch < D; ch += 64) g = fmaxf(g, ksc[ch]);
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) g = fmaxf(g, __shfl_xor(g, o));
-    if (tid == 0) c.k_gmax[st * c.s_k_gmax + grp] = g;
-  }
-  // ---- keys, pass 2
-  {
+      for (int o = 32; o > 0; o >>= 1) g = fmaxf(g, __shfl_xor(g, o));
+      if (tid == 0) c.k_gmax[st * c.s_k_gmax + grp] = g;
+    }
+    // ---- keys, pass 2
     float s[8], rc[8];
     const float4 a = *(const float4*)&ksc[8 * c8], b = *(const float4*)&ksc[8 * c8 + 4];
     s[0] = a.x; s[1] = a.y; s[2] = a.z; s[3] = a.w;
@@ -714,6 +721,128 @@ flush_reg_kernel(CacheDev c, FlushSrc f, int lg_cpr, int lg_gv8) {
       const int r = sl + k * slices;
       if (r < G) store_codes8<KB>(krow + (int64_t)r * wk, c8, encode8<KB, KB>(kr[k], s, rc));
     }
+  } else {
+    // ---- MixKVQ classes: A_d = I_d * S_d (float64), ranked by (-A, d)
+    __shared__ double A[kMaxD];
+    __shared__ float kmx[kMaxD];
+    __shared__ int kcls[kMaxD], kpos[kMaxD];
+    __shared__ __align__(16) uint16_t bst[kMixBf16Stage];  // [row][bf16 position]
+    const int nb = c.n_bf16, n4 = c.n_int4, n2 = D - nb - n4, nint = D - nb;
+    if (tid < D) {
+      kmx[tid] = h2f((uint16_t)kmbits);
+      A[tid] = c.I[st * D + tid] * (double)kmx[tid];
+    }
+    __syncthreads();
+    __shared__ int wcount[kThreads / 64][3];  // channels of each class per wave
+    int cl = 0;
+    if (tid < D) {
+      const double av = A[tid];
+      int rank = 0;
+#pragma unroll 8
+      for (int e = 0; e < D; ++e) {
+        const double bv = A[e];
+        rank += (bv > av) || (bv == av && e < tid);
+      }
+      cl = rank < nb ? 0 : (rank < nb + n4 ? 1 : 2);
+      kcls[tid] = cl;
+    }
+    // position within the class: same-class channels of lower index, from
+    // per-wave ballots (channel = thread index)
+    const int lane = tid & 63, wave = tid >> 6;
+    uint64_t bal[3];
+#pragma unroll
+    for (int k = 0; k < 3; ++k) bal[k] = __ballot(tid < D && cl == k);
+    if (lane == 0) {
+#pragma unroll
+      for (int k = 0; k < 3; ++k) wcount[wave][k] = __popcll(bal[k]);
+    }
+    __syncthreads();
+    if (tid < D) {
+      int before = __popcll(bal[cl] & ((1ull << lane) - 1ull));
+      for (int w = 0; w < wave; ++w) before += wcount[w][cl];
+      const int pos = (cl == 0 ? 0 : (cl == 1 ? nb : nb + n4)) + before;
+      kpos[tid] = pos;
+      c.k_pos[st * c.s_k_pos + grp * D + tid] = (uint8_t)pos;
+      if (cl != 0) {
+        const float sc = group_scale(kmx[tid], cl == 1 ? 7 : 1);
+        ksc[tid] = sc;
+        c.k_scales[st * c.s_k_scales + grp * nint + (pos - nb)] = sc;
+      } else {
+        ksc[tid] = 1.0f;
+      }
+    }
+    __syncthreads();
+    // bound on |k_hat| / code: the largest scale, |K| itself for bf16 channels
+    if (tid < 64) {
+      float g = 0.0f;
+      for (int ch = tid; ch < D; ch += 64) g = fmaxf(g, kcls[ch] == 0 ? kmx[ch] : ksc[ch]);
+#pragma unroll
+      for (int o = 32; o > 0; o >>= 1) g = fmaxf(g, __shfl_xor(g, o));
+      if (tid == 0) c.k_gmax[st * c.s_k_gmax + grp] = g;
+    }
+    // ---- keys, pass 2: codes by class position into LDS (offset code in
+    // the low mantissa bits as in encode8, per-channel qmax), bf16 rows
+    // per channel of the thread: class << 8 | position, 1 / scale
+    constexpr float kM4 = 12582912.0f + 8.0f, kM2 = 12582912.0f + 2.0f;
+    uint32_t cp[8];
+    float rc[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int ch = 8 * c8 + j;
+      cp[j] = ((uint32_t)kcls[ch] << 8) | (uint32_t)kpos[ch];
+      rc[j] = __builtin_amdgcn_rcpf(ksc[ch]);
+    }
+#pragma unroll
+    for (int k = 0; k < kRegRows; ++k) {
+      const int r = sl + k * slices;
+      if (r < G) {
+        const uint32_t wv[4] = {kr[k].x, kr[k].y, kr[k].z, kr[k].w};
+        float x[8], t[8];
+        float dmax = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float mg = (cp[j] >> 8) == 1 ? kM4 : kM2;
+          x[j] = h2f((uint16_t)(wv[j >> 1] >> (16 * (j & 1))));
+          t[j] = __builtin_fmaf(x[j], rc[j], mg);
+          const float dj = fabsf(__builtin_fmaf(x[j], rc[j], -(t[j] - mg)));
+          if ((cp[j] >> 8) != 0) dmax = fmaxf(dmax, dj);
+        }
+        if (!(dmax < kNearTie)) {
+#pragma unroll
+          for (int j = 0; j < 8; ++j)
+            t[j] = rintf(__fdiv_rn(x[j], ksc[8 * c8 + j])) + ((cp[j] >> 8) == 1 ? kM4 : kM2);
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int pj = (int)(cp[j] & 0xFFu);
+          if ((cp[j] >> 8) == 0)
+            bst[r * nb + pj] = f32_to_bf16_rne(x[j]);
+          else
+            vst[r * nint + pj - nb] = (uint8_t)(__builtin_bit_cast(uint32_t, t[j]) & 0xFFu);
+        }
+      }
+    }
+    __syncthreads();
+    const int w4 = words_of(n4, 4), w2 = words_of(n2, 2), wt = w4 + w2;
+    for (int i = tid; i < G * wt; i += kThreads) {
+      const int r = i / wt;
+      int w = i - r * wt;
+      const uint8_t* cr = vst + r * nint;
+      uint32_t word = 0;
+      if (w < w4) {
+        for (int j = 0; j < 8; ++j)
+          if (w * 8 + j < n4) word |= (uint32_t)cr[w * 8 + j] << (4 * j);
+        c.k_int4[st * c.s_k_int4 + (p0 + r) * w4 + w] = word;
+      } else {
+        w -= w4;
+        for (int j = 0; j < 16; ++j)
+          if (w * 16 + j < n2) word |= (uint32_t)cr[n4 + w * 16 + j] << (2 * j);
+        c.k_int2[st * c.s_k_int2 + (p0 + r) * w2 + w] = word;
+      }
+    }
+    for (int i = tid; i < G * nb; i += kThreads)
+      c.k_bf16[st * c.s_k_bf16 + (p0 + i / nb) * nb + i % nb] = bst[i];
+    __syncthreads();  // the value tiles reuse the code staging
   }
   // ---- values: per-token group scales over 2^lg_gv8 adjacent lanes
   const bool tiles = c.v_layout == KVQ_V_TILE32;
@@ -1084,8 +1213,8 @@ hipError_t launch_flush(const CacheDev& c, const uint16_t* k_in,
   dim3 grid((unsigned)n_groups, (unsigned)c.H, (unsigned)c.B);
   auto b248 = [](int b) { return b == 2 || b == 4 || b == 8; };
   const int D = c.D;
-  if (!c.mixed && b248(c.k_bits) && b248(c.v_bits) && D >= 8 && (D & (D - 1)) == 0 &&
-      c.Gv >= 8 && c.G <= kRegRows * (kThreads / (D / 8)) &&
+  if ((c.mixed ? c.G * c.n_bf16 <= kMixBf16Stage : b248(c.k_bits)) && b248(c.v_bits) && D >= 8 &&
+      (D & (D - 1)) == 0 && c.Gv >= 8 && c.G <= kRegRows * (kThreads / (D / 8)) &&
       (((uintptr_t)k_in | (uintptr_t)v_in) % 16) == 0) {
     const int lg_cpr = __builtin_ctz(D / 8), lg_gv8 = __builtin_ctz(c.Gv / 8);
 #define KVQ_FLUSH_REG(KB, VB)                                                   \
@@ -1093,6 +1222,11 @@ hipError_t launch_flush(const CacheDev& c, const uint16_t* k_in,
     flush_reg_kernel<KB, VB><<<grid, kThreads, 0, s>>>(c, f, lg_cpr, lg_gv8);   \
     return hipGetLastError();                                                   \
   }
+    if (c.mixed) {
+      if (c.v_bits == 2) KVQ_FLUSH_REG(0, 2)
+      if (c.v_bits == 4) KVQ_FLUSH_REG(0, 4)
+      if (c.v_bits == 8) KVQ_FLUSH_REG(0, 8)
+    }
     KVQ_FLUSH_REG(2, 2) KVQ_FLUSH_REG(2, 4) KVQ_FLUSH_REG(2, 8)
     KVQ_FLUSH_REG(4, 2) KVQ_FLUSH_REG(4, 4) KVQ_FLUSH_REG(4, 8)
     KVQ_FLUSH_REG(8, 2) KVQ_FLUSH_REG(8, 4) KVQ_FLUSH_REG(8, 8)
