@@ -385,8 +385,8 @@ def test_append_determinism_and_capacity():
 # scales are exactly 2^e, and every other value is a multiple of 2^(e-1): many
 # quotients land exactly on k + 1/2, where round-half-even decides, and the
 # rest one fp16 ulp either side of a tie.  (D, G, Gv, R, k_bits, v_bits, S,
-# append chunks); all but the 3-bit case take the register-resident flush
-# kernel, which the 3-bit case leaves to the general one.
+# append chunks[, mixed-key settings]); all but the 3-bit and D = 96 cases
+# take the register-resident flush kernel.
 TIE_CASES = {
     "k4v2_d128_g128": (128, 128, 32, 128, 4, 2, 1, [300, 1, 400, 63]),
     "k2v4_d64_g32": (64, 32, 16, 64, 2, 4, 0, [100, 157]),
@@ -396,6 +396,14 @@ TIE_CASES = {
     "k2v2_d128_gv128": (128, 128, 128, 128, 2, 2, 0, [300, 229]),
     "k4v4_d256_gv256": (256, 64, 256, 64, 4, 4, 1, [200, 77]),
     "k8v2_d32_gv32": (32, 32, 32, 64, 8, 2, 0, [150]),
+    # mixed keys (classes from key scales alone: no salience window), values
+    # on the half-integer grid of 2-bit codes: exact ties on the int2
+    # channels, near-ties on the int4 ones (scale = absmax / 7); D = 96
+    # takes the general flush kernel
+    "mixed_d128": (128, 128, 32, 128, 2, 2, 0, [300, 229],
+                   dict(mixed=True, n_bf16=8, n_int4=32)),
+    "mixed_d96_general": (96, 32, 32, 64, 2, 2, 1, [200, 57],
+                          dict(mixed=True, n_bf16=8, n_int4=24)),
 }
 
 
@@ -421,14 +429,15 @@ def tie_inputs(seed, B, H, N, D, G, Gv, kb, vb, S):
 
 @pytest.mark.parametrize("name", list(TIE_CASES))
 def test_cache_parity_ties(name):
-    D, G, Gv, R, kb, vb, S, chunks = TIE_CASES[name]
+    D, G, Gv, R, kb, vb, S, chunks = TIE_CASES[name][:8]
+    mkw = TIE_CASES[name][8] if len(TIE_CASES[name]) > 8 else {}
     B, H = 2, 2
     N = sum(chunks)
     say("tie case", name)
     k, v = tie_inputs(11, B, H, N, D, G, Gv, kb, vb, S)
     oc = ocache.Cache(ocache.CacheConfig(B=B, Hkv=H, D=D, S=S, R=R, G=G,
-                                         Gv=Gv, k_bits=kb, v_bits=vb))
-    gc = kvq.Cache(B, H, D, N + 64, kb, vb, G, Gv, R, S=S)
+                                         Gv=Gv, k_bits=kb, v_bits=vb, **mkw))
+    gc = kvq.Cache(B, H, D, N + 64, kb, vb, G, Gv, R, S=S, **mkw)
     t = 0
     for n in chunks:
         oc.append(k[:, :, t:t + n], v[:, :, t:t + n])
