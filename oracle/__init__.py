@@ -16,10 +16,11 @@ and in the pages' order:
 * cache.py     sink / quantized groups / full-precision residual tail
 * attention.py float64 stable-softmax attention over dequantized K, V
 * bytes_model.py  payload byte accounting
+* rotation.py  key-only Walsh-Hadamard rotation (fast transform in float32)
 
 Parity status: every function is pinned by ``tests/test_oracle_*.py`` against
 values printed on the pages, closed forms, invariants, brute force or library
 routines; none is "parity unpinned".
 """
 
-from . import codec, salience, cache, attention, bytes_model  # noqa: F401
+from . import codec, salience, cache, attention, bytes_model, rotation  # noqa: F401
