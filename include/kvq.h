@@ -118,6 +118,26 @@ kvq_status kvq_dequant(const uint32_t* codes, const float* scales,
                        int64_t n_mats, int64_t n_tok, int d, int bits,
                        int axis, int group, float* out, void* stream);
 
+/* Key rotation ("Quantize What Counts: More for Keys, Less for Values",
+ * rotation integration: rotating the keys alone; "Statistical Inference
+ * and Quality Measures of KV Cache Quantisations Inspired by TurboQuant",
+ * the Walsh-Hadamard step of the KQV scheme).  Row by row,
+ *   out[r][:] = H in[r][:] / sqrt(d),
+ * H the Sylvester Walsh-Hadamard matrix of order d (a power of two,
+ * 1 <= d <= 256): orthonormal and its own inverse, so q . k = (Hq) . (Hk)
+ * and rotating the keys before kvq_append and the queries before
+ * kvq_decode_attention leaves the scores unchanged.  Computed in float32
+ * by the fast transform (stages h = 1, 2, 4, ..., d/2: the pair
+ * (x[i], x[i+h]), bit h of i clear, becomes (x[i] + x[i+h], x[i] - x[i+h]))
+ * and one multiply by float32(1/sqrt(d)); a KVQ_F16 output is rounded to
+ * nearest even.  The result is fixed bit for bit.
+ *   in  [n_rows][d] KVQ_F16 or KVQ_F32;  out [n_rows][d] KVQ_F16 or KVQ_F32
+ * out may equal in (same dtype); other overlaps are not allowed.  Pointers
+ * aligned to their element size; 16-byte rows take the fast path.
+ * KVQ_E_ARG for other d, dtypes or a null pointer with n_rows > 0.       */
+kvq_status kvq_hadamard(const void* in, int in_dtype, void* out,
+                        int out_dtype, int64_t n_rows, int d, void* stream);
+
 /* ---------------------------------------------------------------------
  * Cache.
  * ------------------------------------------------------------------ */

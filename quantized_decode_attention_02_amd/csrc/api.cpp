@@ -395,6 +395,19 @@ kvq_status kvq_poll_error(const uint32_t* err_flag, void* stream) {
   return h ? KVQ_E_NONFINITE : KVQ_OK;
 }
 
+kvq_status kvq_hadamard(const void* in, int in_dtype, void* out, int out_dtype, int64_t n_rows,
+                        int d, void* stream) {
+  if (n_rows < 0 || d < 1 || d > kMaxD || (d & (d - 1))) return KVQ_E_ARG;
+  if ((in_dtype != KVQ_F16 && in_dtype != KVQ_F32) || (out_dtype != KVQ_F16 && out_dtype != KVQ_F32))
+    return KVQ_E_ARG;
+  if (n_rows == 0) return KVQ_OK;
+  const size_t ei = in_dtype == KVQ_F16 ? 2 : 4, eo = out_dtype == KVQ_F16 ? 2 : 4;
+  if (!in || !out || !aligned(in, ei) || !aligned(out, eo)) return KVQ_E_ARG;
+  if (in == out && in_dtype != out_dtype) return KVQ_E_ARG;
+  return hip_status(launch_hadamard(in, in_dtype == KVQ_F16, out, out_dtype == KVQ_F16, n_rows, d,
+                                    (hipStream_t)stream));
+}
+
 kvq_status kvq_fill_u32(uint32_t* dst, uint32_t value, int64_t n, void* stream) {
   if (n < 0 || (n > 0 && (!dst || !aligned(dst, 4)))) return KVQ_E_ARG;
   return hip_status(launch_fill_u32(dst, value, n, (hipStream_t)stream));

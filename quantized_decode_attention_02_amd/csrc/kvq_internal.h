@@ -118,6 +118,8 @@ hipError_t launch_dequant(const uint32_t* codes, const float* scales,
                           int axis, int group, float* out, hipStream_t s);
 hipError_t launch_fill_u32(uint32_t* dst, uint32_t v, int64_t n, hipStream_t s);
 constexpr int kStreamReadBlocks = 8192;
+hipError_t launch_hadamard(const void* in, int in_f16, void* out, int out_f16, int64_t n_rows,
+                           int d, hipStream_t s);
 hipError_t launch_stream_read(const void* src, int64_t bytes, uint32_t* sink, hipStream_t s);
 hipError_t launch_fill_f64(double* dst, double v, int64_t n, hipStream_t s);
 

@@ -997,6 +997,93 @@ __global__ void __launch_bounds__(256) salience_kernel(CacheDev c, const uint16_
 }
 
 // ---------------------------------------------------------------------------
+// Key rotation ("Quantize What Counts: More for Keys, Less for Values",
+// rotation integration; the Walsh-Hadamard step of the KQV scheme in
+// "Statistical Inference and Quality Measures of KV Cache Quantisations
+// Inspired by TurboQuant"): y = H x / sqrt(d) per row, H the Sylvester
+// Walsh-Hadamard matrix, by the fast transform in float32: stages h = 1,
+// 2, 4, ..., d/2 replace (x[i], x[i + h]) (bit h of i clear) with
+// (x[i] + x[i + h], x[i] - x[i + h]), then every element is multiplied by
+// float32(1 / sqrt(d)); a float16 output is that value rounded to nearest
+// even.  Every step is one IEEE operation, so the bits are fixed.
+// ---------------------------------------------------------------------------
+template <typename T> __device__ inline float to_f(T v);
+template <> __device__ inline float to_f<float>(float v) { return v; }
+template <> __device__ inline float to_f<uint16_t>(uint16_t v) { return h2f(v); }
+// One float32 multiply, rounded to float32.  Written as the instruction so
+// that the compiler cannot merge it with a following float16 conversion into
+// a mixed-precision fma, which would round once instead of twice.
+__device__ inline float mul_f32(float a, float b) {
+  float y;
+  asm volatile("v_mul_f32 %0, %1, %2" : "=v"(y) : "v"(a), "v"(b));
+  return y;
+}
+__device__ inline void put(float* p, float v) { *p = v; }
+__device__ inline void put(uint16_t* p, float v) {
+  *p = __builtin_bit_cast(uint16_t, (_Float16)v);
+}
+
+// Lane group of d / 8 lanes per row, eight consecutive elements per lane
+// (stages 1, 2, 4 in registers, the rest across lanes).  Rows and lanes:
+// thread t of the grid covers row t / (d / 8), elements 8 (t % (d / 8)) ..
+template <typename TI, typename TO>
+__global__ void __launch_bounds__(256) hadamard_vec_kernel(const TI* __restrict__ in, TO* __restrict__ out,
+                                                           int64_t n_rows, int lg_cpr, float scale) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int cpr = 1 << lg_cpr, d = 8 * cpr;
+  const int64_t row = t >> lg_cpr;
+  const int c8 = (int)(t & (cpr - 1));
+  const bool ok = row < n_rows;
+  const int64_t base = (ok ? row : 0) * d + 8 * c8;
+  float x[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) x[j] = to_f<TI>(in[base + j]);
+#pragma unroll
+  for (int h = 1; h < 8; h <<= 1) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (j & h) continue;
+      const float u = x[j], v = x[j + h];
+      x[j] = u + v;
+      x[j + h] = u - v;
+    }
+  }
+  // stages h = 8 c: partner lane c8 ^ c; the lane with that bit clear keeps
+  // the sum, the other the difference (its own value subtracted from the
+  // partner's)
+  for (int c = 1; c < cpr; c <<= 1) {
+    const bool upper = c8 & c;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const float p = __shfl_xor(x[j], c);
+      x[j] = upper ? p - x[j] : x[j] + p;
+    }
+  }
+  if (ok) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) put(out + base + j, mul_f32(x[j], scale));
+  }
+}
+
+// Any power of two d <= 256, any alignment: one row per thread.
+template <typename TI, typename TO>
+__global__ void __launch_bounds__(256) hadamard_row_kernel(const TI* __restrict__ in, TO* __restrict__ out,
+                                                           int64_t n_rows, int d, float scale) {
+  const int64_t row = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (row >= n_rows) return;
+  float x[kMaxD];
+  for (int i = 0; i < d; ++i) x[i] = to_f<TI>(in[row * d + i]);
+  for (int h = 1; h < d; h <<= 1)
+    for (int i = 0; i < d; ++i) {
+      if (i & h) continue;
+      const float u = x[i], v = x[i + h];
+      x[i] = u + v;
+      x[i + h] = u - v;
+    }
+  for (int i = 0; i < d; ++i) put(out + row * d + i, mul_f32(x[i], scale));
+}
+
+// ---------------------------------------------------------------------------
 // Export: strided copies into dense per-stream arrays, tail ring -> token
 // order, value tiles -> rows, key positions -> classes.
 // ---------------------------------------------------------------------------
@@ -1181,6 +1268,33 @@ hipError_t launch_stream_read(const void* src, int64_t bytes, uint32_t* sink, hi
   if (bytes <= 0) return hipSuccess;
   stream_read_kernel<<<kStreamReadBlocks, 256, 0, s>>>((const u32x4v*)src, bytes / 16, sink);
   return hipGetLastError();
+}
+
+template <typename TI, typename TO>
+hipError_t hadamard_t(const void* in, void* out, int64_t n_rows, int d, hipStream_t s) {
+  const float scale = (float)(1.0 / __builtin_sqrt((double)d));
+  const bool vec = d >= 8 && ((uintptr_t)in % (8 * sizeof(TI))) == 0 &&
+                   ((uintptr_t)out % (8 * sizeof(TO))) == 0;
+  if (vec) {
+    const int lg_cpr = __builtin_ctz(d / 8);
+    const int64_t threads = n_rows << lg_cpr;
+    hadamard_vec_kernel<TI, TO><<<(unsigned)((threads + 255) / 256), 256, 0, s>>>(
+        (const TI*)in, (TO*)out, n_rows, lg_cpr, scale);
+  } else {
+    hadamard_row_kernel<TI, TO><<<(unsigned)((n_rows + 255) / 256), 256, 0, s>>>(
+        (const TI*)in, (TO*)out, n_rows, d, scale);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_hadamard(const void* in, int in_f16, void* out, int out_f16, int64_t n_rows,
+                           int d, hipStream_t s) {
+  if (n_rows <= 0) return hipSuccess;
+  if (in_f16)
+    return out_f16 ? hadamard_t<uint16_t, uint16_t>(in, out, n_rows, d, s)
+                   : hadamard_t<uint16_t, float>(in, out, n_rows, d, s);
+  return out_f16 ? hadamard_t<float, uint16_t>(in, out, n_rows, d, s)
+                 : hadamard_t<float, float>(in, out, n_rows, d, s);
 }
 
 hipError_t launch_fill_f64(double* dst, double v, int64_t n, hipStream_t s) {

@@ -26,6 +26,7 @@ EXPORTED = [
     "kvq_append", "kvq_salience_select", "kvq_cache_check", "kvq_cache_view",
     "kvq_export", "kvq_decode_workspace_bytes", "kvq_decode_attention",
     "kvq_poll_error", "kvq_strerror", "kvq_fill_u32", "kvq_synth_normal_f16", "kvq_stream_read",
+    "kvq_hadamard",
 ]
 
 _c_i32, _c_i64, _c_u64, _c_p, _c_f = (ctypes.c_int32, ctypes.c_int64,
@@ -116,6 +117,7 @@ def lib():
         "kvq_strerror": (ctypes.c_char_p, [_c_i32]),
         "kvq_fill_u32": (_c_i32, [_c_p, ctypes.c_uint32, _c_i64, _c_p]),
         "kvq_stream_read": (_c_i32, [_c_p, _c_i64, _c_p, _c_p]),
+        "kvq_hadamard": (_c_i32, [_c_p, _c_i32, _c_p, _c_i32, _c_i64, _c_i32, _c_p]),
         "kvq_synth_normal_f16": (_c_i32, [_c_p, _c_u64, _c_i32, _c_i32,
                                           _c_i32, _c_i32, _c_i64, _c_i64,
                                           _c_i32, _c_i64, _c_p]),
@@ -199,6 +201,23 @@ def kvq_quantize_v(v, bits, group_ch, err=None):
                                 group_ch, _ptr(codes), _ptr(scales),
                                 _ptr(err), _stream()), "kvq_quantize_v")
     return codes, scales, err
+
+
+def kvq_hadamard(x, out=None, out_dtype=None):
+    """Rotate the last axis of x (float16/float32 device tensor) by the
+    normalized Walsh-Hadamard transform; out (optional, may be x) or a new
+    tensor of out_dtype (default: x's dtype)."""
+    _need_cuda(x)
+    d = x.shape[-1]
+    if out is None:
+        out = torch.empty(x.shape, dtype=out_dtype or x.dtype, device=x.device)
+    _need_cuda(out)
+    if out.shape != x.shape:
+        raise ValueError("out must have the shape of x")
+    n_rows = x.numel() // d if d else 0
+    _check(lib().kvq_hadamard(_ptr(x), _dtype(x), _ptr(out), _dtype(out),
+                              n_rows, d, _stream()), "kvq_hadamard")
+    return out
 
 
 def kvq_dequant(codes, scales, n_tok, d, bits, axis, group):
