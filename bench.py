@@ -190,6 +190,26 @@ def main():
         append_ms = ev[0].elapsed_time(ev[1])
         extra["append_4096_us_per_layer"] = round(1000 * append_ms / layers,
                                                   2)
+        # the optional key rotation of such a chunk (kvq_hadamard: fp16 in
+        # and out, 4096 x 32 rows of 128) and of one step's queries
+        kr = torch.empty_like(kc[0])
+        qh = torch.empty((1, Hq, D), dtype=torch.float16, device=dev)
+        rot = {"keys": [], "query": []}
+        for r in range(6):
+            for name, (src, dst) in (("keys", (kc[r % layers], kr)),
+                                     ("query", (qh, qh))):
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                torch.cuda._sleep(1 << 21)
+                e0.record(stream)
+                kvq.kvq_hadamard(src, out=dst)
+                e1.record(stream)
+                torch.cuda.synchronize()
+                if r:
+                    rot[name].append(1000 * e0.elapsed_time(e1))
+        extra["rotate_keys_4096_us_per_layer"] = round(float(np.median(rot["keys"])), 2)
+        extra["rotate_query_us"] = round(float(np.median(rot["query"])), 2)
+        del kr, qh
         del kc, vc
         for c in caches:
             assert c.kvq_cache_check() == kvq.KVQ_OK

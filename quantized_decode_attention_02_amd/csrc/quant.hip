@@ -1019,6 +1019,40 @@ __device__ inline float mul_f32(float a, float b) {
   return y;
 }
 __device__ inline void put(float* p, float v) { *p = v; }
+__device__ inline void load8(const uint16_t* p, float* x) {
+  const uint4 w = *(const uint4*)p;
+  const uint32_t wv[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int j = 0; j < 8; ++j) x[j] = h2f((uint16_t)(wv[j >> 1] >> (16 * (j & 1))));
+}
+__device__ inline void load8(const float* p, float* x) {
+  const float4 a = *(const float4*)p, b = *(const float4*)(p + 4);
+  x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+  x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+}
+__device__ inline uint32_t f16_bits(float v) { return __builtin_bit_cast(uint16_t, (_Float16)v); }
+__device__ inline void store8(uint16_t* p, const float* x) {
+  *(uint4*)p = make_uint4(f16_bits(x[0]) | f16_bits(x[1]) << 16, f16_bits(x[2]) | f16_bits(x[3]) << 16,
+                          f16_bits(x[4]) | f16_bits(x[5]) << 16, f16_bits(x[6]) | f16_bits(x[7]) << 16);
+}
+__device__ inline void store8(float* p, const float* x) {
+  *(float4*)p = make_float4(x[0], x[1], x[2], x[3]);
+  *(float4*)(p + 4) = make_float4(x[4], x[5], x[6], x[7]);
+}
+// x of lane (this lane xor c), c < 32: ds_swizzle in bit-mask mode
+// (and-mask 0x1F, or-mask 0, xor-mask c, within 32-lane halves)
+__device__ inline float xor_lane(float x, int c) {
+  const int v = __builtin_bit_cast(int, x);
+  int r;
+  switch (c) {
+    case 1: r = __builtin_amdgcn_ds_swizzle(v, 0x041F); break;
+    case 2: r = __builtin_amdgcn_ds_swizzle(v, 0x081F); break;
+    case 4: r = __builtin_amdgcn_ds_swizzle(v, 0x101F); break;
+    case 8: r = __builtin_amdgcn_ds_swizzle(v, 0x201F); break;
+    default: r = __builtin_amdgcn_ds_swizzle(v, 0x401F); break;  // 16
+  }
+  return __builtin_bit_cast(float, r);
+}
 __device__ inline void put(uint16_t* p, float v) {
   *p = __builtin_bit_cast(uint16_t, (_Float16)v);
 }
@@ -1035,9 +1069,9 @@ __global__ void __launch_bounds__(256) hadamard_vec_kernel(const TI* __restrict_
   const int c8 = (int)(t & (cpr - 1));
   const bool ok = row < n_rows;
   const int64_t base = (ok ? row : 0) * d + 8 * c8;
+  // the launcher passes 16-byte aligned rows (8 * sizeof(T) bytes a lane)
   float x[8];
-#pragma unroll
-  for (int j = 0; j < 8; ++j) x[j] = to_f<TI>(in[base + j]);
+  load8(in + base, x);
 #pragma unroll
   for (int h = 1; h < 8; h <<= 1) {
 #pragma unroll
@@ -1051,17 +1085,70 @@ __global__ void __launch_bounds__(256) hadamard_vec_kernel(const TI* __restrict_
   // stages h = 8 c: partner lane c8 ^ c; the lane with that bit clear keeps
   // the sum, the other the difference (its own value subtracted from the
   // partner's)
-  for (int c = 1; c < cpr; c <<= 1) {
+#pragma unroll
+  for (int c = 1; c < 32; c <<= 1) {
+    if (c >= cpr) break;
     const bool upper = c8 & c;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const float p = __shfl_xor(x[j], c);
+      const float p = xor_lane(x[j], c);
       x[j] = upper ? p - x[j] : x[j] + p;
     }
   }
   if (ok) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) put(out + base + j, mul_f32(x[j], scale));
+    for (int j = 0; j < 8; ++j) x[j] = mul_f32(x[j], scale);
+    store8(out + base, x);
+  }
+}
+
+// d >= 32: thirty-two consecutive elements per lane, d / 32 lanes per row
+// (stages 1 .. 16 in registers; 32, 64, 128 across lanes: DPP quad
+// permutations for lane xor 1 and 2, a swizzle for xor 4).
+__device__ inline float lane_xor1(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0xB1, 0xF, 0xF, false));
+}
+__device__ inline float lane_xor2(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x4E, 0xF, 0xF, false));
+}
+template <typename TI, typename TO>
+__global__ void __launch_bounds__(256) hadamard_vec32_kernel(const TI* __restrict__ in, TO* __restrict__ out,
+                                                             int64_t n_rows, int lg_lpr, float scale) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int lpr = 1 << lg_lpr, d = 32 * lpr;
+  const int64_t row = t >> lg_lpr;
+  const int part = (int)(t & (lpr - 1));
+  const bool ok = row < n_rows;
+  const int64_t base = (ok ? row : 0) * d + 32 * part;
+  float x[32];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) load8(in + base + 8 * q, x + 8 * q);
+#pragma unroll
+  for (int h = 1; h < 32; h <<= 1) {
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+      if (j & h) continue;
+      const float u = x[j], v = x[j + h];
+      x[j] = u + v;
+      x[j + h] = u - v;
+    }
+  }
+  // stages 32 c: partner lane part ^ c (every lane of the wave takes part)
+#pragma unroll
+  for (int c = 1; c < 8; c <<= 1) {
+    if (c >= lpr) break;
+    const bool upper = part & c;
+#pragma unroll
+    for (int j = 0; j < 32; ++j) {
+      const float p = c == 1 ? lane_xor1(x[j]) : (c == 2 ? lane_xor2(x[j]) : xor_lane(x[j], 4));
+      x[j] = upper ? p - x[j] : x[j] + p;
+    }
+  }
+  if (ok) {
+#pragma unroll
+    for (int j = 0; j < 32; ++j) x[j] = mul_f32(x[j], scale);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) store8(out + base + 8 * q, x + 8 * q);
   }
 }
 
@@ -1275,7 +1362,12 @@ hipError_t hadamard_t(const void* in, void* out, int64_t n_rows, int d, hipStrea
   const float scale = (float)(1.0 / __builtin_sqrt((double)d));
   const bool vec = d >= 8 && ((uintptr_t)in % (8 * sizeof(TI))) == 0 &&
                    ((uintptr_t)out % (8 * sizeof(TO))) == 0;
-  if (vec) {
+  if (vec && d >= 32) {
+    const int lg_lpr = __builtin_ctz(d / 32);
+    const int64_t threads = n_rows << lg_lpr;
+    hadamard_vec32_kernel<TI, TO><<<(unsigned)((threads + 255) / 256), 256, 0, s>>>(
+        (const TI*)in, (TO*)out, n_rows, lg_lpr, scale);
+  } else if (vec) {
     const int lg_cpr = __builtin_ctz(d / 8);
     const int64_t threads = n_rows << lg_cpr;
     hadamard_vec_kernel<TI, TO><<<(unsigned)((threads + 255) / 256), 256, 0, s>>>(

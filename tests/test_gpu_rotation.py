@@ -23,7 +23,7 @@ def say(*a):
     print(*a, flush=True)
 
 
-@pytest.mark.parametrize("d", [1, 2, 4, 8, 16, 64, 128, 256])
+@pytest.mark.parametrize("d", [1, 2, 4, 8, 16, 32, 64, 128, 256])
 @pytest.mark.parametrize("tin,tout", [(torch.float16, torch.float16),
                                       (torch.float16, torch.float32),
                                       (torch.float32, torch.float32),
