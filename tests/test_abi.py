@@ -86,6 +86,18 @@ def test_host_argument_errors_enqueue_nothing():
                             ctypes.byref(h), None) == kvq.KVQ_E_ARG
     assert L.kvq_synth_normal_f16(p, 1, 9, 0, 0, 1, 0, 1, 8, 8, None) == \
         kvq.KVQ_E_ARG
+    # rotation: d must be a power of two in 1..256, dtypes f16/f32, and an
+    # in-place call keeps its dtype; zero rows is a successful no-op
+    for d in (0, 3, 96, 512):
+        assert L.kvq_hadamard(p, kvq.KVQ_F16, p, kvq.KVQ_F16, 4, d, None) == \
+            kvq.KVQ_E_ARG
+    assert L.kvq_hadamard(p, 7, p, kvq.KVQ_F16, 4, 64, None) == kvq.KVQ_E_ARG
+    assert L.kvq_hadamard(p, kvq.KVQ_F16, p, kvq.KVQ_F32, 4, 64, None) == \
+        kvq.KVQ_E_ARG
+    assert L.kvq_hadamard(ctypes.c_void_p(257), kvq.KVQ_F32, p, kvq.KVQ_F32,
+                          4, 64, None) == kvq.KVQ_E_ARG
+    assert L.kvq_hadamard(None, kvq.KVQ_F16, p, kvq.KVQ_F16, 0, 64, None) == \
+        kvq.KVQ_OK
 
 
 def test_view_validation_and_empty_decode():
