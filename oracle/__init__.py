@@ -17,10 +17,11 @@ and in the pages' order:
 * attention.py float64 stable-softmax attention over dequantized K, V
 * bytes_model.py  payload byte accounting
 * rotation.py  key-only Walsh-Hadamard rotation (fast transform in float32)
+* rope.py      rotary embedding of pre-RoPE cached keys at decode
 
 Parity status: every function is pinned by ``tests/test_oracle_*.py`` against
 values printed on the pages, closed forms, invariants, brute force or library
 routines; none is "parity unpinned".
 """
 
-from . import codec, salience, cache, attention, bytes_model, rotation  # noqa: F401
+from . import codec, salience, cache, attention, bytes_model, rotation, rope  # noqa: F401

@@ -13,7 +13,7 @@ Sources (page title, section):
   measure is the L2 norm of (output - reference) over the L2 norm of the
   reference.
 
-Readings (listed in DESIGN.md): query head h reads KV head h // (Hq/Hkv);
+Readings where the pages leave a step open: query head h reads KV head h // (Hq/Hkv);
 the scale is 1/sqrt(D); there is no mask (a decoding query sees every cached
 token); the output is float32-comparable float64 [Hq][D].
 """

@@ -13,7 +13,7 @@ Sources (page title, section):
 * "KV quantization axes ...", "What rows and columns mean": the symmetric
   rule used for every quantized group (oracle.codec).
 
-Readings (listed in DESIGN.md):
+Readings where the pages leave a step open:
 
 * flush-on-overflow: the tail holds up to R tokens; when one more token
   arrives at a full tail, its oldest G tokens are quantized together as one

@@ -20,7 +20,7 @@ Sources (page title, section):
 * "MixKVQ: Query-Aware Mixed-Precision KV Cache Quantization ...", Figure 3:
   some key channels are kept in BF16.
 
-Readings where the pages leave a step open (each listed in the design doc):
+Readings where the pages leave a step open:
 
 * the largest code for b bits is qmax = 2**(b-1) - 1 (the page prints only
   the int8 value 127), so int2 codes are {-1, 0, 1};

@@ -12,7 +12,7 @@ Sources (page title, section):
   Inspired by TurboQuant", the KQV scheme: a Walsh-Hadamard transform is
   applied before scalar quantization.
 
-Readings where the pages leave a step open (each listed in the design doc):
+Readings where the pages leave a step open:
 
 * the rotation is the Sylvester Walsh-Hadamard matrix of order d (a power
   of two) scaled by 1/sqrt(d), with no random sign flips, so it is

@@ -9,7 +9,7 @@ channel (I) and the channel's key scale (S); the channels with the highest
 product are kept in BF16, the next ones in INT4, the rest in INT2.  Figure 4
 caption: salience is refreshed every R tokens inside the window.
 
-Readings (listed in DESIGN.md):
+Readings where the pages leave a step open:
 
 * I_d is the plain sum of |q| over the last W query rows and over the query
   heads that share the KV head (a sum, not a mean: dividing every channel by
