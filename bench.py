@@ -406,6 +406,44 @@ def main():
         },
         "bytes_per_step": int(bytes_step),
     }
+    # The same caches read as keys stored before the rotary embedding
+    # (kvq_decode_attention_rope), timed apart from the step.  Vector-ALU
+    # bound: per quantized token and KV head the weights of the key codes
+    # take 2 FMA per channel and query head, their products 1, the value
+    # sums 1 (4 g D FMA); the peak is the fp32 vector rate without packed
+    # math, 256 CUs x 4 SIMDs x 16 lanes x 2 flops x 2.4 GHz = 78.6 TFLOP/s.
+    rope_us = {}
+    for pairing in ("half", "interleaved"):
+        ts = []
+        for r in range(4):
+            if flush_buf is not None:
+                flush_buf.view(torch.float32).sum()
+            evs = [[torch.cuda.Event(enable_timing=True) for _ in range(2)]
+                   for _ in caches]
+            for L, c in enumerate(caches):
+                view = c.kvq_cache_view()
+                evs[L][0].record(stream)
+                kvq.kvq_decode_attention_rope(view, q[L], pairing=pairing,
+                                              workspace=ws, out=out)
+                evs[L][1].record(stream)
+            torch.cuda.synchronize()
+            if r:
+                ts += [1000 * e[0].elapsed_time(e[1]) for e in evs]
+        rope_us[pairing] = float(np.median(ts))
+    g = Hq // Hkv
+    fma = sum(4 * g * v.head_dim * v.n_quant * v.batch * v.kv_heads
+              for v in views) / len(views)
+    t_h = rope_us["half"] * 1e-6
+    extra["rope_decode"] = {
+        "us_per_call": {k: round(x, 2) for k, x in rope_us.items()},
+        "bound": "alu",
+        "fma_per_launch": int(fma),
+        "achieved_tflops": round(2 * fma / t_h / 1e12, 2),
+        "peak_tflops": 78.6,
+        "frac": round(2 * fma / t_h / 78.6e12, 4),
+        "hbm_gbs": round(bytes_launch / t_h / 1e9, 1),
+        "kernel": "decode_rope_kernel (+ general kernel for fp16 sink/tail, "
+                  "merge_kernel)"}
     if "salience_select_us" in extra:
         extra["decode_plus_salience_us"] = round(
             res["decode_call_us"]["median"] + extra["salience_select_us"], 2)

@@ -295,6 +295,43 @@ kvq_status kvq_decode_attention(const kvq_kv_view* v, const void* q,
                                 void* workspace, size_t ws_bytes,
                                 void* stream);
 
+/* Keys cached before the rotary position embedding ("KVQuant: Towards 10
+ * Million Context Length LLM Inference with KV Cache Quantization",
+ * "Approach" and the table of measured effects: per-channel key
+ * quantization before RoPE).  Frequency f = 0 .. D/2 - 1 turns by
+ * theta_f = base^(-2f/D) radians per position; at position p the channel
+ * pair (a, b) of frequency f maps (x_a, x_b) to
+ * (x_a cos - x_b sin, x_a sin + x_b cos) with the angle p * theta_f.      */
+enum {
+  KVQ_ROPE_HALF = 0,        /* pairs channel f with channel f + D/2 */
+  KVQ_ROPE_INTERLEAVED = 1  /* pairs channel 2f with channel 2f + 1 */
+};
+
+typedef struct {
+  double base;       /* > 0, finite (10000 in the usual models) */
+  int32_t pairing;   /* KVQ_ROPE_HALF or KVQ_ROPE_INTERLEAVED */
+  int32_t reserved;  /* 0 */
+  int64_t pos0;      /* position of cache-order token 0, >= 0 */
+} kvq_rope;
+
+/* Decode attention as kvq_decode_attention, over a cache whose keys (sink,
+ * quantized groups and tail alike) were appended before the rotary
+ * embedding: the dequantized key of cache-order token i is rotated at
+ * position pos0 + i before its product with q.  q is the query already
+ * rotated at its own position.  D must be even and pos0 + tokens <= 2^40
+ * (else KVQ_E_ARG).  Uniform int8/int4/int2 keys with int4/int2 value
+ * tiles, D = 128, G a multiple of 32, Gv >= 16 and 1 to 8 query heads
+ * per KV head run a dedicated kernel (one launch per pair of query heads
+ * of a KV head, per head when that count is odd); every other view (and
+ * KVQ_DECODE_GENERIC) the general kernel.  The workspace is sized by
+ * kvq_decode_workspace_bytes.  Angles are reduced in float64 and the
+ * cosines and sines evaluated in float32.                                */
+kvq_status kvq_decode_attention_rope(const kvq_kv_view* v, const kvq_rope* rope,
+                                     const void* q, int dtype, int n_q_heads,
+                                     float sm_scale, float* out, int n_splits,
+                                     int flags, void* workspace, size_t ws_bytes,
+                                     void* stream);
+
 /* ---------------------------------------------------------------------
  * Errors and utilities.
  * ------------------------------------------------------------------ */

@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 #include <stdlib.h>
+#include <math.h>
 #include <string.h>
 
 #include "kvq_internal.h"
@@ -350,6 +351,10 @@ size_t kvq_decode_workspace_bytes(const kvq_kv_view* v, int n_q_heads, int n_spl
     int pm = mfma_decode_parts(*v, n_q_heads, n_splits);
     if (pm > parts) parts = pm;
   }
+  if (rope_fast_eligible(*v, n_q_heads)) {
+    int pr = rope_fast_parts(*v, n_q_heads, n_splits) + rope_fp16_parts(*v);
+    if (pr > parts) parts = pr;
+  }
   return (size_t)v->batch * n_q_heads * parts * (v->head_dim + 2) * sizeof(float);
 }
 
@@ -382,6 +387,52 @@ kvq_status kvq_decode_attention(const kvq_kv_view* v, const void* q, int dtype,
     parts = generic_parts(v, n_splits);
     e = launch_decode_generic(*v, q, dtype == KVQ_F16, n_q_heads, sm_scale, partials,
                               parts, s);
+  }
+  if (e == hipSuccess) e = launch_merge(partials, v->batch, n_q_heads, v->head_dim, parts, out, s);
+  return hip_status(e);
+}
+
+kvq_status kvq_decode_attention_rope(const kvq_kv_view* v, const kvq_rope* rope, const void* q,
+                                     int dtype, int n_q_heads, float sm_scale, float* out,
+                                     int n_splits, int flags, void* workspace, size_t ws_bytes,
+                                     void* stream) {
+  if (!view_ok(v) || !rope || !q || !out || !workspace) return KVQ_E_ARG;
+  if (dtype != KVQ_F16 && dtype != KVQ_F32) return KVQ_E_ARG;
+  if (n_q_heads < 1 || n_q_heads % v->kv_heads || n_splits < 0 || n_splits > 16384)
+    return KVQ_E_ARG;
+  if (flags != KVQ_DECODE_AUTO && flags != KVQ_DECODE_GENERIC) return KVQ_E_ARG;
+  if (!aligned(q, dtype == KVQ_F32 ? 4 : 2) || !aligned(out, 4) || !aligned(workspace, 4))
+    return KVQ_E_ARG;
+  if (!(sm_scale > 0.0f) || !__builtin_isfinite(sm_scale)) return KVQ_E_ARG;
+  if (v->head_dim % 2) return KVQ_E_ARG;
+  if (!(rope->base > 0.0) || !__builtin_isfinite(rope->base)) return KVQ_E_ARG;
+  if (rope->pairing != KVQ_ROPE_HALF && rope->pairing != KVQ_ROPE_INTERLEAVED) return KVQ_E_ARG;
+  const int64_t N = v->n_sink + v->n_quant + v->n_tail;
+  if (N == 0) return KVQ_E_ARG;
+  if (rope->pos0 < 0 || rope->pos0 > ((int64_t)1 << 40) - N) return KVQ_E_ARG;
+  if (ws_bytes < kvq_decode_workspace_bytes(v, n_q_heads, n_splits)) return KVQ_E_ARG;
+  if ((int64_t)v->batch * n_q_heads > 0x7FFFFFFF || v->batch > 65535) return KVQ_E_UNSUPPORTED;
+  hipStream_t s = (hipStream_t)stream;
+  float* partials = (float*)workspace;
+  RopeDev rd{};
+  rd.base = rope->base;
+  rd.interleaved = rope->pairing == KVQ_ROPE_INTERLEAVED;
+  rd.pos0 = rope->pos0;
+  for (int f = 0; f < v->head_dim / 2; ++f)
+    rd.phi[f] = pow(rope->base, -2.0 * f / v->head_dim) * 0.15915494309189533577;  // / (2 pi)
+  hipError_t e;
+  int parts;
+  if (flags == KVQ_DECODE_AUTO && rope_fast_eligible(*v, n_q_heads)) {
+    const int pf = rope_fast_parts(*v, n_q_heads, n_splits);
+    parts = pf + rope_fp16_parts(*v);
+    e = launch_decode_rope(*v, q, dtype == KVQ_F16, n_q_heads, sm_scale, rd, partials, pf, s);
+  } else {
+    const size_t lds = generic_lds(n_q_heads / v->kv_heads, v->head_dim) +
+                       sizeof(float) * v->head_dim * (1 + 128);
+    if (lds > 160 * 1024) return KVQ_E_UNSUPPORTED;
+    parts = generic_parts(v, n_splits);
+    e = launch_decode_generic_range(*v, q, dtype == KVQ_F16, n_q_heads, sm_scale, partials, 0,
+                                    N, parts, 0, parts, &rd, s);
   }
   if (e == hipSuccess) e = launch_merge(partials, v->batch, n_q_heads, v->head_dim, parts, out, s);
   return hip_status(e);

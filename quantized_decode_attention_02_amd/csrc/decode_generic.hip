@@ -8,9 +8,16 @@
 // sm_scale * log2(e)), so exp2 replaces exp.  Each split writes a partial
 // (m, l, o): m the largest score, l = sum 2^(s - m), o = sum 2^(s - m) v_hat;
 // the merge combines partials with the log-sum-exp rule.
+//
+// With a rotary embedding (keys cached before it), the key of cache-order
+// token i is turned at position pos0 + i before the product with q (see
+// rope_math.h); that path computes every cosine and sine it uses and is
+// meant for the views the dedicated kernel does not cover, and for the
+// few fp16 sink and tail tokens.
 #include <hip/hip_runtime.h>
 
 #include "kvq_internal.h"
+#include "rope_math.h"
 
 namespace kvq {
 namespace {
@@ -91,21 +98,24 @@ template <> __device__ inline float ldq<uint16_t>(const uint16_t* p, int64_t i) 
   return h2f(p[i]);
 }
 
-template <typename QT>
+template <typename QT, bool ROPE>
 __global__ void __launch_bounds__(kThreads)
 decode_generic_kernel(kvq_kv_view v, const QT* __restrict__ q, int Hq,
                       float qscale, float* __restrict__ partials,
                       int64_t range_lo, int64_t range_hi, int n_parts,
-                      int part_offset, int part_stride) {
+                      int part_offset, int part_stride, int64_t gap_at, int64_t gap_len,
+                      RopeDev rope) {
   extern __shared__ float smem[];
   const int D = v.head_dim;
   const int g = Hq / v.kv_heads;
-  float* qs = smem;                  // [g][D]
+  double* phis = (double*)smem;      // [D/2] turns per position (rotary only)
+  float* qs = smem + (ROPE ? D : 0); // [g][D]
   float* ps = qs + g * D;            // [g][kChunkTok]
   float* os = ps + g * kChunkTok;    // [g][D]
   float* ms = os + g * D;            // [g]
   float* ls = ms + g;                // [g]
   float* as = ls + g;                // [g]
+  float* kr = as + g;                // [kChunkTok][D] turned keys (rotary only)
   const int tid = threadIdx.x;
   const int part = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int64_t s = (int64_t)b * v.kv_heads + kvh;
@@ -123,14 +133,37 @@ decode_generic_kernel(kvq_kv_view v, const QT* __restrict__ q, int Hq,
     ms[tid] = -INFINITY;
     ls[tid] = 0.0f;
   }
+  if (ROPE)
+    for (int f = tid; f < D / 2; f += kThreads) phis[f] = rope.phi[f];
   __syncthreads();
 
   for (int64_t c0 = t_lo; c0 < t_hi; c0 += kChunkTok) {
     const int n = (int)min((int64_t)kChunkTok, t_hi - c0);
+    if (ROPE) {
+      // turn the chunk's keys, one (token, frequency) pair per item: pair
+      // (a, b) of frequency f by the angle (pos0 + i) * theta_f
+      const int hd = D / 2;
+      for (int i = tid; i < n * hd; i += kThreads) {
+        const int t = i / hd, f = i % hd;
+        const int a = rope.interleaved ? 2 * f : f;
+        const int bb = rope.interleaved ? 2 * f + 1 : f + hd;
+        const int64_t ci = c0 + t < gap_at ? c0 + t : c0 + t + gap_len;
+        const float2 cs = rope_cos_sin(rope_turns((double)(rope.pos0 + ci), phis[f]));
+        const float ka = kdeq(v, s, ci, a), kb = kdeq(v, s, ci, bb);
+        kr[t * D + a] = ka * cs.x - kb * cs.y;
+        kr[t * D + bb] = ka * cs.y + kb * cs.x;
+      }
+      __syncthreads();
+    }
     for (int i = tid; i < n * g; i += kThreads) {
       const int t = i % n, h = i / n;
       float acc = 0.0f;
-      for (int d = 0; d < D; ++d) acc += qs[h * D + d] * kdeq(v, s, c0 + t, d);
+      if (ROPE) {
+        for (int d = 0; d < D; ++d) acc += qs[h * D + d] * kr[t * D + d];
+      } else {
+        const int64_t ci = c0 + t < gap_at ? c0 + t : c0 + t + gap_len;
+        for (int d = 0; d < D; ++d) acc += qs[h * D + d] * kdeq(v, s, ci, d);
+      }
       ps[h * kChunkTok + t] = acc;
     }
     __syncthreads();
@@ -155,7 +188,10 @@ decode_generic_kernel(kvq_kv_view v, const QT* __restrict__ q, int Hq,
     for (int i = tid; i < g * D; i += kThreads) {
       const int h = i / D, d = i % D;
       float acc = os[i] * as[h];
-      for (int t = 0; t < n; ++t) acc += ps[h * kChunkTok + t] * vdeq(v, s, c0 + t, d);
+      for (int t = 0; t < n; ++t) {
+        const int64_t ci = c0 + t < gap_at ? c0 + t : c0 + t + gap_len;
+        acc += ps[h * kChunkTok + t] * vdeq(v, s, ci, d);
+      }
       os[i] = acc;
     }
     __syncthreads();
@@ -251,33 +287,46 @@ merge_kernel(const float* __restrict__ partials, int D, int n_parts,
   }
 }
 
+template <bool ROPE>
+hipError_t launch_generic_t(const kvq_kv_view& v, const void* q, int f16, int Hq,
+                            float qscale, float* partials, int64_t range_lo, int64_t range_hi,
+                            int n_parts, int part_offset, int part_stride, int64_t gap_at,
+                            int64_t gap_len, const RopeDev& rope, hipStream_t s) {
+  const int g = Hq / v.kv_heads;
+  const size_t lds =
+      sizeof(float) * ((size_t)g * v.head_dim * 2 + (size_t)g * kChunkTok + 3 * (size_t)g +
+                       (ROPE ? (size_t)v.head_dim * (1 + kChunkTok) : 0));
+  dim3 grid((unsigned)n_parts, (unsigned)v.kv_heads, (unsigned)v.batch);
+  const void* fn = f16 ? (const void*)decode_generic_kernel<uint16_t, ROPE>
+                       : (const void*)decode_generic_kernel<float, ROPE>;
+  if (lds > 64 * 1024) {
+    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  if (f16)
+    decode_generic_kernel<uint16_t, ROPE><<<grid, kThreads, lds, s>>>(
+        v, (const uint16_t*)q, Hq, qscale, partials, range_lo, range_hi, n_parts, part_offset,
+        part_stride, gap_at, gap_len, rope);
+  else
+    decode_generic_kernel<float, ROPE><<<grid, kThreads, lds, s>>>(
+        v, (const float*)q, Hq, qscale, partials, range_lo, range_hi, n_parts, part_offset,
+        part_stride, gap_at, gap_len, rope);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_decode_generic_range(const kvq_kv_view& v, const void* q, int f16,
                                        int Hq, float sm_scale, float* partials,
                                        int64_t range_lo, int64_t range_hi, int n_parts,
-                                       int part_offset, int part_stride, hipStream_t s) {
-  const int g = Hq / v.kv_heads;
-  const size_t lds = sizeof(float) * ((size_t)g * v.head_dim * 2 +
-                                      (size_t)g * kChunkTok + 3 * (size_t)g);
-  dim3 grid((unsigned)n_parts, (unsigned)v.kv_heads, (unsigned)v.batch);
+                                       int part_offset, int part_stride, const RopeDev* rope,
+                                       hipStream_t s, int64_t gap_at, int64_t gap_len) {
   const float qscale = sm_scale * kLog2e;
-  if (lds > 64 * 1024) {
-    hipError_t e = f16 ? hipFuncSetAttribute((const void*)decode_generic_kernel<uint16_t>,
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds)
-                       : hipFuncSetAttribute((const void*)decode_generic_kernel<float>,
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
-  }
-  if (f16)
-    decode_generic_kernel<uint16_t><<<grid, kThreads, lds, s>>>(
-        v, (const uint16_t*)q, Hq, qscale, partials, range_lo, range_hi, n_parts, part_offset,
-        part_stride);
-  else
-    decode_generic_kernel<float><<<grid, kThreads, lds, s>>>(
-        v, (const float*)q, Hq, qscale, partials, range_lo, range_hi, n_parts, part_offset,
-        part_stride);
-  return hipGetLastError();
+  if (rope)
+    return launch_generic_t<true>(v, q, f16, Hq, qscale, partials, range_lo, range_hi, n_parts,
+                                  part_offset, part_stride, gap_at, gap_len, *rope, s);
+  return launch_generic_t<false>(v, q, f16, Hq, qscale, partials, range_lo, range_hi, n_parts,
+                                 part_offset, part_stride, gap_at, gap_len, RopeDev{}, s);
 }
 
 hipError_t launch_decode_generic(const kvq_kv_view& v, const void* q, int f16,
@@ -285,7 +334,7 @@ hipError_t launch_decode_generic(const kvq_kv_view& v, const void* q, int f16,
                                  int n_parts, hipStream_t s) {
   const int64_t N = v.n_sink + v.n_quant + v.n_tail;
   return launch_decode_generic_range(v, q, f16, Hq, sm_scale, partials, 0, N, n_parts, 0,
-                                     n_parts, s);
+                                     n_parts, nullptr, s);
 }
 
 hipError_t launch_merge(const float* partials, int B, int Hq, int D,

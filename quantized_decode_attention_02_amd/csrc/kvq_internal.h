@@ -6,6 +6,7 @@
 #include <stdint.h>
 
 #include "../../include/kvq.h"
+#include "rope_math.h"
 
 namespace kvq {
 
@@ -150,17 +151,33 @@ hipError_t launch_synth(uint16_t* out, uint64_t seed, int tensor, int layer,
 hipError_t launch_decode_generic(const kvq_kv_view& v, const void* q, int f16,
                                  int Hq, float sm_scale, float* partials,
                                  int n_parts, hipStream_t s);
-// Tokens [range_lo, range_hi) of the cache order split into n_parts
-// partials written at slots part_offset .. of part_stride per head.
+// Tokens [range_lo, range_hi) split into n_parts partials written at slots
+// part_offset .. of part_stride per head.  Range index i is cache-order
+// token i below gap_at and token i + gap_len from there on (so the sink and
+// the tail, with the quantized tokens between them skipped, make one range).
 hipError_t launch_decode_generic_range(const kvq_kv_view& v, const void* q, int f16,
                                        int Hq, float sm_scale, float* partials,
                                        int64_t range_lo, int64_t range_hi, int n_parts,
-                                       int part_offset, int part_stride, hipStream_t s);
+                                       int part_offset, int part_stride, const RopeDev* rope,
+                                       hipStream_t s, int64_t gap_at = INT64_MAX,
+                                       int64_t gap_len = 0);
 bool mfma_decode_eligible(const kvq_kv_view& v, int Hq);
 int mfma_decode_parts(const kvq_kv_view& v, int Hq, int n_splits);
 hipError_t launch_decode_mfma(const kvq_kv_view& v, const void* q, int f16,
                               int Hq, float sm_scale, float* partials,
                               int n_splits, hipStream_t s);
+// Rotary decode over keys cached before the embedding (decode_rope.hip).
+// The dedicated kernel covers uniform int8/int4/int2 keys, int4/int2 value
+// tiles, D = 128, G a multiple of 32, Gv >= 16 and 1 to 8 query heads per
+// KV head; it writes rope_fast_parts(...) partials for the quantized
+// tokens and rope_fp16_parts(v) more (sink, then tail; 64 tokens each) from
+// the general kernel.
+bool rope_fast_eligible(const kvq_kv_view& v, int Hq);
+int rope_fast_parts(const kvq_kv_view& v, int Hq, int n_splits);
+int rope_fp16_parts(const kvq_kv_view& v);
+hipError_t launch_decode_rope(const kvq_kv_view& v, const void* q, int f16, int Hq,
+                              float sm_scale, const RopeDev& rope, float* partials,
+                              int n_parts, hipStream_t s);
 hipError_t launch_merge(const float* partials, int B, int Hq, int D,
                         int n_parts, float* out, hipStream_t s);
 

@@ -19,6 +19,7 @@ KVQ_F32, KVQ_F16 = 0, 1
 KVQ_PER_CHANNEL, KVQ_PER_TOKEN = 0, 1
 KVQ_V_ROWS, KVQ_V_TILE32 = 0, 1
 KVQ_DECODE_AUTO, KVQ_DECODE_GENERIC = 0, 1
+KVQ_ROPE_HALF, KVQ_ROPE_INTERLEAVED = 0, 1
 
 EXPORTED = [
     "kvq_words", "kvq_quantize_k", "kvq_quantize_v", "kvq_dequant",
@@ -26,7 +27,7 @@ EXPORTED = [
     "kvq_append", "kvq_salience_select", "kvq_cache_check", "kvq_cache_view",
     "kvq_export", "kvq_decode_workspace_bytes", "kvq_decode_attention",
     "kvq_poll_error", "kvq_strerror", "kvq_fill_u32", "kvq_synth_normal_f16", "kvq_stream_read",
-    "kvq_hadamard",
+    "kvq_hadamard", "kvq_decode_attention_rope",
 ]
 
 _c_i32, _c_i64, _c_u64, _c_p, _c_f = (ctypes.c_int32, ctypes.c_int64,
@@ -40,6 +41,11 @@ class CacheCfg(ctypes.Structure):
                 ("group_ch", _c_i32), ("residual", _c_i32), ("sink", _c_i32),
                 ("k_mixed", _c_i32), ("n_bf16", _c_i32), ("n_int4", _c_i32),
                 ("max_tokens", _c_i64)]
+
+
+class Rope(ctypes.Structure):
+    _fields_ = [("base", ctypes.c_double), ("pairing", _c_i32),
+                ("reserved", _c_i32), ("pos0", _c_i64)]
 
 
 class KvView(ctypes.Structure):
@@ -113,6 +119,9 @@ def lib():
         "kvq_decode_attention": (_c_i32, [
             ctypes.POINTER(KvView), _c_p, _c_i32, _c_i32, _c_f, _c_p, _c_i32,
             _c_i32, _c_p, ctypes.c_size_t, _c_p]),
+        "kvq_decode_attention_rope": (_c_i32, [
+            ctypes.POINTER(KvView), ctypes.POINTER(Rope), _c_p, _c_i32, _c_i32, _c_f, _c_p,
+            _c_i32, _c_i32, _c_p, ctypes.c_size_t, _c_p]),
         "kvq_poll_error": (_c_i32, [_c_p, _c_p]),
         "kvq_strerror": (ctypes.c_char_p, [_c_i32]),
         "kvq_fill_u32": (_c_i32, [_c_p, ctypes.c_uint32, _c_i64, _c_p]),
@@ -381,6 +390,32 @@ def kvq_decode_attention(view, q, sm_scale=None, n_splits=0,
         ctypes.byref(view), _ptr(q), _dtype(q), hq, sm_scale, _ptr(out),
         n_splits, flags, _ptr(workspace), workspace.numel(), _stream()),
         "kvq_decode_attention")
+    return out
+
+
+def kvq_decode_attention_rope(view, q, base=10000.0, pairing="half", pos0=0,
+                              sm_scale=None, n_splits=0, flags=KVQ_DECODE_AUTO,
+                              workspace=None, out=None):
+    """Decode over keys cached before the rotary embedding: cache-order
+    token i is rotated at position pos0 + i.  q: [B][Hq][D] f16/f32, already
+    rotated at its own position -> out [B][Hq][D] float32."""
+    _need_cuda(q)
+    B, hq, D = q.shape
+    if sm_scale is None:
+        sm_scale = 1.0 / D ** 0.5
+    pr = {"half": KVQ_ROPE_HALF, "interleaved": KVQ_ROPE_INTERLEAVED}.get(pairing, -1)
+    rope = Rope(base=base, pairing=pr, reserved=0, pos0=pos0)
+    ws_bytes = kvq_decode_workspace_bytes(view, hq, n_splits)
+    if ws_bytes == 0:
+        raise KvqError(KVQ_E_ARG, "kvq_decode_workspace_bytes")
+    if workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    if out is None:
+        out = torch.empty((B, hq, D), dtype=torch.float32, device=q.device)
+    _check(lib().kvq_decode_attention_rope(
+        ctypes.byref(view), ctypes.byref(rope), _ptr(q), _dtype(q), hq, sm_scale, _ptr(out),
+        n_splits, flags, _ptr(workspace), workspace.numel(), _stream()),
+        "kvq_decode_attention_rope")
     return out
 
 

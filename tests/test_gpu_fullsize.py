@@ -11,7 +11,7 @@ import pytest
 import torch
 
 import synth
-from oracle import attention, cache as ocache, salience
+from oracle import attention, cache as ocache, rope, salience
 from quantized_decode_attention_02_amd import kvq
 
 pytestmark = pytest.mark.gpu
@@ -58,6 +58,17 @@ def check_heads(out, q, oc, b, kvh, g):
     assert err <= TOL
 
 
+def check_heads_rope(out, q, oc, b, kvh, g, pos0=0, pairing="half"):
+    """The same cache read as keys stored before the rotary embedding."""
+    kh, vh = oc.dequantized(0, 0)
+    heads = list(range(kvh * g, (kvh + 1) * g))
+    ref = rope.attention(q[b, heads].astype(np.float64), kh[None], vh[None],
+                         pos0=pos0, pairing=pairing)
+    err = attention.max_row_relative_error(out[b, heads], ref)
+    say(f"  stream (b={b}, kvh={kvh}) rotary decode err {err:.3e}")
+    assert err <= TOL
+
+
 def build_host_cache(w, name, k_bits=None, v_bits=None, seed=7):
     ikw = {k: w[k] for k in ("outliers", "n_out", "out_factor", "frac",
                              "fmin", "fmax", "sink_factor") if k in w}
@@ -100,10 +111,14 @@ def test_gqa_128k_sampled(bits):
     out = kvq.kvq_decode_attention(view, torch.from_numpy(q).to(DEV))
     out = out.cpu().numpy()
     g = w["Hq"] // w["Hkv"]
+    pairing = "half" if kb == 4 else "interleaved"
+    out_r = kvq.kvq_decode_attention_rope(view, torch.from_numpy(q).to(DEV),
+                                          pairing=pairing, pos0=100).cpu().numpy()
     for h in (0, 5):
         oc = oracle_stream(w, k[0, h], v[0, h], k_bits=kb, v_bits=vb)
         compare_stream(view, 0, h, oc)
         check_heads(out, q, oc, 0, h, g)
+        check_heads_rope(out_r, q, oc, 0, h, g, pos0=100, pairing=pairing)
 
 
 def test_mixkvq_32k_sampled():
@@ -154,6 +169,7 @@ def test_1m_context_one_layer_sampled():
     view = c.kvq_cache_view()
     assert (view.n_sink, view.n_quant, view.n_tail) == (1, 1048448, 127)
     out = kvq.kvq_decode_attention(view, q).cpu().numpy()
+    out_r = kvq.kvq_decode_attention_rope(view, q).cpu().numpy()
     qn = q.cpu().numpy()
     assert np.array_equal(qn[0].view(np.uint16),
                           synth.counter_query(seed, layer, Hq, D).view(
@@ -163,3 +179,4 @@ def test_1m_context_one_layer_sampled():
     oc = oracle_stream(w, kh[0], vh[0])
     compare_stream(view, 0, h, oc)
     check_heads(out, qn, oc, 0, h, 1)
+    check_heads_rope(out_r, qn, oc, 0, h, 1)
