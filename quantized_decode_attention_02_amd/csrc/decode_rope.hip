@@ -90,26 +90,47 @@ __device__ constexpr int lo_e(int i) { return KB == 8 ? (i & 1) + 4 * (i >> 1) :
 template <int KB>
 __device__ constexpr int hi_e(int i) { return KB == 8 ? lo_e<KB>(i) + 2 : i + 4; }
 
-template <int KB>
+// Key words one lane loads per token.  Interleaved pairs: channels
+// 8c .. 8c + 7, one or two consecutive words.  Half pairs: channels
+// 4c .. 4c + 3 and 64 + 4c .. 64 + 4c + 3 (both members of four pairs), from
+// two words; lane channel e < 4 is 4c + e, e >= 4 is 64 + 4c + e - 4.
+template <int KB, bool INTER>
 struct KWords {
-  typedef typename std::conditional<KB == 8, u32x2, uint32_t>::type T;
+  typedef typename std::conditional<KB == 8 || !INTER, u32x2, uint32_t>::type T;
 };
 
-template <int KB>
-__device__ inline void key_pairs(typename KWords<KB>::T w, int c, half2v p[4]) {
-  if constexpr (KB == 4) {
-#pragma unroll
-    for (int i = 0; i < 4; ++i) p[i] = code_pair<4>(w >> (4 * i));
-  } else if constexpr (KB == 8) {
+// The lane's 8 codes as 4 fp16 pairs; pair i holds lane channels
+// (lo_e(i), hi_e(i)).
+template <int KB, bool INTER>
+__device__ inline void key_pairs(typename KWords<KB, INTER>::T w, int c, half2v p[4]) {
+  if constexpr (KB == 8) {
     p[0] = code_pair<8>(w[0]);
     p[1] = code_pair<8>(w[0] >> 8);
     p[2] = code_pair<8>(w[1]);
     p[3] = code_pair<8>(w[1] >> 8);
   } else {
-    const uint32_t y = w >> (16 * (c & 1));
-    const uint32_t z = (y & 0xFFu) | ((y << 8) & 0x00FF0000u);
+    uint32_t z;
+    if constexpr (KB == 4) {
+      if constexpr (INTER) {
+        z = w;
+      } else {
+        const int sh = 16 * (c & 1);
+        z = ((w[0] >> sh) & 0xFFFFu) | ((w[1] >> sh) << 16);
+      }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) p[i] = code_pair<2>(z >> (2 * i));
+      for (int i = 0; i < 4; ++i) p[i] = code_pair<4>(z >> (4 * i));
+    } else {
+      uint32_t y;
+      if constexpr (INTER) {
+        y = w >> (16 * (c & 1));
+      } else {
+        const int sh = 8 * (c & 3);
+        y = ((w[0] >> sh) & 0xFFu) | (((w[1] >> sh) & 0xFFu) << 8);
+      }
+      z = (y & 0xFFu) | ((y << 8) & 0x00FF0000u);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) p[i] = code_pair<2>(z >> (2 * i));
+    }
   }
 }
 
@@ -173,9 +194,15 @@ decode_rope_kernel(kvq_kv_view v, const QT* __restrict__ q, int Hq, float qscale
   const uint32_t* vc = v.v_codes + s * v.v_codes_stride;
   const float* vsc_base = v.v_scales + s * v.v_scales_stride;
   constexpr uint32_t KWD = kRD * KB / 32;  // key words per token
-  const uint32_t kcol = KB == 4 ? c : KB == 8 ? 2 * c : (c >> 1);
+  // first key word of the lane, and (half pairs) the second one
+  const uint32_t kcol = INTER ? (KB == 4 ? c : KB == 8 ? 2 * c : (c >> 1))
+                              : (KB == 4 ? (c >> 1) : KB == 8 ? c : (c >> 2));
+  constexpr uint32_t kcol2 = KWD / 2;
   const uint32_t vgc = c & (NG - 1);       // lanes past the value groups repeat them
-  const int fbase = INTER ? 4 * c : (8 * c) & (kRNF - 1);
+  const int fbase = 4 * c;                 // the lane's four frequencies
+  // lane channel e: its channel, and its frequency's offset from fbase
+  auto chan = [&](int e) { return INTER ? 8 * c + e : (e < 4 ? 4 * c + e : kRNF + 4 * c + e - 4); };
+  auto fi = [](int e) { return INTER ? e >> 1 : e & 3; };
 
   float m_run[GQ], l_run[GQ], o[GQ][kRBlocks];
 #pragma unroll
@@ -189,7 +216,7 @@ decode_rope_kernel(kvq_kv_view v, const QT* __restrict__ q, int Hq, float qscale
   // One register buffer per kind, refilled for the wave's next tile right
   // after its last use in the current one (offsets within a stream are
   // 32-bit: the view's eligibility bounds them).
-  typedef typename KWords<KB>::T KW;
+  typedef typename KWords<KB, INTER>::T KW;
   KW kw[kRSteps];
   u32x4 vw[VB == 4 ? 2 : 1];
   float vs[kRSteps];
@@ -198,8 +225,14 @@ decode_rope_kernel(kvq_kv_view v, const QT* __restrict__ q, int Hq, float qscale
 #pragma unroll
     for (int st = 0; st < kRSteps; ++st) {
       const uint32_t off = (row0 + 4 * st) * KWD + kcol;
-      if constexpr (KB == 8) kw[st] = ldnt((const u32x2*)(kc + off));
-      else kw[st] = ldnt(kc + off);
+      if constexpr (!INTER) {
+        kw[st][0] = ldnt(kc + off);
+        kw[st][1] = ldnt(kc + off + kcol2);
+      } else if constexpr (KB == 8) {
+        kw[st] = ldnt((const u32x2*)(kc + off));
+      } else {
+        kw[st] = ldnt(kc + off);
+      }
     }
   };
   auto load_vs = [&](int64_t T) {
@@ -227,8 +260,8 @@ decode_rope_kernel(kvq_kv_view v, const QT* __restrict__ q, int Hq, float qscale
     const int64_t grp = qt0 / v.group_tok;
     if (grp != cur_grp) {
       cur_grp = grp;
-      const float4v a = *(const float4v*)(ksc + grp * kRD + 8 * c);
-      const float4v bq = *(const float4v*)(ksc + grp * kRD + 8 * c + 4);
+      const float4v a = *(const float4v*)(ksc + grp * kRD + chan(0));
+      const float4v bq = *(const float4v*)(ksc + grp * kRD + chan(4));
       ks[0] = a[0]; ks[1] = a[1]; ks[2] = a[2]; ks[3] = a[3];
       ks[4] = bq[0]; ks[5] = bq[1]; ks[6] = bq[2]; ks[7] = bq[3];
     }
@@ -242,10 +275,10 @@ decode_rope_kernel(kvq_kv_view v, const QT* __restrict__ q, int Hq, float qscale
     float Q1[GQ][8], Q2[GQ][8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const float2 cs = L.base[wave][fbase + (INTER ? e >> 1 : e)];
+      const float2 cs = L.base[wave][fbase + fi(e)];
 #pragma unroll
       for (int h = 0; h < GQ; ++h) {
-        const float2 qq = L.qs[h][8 * c + e];
+        const float2 qq = L.qs[h][chan(e)];
         Q1[h][e] = ks[e] * (cs.x * qq.x + cs.y * qq.y);
         Q2[h][e] = ks[e] * (cs.x * qq.y - cs.y * qq.x);
       }
@@ -254,23 +287,23 @@ decode_rope_kernel(kvq_kv_view v, const QT* __restrict__ q, int Hq, float qscale
 #pragma unroll
     for (int st = 0; st < kRSteps; ++st) {
       const int j = 4 * st + r;
-      float2 t[INTER ? 4 : 8];
+      float2 t[4];
       const float4v* tp = (const float4v*)&L.tab[j][fbase];
 #pragma unroll
-      for (int k = 0; k < (INTER ? 2 : 4); ++k) {
+      for (int k = 0; k < 2; ++k) {
         const float4v x = tp[k];
         t[2 * k] = make_float2(x[0], x[1]);
         t[2 * k + 1] = make_float2(x[2], x[3]);
       }
       half2v pr[4];
-      key_pairs<KB>(kw[st], c, pr);
+      key_pairs<KB, INTER>(kw[st], c, pr);
 #pragma unroll
       for (int h = 0; h < GQ; ++h) {
         float acc = 0.0f;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int el = lo_e<KB>(i), eh = hi_e<KB>(i);
-          const float2 tl = t[INTER ? el >> 1 : el], th = t[INTER ? eh >> 1 : eh];
+          const float2 tl = t[fi(el)], th = t[fi(eh)];
           const float wl = tl.x * Q1[h][el] + tl.y * Q2[h][el];
           const float wh = th.x * Q1[h][eh] + th.y * Q2[h][eh];
           acc = __builtin_fmaf((float)pr[i][0], wl, acc);
