@@ -37,6 +37,11 @@ __device__ inline uint32_t field(uint32_t w, int j, int bits) {
   return (w >> (j * bits)) & ((1u << bits) - 1u);
 }
 
+// Ring row of past-sink index p in the tail (32-bit remainder when p fits).
+__device__ inline int64_t ring_row(int64_t p, int R) {
+  return p <= 0x7FFFFFFF ? (int64_t)((uint32_t)p % (uint32_t)R) : p % R;
+}
+
 // Dequantized key of token t (cache order: sink, quantized, tail) channel d.
 __device__ float kdeq(const kvq_kv_view& v, int64_t s, int64_t t, int d) {
   const int D = v.head_dim;
@@ -65,7 +70,7 @@ __device__ float kdeq(const kvq_kv_view& v, int64_t s, int64_t t, int d) {
     return (float)((int)field(w, k % 16, 2) - 2) * sc;
   }
   t -= v.n_quant;
-  return h2f(v.tail_k[s * v.tail_stride + ((v.n_quant + t) % v.residual) * D + d]);
+  return h2f(v.tail_k[s * v.tail_stride + ring_row(v.n_quant + t, v.residual) * D + d]);
 }
 
 __device__ float vdeq(const kvq_kv_view& v, int64_t s, int64_t t, int d) {
@@ -89,7 +94,40 @@ __device__ float vdeq(const kvq_kv_view& v, int64_t s, int64_t t, int d) {
            v.v_scales[s * v.v_scales_stride + t * ng + d / v.group_ch];
   }
   t -= v.n_quant;
-  return h2f(v.tail_v[s * v.tail_stride + ((v.n_quant + t) % v.residual) * D + d]);
+  return h2f(v.tail_v[s * v.tail_stride + ring_row(v.n_quant + t, v.residual) * D + d]);
+}
+
+// Dequantized keys (or values) of range tokens c0 .. c0 + n - 1 into
+// dst[t][D], eight channels per item: an fp16 sink or tail row moves with
+// one 16-byte load (every item's load is independent of the others), a
+// quantized row goes through kdeq / vdeq.
+__device__ inline void stage_rows(const kvq_kv_view& v, int64_t s, int64_t c0, int n,
+                                  int64_t gap_at, int64_t gap_len, bool keys, float* dst) {
+  const int D = v.head_dim;
+  const int nb = (D + 7) / 8;
+  for (int i = threadIdx.x; i < n * nb; i += blockDim.x) {
+    const int t = i / nb, d0 = 8 * (i % nb);
+    const int64_t ci = c0 + t < gap_at ? c0 + t : c0 + t + gap_len;
+    const uint16_t* row = nullptr;
+    if (ci < v.n_sink) {
+      row = (keys ? v.sink_k : v.sink_v) + s * v.sink_stride + ci * D;
+    } else if (ci >= v.n_sink + v.n_quant) {
+      row = (keys ? v.tail_k : v.tail_v) + s * v.tail_stride +
+            ring_row(ci - v.n_sink, v.residual) * D;
+    }
+    if (row && d0 + 8 <= D && ((uintptr_t)(row + d0) & 15) == 0) {
+      const uint4 w = *(const uint4*)(row + d0);
+      const uint32_t u[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        dst[t * D + d0 + 2 * k] = h2f((uint16_t)(u[k] & 0xFFFFu));
+        dst[t * D + d0 + 2 * k + 1] = h2f((uint16_t)(u[k] >> 16));
+      }
+    } else {
+      for (int d = d0; d < D && d < d0 + 8; ++d)
+        dst[t * D + d] = keys ? kdeq(v, s, ci, d) : vdeq(v, s, ci, d);
+    }
+  }
 }
 
 template <typename T> __device__ inline float ldq(const T* p, int64_t i);
@@ -140,8 +178,12 @@ decode_generic_kernel(kvq_kv_view v, const QT* __restrict__ q, int Hq,
   for (int64_t c0 = t_lo; c0 < t_hi; c0 += kChunkTok) {
     const int n = (int)min((int64_t)kChunkTok, t_hi - c0);
     if (ROPE) {
-      // turn the chunk's keys, one (token, frequency) pair per item: pair
-      // (a, b) of frequency f by the angle (pos0 + i) * theta_f
+      // the chunk's dequantized keys into LDS, eight channels per item
+      // (fp16 rows with one 16-byte load), then turned in place, one
+      // (token, frequency) pair per item: pair (a, b) of frequency f by the
+      // angle (pos0 + i) * theta_f
+      stage_rows(v, s, c0, n, gap_at, gap_len, true, kr);
+      __syncthreads();
       const int hd = D / 2;
       for (int i = tid; i < n * hd; i += kThreads) {
         const int t = i / hd, f = i % hd;
@@ -149,18 +191,31 @@ decode_generic_kernel(kvq_kv_view v, const QT* __restrict__ q, int Hq,
         const int bb = rope.interleaved ? 2 * f + 1 : f + hd;
         const int64_t ci = c0 + t < gap_at ? c0 + t : c0 + t + gap_len;
         const float2 cs = rope_cos_sin(rope_turns((double)(rope.pos0 + ci), phis[f]));
-        const float ka = kdeq(v, s, ci, a), kb = kdeq(v, s, ci, bb);
+        const float ka = kr[t * D + a], kb = kr[t * D + bb];
         kr[t * D + a] = ka * cs.x - kb * cs.y;
         kr[t * D + bb] = ka * cs.y + kb * cs.x;
       }
       __syncthreads();
     }
-    for (int i = tid; i < n * g; i += kThreads) {
+    if (ROPE) {
+      // scores from the turned keys: four lanes per (token, head), each
+      // summing every fourth channel, then a 4-lane sum
+      for (int i0 = 0; i0 < n * g * 4; i0 += kThreads) {
+        const int i = i0 + tid;
+        const int it = i >> 2, qd = i & 3;
+        const int t = it % n, h = it / n;
+        float acc = 0.0f;
+        if (i < n * g * 4)
+          for (int d = qd; d < D; d += 4) acc += qs[h * D + d] * kr[t * D + d];
+        acc += __shfl_xor(acc, 1);
+        acc += __shfl_xor(acc, 2);
+        if (i < n * g * 4 && qd == 0) ps[h * kChunkTok + t] = acc;
+      }
+    }
+    for (int i = tid; i < (ROPE ? 0 : n * g); i += kThreads) {
       const int t = i % n, h = i / n;
       float acc = 0.0f;
-      if (ROPE) {
-        for (int d = 0; d < D; ++d) acc += qs[h * D + d] * kr[t * D + d];
-      } else {
+      {
         const int64_t ci = c0 + t < gap_at ? c0 + t : c0 + t + gap_len;
         for (int d = 0; d < D; ++d) acc += qs[h * D + d] * kdeq(v, s, ci, d);
       }
@@ -185,12 +240,23 @@ decode_generic_kernel(kvq_kv_view v, const QT* __restrict__ q, int Hq,
       for (int t = 0; t < n; ++t) l += ps[tid * kChunkTok + t];
       ls[tid] = l;
     }
+    if (ROPE) {
+      // the chunk's values into the (now free) LDS rows of the turned keys
+      stage_rows(v, s, c0, n, gap_at, gap_len, false, kr);
+      __syncthreads();
+    }
     for (int i = tid; i < g * D; i += kThreads) {
       const int h = i / D, d = i % D;
       float acc = os[i] * as[h];
       for (int t = 0; t < n; ++t) {
-        const int64_t ci = c0 + t < gap_at ? c0 + t : c0 + t + gap_len;
-        acc += ps[h * kChunkTok + t] * vdeq(v, s, ci, d);
+        float vv;
+        if (ROPE) {
+          vv = kr[t * D + d];
+        } else {
+          const int64_t ci = c0 + t < gap_at ? c0 + t : c0 + t + gap_len;
+          vv = vdeq(v, s, ci, d);
+        }
+        acc += ps[h * kChunkTok + t] * vv;
       }
       os[i] = acc;
     }

@@ -25,7 +25,7 @@
 // completes each score.  Values keep the value-tile layout: lane 16 q + m
 // holds channel 16 jb + m at eight tokens of the tile and reads their
 // softmax weights, times the token's value scale, from LDS.  The fp16 sink
-// and tail tokens go through the general kernel as one range, 64 tokens per
+// and tail tokens go through the general kernel as one range, 32 tokens per
 // partial.
 #include <hip/hip_runtime.h>
 
@@ -158,7 +158,6 @@ decode_rope_kernel(kvq_kv_view v, const QT* __restrict__ q, int Hq, float qscale
   const int c = lane & 15, r = lane >> 4;  // key role: channel chunk, token
   const int q4 = r, m16 = c;               // value role: token quarter, channel
   const int NG = kRD >> gv_shift;
-  const int bpg = 1 << (gv_shift - 4);     // value blocks per value group
 
   for (int f = tid; f < kRNF; f += kRThreads) L.phi[f] = rope.phi[f];
   for (int i = tid; i < GQ * kRD; i += kRThreads) {
@@ -322,12 +321,14 @@ decode_rope_kernel(kvq_kv_view v, const QT* __restrict__ q, int Hq, float qscale
       for (int st = 1; st < kRSteps; ++st) mx = fmaxf(mx, sc[h][st]);
       mx = fmaxf(fmaxf(lane_f(mx, 0), lane_f(mx, 16)), fmaxf(lane_f(mx, 32), lane_f(mx, 48)));
       const float mnew = fmaxf(m_run[h], mx);
-      const float alpha = exp2f(m_run[h] - mnew);
+      // v_exp_f32 flushes results below 2^-126 to zero: such a weight next
+      // to the running maximum's weight 1 cannot change a float32 sum
+      const float alpha = __builtin_amdgcn_exp2f(m_run[h] - mnew);
       m_run[h] = mnew;
       float psum = 0.0f;
 #pragma unroll
       for (int st = 0; st < kRSteps; ++st) {
-        const float p = exp2f(sc[h][st] - mnew);
+        const float p = __builtin_amdgcn_exp2f(sc[h][st] - mnew);
         psum += p;
         L.pv[wave][h][c][4 * st + r] = p * vs[st];
       }
@@ -338,18 +339,15 @@ decode_rope_kernel(kvq_kv_view v, const QT* __restrict__ q, int Hq, float qscale
     if (more) load_vs(T + kRWaves);
     __builtin_amdgcn_wave_barrier();
 
-    // values: channel 16 jb + m16 at tokens tau(q4, s), s = 0..7; a value
-    // group spans bpg = Gv / 16 blocks, whose weights are read once
-    float4v wlo[GQ], whi[GQ];
+    // values: channel 16 jb + m16 at tokens tau(q4, s), s = 0..7
 #pragma unroll
     for (int jb = 0; jb < kRBlocks; ++jb) {
-      if ((jb & (bpg - 1)) == 0) {
-        const float* pw = &L.pv[wave][0][jb >> (gv_shift - 4)][4 * q4];
+      const float* pw = &L.pv[wave][0][(16 * jb) >> gv_shift][4 * q4];
+      float4v wlo[GQ], whi[GQ];
 #pragma unroll
-        for (int h = 0; h < GQ; ++h) {
-          wlo[h] = *(const float4v*)(pw + h * kRPvSlots * kRTile);
-          whi[h] = *(const float4v*)(pw + h * kRPvSlots * kRTile + 16);
-        }
+      for (int h = 0; h < GQ; ++h) {
+        wlo[h] = *(const float4v*)(pw + h * kRPvSlots * kRTile);
+        whi[h] = *(const float4v*)(pw + h * kRPvSlots * kRTile + 16);
       }
       half2v pr[4];
       if constexpr (VB == 2) {
@@ -495,7 +493,7 @@ int rope_fast_parts(const kvq_kv_view& v, int Hq, int n_splits) {
 
 int rope_fp16_parts(const kvq_kv_view& v) {
   const int64_t n = v.n_sink + v.n_tail;
-  return n > 0 ? (int)((n + 63) / 64) : 0;
+  return n > 0 ? (int)((n + 31) / 32) : 0;
 }
 
 hipError_t launch_decode_rope(const kvq_kv_view& v, const void* q, int f16, int Hq,
@@ -518,7 +516,7 @@ hipError_t launch_decode_rope(const kvq_kv_view& v, const void* q, int f16, int 
 #undef KVQ_ROPE_CASE
   if (e != hipSuccess || fp == 0) return e;
   // the fp16 sink and tail tokens as one range that skips the quantized
-  // ones, 64 tokens per partial
+  // ones, 32 tokens per partial
   return launch_decode_generic_range(v, q, f16, Hq, sm_scale, partials, 0, nf, fp, n_parts,
                                      stride, &rope, s, ns, nq);
 }

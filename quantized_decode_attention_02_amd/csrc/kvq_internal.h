@@ -170,7 +170,7 @@ hipError_t launch_decode_mfma(const kvq_kv_view& v, const void* q, int f16,
 // The dedicated kernel covers uniform int8/int4/int2 keys, int4/int2 value
 // tiles, D = 128, G a multiple of 32, Gv >= 16 and 1 to 8 query heads per
 // KV head; it writes rope_fast_parts(...) partials for the quantized
-// tokens and rope_fp16_parts(v) more (sink, then tail; 64 tokens each) from
+// tokens and rope_fp16_parts(v) more (sink, then tail; 32 tokens each) from
 // the general kernel.
 bool rope_fast_eligible(const kvq_kv_view& v, int Hq);
 int rope_fast_parts(const kvq_kv_view& v, int Hq, int n_splits);
