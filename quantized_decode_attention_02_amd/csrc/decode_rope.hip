@@ -256,7 +256,7 @@ decode_rope_kernel(kvq_kv_view v, const QT* __restrict__ q, int Hq, float qscale
   for (; T < t_hi; T += kRWaves) {
     const bool more = T + kRWaves < t_hi;
     const int64_t qt0 = T * kRTile;
-    const int64_t grp = qt0 / v.group_tok;
+    const int64_t grp = (uint32_t)qt0 / (uint32_t)v.group_tok;  // qt0 < 2^26
     if (grp != cur_grp) {
       cur_grp = grp;
       const float4v a = *(const float4v*)(ksc + grp * kRD + chan(0));
