@@ -116,3 +116,43 @@ def test_view_validation_and_empty_decode():
     # quantized tokens but no code arrays
     v.n_quant, v.group_tok, v.group_ch, v.k_bits, v.v_bits = 64, 64, 32, 4, 2
     assert L.kvq_decode_workspace_bytes(ctypes.byref(v), 1, 0) == 0
+
+
+def test_rope_decode_argument_errors():
+    """Every argument error of kvq_decode_attention_rope returns before any
+    launch (so this runs without a GPU)."""
+    L = kvq.lib()
+    p = ctypes.c_void_p(256)
+    v = kvq.KvView()
+    v.batch, v.kv_heads, v.head_dim = 1, 1, 32
+    v.n_sink, v.sink_k, v.sink_v, v.sink_stride = 1, 256, 256, 32
+    ws = 1 << 20
+
+    def call(rope, view=v, hq=1, sm=0.1):
+        return L.kvq_decode_attention_rope(
+            ctypes.byref(view), None if rope is None else ctypes.byref(rope), p, kvq.KVQ_F16,
+            hq, sm, p, 0, 0, p, ws, None)
+
+    def rope(**kw):
+        r = kvq.Rope(base=10000.0, pairing=kvq.KVQ_ROPE_HALF, reserved=0, pos0=0)
+        for k, x in kw.items():
+            setattr(r, k, x)
+        return r
+
+    assert call(None) == kvq.KVQ_E_ARG
+    for bad in ({"base": 0.0}, {"base": -2.0}, {"base": float("nan")},
+                {"base": float("inf")}, {"pairing": 2}, {"pos0": -1},
+                {"pos0": 1 << 40}):
+        assert call(rope(**bad)) == kvq.KVQ_E_ARG, bad
+    assert call(rope(), sm=0.0) == kvq.KVQ_E_ARG
+    two = kvq.KvView()
+    two.batch, two.kv_heads, two.head_dim = 1, 2, 32
+    two.n_sink, two.sink_k, two.sink_v, two.sink_stride = 1, 256, 256, 32
+    assert call(rope(), view=two, hq=3) == kvq.KVQ_E_ARG  # Hq not a multiple of Hkv
+    odd = kvq.KvView()
+    odd.batch, odd.kv_heads, odd.head_dim = 1, 1, 33
+    odd.n_sink, odd.sink_k, odd.sink_v, odd.sink_stride = 1, 256, 256, 33
+    assert call(rope(), view=odd) == kvq.KVQ_E_ARG       # odd head_dim
+    empty = kvq.KvView()
+    empty.batch, empty.kv_heads, empty.head_dim = 1, 1, 32
+    assert call(rope(), view=empty) == kvq.KVQ_E_ARG     # no tokens
