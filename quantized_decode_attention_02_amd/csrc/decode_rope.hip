@@ -44,7 +44,7 @@ constexpr int kRNF = kRD / 2;        // frequencies
 constexpr int kRTile = 32;           // tokens per tile
 constexpr int kRSteps = 8;           // wave steps per tile, 4 tokens each
 constexpr int kRBlocks = kRD / 16;   // value channel blocks
-constexpr int kRPvSlots = 16;        // weight slots per token: one per key lane
+constexpr int kRMaxGroups = 8;       // value groups per token (Gv >= 16)
 constexpr float kRLog2e = 1.4426950408889634f;
 
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
@@ -79,6 +79,37 @@ __device__ inline float row_sum16(float x) {
   x += dpp_f<0x122>(x);
   x += dpp_f<0x121>(x);
   return x;
+}
+// Max over the 16 lanes of a row (every lane gets it).
+__device__ inline float row_max16(float x) {
+  x = fmaxf(x, dpp_f<0x128>(x));
+  x = fmaxf(x, dpp_f<0x124>(x));
+  x = fmaxf(x, dpp_f<0x122>(x));
+  x = fmaxf(x, dpp_f<0x121>(x));
+  return x;
+}
+// Reduce-scatter of eight per-lane partial sums over the 16 lanes of a row:
+// lane c ends with the full sum of entry 4 b3 + 2 b1 + b0 (bits of c), as
+// does lane c ^ 4.  Partners c ^ 8 (DPP row_ror 8), c ^ 2 and c ^ 1 (DPP
+// quad permutations) each take the half the lane keeps; c ^ 4 (swizzle)
+// completes the sum.
+__device__ inline float row_reduce_scatter8(const float a[8], int c) {
+  const bool b3 = c & 8, b1 = c & 2, b0 = c & 1;
+  float t1[4], t2[2];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const float keep = b3 ? a[k + 4] : a[k], give = b3 ? a[k] : a[k + 4];
+    t1[k] = keep + dpp_f<0x128>(give);
+  }
+#pragma unroll
+  for (int k = 0; k < 2; ++k) {
+    const float keep = b1 ? t1[k + 2] : t1[k], give = b1 ? t1[k] : t1[k + 2];
+    t2[k] = keep + dpp_f<0x4E>(give);  // quad_perm [2, 3, 0, 1]: lane ^ 2
+  }
+  const float keep = b0 ? t2[1] : t2[0], give = b0 ? t2[0] : t2[1];
+  const float t3 = keep + dpp_f<0xB1>(give);  // quad_perm [1, 0, 3, 2]: lane ^ 1
+  return t3 + __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(
+                                            __builtin_bit_cast(int, t3), (4 << 10) | 0x1F));
 }
 __device__ inline float lane_f(float x, int l) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), l));
@@ -134,24 +165,33 @@ __device__ inline void key_pairs(typename KWords<KB, INTER>::T w, int c, half2v 
   }
 }
 
-template <int GQ>
+// Weight slots per token in LDS: RS kernels write one per value group,
+// the others one per key lane (groups past D/Gv are never read).
+template <bool RS>
+constexpr int pv_slots() { return RS ? kRMaxGroups : 16; }
+
+template <int GQ, bool RS>
 struct RopeLds {
   double phi[kRNF];                       // turns per position
   float2 tab[kRTile][kRNF];               // (cos, sin) of j * theta_f
   float2 qs[GQ][kRD];                     // (q_d, sigma q_e) * qscale
   float2 base[kRWaves][kRNF];             // (cos, sin) of t0 * theta_f
-  float pv[kRWaves][GQ][kRPvSlots][kRTile];  // weight * value scale (groups < D/Gv)
+  float pv[kRWaves][GQ][pv_slots<RS>()][kRTile];  // weight * value scale
   float comb[kRWaves][GQ][kRD + 2];       // per-wave (m, l, o)
 };
 
 // GQ query heads h_off .. h_off + GQ - 1 of each KV head's g = Hq / Hkv.
-template <int KB, int VB, int GQ, bool INTER, typename QT>
+// RS: scores summed by a reduce-scatter (one token per lane afterwards: one
+// exp per lane and tile); otherwise every lane gets all eight row sums.
+// The one-head kernel keeps the latter: it then fits three waves per SIMD.
+template <int KB, int VB, int GQ, bool INTER, typename QT, bool RS = (GQ >= 2)>
 __global__ void __launch_bounds__(kRThreads)
-__attribute__((amdgpu_waves_per_eu(GQ >= 2 ? 2 : 3)))
+__attribute__((amdgpu_waves_per_eu(RS ? 2 : 3)))
 decode_rope_kernel(kvq_kv_view v, const QT* __restrict__ q, int Hq, float qscale,
                    RopeDev rope, float* __restrict__ partials, int n_parts, int part_stride,
                    int gv_shift, int h_off) {
-  __shared__ RopeLds<GQ> L;
+  __shared__ RopeLds<GQ, RS> L;
+  constexpr int kSlots = pv_slots<RS>();
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int part = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int64_t s = (int64_t)b * v.kv_heads + kvh;
@@ -197,7 +237,8 @@ decode_rope_kernel(kvq_kv_view v, const QT* __restrict__ q, int Hq, float qscale
   const uint32_t kcol = INTER ? (KB == 4 ? c : KB == 8 ? 2 * c : (c >> 1))
                               : (KB == 4 ? (c >> 1) : KB == 8 ? c : (c >> 2));
   constexpr uint32_t kcol2 = KWD / 2;
-  const uint32_t vgc = c & (NG - 1);       // lanes past the value groups repeat them
+  // after the score reduce-scatter this lane holds token 4 ks_tok + r
+  const int ks_tok = ((c >> 3) & 1) * 4 + ((c >> 1) & 1) * 2 + (c & 1);
   const int fbase = 4 * c;                 // the lane's four frequencies
   // lane channel e: its channel, and its frequency's offset from fbase
   auto chan = [&](int e) { return INTER ? 8 * c + e : (e < 4 ? 4 * c + e : kRNF + 4 * c + e - 4); };
@@ -218,7 +259,7 @@ decode_rope_kernel(kvq_kv_view v, const QT* __restrict__ q, int Hq, float qscale
   typedef typename KWords<KB, INTER>::T KW;
   KW kw[kRSteps];
   u32x4 vw[VB == 4 ? 2 : 1];
-  float vs[kRSteps];
+  float vs[RS ? kRMaxGroups : kRSteps];
   auto load_k = [&](int64_t T) {
     const uint32_t row0 = (uint32_t)T * kRTile + r;
 #pragma unroll
@@ -235,9 +276,17 @@ decode_rope_kernel(kvq_kv_view v, const QT* __restrict__ q, int Hq, float qscale
     }
   };
   auto load_vs = [&](int64_t T) {
-    const uint32_t row0 = (uint32_t)T * kRTile + r;
+    if constexpr (RS) {
+      const uint32_t row = (uint32_t)T * kRTile + 4 * ks_tok + r;
 #pragma unroll
-    for (int st = 0; st < kRSteps; ++st) vs[st] = ldnt(vsc_base + (row0 + 4 * st) * NG + vgc);
+      for (int g = 0; g < kRMaxGroups; ++g)
+        if (g < NG) vs[g] = ldnt(vsc_base + row * NG + g);
+    } else {
+      const uint32_t row0 = (uint32_t)T * kRTile + r;
+#pragma unroll
+      for (int st = 0; st < kRSteps; ++st)
+        vs[st] = ldnt(vsc_base + (row0 + 4 * st) * NG + (c & (NG - 1)));
+    }
   };
   auto load_v = [&](int64_t T) {
     const uint32_t* tw = vc + (uint32_t)T * (uint32_t)(kRD * VB);
@@ -308,17 +357,25 @@ decode_rope_kernel(kvq_kv_view v, const QT* __restrict__ q, int Hq, float qscale
           acc = __builtin_fmaf((float)pr[i][0], wl, acc);
           acc = __builtin_fmaf((float)pr[i][1], wh, acc);
         }
-        sc[h][st] = row_sum16(acc);
+        sc[h][st] = RS ? acc : row_sum16(acc);  // RS: summed below
       }
     }
     if (more) load_k(T + kRWaves);
 
-    // online softmax over the tile; weights times value scales into LDS
+    // online softmax over the tile; weights times value scales into LDS.
+    // RS: lane 16 r + c holds the score of token 4 ks + r (ks = 4 b3 + 2 b1
+    // + b0 of c; lanes c and c ^ 4 alike); otherwise all eight of its row.
 #pragma unroll
     for (int h = 0; h < GQ; ++h) {
-      float mx = sc[h][0];
+      float mx, sv = 0.0f;
+      if constexpr (RS) {
+        sv = row_reduce_scatter8(sc[h], c);
+        mx = row_max16(sv);
+      } else {
+        mx = sc[h][0];
 #pragma unroll
-      for (int st = 1; st < kRSteps; ++st) mx = fmaxf(mx, sc[h][st]);
+        for (int st = 1; st < kRSteps; ++st) mx = fmaxf(mx, sc[h][st]);
+      }
       mx = fmaxf(fmaxf(lane_f(mx, 0), lane_f(mx, 16)), fmaxf(lane_f(mx, 32), lane_f(mx, 48)));
       const float mnew = fmaxf(m_run[h], mx);
       // v_exp_f32 flushes results below 2^-126 to zero: such a weight next
@@ -326,11 +383,19 @@ decode_rope_kernel(kvq_kv_view v, const QT* __restrict__ q, int Hq, float qscale
       const float alpha = __builtin_amdgcn_exp2f(m_run[h] - mnew);
       m_run[h] = mnew;
       float psum = 0.0f;
+      if constexpr (RS) {
+        const float p = __builtin_amdgcn_exp2f(sv - mnew);
 #pragma unroll
-      for (int st = 0; st < kRSteps; ++st) {
-        const float p = __builtin_amdgcn_exp2f(sc[h][st] - mnew);
-        psum += p;
-        L.pv[wave][h][c][4 * st + r] = p * vs[st];
+        for (int g = 0; g < kRMaxGroups; ++g)
+          if (g < NG) L.pv[wave][h][g][4 * ks_tok + r] = p * vs[g];
+        psum = (c & 4) ? 0.0f : p;  // each token counted once
+      } else {
+#pragma unroll
+        for (int st = 0; st < kRSteps; ++st) {
+          const float p = __builtin_amdgcn_exp2f(sc[h][st] - mnew);
+          psum += p;
+          L.pv[wave][h][c][4 * st + r] = p * vs[st];
+        }
       }
       l_run[h] = l_run[h] * alpha + psum;
 #pragma unroll
@@ -346,8 +411,8 @@ decode_rope_kernel(kvq_kv_view v, const QT* __restrict__ q, int Hq, float qscale
       float4v wlo[GQ], whi[GQ];
 #pragma unroll
       for (int h = 0; h < GQ; ++h) {
-        wlo[h] = *(const float4v*)(pw + h * kRPvSlots * kRTile);
-        whi[h] = *(const float4v*)(pw + h * kRPvSlots * kRTile + 16);
+        wlo[h] = *(const float4v*)(pw + h * kSlots * kRTile);
+        whi[h] = *(const float4v*)(pw + h * kSlots * kRTile + 16);
       }
       half2v pr[4];
       if constexpr (VB == 2) {
@@ -380,8 +445,9 @@ decode_rope_kernel(kvq_kv_view v, const QT* __restrict__ q, int Hq, float qscale
   // per wave: l over the four token rows, o over the four token quarters
 #pragma unroll
   for (int h = 0; h < GQ; ++h) {
-    const float lw = lane_f(l_run[h], 0) + lane_f(l_run[h], 16) + lane_f(l_run[h], 32) +
-                     lane_f(l_run[h], 48);
+    // RS: lanes hold their own tokens' sums; otherwise every lane its row's
+    const float lrow = RS ? row_sum16(l_run[h]) : l_run[h];
+    const float lw = lane_f(lrow, 0) + lane_f(lrow, 16) + lane_f(lrow, 32) + lane_f(lrow, 48);
 #pragma unroll
     for (int jb = 0; jb < kRBlocks; ++jb) {
       float x = o[h][jb];
