@@ -442,8 +442,10 @@ def main():
         "peak_tflops": 78.6,
         "frac": round(2 * fma / t_h / 78.6e12, 4),
         "hbm_gbs": round(bytes_launch / t_h / 1e9, 1),
-        "kernel": "decode_rope_kernel (+ general kernel for fp16 sink/tail, "
-                  "merge_kernel)"}
+        "kernel": ("decode_generic_kernel (rotary form: mixed keys) + merge_kernel"
+                   if views[0].k_mixed else
+                   "decode_rope_kernel (+ general kernel for fp16 sink/tail, "
+                   "merge_kernel)")}
     if "salience_select_us" in extra:
         extra["decode_plus_salience_us"] = round(
             res["decode_call_us"]["median"] + extra["salience_select_us"], 2)

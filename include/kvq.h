@@ -322,7 +322,8 @@ typedef struct {
  * (else KVQ_E_ARG).  Uniform int8/int4/int2 keys with int4/int2 value
  * tiles, D = 128, G a multiple of 32, Gv >= 16 and 1 to 8 query heads
  * per KV head run a dedicated kernel (one launch per pair of query heads
- * of a KV head, per head when that count is odd); every other view (and
+ * of a KV head, the last one alone when that count is odd); every other
+ * view (and
  * KVQ_DECODE_GENERIC) the general kernel.  The workspace is sized by
  * kvq_decode_workspace_bytes.  Angles are reduced in float64 and the
  * cosines and sines evaluated in float32.                                */

@@ -115,7 +115,48 @@ __device__ inline void stage_rows(const kvq_kv_view& v, int64_t s, int64_t c0, i
       row = (keys ? v.tail_k : v.tail_v) + s * v.tail_stride +
             ring_row(ci - v.n_sink, v.residual) * D;
     }
-    if (row && d0 + 8 <= D && ((uintptr_t)(row + d0) & 15) == 0) {
+    if (!row && keys && v.k_mixed && d0 + 8 <= D) {
+      // a quantized mixed-key row: the eight channels' class positions
+      // first, then every channel's code (or bf16 value) and scale, each
+      // round issued as independent loads
+      const int64_t q = ci - v.n_sink;
+      const int64_t g = q / v.group_tok;
+      const int nb = v.n_bf16, n4 = v.n_int4, n2 = D - nb - n4;
+      const int w4 = words_of(n4, 4), w2 = words_of(n2, 2);
+      const uint8_t* kp = v.k_pos + s * v.k_pos_stride + g * D + d0;
+      int pos[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) pos[k] = kp[k];
+      uint32_t raw[8];
+      float sc[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int ps = pos[k];
+        if (ps < nb) {
+          raw[k] = v.k_bf16[s * v.k_bf16_stride + q * nb + ps];
+          sc[k] = 1.0f;
+        } else if (ps < nb + n4) {
+          raw[k] = v.k_int4[s * v.k_int4_stride + q * w4 + (ps - nb) / 8];
+          sc[k] = v.k_scales[s * v.k_scales_stride + g * (n4 + n2) + (ps - nb)];
+        } else {
+          raw[k] = v.k_int2[s * v.k_int2_stride + q * w2 + (ps - nb - n4) / 16];
+          sc[k] = v.k_scales[s * v.k_scales_stride + g * (n4 + n2) + (ps - nb)];
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int ps = pos[k];
+        float x;
+        if (ps < nb) {
+          x = bf2f((uint16_t)raw[k]);
+        } else if (ps < nb + n4) {
+          x = (float)((int)field(raw[k], (ps - nb) % 8, 4) - 8) * sc[k];
+        } else {
+          x = (float)((int)field(raw[k], (ps - nb - n4) % 16, 2) - 2) * sc[k];
+        }
+        dst[t * D + d0 + k] = x;
+      }
+    } else if (row && d0 + 8 <= D && ((uintptr_t)(row + d0) & 15) == 0) {
       const uint4 w = *(const uint4*)(row + d0);
       const uint32_t u[4] = {w.x, w.y, w.z, w.w};
 #pragma unroll

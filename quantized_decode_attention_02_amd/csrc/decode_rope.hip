@@ -496,17 +496,16 @@ hipError_t launch_rope_t(const kvq_kv_view& v, const void* q, int f16, int Hq, f
   return hipGetLastError();
 }
 
-// Query heads per KV head taken two at a time (one at a time when odd);
-// each launch reads the cache once.
+// Query heads per KV head taken two at a time (the last alone when their
+// count is odd); each launch reads the cache once.
 template <int KB, int VB>
 hipError_t launch_rope_g(const kvq_kv_view& v, const void* q, int f16, int Hq, float qscale,
                          const RopeDev& rope, float* partials, int n_parts, int part_stride,
                          int gv_shift, hipStream_t s) {
   const int g = Hq / v.kv_heads;
-  const int step = g % 2 ? 1 : 2;
-  for (int h0 = 0; h0 < g; h0 += step) {
+  for (int h0 = 0; h0 < g; h0 += 2) {
     hipError_t e;
-    if (step == 1)
+    if (h0 + 2 > g)
       e = rope.interleaved
               ? launch_rope_t<KB, VB, 1, true>(v, q, f16, Hq, qscale, rope, partials, n_parts,
                                                part_stride, gv_shift, h0, s)
