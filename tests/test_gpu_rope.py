@@ -6,8 +6,8 @@ dequantizes it, rotates the key of cache-order token i at position pos0 + i
 and runs float64 attention.  The decode output must be within 2e-3 (max row
 relative L2 error).  Cases span several 32-token tiles with a ragged fp16
 tail, both pair layouts, every key/value bit width the dedicated kernel
-takes, 1, 2 and 4 query heads per KV head (and 8, which takes the general
-kernel), sinks, large position offsets, and views only the general kernel
+takes, 1 to 5 and 8 query heads per KV head (run as head pairs and single
+heads), sinks, large position offsets, and views only the general kernel
 covers (mixed keys, row-layout values, head_dim 64).
 """
 import numpy as np
@@ -69,7 +69,7 @@ def run_case(B=1, Hq=8, Hkv=2, N=1500, D=128, kb=4, vb=2, G=128, Gv=32, R=128, S
 
 
 @pytest.mark.parametrize("pairing", ["half", "interleaved"])
-@pytest.mark.parametrize("g", [1, 2, 4, 8])
+@pytest.mark.parametrize("g", [1, 2, 3, 4, 5, 8])
 def test_rope_heads_per_kv_head(pairing, g):
     Hkv = 2 if g < 8 else 1
     run_case(Hq=g * Hkv, Hkv=Hkv, pairing=pairing, S=1, seed=g)
