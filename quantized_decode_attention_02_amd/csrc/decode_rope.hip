@@ -20,9 +20,11 @@
 // Work split: a 256-thread workgroup takes a range of 32-token tiles of one
 // (batch, KV head) stream; its four waves take every fourth tile and keep
 // their own running max, sum and output, combined in LDS at the end into
-// one partial (m, l, o).  In a tile, lane 16 r + c scores channels
-// 8c .. 8c + 7 of the tokens 4 s + r (s = 0..7) and a 16-lane DPP sum
-// completes each score.  Values keep the value-tile layout: lane 16 q + m
+// one partial (m, l, o).  In a tile, lane 16 r + c scores eight channels of
+// the tokens 4 s + r (s = 0..7): 8c .. 8c + 7 for interleaved pairs,
+// 4c .. 4c + 3 and 64 + 4c .. 64 + 4c + 3 for half pairs (both members of
+// four pairs either way), and 16-lane DPP sums complete the scores.  Values
+// keep the value-tile layout: lane 16 q + m
 // holds channel 16 jb + m at eight tokens of the tile and reads their
 // softmax weights, times the token's value scale, from LDS.  The fp16 sink
 // and tail tokens go through the general kernel as one range, 32 tokens per
