@@ -132,26 +132,8 @@ struct KWords {
   typedef typename std::conditional<KB == 8 || !INTER, u32x2, uint32_t>::type T;
 };
 
-// Two codes masked in place, 16 bits apart: with the field at bit SH of
-// each half, OR-ing 0x6400 makes 1024 + u * 2^SH (exact: the field stays in
-// the fp16 mantissa), and one packed subtract leaves (u - 2^(BITS-1)) * 2^SH.
-template <int BITS, int SH>
-__device__ inline half2v code_pair_at(uint32_t x) {
-  constexpr uint32_t mask = (((1u << BITS) - 1u) << SH) * 0x00010001u;
-  const half2v h = __builtin_bit_cast(half2v, (x & mask) | 0x64006400u);
-  constexpr _Float16 off = (_Float16)(1024 + ((1 << (BITS - 1)) << SH));
-  return h - half2v{off, off};
-}
-
 // The lane's 8 codes as 4 fp16 pairs; pair i holds lane channels
-// (lo_e(i), hi_e(i)) times key_fac(e) (a power of two that the channel's
-// scale divides back out).  One v_perm_b32 gathers the lane's key bytes so
-// that lane channel e < 4 sits in the low half-word and e >= 4 in the high.
-template <int KB>
-__device__ constexpr float key_fac(int e) {
-  return KB == 2 ? (float)(1 << (2 * (e & 3))) : KB == 4 ? ((e & 1) ? 16.0f : 1.0f) : 1.0f;
-}
-
+// (lo_e(i), hi_e(i)).
 template <int KB, bool INTER>
 __device__ inline void key_pairs(typename KWords<KB, INTER>::T w, int c, half2v p[4]) {
   if constexpr (KB == 8) {
@@ -159,37 +141,34 @@ __device__ inline void key_pairs(typename KWords<KB, INTER>::T w, int c, half2v 
     p[1] = code_pair<8>(w[0] >> 8);
     p[2] = code_pair<8>(w[1]);
     p[3] = code_pair<8>(w[1] >> 8);
-  } else if constexpr (KB == 4) {
-    uint32_t z;
-    if constexpr (INTER) {
-      z = w;
-    } else {
-      // bytes 2(c & 1), 2(c & 1) + 1 of the two words
-      const uint32_t b = 2 * (c & 1);
-      z = __builtin_amdgcn_perm(w[1], w[0], b | (b + 1) << 8 | (b + 4) << 16 | (b + 5) << 24);
-    }
-    const uint32_t z8 = z >> 8;
-    p[0] = code_pair_at<4, 0>(z);
-    p[1] = code_pair_at<4, 4>(z);
-    p[2] = code_pair_at<4, 0>(z8);
-    p[3] = code_pair_at<4, 4>(z8);
   } else {
-    // byte0 <- lane channels 0..3, byte2 <- 4..7, bytes 1 and 3 zero
     uint32_t z;
-    if constexpr (INTER) {
-      const uint32_t b = 2 * (c & 1);
-      z = __builtin_amdgcn_perm(0u, w, b | 0x0Cu << 8 | (b + 1) << 16 | 0x0Cu << 24);
+    if constexpr (KB == 4) {
+      if constexpr (INTER) {
+        z = w;
+      } else {
+        const int sh = 16 * (c & 1);
+        z = ((w[0] >> sh) & 0xFFFFu) | ((w[1] >> sh) << 16);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) p[i] = code_pair<4>(z >> (4 * i));
     } else {
-      const uint32_t b = c & 3;
-      z = __builtin_amdgcn_perm(w[1], w[0], b | 0x0Cu << 8 | (b + 4) << 16 | 0x0Cu << 24);
+      uint32_t y;
+      if constexpr (INTER) {
+        y = w >> (16 * (c & 1));
+      } else {
+        const int sh = 8 * (c & 3);
+        y = ((w[0] >> sh) & 0xFFu) | (((w[1] >> sh) & 0xFFu) << 8);
+      }
+      z = (y & 0xFFu) | ((y << 8) & 0x00FF0000u);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) p[i] = code_pair<2>(z >> (2 * i));
     }
-    p[0] = code_pair_at<2, 0>(z);
-    p[1] = code_pair_at<2, 2>(z);
-    p[2] = code_pair_at<2, 4>(z);
-    p[3] = code_pair_at<2, 6>(z);
   }
 }
 
+// Weight slots per token in LDS: RS kernels write one per value group,
+// the others one per key lane (groups past D/Gv are never read).
 template <bool RS>
 constexpr int pv_slots() { return RS ? kRMaxGroups : 16; }
 
@@ -335,8 +314,6 @@ decode_rope_kernel(kvq_kv_view v, const QT* __restrict__ q, int Hq, float qscale
       const float4v bq = *(const float4v*)(ksc + grp * kRD + chan(4));
       ks[0] = a[0]; ks[1] = a[1]; ks[2] = a[2]; ks[3] = a[3];
       ks[4] = bq[0]; ks[5] = bq[1]; ks[6] = bq[2]; ks[7] = bq[3];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) ks[e] *= 1.0f / key_fac<KB>(e);  // exact: powers of two
     }
     // (cos, sin) of the tile's first position at every frequency
     const double p0 = (double)(rope.pos0 + v.n_sink + qt0);
