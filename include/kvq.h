@@ -274,7 +274,8 @@ enum {
   KVQ_DECODE_GENERIC = 1   /* always the general vector kernel */
 };
 
-/* Bytes of the split workspace for n_splits (0 = automatic). */
+/* Bytes of the split workspace for n_splits (0 = automatic), enough for
+ * kvq_decode_attention and kvq_decode_attention_rope alike. */
 size_t kvq_decode_workspace_bytes(const kvq_kv_view* v, int n_q_heads,
                                   int n_splits);
 
