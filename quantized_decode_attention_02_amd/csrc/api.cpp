@@ -142,6 +142,20 @@ int generic_parts(const kvq_kv_view* v, int n_splits) {
   return (int)p;
 }
 
+// Split count of the general kernel's rotary form (32-token chunks, small
+// LDS footprint): about 4096 workgroups, at least 32 tokens each.
+int rope_generic_parts(const kvq_kv_view* v, int n_splits) {
+  const int64_t N = v->n_sink + v->n_quant + v->n_tail;
+  if (n_splits > 0) return n_splits;
+  const int64_t streams = (int64_t)v->batch * v->kv_heads;
+  int64_t p = (4096 + streams - 1) / streams;
+  int64_t by_len = (N + 31) / 32;
+  if (p > by_len) p = by_len;
+  if (p < 1) p = 1;
+  if (p > 4096) p = 4096;
+  return (int)p;
+}
+
 size_t generic_lds(int g, int D) {
   return sizeof(float) * ((size_t)g * D * 2 + (size_t)g * 128 + 3 * (size_t)g);
 }
@@ -355,6 +369,10 @@ size_t kvq_decode_workspace_bytes(const kvq_kv_view* v, int n_q_heads, int n_spl
     int pr = rope_fast_parts(*v, n_q_heads, n_splits) + rope_fp16_parts(*v);
     if (pr > parts) parts = pr;
   }
+  if (v->head_dim % 2 == 0) {
+    int pg = rope_generic_parts(v, n_splits);
+    if (pg > parts) parts = pg;
+  }
   return (size_t)v->batch * n_q_heads * parts * (v->head_dim + 2) * sizeof(float);
 }
 
@@ -427,10 +445,12 @@ kvq_status kvq_decode_attention_rope(const kvq_kv_view* v, const kvq_rope* rope,
     parts = pf + rope_fp16_parts(*v);
     e = launch_decode_rope(*v, q, dtype == KVQ_F16, n_q_heads, sm_scale, rd, partials, pf, s);
   } else {
-    const size_t lds = generic_lds(n_q_heads / v->kv_heads, v->head_dim) +
-                       sizeof(float) * v->head_dim * (1 + 128);
+    // the rotary form of the general kernel: 32-token chunks, their keys
+    // and values staged in LDS
+    const size_t g = n_q_heads / v->kv_heads, D = v->head_dim;
+    const size_t lds = sizeof(float) * (g * D * 2 + g * 32 + 3 * g + D * (1 + 32));
     if (lds > 160 * 1024) return KVQ_E_UNSUPPORTED;
-    parts = generic_parts(v, n_splits);
+    parts = rope_generic_parts(v, n_splits);
     e = launch_decode_generic_range(*v, q, dtype == KVQ_F16, n_q_heads, sm_scale, partials, 0,
                                     N, parts, 0, parts, &rd, s);
   }

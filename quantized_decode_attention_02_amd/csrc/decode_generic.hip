@@ -24,6 +24,11 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr int kChunkTok = 128;
+// The rotary form stages a chunk's keys and values in LDS: smaller chunks
+// keep its footprint near 26 KB so that several workgroups share a CU.
+constexpr int kRopeChunkTok = 32;
+template <bool ROPE>
+constexpr int chunk_tok() { return ROPE ? kRopeChunkTok : kChunkTok; }
 constexpr float kLog2e = 1.4426950408889634f;
 
 __device__ inline float h2f(uint16_t u) {
@@ -184,17 +189,18 @@ decode_generic_kernel(kvq_kv_view v, const QT* __restrict__ q, int Hq,
                       int64_t range_lo, int64_t range_hi, int n_parts,
                       int part_offset, int part_stride, int64_t gap_at, int64_t gap_len,
                       RopeDev rope) {
+  constexpr int CT = chunk_tok<ROPE>();
   extern __shared__ float smem[];
   const int D = v.head_dim;
   const int g = Hq / v.kv_heads;
   double* phis = (double*)smem;      // [D/2] turns per position (rotary only)
   float* qs = smem + (ROPE ? D : 0); // [g][D]
-  float* ps = qs + g * D;            // [g][kChunkTok]
-  float* os = ps + g * kChunkTok;    // [g][D]
+  float* ps = qs + g * D;            // [g][CT]
+  float* os = ps + g * CT;           // [g][D]
   float* ms = os + g * D;            // [g]
   float* ls = ms + g;                // [g]
   float* as = ls + g;                // [g]
-  float* kr = as + g;                // [kChunkTok][D] turned keys (rotary only)
+  float* kr = as + g;                // [CT][D] turned keys (rotary only)
   const int tid = threadIdx.x;
   const int part = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int64_t s = (int64_t)b * v.kv_heads + kvh;
@@ -216,8 +222,8 @@ decode_generic_kernel(kvq_kv_view v, const QT* __restrict__ q, int Hq,
     for (int f = tid; f < D / 2; f += kThreads) phis[f] = rope.phi[f];
   __syncthreads();
 
-  for (int64_t c0 = t_lo; c0 < t_hi; c0 += kChunkTok) {
-    const int n = (int)min((int64_t)kChunkTok, t_hi - c0);
+  for (int64_t c0 = t_lo; c0 < t_hi; c0 += CT) {
+    const int n = (int)min((int64_t)CT, t_hi - c0);
     if (ROPE) {
       // the chunk's dequantized keys into LDS, eight channels per item
       // (fp16 rows with one 16-byte load), then turned in place, one
@@ -250,7 +256,7 @@ decode_generic_kernel(kvq_kv_view v, const QT* __restrict__ q, int Hq,
           for (int d = qd; d < D; d += 4) acc += qs[h * D + d] * kr[t * D + d];
         acc += __shfl_xor(acc, 1);
         acc += __shfl_xor(acc, 2);
-        if (i < n * g * 4 && qd == 0) ps[h * kChunkTok + t] = acc;
+        if (i < n * g * 4 && qd == 0) ps[h * CT + t] = acc;
       }
     }
     for (int i = tid; i < (ROPE ? 0 : n * g); i += kThreads) {
@@ -260,12 +266,12 @@ decode_generic_kernel(kvq_kv_view v, const QT* __restrict__ q, int Hq,
         const int64_t ci = c0 + t < gap_at ? c0 + t : c0 + t + gap_len;
         for (int d = 0; d < D; ++d) acc += qs[h * D + d] * kdeq(v, s, ci, d);
       }
-      ps[h * kChunkTok + t] = acc;
+      ps[h * CT + t] = acc;
     }
     __syncthreads();
     if (tid < g) {
       float mx = -INFINITY;
-      for (int t = 0; t < n; ++t) mx = fmaxf(mx, ps[tid * kChunkTok + t]);
+      for (int t = 0; t < n; ++t) mx = fmaxf(mx, ps[tid * CT + t]);
       const float mnew = fmaxf(ms[tid], mx);
       as[tid] = exp2f(ms[tid] - mnew);
       ms[tid] = mnew;
@@ -273,12 +279,12 @@ decode_generic_kernel(kvq_kv_view v, const QT* __restrict__ q, int Hq,
     __syncthreads();
     for (int i = tid; i < n * g; i += kThreads) {
       const int t = i % n, h = i / n;
-      ps[h * kChunkTok + t] = exp2f(ps[h * kChunkTok + t] - ms[h]);
+      ps[h * CT + t] = exp2f(ps[h * CT + t] - ms[h]);
     }
     __syncthreads();
     if (tid < g) {
       float l = ls[tid] * as[tid];
-      for (int t = 0; t < n; ++t) l += ps[tid * kChunkTok + t];
+      for (int t = 0; t < n; ++t) l += ps[tid * CT + t];
       ls[tid] = l;
     }
     if (ROPE) {
@@ -297,7 +303,7 @@ decode_generic_kernel(kvq_kv_view v, const QT* __restrict__ q, int Hq,
           const int64_t ci = c0 + t < gap_at ? c0 + t : c0 + t + gap_len;
           vv = vdeq(v, s, ci, d);
         }
-        acc += ps[h * kChunkTok + t] * vv;
+        acc += ps[h * CT + t] * vv;
       }
       os[i] = acc;
     }
@@ -401,8 +407,8 @@ hipError_t launch_generic_t(const kvq_kv_view& v, const void* q, int f16, int Hq
                             int64_t gap_len, const RopeDev& rope, hipStream_t s) {
   const int g = Hq / v.kv_heads;
   const size_t lds =
-      sizeof(float) * ((size_t)g * v.head_dim * 2 + (size_t)g * kChunkTok + 3 * (size_t)g +
-                       (ROPE ? (size_t)v.head_dim * (1 + kChunkTok) : 0));
+      sizeof(float) * ((size_t)g * v.head_dim * 2 + (size_t)g * chunk_tok<ROPE>() + 3 * (size_t)g +
+                       (ROPE ? (size_t)v.head_dim * (1 + chunk_tok<ROPE>()) : 0));
   dim3 grid((unsigned)n_parts, (unsigned)v.kv_heads, (unsigned)v.batch);
   const void* fn = f16 ? (const void*)decode_generic_kernel<uint16_t, ROPE>
                        : (const void*)decode_generic_kernel<float, ROPE>;
