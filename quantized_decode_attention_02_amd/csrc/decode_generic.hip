@@ -161,6 +161,32 @@ __device__ inline void stage_rows(const kvq_kv_view& v, int64_t s, int64_t c0, i
         }
         dst[t * D + d0 + k] = x;
       }
+    } else if (!row && !keys && d0 + 8 <= D) {
+      // a quantized value row: the eight channels' code words (either
+      // layout) and scales as independent loads, then the codes
+      const int64_t q = ci - v.n_sink;
+      const int vb = v.v_bits, ng = D / v.group_ch;
+      uint32_t wv[8];
+      int bit[8];
+      float sc[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int d = d0 + k;
+        int64_t widx;
+        if (v.v_layout == KVQ_V_ROWS) {
+          const int pw = fields_per_word(vb);
+          widx = q * words_of(D, vb) + d / pw;
+          bit[k] = (d % pw) * vb;
+        } else {
+          v_tile_pos(q, d, D, vb, &widx, &bit[k]);
+        }
+        wv[k] = v.v_codes[s * v.v_codes_stride + widx];
+        sc[k] = v.v_scales[s * v.v_scales_stride + q * ng + d / v.group_ch];
+      }
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        dst[t * D + d0 + k] =
+            (float)((int)((wv[k] >> bit[k]) & ((1u << vb) - 1u)) - qmax_of(vb) - 1) * sc[k];
     } else if (row && d0 + 8 <= D && ((uintptr_t)(row + d0) & 15) == 0) {
       const uint4 w = *(const uint4*)(row + d0);
       const uint32_t u[4] = {w.x, w.y, w.z, w.w};
