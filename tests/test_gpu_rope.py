@@ -124,3 +124,20 @@ def test_rope_arguments():
                {"pos0": -1}, {"pos0": 1 << 40}):
         with pytest.raises(kvq.KvqError):
             kvq.kvq_decode_attention_rope(view, qt, **kw)
+
+
+@pytest.mark.parametrize("n_splits", [1, 7, 500])
+def test_rope_split_counts(n_splits):
+    # explicit split counts, more splits than tiles included, batch > 1
+    run_case(B=2, Hq=4, Hkv=2, N=1300, n_splits=n_splits, seed=50 + n_splits)
+
+
+def test_rope_workspace_too_small():
+    q, k, v = synth.kv_inputs(6, 1, 4, 2, 700, 128)
+    c = kvq.Cache(1, 2, 128, 800, 4, 2, 128, 32, 128)
+    c.kvq_append(torch.from_numpy(k).to(DEV), torch.from_numpy(v).to(DEV))
+    view = c.kvq_cache_view()
+    need = kvq.kvq_decode_workspace_bytes(view, 4, 0)
+    ws = torch.empty(need - 4, dtype=torch.uint8, device=DEV)
+    with pytest.raises(kvq.KvqError):
+        kvq.kvq_decode_attention_rope(view, torch.from_numpy(q).to(DEV), workspace=ws)
