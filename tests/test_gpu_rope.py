@@ -141,3 +141,28 @@ def test_rope_workspace_too_small():
     ws = torch.empty(need - 4, dtype=torch.uint8, device=DEV)
     with pytest.raises(kvq.KvqError):
         kvq.kvq_decode_attention_rope(view, torch.from_numpy(q).to(DEV), workspace=ws)
+
+
+def _sweep_cases(n=10):
+    """Seeded mixes of shape and cache parameters (both kernels)."""
+    rng = np.random.default_rng(2024)
+    cases = []
+    for i in range(n):
+        D = int(rng.choice([64, 128, 128, 128]))
+        kb, vb = [(8, 4), (8, 2), (4, 4), (4, 2), (2, 4), (2, 2), (3, 2), (4, 8)][rng.integers(8)]
+        G = int(rng.choice([32, 64, 128]))
+        R = G * int(rng.integers(1, 3))
+        Gv = int(rng.choice([g for g in (16, 32, 64) if D % g == 0]))
+        Hkv = int(rng.integers(1, 3))
+        g = int(rng.choice([1, 2, 3, 4, 6]))
+        cases.append(dict(B=int(rng.integers(1, 3)), Hq=g * Hkv, Hkv=Hkv, D=D, kb=kb, vb=vb,
+                          G=G, Gv=Gv, R=R, N=int(rng.integers(200, 1800)),
+                          S=int(rng.integers(0, 3)),
+                          pairing=["half", "interleaved"][int(rng.integers(2))],
+                          pos0=int(rng.integers(0, 1 << 20)), seed=100 + i))
+    return cases
+
+
+@pytest.mark.parametrize("case", _sweep_cases(), ids=lambda c: f"seed{c['seed']}")
+def test_rope_sweep(case):
+    run_case(**case)
