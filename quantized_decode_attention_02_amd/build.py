@@ -2,8 +2,8 @@
 
     python -m quantized_decode_attention_02_amd.build
 
-Compiles every HIP source under csrc/ into one shared library next to this
-file.  Flags: IEEE float32 division and square root and denormals are the
+Compiles every HIP source under csrc/ to an object (in parallel) and links
+them into one shared library next to this file.  Flags: IEEE float32 division and square root and denormals are the
 hipcc defaults and are left alone (the quantizers rely on correctly rounded
 division); packed fp32 instructions are disabled.
 """
@@ -25,13 +25,12 @@ def hipcc():
     return "hipcc"
 
 
-def build(verbose=False):
-    out_tmp = LIB + ".tmp"
-    cmd = [hipcc(), f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC",
-           "-shared", "-Xclang", "-target-feature", "-Xclang",
-           "-packed-fp32-ops", "-x", "hip"]
-    cmd += [os.path.join(CSRC, s) for s in SOURCES]
-    cmd += ["-o", out_tmp]
+def _flags():
+    return [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-Xclang",
+            "-target-feature", "-Xclang", "-packed-fp32-ops"]
+
+
+def _run(cmd, verbose):
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)
@@ -41,6 +40,22 @@ def build(verbose=False):
         raise RuntimeError(f"hipcc failed ({res.returncode}):\n{errs}")
     if errs.strip() and verbose:
         print(errs, file=sys.stderr)
+
+
+def build(verbose=False):
+    """Compile every source to an object (in parallel), then link."""
+    from concurrent.futures import ThreadPoolExecutor
+    objdir = os.path.join(HERE, "_build")
+    os.makedirs(objdir, exist_ok=True)
+    objs = [os.path.join(objdir, s + ".o") for s in SOURCES]
+    cmds = [[hipcc()] + _flags() + ["-c", "-x", "hip", os.path.join(CSRC, s),
+                                    "-o", o] for s, o in zip(SOURCES, objs)]
+    with ThreadPoolExecutor(max_workers=min(len(cmds), 8)) as ex:
+        for f in [ex.submit(_run, c, verbose) for c in cmds]:
+            f.result()
+    out_tmp = LIB + ".tmp"
+    _run([hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC"] + objs +
+         ["-o", out_tmp], verbose)
     os.replace(out_tmp, LIB)
     return LIB
 

@@ -306,6 +306,62 @@ __device__ void fp16_rows_partial(const MfmaArgs& a, int chunk, int part, int kv
   }
 }
 
+template <int CTRL>
+__device__ inline float dpp_f(float x) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+// Max / sum over the 16 lanes of a row (row_ror 8, 4, 2, 1).  The max is
+// one v_max_f32 with a DPP source per step (the builtin form adds a copy
+// and a canonicalizing max); the s_nop covers the VALU-write-to-DPP-read
+// wait states.
+template <int ROR>
+__device__ inline float max_ror(float x) {
+  float r;
+  asm("s_nop 1\n\tv_max_f32_dpp %0, %1, %1 row_ror:%2 row_mask:0xf bank_mask:0xf"
+      : "=v"(r)
+      : "v"(x), "i"(ROR));
+  return r;
+}
+__device__ inline float row_max16(float x) {
+  return max_ror<1>(max_ror<2>(max_ror<4>(max_ror<8>(x))));
+}
+__device__ inline float row_sum16(float x) {
+  x += dpp_f<0x128>(x);
+  x += dpp_f<0x124>(x);
+  x += dpp_f<0x122>(x);
+  x += dpp_f<0x121>(x);
+  return x;
+}
+
+// Value prescale.  P' = p * v_scale / f is rounded to one fp16 number, so
+// a unit's value scales are multiplied by a power of two sigma_v = 2^(14 - e)
+// before P' is formed, e being the exponent of a recent unit's largest value
+// scale: the largest scale times sigma_v stays in [2^8, 2^15), which keeps
+// P' below the fp16 maximum and, down to p * v_scale / v_max = 2^-16, in the
+// normal range (relative rounding 2^-11).  The output accumulators carry the
+// same factor: when a unit's scales leave that window, e moves to the
+// unit's exponent and the accumulators are multiplied by the (exact) power
+// of two between the two factors; at the end they are divided by sigma_v.
+// Exponent of the largest of the n value scales a wave holds (float4 j of
+// lane l is scale group l + 64 j); the result is wave-uniform.
+template <int K>
+__device__ inline int unit_vscale_exp(const float4v (&vsn)[K], int lane, int n) {
+  float mx = 0.0f;
+#pragma unroll
+  for (int j = 0; j < K; ++j)
+    if (lane + 64 * j < n)
+      mx = fmaxf(mx, fmaxf(fmaxf(vsn[j][0], vsn[j][1]), fmaxf(vsn[j][2], vsn[j][3])));
+  mx = row_max16(mx);
+  const uint32_t b = __builtin_bit_cast(uint32_t, mx);
+  const uint32_t r0 = __builtin_amdgcn_readlane(b, 0), r1 = __builtin_amdgcn_readlane(b, 16);
+  const uint32_t r2 = __builtin_amdgcn_readlane(b, 32), r3 = __builtin_amdgcn_readlane(b, 48);
+  const uint32_t m = max(max(r0, r1), max(r2, r3));  // positive floats order as integers
+  int e = (int)(m >> 23) - 127;
+  return e < -100 ? -100 : e;
+}
+__device__ inline float pow2f(int k) { return __builtin_bit_cast(float, (uint32_t)(127 + k) << 23); }
+
 // Value of the next lane of the 16-lane row (DPP row_shl:1); lane 15 gets 0.
 __device__ inline float from_next_lane(float x) {
   return __builtin_bit_cast(
@@ -476,13 +532,29 @@ decode_mfma_kernel(MfmaArgs a) {
     load_scales(u_first);
   }
 
+  int ev = 0;            // sigma_v = 2^(14 - ev) (see unit_vscale_exp)
+  bool ev_set = false;
   for (int u = u_first; u < u_hi; u += kWaves) {
     const int grp = u / upg;
-    // ---- commit this unit's scales to LDS, then fetch the next unit's
+    // ---- commit this unit's scales to LDS (times sigma_v), then fetch the
+    //      next unit's
+    {
+      const int e = unit_vscale_exp(vsn, lane, n_vs4);
+      if (!ev_set || e > ev || e < ev - 6) {
+        if (ev_set) {
+          const float r = pow2f(ev - e);
+#pragma unroll
+          for (int jb = 0; jb < 8; ++jb) o[jb] *= r;
+        }
+        ev = e;
+        ev_set = true;
+      }
+    }
+    const float sig_v = pow2f(14 - ev);
 #pragma unroll
     for (int j = 0; j < kVs4; ++j) {
       const int idx = lane + 64 * j;
-      if (idx < n_vs4) ((float4v*)my_vs)[idx] = vsn[j];
+      if (idx < n_vs4) ((float4v*)my_vs)[idx] = vsn[j] * sig_v;
     }
     // sigma_g: power of two bringing the group's largest scale below 2^13
     int exg = (int)((__builtin_bit_cast(uint32_t, kgn) >> 23) & 0xFF) - 127;
@@ -640,8 +712,14 @@ decode_mfma_kernel(MfmaArgs a) {
   }
 
   // ---- per-wave state to LDS: m, l (summed over the 4 lane groups), O
+  //      (divided by sigma_v)
   l_run += __shfl_xor(l_run, 16);
   l_run += __shfl_xor(l_run, 32);
+  if (ev_set) {
+    const float r = pow2f(ev - 14);
+#pragma unroll
+    for (int jb = 0; jb < 8; ++jb) o[jb] *= r;
+  }
   if (PACKED) {
     if (lq == 0 && col_valid && cc == 0) {
       sm_m[wave][hh] = m_run;
@@ -729,34 +807,6 @@ struct RsLds {
 template <int NC, bool KM>
 constexpr size_t rs_lds_bytes() {
   return sizeof(RsLds<NC, KM>) > sizeof(RowsLds) ? sizeof(RsLds<NC, KM>) : sizeof(RowsLds);
-}
-
-template <int CTRL>
-__device__ inline float dpp_f(float x) {
-  return __builtin_bit_cast(
-      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
-}
-// Max / sum over the 16 lanes of a row (row_ror 8, 4, 2, 1).  The max is
-// one v_max_f32 with a DPP source per step (the builtin form adds a copy
-// and a canonicalizing max); the s_nop covers the VALU-write-to-DPP-read
-// wait states.
-template <int ROR>
-__device__ inline float max_ror(float x) {
-  float r;
-  asm("s_nop 1\n\tv_max_f32_dpp %0, %1, %1 row_ror:%2 row_mask:0xf bank_mask:0xf"
-      : "=v"(r)
-      : "v"(x), "i"(ROR));
-  return r;
-}
-__device__ inline float row_max16(float x) {
-  return max_ror<1>(max_ror<2>(max_ror<4>(max_ror<8>(x))));
-}
-__device__ inline float row_sum16(float x) {
-  x += dpp_f<0x128>(x);
-  x += dpp_f<0x124>(x);
-  x += dpp_f<0x122>(x);
-  x += dpp_f<0x121>(x);
-  return x;
 }
 
 // KB: uniform key bits (4 or 2), or 0 for mixed keys (bf16 / int4 / int2
@@ -881,6 +931,9 @@ __global__ void __launch_bounds__(kThreads, (rs_waves<KB, VB, NC, HS>())) decode
   for (int jb = 0; jb < 8; ++jb) o[jb] = (float4v){0.0f, 0.0f, 0.0f, 0.0f};
   uint32_t magic = 0x64006400u;
   asm volatile("" : "+v"(magic));  // keep the fp16 magic in a VGPR
+
+  int ev = 0;            // sigma_v = 2^(14 - ev) (see unit_vscale_exp)
+  bool ev_set = false;
 
   // Rolling prefetch (as in the column kernel above).  The first unit is
   // requested before the query prologue so the two latencies overlap.
@@ -1050,10 +1103,23 @@ __global__ void __launch_bounds__(kThreads, (rs_waves<KB, VB, NC, HS>())) decode
         //      unit's, and build Q' for the unit's key group (every unit,
         //      so that Q' is not carried from one unit to the next, which
         //      costs registers)
+        {
+          const int e = unit_vscale_exp(vsn, lane, n_vs4);
+          if (!ev_set || e > ev || e < ev - 6) {
+            if (ev_set) {
+              const float r = pow2f(ev - e);
+#pragma unroll
+              for (int jb = 0; jb < 8; ++jb) o[jb] *= r;
+            }
+            ev = e;
+            ev_set = true;
+          }
+        }
+        const float sig_v = pow2f(14 - ev);
 #pragma unroll
         for (int j = 0; j < kVs4; ++j) {
           const int idx = lane + 64 * j;
-          if (idx < n_vs4) ((float4v*)my_vs)[idx] = vsn[j];
+          if (idx < n_vs4) ((float4v*)my_vs)[idx] = vsn[j] * sig_v;
         }
         int exg = (int)((__builtin_bit_cast(uint32_t, kgn) >> 23) & 0xFF) - 127;
         exg = exg < -100 ? -100 : exg;
@@ -1308,9 +1374,15 @@ __global__ void __launch_bounds__(kThreads, (rs_waves<KB, VB, NC, HS>())) decode
     __builtin_amdgcn_wave_barrier();
   }
 
-  // ---- per-wave state to LDS (after every wave is done with its P' buffer)
+  // ---- per-wave state to LDS (after every wave is done with its P' buffer);
+  //      the output divided by sigma_v
 #pragma unroll
   for (int hl = 0; hl < HS; ++hl) l_part[hl] = row_sum16(l_part[hl]);
+  if (ev_set) {
+    const float r = pow2f(ev - 14);
+#pragma unroll
+    for (int jb = 0; jb < 8; ++jb) o[jb] *= r;
+  }
   __syncthreads();
   if (ln == 0 && lq < rgd) {
 #pragma unroll
@@ -1519,7 +1591,8 @@ bool mfma_decode_eligible(const kvq_kv_view& v, int Hq) {
     return false;
   }
   if (v.v_bits != 4 && v.v_bits != 2) return false;
-  if (v.v_layout != KVQ_V_TILE32 || v.group_tok % 32 || v.n_quant % 32) return false;
+  // whole key groups only: a work unit never spans a partial group
+  if (v.v_layout != KVQ_V_TILE32 || v.group_tok % 32 || v.n_quant % v.group_tok) return false;
   // the column kernel's units need groups of at most four tiles or whole
   // multiples of four (the row-score kernel takes any multiple of a tile)
   if (!rows_kernel(v, Hq) && v.group_tok > 32 * kUnitTiles && v.group_tok % (32 * kUnitTiles))

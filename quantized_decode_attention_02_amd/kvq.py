@@ -173,6 +173,19 @@ def _need_cuda(*ts):
             raise ValueError("device tensors must be contiguous CUDA tensors")
 
 
+def _need_shape(t, shape, where, what):
+    """Raise KvqError(KVQ_E_ARG) unless t has exactly `shape`."""
+    if tuple(t.shape) != tuple(shape):
+        raise KvqError(KVQ_E_ARG, f"{where}: {what} has shape "
+                       f"{tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _need_bytes(t, n, where, what):
+    if t.numel() * t.element_size() < n:
+        raise KvqError(KVQ_E_ARG, f"{where}: {what} holds "
+                       f"{t.numel() * t.element_size()} bytes, needs {n}")
+
+
 def kvq_words(n_fields, bits):
     return lib().kvq_words(n_fields, bits)
 
@@ -275,7 +288,12 @@ class Cache:
     """A kvq_cache bound to one torch-allocated device buffer."""
 
     def __init__(self, B, Hkv, D, max_tokens, k_bits, v_bits, G, Gv, R, S=0,
-                 mixed=False, n_bf16=0, n_int4=0, device="cuda"):
+                 mixed=False, n_bf16=0, n_int4=0, device="cuda", buf=None,
+                 n_tokens=0):
+        """A new empty cache in a fresh buffer, or (buf, n_tokens > 0) one
+        re-attached to a device buffer that already holds n_tokens tokens
+        (a copy of another cache's buffer, e.g. restored from a
+        checkpoint)."""
         self.cfg = CacheCfg(batch=B, kv_heads=Hkv, head_dim=D, k_bits=k_bits,
                             v_bits=v_bits, group_tok=G, group_ch=Gv,
                             residual=R, sink=S, k_mixed=int(mixed),
@@ -284,10 +302,15 @@ class Cache:
         nbytes = lib().kvq_cache_bytes(ctypes.byref(self.cfg))
         if nbytes == 0:
             raise KvqError(KVQ_E_ARG, "kvq_cache_bytes")
-        self.buf = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        if buf is None:
+            buf = torch.empty(nbytes, dtype=torch.uint8, device=device)
+        _need_cuda(buf)
+        _need_bytes(buf, nbytes, "kvq_cache_init", "buf")
+        self.buf = buf
         h = ctypes.c_void_p()
         _check(lib().kvq_cache_init(ctypes.byref(self.cfg), _ptr(self.buf),
-                                    nbytes, 0, ctypes.byref(h), _stream()),
+                                    buf.numel() * buf.element_size(),
+                                    n_tokens, ctypes.byref(h), _stream()),
                "kvq_cache_init")
         self.handle = h
         self.mixed = mixed
@@ -304,13 +327,25 @@ class Cache:
 
     def kvq_append(self, k_new, v_new):
         _need_cuda(k_new, v_new)
+        c = self.cfg
+        if k_new.dim() != 4:
+            raise KvqError(KVQ_E_ARG, "kvq_append: k_new must be [B][Hkv][n][D]")
         n_new = k_new.shape[2]
+        _need_shape(k_new, (c.batch, c.kv_heads, n_new, c.head_dim),
+                    "kvq_append", "k_new")
+        _need_shape(v_new, tuple(k_new.shape), "kvq_append", "v_new")
+        if v_new.dtype != k_new.dtype:
+            raise KvqError(KVQ_E_ARG, "kvq_append: k_new and v_new dtypes differ")
         _check(lib().kvq_append(self.handle, _ptr(k_new), _ptr(v_new),
                                 _dtype(k_new), n_new, _stream()),
                "kvq_append")
 
     def kvq_salience_select(self, q_win):
         _need_cuda(q_win)
+        if q_win.dim() != 4 or q_win.shape[0] != self.cfg.batch or \
+                q_win.shape[3] != self.cfg.head_dim:
+            raise KvqError(KVQ_E_ARG, "kvq_salience_select: q_win must be "
+                           "[B][w_rows][Hq][D]")
         _, w, hq, _ = q_win.shape
         _check(lib().kvq_salience_select(self.handle, _ptr(q_win),
                                          _dtype(q_win), w, hq, _stream()),
@@ -372,23 +407,43 @@ def kvq_decode_workspace_bytes(view, n_q_heads, n_splits=0):
                                             n_splits)
 
 
-def kvq_decode_attention(view, q, sm_scale=None, n_splits=0,
-                         flags=KVQ_DECODE_AUTO, workspace=None, out=None):
-    """q: [B][Hq][D] f16/f32 -> out [B][Hq][D] float32."""
+def _decode_args(where, view, q, n_splits, workspace, out):
+    """Shape checks shared by the decode calls; returns (hq, sm default,
+    workspace, out)."""
     _need_cuda(q)
+    if q.dim() != 3:
+        raise KvqError(KVQ_E_ARG, f"{where}: q must be [B][Hq][D]")
     B, hq, D = q.shape
-    if sm_scale is None:
-        sm_scale = 1.0 / D ** 0.5
+    if B != view.batch or D != view.head_dim:
+        raise KvqError(KVQ_E_ARG, f"{where}: q is [{B}][{hq}][{D}], the view "
+                       f"holds batch {view.batch}, head_dim {view.head_dim}")
     ws_bytes = kvq_decode_workspace_bytes(view, hq, n_splits)
     if ws_bytes == 0:
         raise KvqError(KVQ_E_ARG, "kvq_decode_workspace_bytes")
     if workspace is None:
         workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    _need_cuda(workspace)
+    _need_bytes(workspace, ws_bytes, where, "workspace")
     if out is None:
         out = torch.empty((B, hq, D), dtype=torch.float32, device=q.device)
+    _need_cuda(out)
+    _need_shape(out, (B, hq, D), where, "out")
+    if out.dtype != torch.float32:
+        raise KvqError(KVQ_E_ARG, f"{where}: out must be float32")
+    return hq, 1.0 / D ** 0.5, workspace, out
+
+
+def kvq_decode_attention(view, q, sm_scale=None, n_splits=0,
+                         flags=KVQ_DECODE_AUTO, workspace=None, out=None):
+    """q: [B][Hq][D] f16/f32 -> out [B][Hq][D] float32."""
+    hq, sm0, workspace, out = _decode_args("kvq_decode_attention", view, q,
+                                           n_splits, workspace, out)
+    if sm_scale is None:
+        sm_scale = sm0
     _check(lib().kvq_decode_attention(
         ctypes.byref(view), _ptr(q), _dtype(q), hq, sm_scale, _ptr(out),
-        n_splits, flags, _ptr(workspace), workspace.numel(), _stream()),
+        n_splits, flags, _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _stream()),
         "kvq_decode_attention")
     return out
 
@@ -399,22 +454,16 @@ def kvq_decode_attention_rope(view, q, base=10000.0, pairing="half", pos0=0,
     """Decode over keys cached before the rotary embedding: cache-order
     token i is rotated at position pos0 + i.  q: [B][Hq][D] f16/f32, already
     rotated at its own position -> out [B][Hq][D] float32."""
-    _need_cuda(q)
-    B, hq, D = q.shape
+    hq, sm0, workspace, out = _decode_args("kvq_decode_attention_rope", view,
+                                           q, n_splits, workspace, out)
     if sm_scale is None:
-        sm_scale = 1.0 / D ** 0.5
+        sm_scale = sm0
     pr = {"half": KVQ_ROPE_HALF, "interleaved": KVQ_ROPE_INTERLEAVED}.get(pairing, -1)
     rope = Rope(base=base, pairing=pr, reserved=0, pos0=pos0)
-    ws_bytes = kvq_decode_workspace_bytes(view, hq, n_splits)
-    if ws_bytes == 0:
-        raise KvqError(KVQ_E_ARG, "kvq_decode_workspace_bytes")
-    if workspace is None:
-        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
-    if out is None:
-        out = torch.empty((B, hq, D), dtype=torch.float32, device=q.device)
     _check(lib().kvq_decode_attention_rope(
         ctypes.byref(view), ctypes.byref(rope), _ptr(q), _dtype(q), hq, sm_scale, _ptr(out),
-        n_splits, flags, _ptr(workspace), workspace.numel(), _stream()),
+        n_splits, flags, _ptr(workspace), workspace.numel() * workspace.element_size(),
+        _stream()),
         "kvq_decode_attention_rope")
     return out
 

@@ -240,10 +240,14 @@ MIXED_CASES = {
 }
 
 
-def build_both(name, cases, seed=7):
+def build_both(name, cases, seed=7, kmul=1.0, vmul=1.0):
     ckw, B, Hq, Hkv, N, chunks, ikw = cases[name]
     D = ckw["D"]
     q, k, v = synth.kv_inputs(seed, B, Hq, Hkv, N, D, **ikw)
+    if kmul != 1.0:
+        k = (k.astype(np.float32) * np.float32(kmul)).astype(np.float16)
+    if vmul != 1.0:
+        v = (v.astype(np.float32) * np.float32(vmul)).astype(np.float16)
     ocfg = ocache.CacheConfig(B=B, Hkv=Hkv, D=D, S=ckw["S"], R=ckw["R"],
                               G=ckw["G"], Gv=ckw["Gv"], k_bits=ckw["k_bits"],
                               v_bits=ckw["v_bits"],
@@ -289,14 +293,72 @@ def compare_exports(oc, gc):
     return view
 
 
-def oracle_decode(q, oc, Hkv):
+def oracle_decode(q, oc, Hkv, sm_scale=None):
     B = q.shape[0]
     outs = []
     for b in range(B):
         kh = np.stack([oc.dequantized(b, h)[0] for h in range(Hkv)])
         vh = np.stack([oc.dequantized(b, h)[1] for h in range(Hkv)])
-        outs.append(attention.attention(q[b].astype(np.float64), kh, vh))
+        outs.append(attention.attention(q[b].astype(np.float64), kh, vh,
+                                        sm_scale=sm_scale))
     return np.stack(outs)
+
+
+def split_bound(q, oc, Hkv, weight_round, chain, sm_scale=None):
+    """Per output row, a bound on |o(n_splits = a) - o(n_splits = b)|_2
+    from the arithmetic of the kernels, evaluated on the oracle's K_hat,
+    V_hat in float64.
+
+    Every softmax weight p_t reaches the output as p_t (1 + e_t) with
+    |e_t| <= eta: eta = weight_round (2^-11 where P' = p v_scale / f is one
+    fp16 number, 2^-24 where it stays float32) plus the error of the score
+    in natural-log units, (2^-20 + D 2^-24) sm sum_d |q_d k_td| (float32
+    products and a D-term float32 sum, the query split into fp16 limbs,
+    exp2).  Since o = sum p v / sum p, such weight errors move o_d by at
+    most eta / (1 - eta) * sum_t p_t |v_td - o_d| / sum_t p_t.  Float32
+    accumulation along a chain of at most `chain` additions (tiles of one
+    accumulator, partial merges) adds chain 2^-24 (sum p |v| / sum p + |o|).
+    P' values below the fp16 normal range add an absolute 2^-30 max|v|
+    per token at most.  The difference of two split counts is at most
+    twice the sum.
+    """
+    B, Hq, D = q.shape
+    g = Hq // Hkv
+    sm = 1.0 / np.sqrt(D) if sm_scale is None else sm_scale
+    rows = []
+    for b in range(B):
+        for h in range(Hq):
+            kh, vh = oc.dequantized(b, h // g)
+            qq = q[b, h].astype(np.float64)
+            s = (kh @ qq) * sm
+            p = np.exp(s - s.max())
+            o = p @ vh / p.sum()
+            dev = (p @ np.abs(vh - o)) / p.sum()
+            mag = (p @ np.abs(vh)) / p.sum() + np.abs(o)
+            ds = (2.0 ** -20 + D * 2.0 ** -24) * sm * (np.abs(kh) @ np.abs(qq))
+            eta = weight_round + float(ds.max())
+            n = kh.shape[0]
+            rows.append(2 * (eta / (1 - eta) * np.linalg.norm(dev) +
+                             chain * 2.0 ** -24 * np.linalg.norm(mag) +
+                             n * 2.0 ** -30 * np.abs(vh).max() * np.sqrt(D)))
+    return np.array(rows).reshape(B, Hq)
+
+
+def assert_split_invariance(outs, q, oc, Hkv, n_tok, sm_scale=None):
+    """outs: {(flags, splits): out}; the matrix-core path rounds P' to fp16,
+    the general kernel keeps float32 weights; the general kernel's chain is
+    at most the tokens of one partial, the matrix-core one the tiles of one
+    wave plus the merges."""
+    for flags, wr, chain in ((kvq.KVQ_DECODE_AUTO, 2.0 ** -11, n_tok // 32 + 64),
+                             (kvq.KVQ_DECODE_GENERIC, 2.0 ** -24, n_tok + 64)):
+        keys = sorted(s for f, s in outs if f == flags)
+        if len(keys) < 2:
+            continue
+        bound = split_bound(q, oc, Hkv, wr, chain, sm_scale)
+        a = outs[(flags, keys[0])]
+        for s in keys[1:]:
+            diff = np.linalg.norm(outs[(flags, s)] - a, axis=-1)
+            assert np.all(diff <= bound), (flags, s, float(np.max(diff / bound)))
 
 
 @pytest.mark.parametrize("name", list(CACHE_CASES) + list(MIXED_CASES))
@@ -317,16 +379,11 @@ def test_cache_parity(name):
             say(f"  flags={flags} splits={splits} err={err:.3e}")
             assert err <= TOL
             outs[(flags, splits)] = out
-    # The split count changes the summation order, and on the matrix-core
-    # path also the running max against which P' = p * v_scale is rounded to
-    # fp16 (relative 2^-11 per element): bounds 1e-4 (general, float32) and
-    # 1e-3 (matrix core).
-    for flags, bound in ((kvq.KVQ_DECODE_AUTO, 1e-3),
-                         (kvq.KVQ_DECODE_GENERIC, 1e-4)):
-        a = outs[(flags, 1)]
-        for s in (0, 3):
-            rel = np.max(np.abs(outs[(flags, s)] - a)) / np.max(np.abs(a))
-            assert rel <= bound
+    # The split count changes the summation order and, on the matrix-core
+    # path, the running max against which P' is rounded to fp16: bounded by
+    # the error analysis of split_bound.
+    assert_split_invariance(outs, q, oc, Hkv,
+                            view.n_sink + view.n_quant + view.n_tail)
     # fp32 query gives the same result as its fp16 values
     out32 = kvq.kvq_decode_attention(view, qt.float()).cpu().numpy()
     assert attention.max_row_relative_error(out32, ref) <= TOL
@@ -361,6 +418,69 @@ def test_decode_query_and_scale_range(qmul, sm):
         err = attention.max_row_relative_error(out, ref)
         say(f"  flags={flags} err={err:.3e}")
         assert err <= TOL
+
+
+SMALL_CASES = {
+    "k2v4_g1": (dict(D=128, S=1, G=64, Gv=32, R=64, k_bits=2, v_bits=4),
+                1, 2, 2, 1200, [1200], dict(outliers="none")),
+}
+
+
+@pytest.mark.parametrize("name", ["k4v2_gqa_sink", "k2v4_g1", "mixkvq_small",
+                                  "mixed_nb4_v4"])
+@pytest.mark.parametrize("kmul,vmul", [(1.0, 2.0 ** -6), (1.0, 2.0 ** -10),
+                                       (1.0, 2.0 ** -14), (1.0, 2.0 ** -20),
+                                       (1.0, 2.0 ** 8), (2.0 ** -10, 1.0),
+                                       (2.0 ** -20, 2.0 ** -20)])
+def test_small_and_large_magnitudes(name, kmul, vmul):
+    """Key and value caches far from unit magnitude (down to fp16
+    subnormal inputs): the matrix-core path scales each unit's value scales
+    and each key group's query by powers of two, so its error stays within
+    the bound at every magnitude."""
+    say("magnitude case", name, kmul, vmul)
+    cases = dict(CACHE_CASES, **MIXED_CASES, **SMALL_CASES)
+    q, oc, gc, Hkv = build_both(name, cases, kmul=kmul, vmul=vmul)
+    assert gc.kvq_cache_check() == kvq.KVQ_OK
+    view = compare_exports(oc, gc)
+    assert view.n_quant >= 512
+    ref = oracle_decode(q, oc, Hkv)
+    qt = torch.from_numpy(q).to(DEV)
+    outs = {}
+    for flags in (kvq.KVQ_DECODE_AUTO, kvq.KVQ_DECODE_GENERIC):
+        for splits in (0, 3):
+            out = kvq.kvq_decode_attention(view, qt, n_splits=splits,
+                                           flags=flags).cpu().numpy()
+            err = attention.max_row_relative_error(out, ref)
+            say(f"  flags={flags} splits={splits} err={err:.3e}")
+            assert err <= TOL
+            outs[(flags, splits)] = out
+    assert_split_invariance(outs, q, oc, Hkv,
+                            view.n_sink + view.n_quant + view.n_tail)
+
+
+@pytest.mark.parametrize("name", ["k4v2_gqa_sink", "mixkvq_small",
+                                  "k2v2_g32_mha", "k4v2_g16_wide"])
+def test_more_splits_than_units(name):
+    """Split counts far above the number of work units: most splits are
+    empty and write neutral partials (l = 0) that the merge skips."""
+    say("many splits", name)
+    cases = dict(CACHE_CASES, **MIXED_CASES)
+    q, oc, gc, Hkv = build_both(name, cases)
+    view = gc.kvq_cache_view()
+    ref = oracle_decode(q, oc, Hkv)
+    qt = torch.from_numpy(q).to(DEV)
+    outs = {}
+    n_units = view.n_quant // 32
+    for flags in (kvq.KVQ_DECODE_AUTO, kvq.KVQ_DECODE_GENERIC):
+        for splits in (1, n_units + 7, 4 * n_units + 100):
+            out = kvq.kvq_decode_attention(view, qt, n_splits=splits,
+                                           flags=flags).cpu().numpy()
+            err = attention.max_row_relative_error(out, ref)
+            say(f"  flags={flags} splits={splits} err={err:.3e}")
+            assert err <= TOL
+            outs[(flags, splits)] = out
+    assert_split_invariance(outs, q, oc, Hkv,
+                            view.n_sink + view.n_quant + view.n_tail)
 
 
 def test_append_determinism_and_capacity():
