@@ -29,8 +29,10 @@
  * Conventions for every call:
  *  - All data pointers are DEVICE pointers unless the comment says host.
  *    The caller allocates every device buffer; the library never allocates
- *    device memory.  Host handles (kvq_cache) are malloc'ed by
- *    kvq_cache_init and released by kvq_cache_free.
+ *    device memory (its only device memory of its own is the fixed scratch
+ *    array of kvq_decode_attention_noalloc, loaded with the library).  Host
+ *    handles (kvq_cache) are malloc'ed by kvq_cache_init and released by
+ *    kvq_cache_free.
  *  - `stream` is a hipStream_t (NULL = the default stream).  Calls only
  *    enqueue work and return; results are valid once the stream reaches
  *    them.  Calls on one cache or one output buffer must be ordered by the
@@ -62,7 +64,9 @@ typedef enum {
   KVQ_E_NONFINITE = 3,  /* a kernel saw NaN/Inf input (sticky flag set) */
   KVQ_E_HIP = 4,        /* a HIP runtime call failed */
   KVQ_E_POISONED = 5,   /* cache saw NaN/Inf earlier; re-initialise it */
-  KVQ_E_UNSUPPORTED = 6 /* valid request the library does not implement */
+  KVQ_E_UNSUPPORTED = 6, /* valid request the library does not implement */
+  KVQ_E_SCRATCH = 7      /* kvq_decode_attention_noalloc: the split partials
+                            would not fit the library's fixed scratch */
 } kvq_status;
 
 typedef enum { KVQ_F32 = 0, KVQ_F16 = 1 } kvq_dtype;
@@ -295,6 +299,22 @@ kvq_status kvq_decode_attention(const kvq_kv_view* v, const void* q,
                                 float* out, int n_splits, int flags,
                                 void* workspace, size_t ws_bytes,
                                 void* stream);
+
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * decode as kvq_decode_attention, with the split partials in a fixed array
+ * of KVQ_NOALLOC_SCRATCH_BYTES of the library's own device memory (one per
+ * GPU, held until the process ends) instead of a caller workspace.  The
+ * caller still passes q and out.  The call allocates nothing.  It needs
+ * kvq_decode_workspace_bytes(v, n_q_heads, n_splits) <= the scratch size,
+ * else KVQ_E_SCRATCH and nothing is enqueued.  Every call on one GPU shares
+ * its array: calls that overlap on one GPU (several streams, or threads
+ * without ordering) race and must be serialized by the caller.            */
+#define KVQ_NOALLOC_SCRATCH_BYTES (16u << 20)
+kvq_status kvq_decode_attention_noalloc(const kvq_kv_view* v, const void* q,
+                                        int dtype, int n_q_heads,
+                                        float sm_scale, float* out,
+                                        int n_splits, int flags, void* stream);
 
 /* Keys cached before the rotary position embedding ("KVQuant: Towards 10
  * Million Context Length LLM Inference with KV Cache Quantization",

@@ -14,7 +14,8 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libkvq.so")
-SOURCES = ["api.cpp", "quant.hip", "decode_generic.hip", "decode_mfma.hip", "decode_rope.hip"]
+SOURCES = ["api.cpp", "quant.hip", "decode_generic.hip", "decode_mfma.hip", "decode_rope.hip",
+           "noalloc.hip"]
 ARCH = "gfx950"
 
 

@@ -178,6 +178,7 @@ const char* kvq_strerror(kvq_status s) {
     case KVQ_E_HIP: return "HIP runtime error";
     case KVQ_E_POISONED: return "cache poisoned by an earlier NaN/Inf input";
     case KVQ_E_UNSUPPORTED: return "unsupported configuration";
+    case KVQ_E_SCRATCH: return "decode partials exceed the fixed scratch of the no-allocation entry point";
   }
   return "unknown status";
 }
@@ -379,6 +380,17 @@ size_t kvq_decode_workspace_bytes(const kvq_kv_view* v, int n_q_heads, int n_spl
 kvq_status kvq_decode_attention(const kvq_kv_view* v, const void* q, int dtype,
                                 int n_q_heads, float sm_scale, float* out, int n_splits,
                                 int flags, void* workspace, size_t ws_bytes, void* stream) {
+  return kvq::decode_attention_impl(v, q, dtype, n_q_heads, sm_scale, out, n_splits, flags,
+                                    workspace, ws_bytes, stream);
+}
+
+}  // extern "C"
+
+namespace kvq {
+
+kvq_status decode_attention_impl(const kvq_kv_view* v, const void* q, int dtype, int n_q_heads,
+                                 float sm_scale, float* out, int n_splits, int flags,
+                                 void* workspace, size_t ws_bytes, void* stream) {
   if (!view_ok(v) || !q || !out || !workspace) return KVQ_E_ARG;
   if (dtype != KVQ_F16 && dtype != KVQ_F32) return KVQ_E_ARG;
   if (n_q_heads < 1 || n_q_heads % v->kv_heads || n_splits < 0 || n_splits > 16384)
@@ -409,6 +421,10 @@ kvq_status kvq_decode_attention(const kvq_kv_view* v, const void* q, int dtype,
   if (e == hipSuccess) e = launch_merge(partials, v->batch, n_q_heads, v->head_dim, parts, out, s);
   return hip_status(e);
 }
+
+}  // namespace kvq
+
+extern "C" {
 
 kvq_status kvq_decode_attention_rope(const kvq_kv_view* v, const kvq_rope* rope, const void* q,
                                      int dtype, int n_q_heads, float sm_scale, float* out,

@@ -180,5 +180,10 @@ hipError_t launch_decode_rope(const kvq_kv_view& v, const void* q, int f16, int 
                               int n_parts, hipStream_t s);
 hipError_t launch_merge(const float* partials, int B, int Hq, int D,
                         int n_parts, float* out, hipStream_t s);
+// kvq_decode_attention with the partials in `workspace` (api.cpp); the
+// scratch-backed entry point calls it too.
+kvq_status decode_attention_impl(const kvq_kv_view* v, const void* q, int dtype, int n_q_heads,
+                                 float sm_scale, float* out, int n_splits, int flags,
+                                 void* workspace, size_t ws_bytes, void* stream);
 
 }  // namespace kvq

@@ -14,7 +14,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libkvq.so")
 
 KVQ_OK, KVQ_E_ARG, KVQ_E_CAPACITY, KVQ_E_NONFINITE, KVQ_E_HIP, \
-    KVQ_E_POISONED, KVQ_E_UNSUPPORTED = range(7)
+    KVQ_E_POISONED, KVQ_E_UNSUPPORTED, KVQ_E_SCRATCH = range(8)
+NOALLOC_SCRATCH_BYTES = 16 << 20  # KVQ_NOALLOC_SCRATCH_BYTES
 KVQ_F32, KVQ_F16 = 0, 1
 KVQ_PER_CHANNEL, KVQ_PER_TOKEN = 0, 1
 KVQ_V_ROWS, KVQ_V_TILE32 = 0, 1
@@ -27,7 +28,7 @@ EXPORTED = [
     "kvq_append", "kvq_salience_select", "kvq_cache_check", "kvq_cache_view",
     "kvq_export", "kvq_decode_workspace_bytes", "kvq_decode_attention",
     "kvq_poll_error", "kvq_strerror", "kvq_fill_u32", "kvq_synth_normal_f16", "kvq_stream_read",
-    "kvq_hadamard", "kvq_decode_attention_rope",
+    "kvq_hadamard", "kvq_decode_attention_rope", "kvq_decode_attention_noalloc",
 ]
 
 _c_i32, _c_i64, _c_u64, _c_p, _c_f = (ctypes.c_int32, ctypes.c_int64,
@@ -119,6 +120,9 @@ def lib():
         "kvq_decode_attention": (_c_i32, [
             ctypes.POINTER(KvView), _c_p, _c_i32, _c_i32, _c_f, _c_p, _c_i32,
             _c_i32, _c_p, ctypes.c_size_t, _c_p]),
+        "kvq_decode_attention_noalloc": (_c_i32, [
+            ctypes.POINTER(KvView), _c_p, _c_i32, _c_i32, _c_f, _c_p, _c_i32,
+            _c_i32, _c_p]),
         "kvq_decode_attention_rope": (_c_i32, [
             ctypes.POINTER(KvView), ctypes.POINTER(Rope), _c_p, _c_i32, _c_i32, _c_f, _c_p,
             _c_i32, _c_i32, _c_p, ctypes.c_size_t, _c_p]),
@@ -445,6 +449,27 @@ def kvq_decode_attention(view, q, sm_scale=None, n_splits=0,
         n_splits, flags, _ptr(workspace), workspace.numel() * workspace.element_size(),
         _stream()),
         "kvq_decode_attention")
+    return out
+
+
+def kvq_decode_attention_noalloc(view, q, out, sm_scale=None, n_splits=0,
+                                 flags=KVQ_DECODE_AUTO):
+    """kvq_decode_attention with the split partials in the library's fixed
+    scratch: q [B][Hq][D] f16/f32, out [B][Hq][D] float32 (the caller's);
+    nothing is allocated."""
+    _need_cuda(q, out)
+    if q.dim() != 3 or q.shape[0] != view.batch or q.shape[2] != view.head_dim:
+        raise KvqError(KVQ_E_ARG, "kvq_decode_attention_noalloc: q must be "
+                       "[B][Hq][D] of the view")
+    _need_shape(out, tuple(q.shape), "kvq_decode_attention_noalloc", "out")
+    if out.dtype != torch.float32:
+        raise KvqError(KVQ_E_ARG, "kvq_decode_attention_noalloc: out must be float32")
+    hq, D = q.shape[1], q.shape[2]
+    if sm_scale is None:
+        sm_scale = 1.0 / D ** 0.5
+    _check(lib().kvq_decode_attention_noalloc(
+        ctypes.byref(view), _ptr(q), _dtype(q), hq, sm_scale, _ptr(out),
+        n_splits, flags, _stream()), "kvq_decode_attention_noalloc")
     return out
 
 
