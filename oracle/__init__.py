@@ -18,10 +18,13 @@ and in the pages' order:
 * bytes_model.py  payload byte accounting
 * rotation.py  key-only Walsh-Hadamard rotation (fast transform in float32)
 * rope.py      rotary embedding of pre-RoPE cached keys at decode
+* nuq.py       non-uniform (codebook) datatype with per-vector dense-and-sparse
+               outliers
+* qjl.py       value-side 1-bit residual sketch of the KQV scheme
 
 Parity status: every function is pinned by ``tests/test_oracle_*.py`` against
 values printed on the pages, closed forms, invariants, brute force or library
 routines; none is "parity unpinned".
 """
 
-from . import codec, salience, cache, attention, bytes_model, rotation, rope  # noqa: F401
+from . import codec, salience, cache, attention, bytes_model, rotation, rope, nuq, qjl  # noqa: F401,E501

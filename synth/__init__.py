@@ -183,3 +183,38 @@ WORKLOADS = {
                        Gv=32, R=128, k_bits=2, v_bits=2, layers=32,
                        chunk=4096),
 }
+
+
+# ---------------------------------------------------------------------------
+# inputs of the non-uniform datatype and of the 1-bit residual sketch
+# ---------------------------------------------------------------------------
+
+
+def nuq_codebook(bits):
+    """A synthetic non-uniform codebook of 2**bits levels in [-1, 1].
+
+    The pages' codebooks come from a sensitivity-weighted k-means over real
+    activations ("KVQuant ...", Approach), which needs model data; this one
+    is built the way NormalFloat levels are (the page names NormalFloat as a
+    basis): quantiles of N(0, 1), 2**(bits-1) positive and 2**(bits-1) - 1
+    negative ones at evenly spaced probabilities in (0.5, 0.97], each side
+    normalized so its outermost level is exactly +-1, plus an exact 0, every
+    level rounded to fp16.  Returns float32 [2**bits], strictly ascending.
+    """
+    from scipy.stats import norm
+
+    n = 1 << bits
+    n_pos, n_neg = n // 2, n // 2 - 1
+    pos = norm.ppf(np.linspace(0.5, 0.97, n_pos + 1)[1:])
+    neg = norm.ppf(np.linspace(0.5, 0.97, n_neg + 1)[1:]) if n_neg else np.zeros(0)
+    pos = pos / pos[-1]
+    neg = -(neg / neg[-1]) if n_neg else neg
+    levels = np.concatenate([neg[::-1], [0.0], pos]).astype(np.float16)
+    return levels.astype(np.float32)
+
+
+def jl_matrix(seed, m, d):
+    """The Gaussian projection of the 1-bit sketch: float32 [m][d], i.i.d.
+    N(0, 1) from default_rng(seed + 2_000_003)."""
+    rng = np.random.default_rng(seed + 2_000_003)
+    return rng.standard_normal((m, d), dtype=np.float32)
