@@ -355,6 +355,113 @@ kvq_status kvq_decode_attention_rope(const kvq_kv_view* v, const kvq_rope* rope,
                                      void* stream);
 
 /* ---------------------------------------------------------------------
+ * Extended formats: the non-uniform codebook datatype with dense-and-sparse
+ * outliers, and the value-side 1-bit residual sketch.
+ * ------------------------------------------------------------------ */
+
+/* Non-uniform codebook datatype with per-vector dense-and-sparse outliers
+ * ("KVQuant: Towards 10 Million Context Length LLM Inference with KV Cache
+ * Quantization", summary and "Approach": nuqX datatypes and per-vector
+ * dense-and-sparse outlier isolation; table "Measured effects reported in
+ * the paper": 1% outliers, per-vector thresholds, keys per channel and
+ * values per token).  A vector is what one scale covers: for keys one
+ * channel of a group of group_tok tokens, for values one group of group_ch
+ * channels of one token.  In each vector the n_out entries of largest
+ * magnitude (ties to the lower position) are kept exactly; the rest (those
+ * entries set to 0) get scale = max|x| / max|lut| (IEEE float32 division;
+ * 1 for an all-zero rest) and per entry the index of the codebook level
+ * nearest to fl32(x / scale) (ties to the lower level).  Reconstruction:
+ * lut[code] * scale plus the kept entries.
+ *   k, v      [n_mats][n_tok][d] float16 (device)
+ *   lut       HOST float32 [2^bits], bits 2, 3 or 4: strictly ascending
+ *             fp16 numbers including 0 (a synthetic or calibrated codebook)
+ *   codes     [n_mats][n_tok][kvq_words(d, bits)] uint32: level indices,
+ *             LSB-first (plain indices, no offset)
+ *   scales    keys [n_mats][ceil(n_tok / group_tok)][d];
+ *             values [n_mats][n_tok][d / group_ch] float32
+ *   outliers  uint32 (position in the vector << 16 | fp16 bits of the
+ *             value), positions ascending; keys
+ *             [n_mats][ceil(n_tok/group_tok)][d][n_out], values
+ *             [n_mats][n_tok][d / group_ch][n_out]; slots past a vector
+ *             shorter than n_out hold 0
+ * Requires 1 <= d <= 256, 0 <= n_out <= 16, n_out < 65536 entries per
+ * vector, keys group_tok * d <= 32768; else KVQ_E_ARG.  NaN/Inf input sets
+ * bit 0 of err_flag (nullable).                                          */
+kvq_status kvq_quantize_nuq_k(const void* k, int64_t n_mats, int64_t n_tok, int d, int bits,
+                              int group_tok, const float* lut, int n_out, uint32_t* codes,
+                              float* scales, uint32_t* outliers, uint32_t* err_flag,
+                              void* stream);
+kvq_status kvq_quantize_nuq_v(const void* v, int64_t n_mats, int64_t n_tok, int d, int bits,
+                              int group_ch, const float* lut, int n_out, uint32_t* codes,
+                              float* scales, uint32_t* outliers, uint32_t* err_flag,
+                              void* stream);
+
+/* Values with the 1-bit residual sketch of the KQV scheme ("Statistical
+ * Inference and Quality Measures of KV Cache Quantisations Inspired by
+ * TurboQuant", "Quantization Schemes": values rotated by a Walsh-Hadamard
+ * transform, scalar-quantized with n - 1 bits, plus a 1-bit QJL sketch of
+ * the residual; "1. Theoretical Proof of QJL Harm on Keys": the sketch is
+ * an unbiased estimator).  v is the already rotated value (kvq_hadamard);
+ * per token the symmetric rule of kvq_quantize_v with `bits` bits in groups
+ * of group_ch channels, then the residual r = v - fl32(code * scale) (exact
+ * in float32), sketch bit i = [<S_i, r> >= 0] for the m rows of S (dot
+ * products in float64), and rnorm = ||r||_2 (float64, rounded to float32).
+ *   v       [n_mats][n_tok][d] KVQ_F16 or KVQ_F32
+ *   jl      [m][d] float32 device: the Gaussian projection S (an input;
+ *           one matrix for the whole cache)
+ *   codes   [n_mats][n_tok][kvq_words(d, bits)]; scales [..][d/group_ch]
+ *   sketch  [n_mats][n_tok][m / 32] uint32 (bit i of word w: row 32 w + i)
+ *   rnorm   [n_mats][n_tok] float32
+ * Requires m a multiple of 32, 32 <= m <= 256, 1 <= d <= 256.            */
+kvq_status kvq_quantize_v_qjl(const void* v, int dtype, int64_t n_mats, int64_t n_tok, int d,
+                              int bits, int group_ch, const float* jl, int m, uint32_t* codes,
+                              float* scales, uint32_t* sketch, float* rnorm,
+                              uint32_t* err_flag, void* stream);
+
+/* A view over the outputs of the quantizers above (and kvq_quantize_k/v),
+ * rows layout, per (batch, KV head) stream s = b * kv_heads + h (strides
+ * in elements of each array's type).  Keys: codes with per-channel scales
+ * per group of group_tok tokens, symmetric (k_nuq 0, k_bits 8|4|3|2) or
+ * codebook (k_nuq 1, k_bits 2|3|4, k_lut, k_n_out outliers per vector).
+ * Values: per-token scales per group_ch channels, symmetric or codebook
+ * likewise, optionally with the residual sketch (v_qjl 1: v_sketch,
+ * v_rnorm, jl [qjl_m][head_dim]); v_rotated 1 turns the output back with
+ * the Walsh-Hadamard transform (values stored rotated; head_dim a power of
+ * two).  Host-side codebooks are copied into the call.                   */
+typedef struct {
+  int32_t batch, kv_heads, head_dim, reserved0;
+  int64_t n_tok;
+  int32_t k_bits, group_tok, k_nuq, k_n_out;
+  const uint32_t* k_codes; int64_t k_codes_stride;
+  const float* k_scales; int64_t k_scales_stride;
+  const uint32_t* k_outliers; int64_t k_outliers_stride;
+  float k_lut[16];
+  int32_t v_bits, group_ch, v_nuq, v_n_out;
+  const uint32_t* v_codes; int64_t v_codes_stride;
+  const float* v_scales; int64_t v_scales_stride;
+  const uint32_t* v_outliers; int64_t v_outliers_stride;
+  float v_lut[16];
+  int32_t v_qjl, qjl_m, v_rotated, reserved1;
+  const uint32_t* v_sketch; int64_t v_sketch_stride;
+  const float* v_rnorm; int64_t v_rnorm_stride;
+  const float* jl;
+} kvq_ext_view;
+
+/* Workspace bytes of kvq_decode_attention_ext (0 if the view is invalid). */
+size_t kvq_decode_ext_workspace_bytes(const kvq_ext_view* v, int n_q_heads, int n_splits);
+
+/* Decode attention over an extended view: out = softmax(q K_hat^T *
+ * sm_scale) V_hat per query head ("KV quantization axes ...", "Separate the
+ * two error paths"), K_hat and V_hat the reconstructions above (the sketch
+ * contributes sqrt(pi/2)/m * rnorm * S^T b per token; rotated values are
+ * turned back).  q [B][n_q_heads][D] KVQ_F16 or KVQ_F32; out float32.
+ * Requires head_dim <= 128, (n_q_heads / kv_heads) * head_dim <= 1024,
+ * (n_q_heads / kv_heads) * qjl_m <= 1024, n_splits <= 4096, n_tok >= 1.  */
+kvq_status kvq_decode_attention_ext(const kvq_ext_view* v, const void* q, int dtype,
+                                    int n_q_heads, float sm_scale, float* out, int n_splits,
+                                    void* workspace, size_t ws_bytes, void* stream);
+
+/* ---------------------------------------------------------------------
  * Errors and utilities.
  * ------------------------------------------------------------------ */
 

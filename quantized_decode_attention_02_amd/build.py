@@ -15,7 +15,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libkvq.so")
 SOURCES = ["api.cpp", "quant.hip", "decode_generic.hip", "decode_mfma.hip", "decode_rope.hip",
-           "noalloc.hip"]
+           "noalloc.hip", "ext.hip"]
 ARCH = "gfx950"
 
 

@@ -474,6 +474,167 @@ kvq_status kvq_decode_attention_rope(const kvq_kv_view* v, const kvq_rope* rope,
   return hip_status(e);
 }
 
+}  // extern "C"
+
+namespace {
+
+// fp16 numbers: at most 11 significant bits, within the fp16 range.
+bool fp16_exact(float x) {
+  const double a = fabs((double)x);
+  if (a == 0.0) return true;
+  if (!(a <= 65504.0)) return false;
+  if (a < 6.103515625e-05) {  // subnormal: a multiple of 2^-24
+    const double t = a * 16777216.0;
+    return t == rint(t);
+  }
+  int e;
+  const double m = frexp(a, &e);
+  return m * 2048.0 == rint(m * 2048.0);
+}
+
+// Host codebook -> kernel arguments; false if it is not a valid one
+// (2^bits strictly ascending fp16 numbers including 0, every midpoint of
+// neighbours a float32 number).
+bool make_lut(const float* lut, int bits, ExtLut* out) {
+  if (!lut || bits < 2 || bits > 4) return false;
+  const int n = 1 << bits;
+  bool zero = false;
+  ExtLut L{};
+  L.n = n;
+  for (int j = 0; j < n; ++j) {
+    const float x = lut[j];
+    if (!__builtin_isfinite(x) || !fp16_exact(x)) return false;
+    if (j > 0 && !(x > lut[j - 1])) return false;
+    if (x == 0.0f) zero = true;
+    L.lvl[j] = x;
+  }
+  if (!zero) return false;
+  for (int j = 0; j + 1 < n; ++j) {
+    const double mid = ((double)lut[j] + (double)lut[j + 1]) * 0.5;
+    if ((double)(float)mid != mid) return false;
+    L.mid[j] = (float)mid;
+  }
+  L.absmax = fmaxf(fabsf(lut[0]), fabsf(lut[n - 1]));
+  *out = L;
+  return true;
+}
+
+bool ext_view_ok(const kvq_ext_view* v, int n_q_heads) {
+  if (!v) return false;
+  if (v->batch < 1 || v->kv_heads < 1 || v->head_dim < 1 || v->head_dim > 128) return false;
+  if (v->n_tok < 1 || n_q_heads < 1 || n_q_heads % v->kv_heads) return false;
+  const int g = n_q_heads / v->kv_heads;
+  if (g * v->head_dim > 1024) return false;
+  if (v->group_tok < 1 || v->group_ch < 1 || v->head_dim % v->group_ch) return false;
+  if (!v->k_codes || !v->k_scales || !v->v_codes || !v->v_scales) return false;
+  if (v->k_nuq ? (v->k_bits < 2 || v->k_bits > 4) : !bits_ok(v->k_bits)) return false;
+  if (v->v_nuq ? (v->v_bits < 2 || v->v_bits > 4) : !bits_ok(v->v_bits)) return false;
+  if (v->k_n_out < 0 || v->k_n_out > 16 || v->v_n_out < 0 || v->v_n_out > 16) return false;
+  if ((!v->k_nuq && v->k_n_out) || (!v->v_nuq && v->v_n_out)) return false;
+  if (v->k_n_out && !v->k_outliers) return false;
+  if (v->v_n_out && !v->v_outliers) return false;
+  if (v->v_qjl) {
+    if (v->qjl_m < 32 || v->qjl_m > 256 || v->qjl_m % 32) return false;
+    if (g * v->qjl_m > 1024 || !v->v_sketch || !v->v_rnorm || !v->jl) return false;
+  }
+  if (v->v_rotated && (v->head_dim & (v->head_dim - 1))) return false;
+  if (!aligned(v->k_codes, 4) || !aligned(v->v_codes, 4) || !aligned(v->k_scales, 4) ||
+      !aligned(v->v_scales, 4))
+    return false;
+  return true;
+}
+
+}  // namespace
+
+extern "C" {
+
+kvq_status kvq_quantize_nuq_k(const void* k, int64_t n_mats, int64_t n_tok, int d, int bits,
+                              int group_tok, const float* lut, int n_out, uint32_t* codes,
+                              float* scales, uint32_t* outliers, uint32_t* err_flag,
+                              void* stream) {
+  ExtLut L;
+  if (!make_lut(lut, bits, &L)) return KVQ_E_ARG;
+  if (n_mats < 0 || n_tok < 0 || d < 1 || d > kMaxD || group_tok < 1 || n_out < 0 || n_out > 16)
+    return KVQ_E_ARG;
+  if ((int64_t)group_tok * d > 32768 || group_tok > 65535) return KVQ_E_ARG;
+  if (n_mats == 0 || n_tok == 0) return KVQ_OK;
+  if (!k || !codes || !scales || (n_out && !outliers) || !aligned(k, 2) || !aligned(codes, 4) ||
+      !aligned(scales, 4) || (outliers && !aligned(outliers, 4)) ||
+      (err_flag && !aligned(err_flag, 4)))
+    return KVQ_E_ARG;
+  if ((n_tok + group_tok - 1) / group_tok > 0x7FFFFFFF || n_mats > 65535) return KVQ_E_UNSUPPORTED;
+  return hip_status(launch_quantize_nuq_k((const uint16_t*)k, n_mats, n_tok, d, bits, group_tok,
+                                          L, n_out, codes, scales, outliers, err_flag,
+                                          (hipStream_t)stream));
+}
+
+kvq_status kvq_quantize_nuq_v(const void* v, int64_t n_mats, int64_t n_tok, int d, int bits,
+                              int group_ch, const float* lut, int n_out, uint32_t* codes,
+                              float* scales, uint32_t* outliers, uint32_t* err_flag,
+                              void* stream) {
+  ExtLut L;
+  if (!make_lut(lut, bits, &L)) return KVQ_E_ARG;
+  if (n_mats < 0 || n_tok < 0 || d < 1 || d > kMaxD || group_ch < 1 || d % group_ch ||
+      n_out < 0 || n_out > 16)
+    return KVQ_E_ARG;
+  if (n_mats == 0 || n_tok == 0) return KVQ_OK;
+  if (!v || !codes || !scales || (n_out && !outliers) || !aligned(v, 2) || !aligned(codes, 4) ||
+      !aligned(scales, 4) || (outliers && !aligned(outliers, 4)) ||
+      (err_flag && !aligned(err_flag, 4)))
+    return KVQ_E_ARG;
+  if ((n_tok + 31) / 32 > 0x7FFFFFFF || n_mats > 65535) return KVQ_E_UNSUPPORTED;
+  return hip_status(launch_quantize_nuq_v((const uint16_t*)v, n_mats, n_tok, d, bits, group_ch, L,
+                                          n_out, codes, scales, outliers, err_flag,
+                                          (hipStream_t)stream));
+}
+
+kvq_status kvq_quantize_v_qjl(const void* v, int dtype, int64_t n_mats, int64_t n_tok, int d,
+                              int bits, int group_ch, const float* jl, int m, uint32_t* codes,
+                              float* scales, uint32_t* sketch, float* rnorm,
+                              uint32_t* err_flag, void* stream) {
+  if (dtype != KVQ_F32 && dtype != KVQ_F16) return KVQ_E_ARG;
+  if (n_mats < 0 || n_tok < 0 || d < 1 || d > kMaxD || !bits_ok(bits) || group_ch < 1 ||
+      d % group_ch || m < 32 || m > 256 || m % 32)
+    return KVQ_E_ARG;
+  if (n_mats == 0 || n_tok == 0) return KVQ_OK;
+  if (!v || !jl || !codes || !scales || !sketch || !rnorm ||
+      !aligned(v, dtype == KVQ_F32 ? 4 : 2) || !aligned(jl, 4) || !aligned(codes, 4) ||
+      !aligned(scales, 4) || !aligned(sketch, 4) || !aligned(rnorm, 4) ||
+      (err_flag && !aligned(err_flag, 4)))
+    return KVQ_E_ARG;
+  if ((n_tok + 31) / 32 > 0x7FFFFFFF || n_mats > 65535) return KVQ_E_UNSUPPORTED;
+  return hip_status(launch_quantize_v_qjl(v, dtype == KVQ_F16, n_mats, n_tok, d, bits, group_ch, jl,
+                                          m, codes, scales, sketch, rnorm, err_flag,
+                                          (hipStream_t)stream));
+}
+
+size_t kvq_decode_ext_workspace_bytes(const kvq_ext_view* v, int n_q_heads, int n_splits) {
+  if (!ext_view_ok(v, n_q_heads) || n_splits < 0 || n_splits > 4096) return 0;
+  const int parts = ext_decode_parts(*v, n_splits);
+  const int M = v->v_qjl ? v->qjl_m : 0;
+  return (size_t)v->batch * n_q_heads * parts * (v->head_dim + 2 + M) * sizeof(float);
+}
+
+kvq_status kvq_decode_attention_ext(const kvq_ext_view* v, const void* q, int dtype,
+                                    int n_q_heads, float sm_scale, float* out, int n_splits,
+                                    void* workspace, size_t ws_bytes, void* stream) {
+  if (!ext_view_ok(v, n_q_heads) || !q || !out || !workspace) return KVQ_E_ARG;
+  if (dtype != KVQ_F16 && dtype != KVQ_F32) return KVQ_E_ARG;
+  if (n_splits < 0 || n_splits > 4096) return KVQ_E_ARG;
+  if (!aligned(q, dtype == KVQ_F32 ? 4 : 2) || !aligned(out, 4) || !aligned(workspace, 4))
+    return KVQ_E_ARG;
+  if (!(sm_scale > 0.0f) || !__builtin_isfinite(sm_scale)) return KVQ_E_ARG;
+  if (ws_bytes < kvq_decode_ext_workspace_bytes(v, n_q_heads, n_splits)) return KVQ_E_ARG;
+  if ((int64_t)v->batch * n_q_heads > 0x7FFFFFFF || v->batch > 65535) return KVQ_E_UNSUPPORTED;
+  ExtLut lk{}, lv{};
+  if (v->k_nuq && !make_lut(v->k_lut, v->k_bits, &lk)) return KVQ_E_ARG;
+  if (v->v_nuq && !make_lut(v->v_lut, v->v_bits, &lv)) return KVQ_E_ARG;
+  if (ext_decode_lds(*v, n_q_heads) > 160 * 1024) return KVQ_E_UNSUPPORTED;
+  const int parts = ext_decode_parts(*v, n_splits);
+  return hip_status(launch_decode_ext(*v, lk, lv, q, dtype == KVQ_F16, n_q_heads, sm_scale,
+                                      (float*)workspace, parts, out, (hipStream_t)stream));
+}
+
 kvq_status kvq_poll_error(const uint32_t* err_flag, void* stream) {
   if (!err_flag || !aligned(err_flag, 4)) return KVQ_E_ARG;
   if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return KVQ_E_HIP;

@@ -180,6 +180,33 @@ hipError_t launch_decode_rope(const kvq_kv_view& v, const void* q, int f16, int 
                               int n_parts, hipStream_t s);
 hipError_t launch_merge(const float* partials, int B, int Hq, int D,
                         int n_parts, float* out, hipStream_t s);
+// Codebook of the non-uniform datatype as kernel arguments: levels
+// (ascending fp16 numbers including 0), the midpoints between neighbours
+// (exact in float32) and the largest level magnitude.
+struct ExtLut {
+  float lvl[16];
+  float mid[15];
+  float absmax;
+  int n;
+};
+hipError_t launch_quantize_nuq_k(const uint16_t* k, int64_t n_mats, int64_t n_tok, int d,
+                                 int bits, int G, const ExtLut& L, int n_out, uint32_t* codes,
+                                 float* scales, uint32_t* outl, uint32_t* err, hipStream_t s);
+hipError_t launch_quantize_nuq_v(const uint16_t* v, int64_t n_mats, int64_t n_tok, int d,
+                                 int bits, int Gv, const ExtLut& L, int n_out, uint32_t* codes,
+                                 float* scales, uint32_t* outl, uint32_t* err, hipStream_t s);
+hipError_t launch_quantize_v_qjl(const void* v, int f16, int64_t n_mats, int64_t n_tok, int d,
+                                 int bits, int Gv, const float* S, int m, uint32_t* codes,
+                                 float* scales, uint32_t* sketch, float* rnorm, uint32_t* err,
+                                 hipStream_t s);
+size_t ext_decode_lds(const kvq_ext_view& v, int Hq);
+int ext_decode_parts(const kvq_ext_view& v, int n_splits);
+// Decode over an extended view: partials [B][Hq][n_parts][D + 2 + M], then
+// the merge (with the sketch term and the inverse rotation) into out.
+hipError_t launch_decode_ext(const kvq_ext_view& v, const ExtLut& lk, const ExtLut& lv,
+                             const void* q, int f16, int Hq, float sm_scale, float* partials,
+                             int n_parts, float* out, hipStream_t s);
+
 // kvq_decode_attention with the partials in `workspace` (api.cpp); the
 // scratch-backed entry point calls it too.
 kvq_status decode_attention_impl(const kvq_kv_view* v, const void* q, int dtype, int n_q_heads,

@@ -29,6 +29,8 @@ EXPORTED = [
     "kvq_export", "kvq_decode_workspace_bytes", "kvq_decode_attention",
     "kvq_poll_error", "kvq_strerror", "kvq_fill_u32", "kvq_synth_normal_f16", "kvq_stream_read",
     "kvq_hadamard", "kvq_decode_attention_rope", "kvq_decode_attention_noalloc",
+    "kvq_quantize_nuq_k", "kvq_quantize_nuq_v", "kvq_quantize_v_qjl",
+    "kvq_decode_ext_workspace_bytes", "kvq_decode_attention_ext",
 ]
 
 _c_i32, _c_i64, _c_u64, _c_p, _c_f = (ctypes.c_int32, ctypes.c_int64,
@@ -67,6 +69,28 @@ class KvView(ctypes.Structure):
                 ("v_codes", _c_p), ("v_codes_stride", _c_i64),
                 ("v_scales", _c_p), ("v_scales_stride", _c_i64),
                 ("err_flag", _c_p)]
+
+
+class ExtView(ctypes.Structure):
+    _fields_ = [("batch", _c_i32), ("kv_heads", _c_i32), ("head_dim", _c_i32),
+                ("reserved0", _c_i32), ("n_tok", _c_i64),
+                ("k_bits", _c_i32), ("group_tok", _c_i32), ("k_nuq", _c_i32),
+                ("k_n_out", _c_i32),
+                ("k_codes", _c_p), ("k_codes_stride", _c_i64),
+                ("k_scales", _c_p), ("k_scales_stride", _c_i64),
+                ("k_outliers", _c_p), ("k_outliers_stride", _c_i64),
+                ("k_lut", _c_f * 16),
+                ("v_bits", _c_i32), ("group_ch", _c_i32), ("v_nuq", _c_i32),
+                ("v_n_out", _c_i32),
+                ("v_codes", _c_p), ("v_codes_stride", _c_i64),
+                ("v_scales", _c_p), ("v_scales_stride", _c_i64),
+                ("v_outliers", _c_p), ("v_outliers_stride", _c_i64),
+                ("v_lut", _c_f * 16),
+                ("v_qjl", _c_i32), ("qjl_m", _c_i32), ("v_rotated", _c_i32),
+                ("reserved1", _c_i32),
+                ("v_sketch", _c_p), ("v_sketch_stride", _c_i64),
+                ("v_rnorm", _c_p), ("v_rnorm_stride", _c_i64),
+                ("jl", _c_p)]
 
 
 class ExportBufs(ctypes.Structure):
@@ -120,6 +144,20 @@ def lib():
         "kvq_decode_attention": (_c_i32, [
             ctypes.POINTER(KvView), _c_p, _c_i32, _c_i32, _c_f, _c_p, _c_i32,
             _c_i32, _c_p, ctypes.c_size_t, _c_p]),
+        "kvq_quantize_nuq_k": (_c_i32, [_c_p, _c_i64, _c_i64, _c_i32, _c_i32,
+                                        _c_i32, _c_p, _c_i32, _c_p, _c_p, _c_p,
+                                        _c_p, _c_p]),
+        "kvq_quantize_nuq_v": (_c_i32, [_c_p, _c_i64, _c_i64, _c_i32, _c_i32,
+                                        _c_i32, _c_p, _c_i32, _c_p, _c_p, _c_p,
+                                        _c_p, _c_p]),
+        "kvq_quantize_v_qjl": (_c_i32, [_c_p, _c_i32, _c_i64, _c_i64, _c_i32,
+                                        _c_i32, _c_i32, _c_p, _c_i32, _c_p, _c_p,
+                                        _c_p, _c_p, _c_p, _c_p]),
+        "kvq_decode_ext_workspace_bytes": (ctypes.c_size_t, [
+            ctypes.POINTER(ExtView), _c_i32, _c_i32]),
+        "kvq_decode_attention_ext": (_c_i32, [
+            ctypes.POINTER(ExtView), _c_p, _c_i32, _c_i32, _c_f, _c_p, _c_i32,
+            _c_p, ctypes.c_size_t, _c_p]),
         "kvq_decode_attention_noalloc": (_c_i32, [
             ctypes.POINTER(KvView), _c_p, _c_i32, _c_i32, _c_f, _c_p, _c_i32,
             _c_i32, _c_p]),
@@ -530,3 +568,152 @@ def stream_view(view, b, kvh):
         if p:
             setattr(v, name, p + s * getattr(view, stride) * size)
     return v
+
+
+# --------------------------------------------------------------------------
+# extended formats: codebook datatype with dense-and-sparse outliers, value
+# residual sketch, and their decode
+# --------------------------------------------------------------------------
+
+def _host_lut(lut, bits):
+    import numpy as np
+    a = np.ascontiguousarray(np.asarray(lut, dtype=np.float32))
+    if a.shape != (1 << bits,):
+        raise KvqError(KVQ_E_ARG, "codebook must hold 2**bits levels")
+    return a, a.ctypes.data_as(ctypes.c_void_p)
+
+
+def kvq_quantize_nuq_k(k, bits, group_tok, lut, n_out, err=None):
+    """k: [n_mats][n_tok][d] float16 -> (codes int32 [n_mats][n_tok][words],
+    scales f32 [n_mats][ng][d], outliers int32 [n_mats][ng][d][n_out], err)."""
+    _need_cuda(k)
+    if k.dtype != torch.float16 or k.dim() != 3:
+        raise KvqError(KVQ_E_ARG, "kvq_quantize_nuq_k: k must be float16 [n_mats][n_tok][d]")
+    n_mats, n_tok, d = k.shape
+    ng = (n_tok + group_tok - 1) // group_tok if group_tok > 0 else 0
+    codes = torch.empty((n_mats, n_tok, max(kvq_words(d, bits), 0)),
+                        dtype=torch.int32, device=k.device)
+    scales = torch.empty((n_mats, ng, d), dtype=torch.float32, device=k.device)
+    outl = torch.empty((n_mats, ng, d, max(n_out, 0)), dtype=torch.int32, device=k.device)
+    if err is None:
+        err = torch.zeros(1, dtype=torch.int32, device=k.device)
+    keep, lp = _host_lut(lut, bits)
+    _check(lib().kvq_quantize_nuq_k(_ptr(k), n_mats, n_tok, d, bits, group_tok, lp,
+                                    n_out, _ptr(codes), _ptr(scales),
+                                    _ptr(outl) if outl.numel() else None,
+                                    _ptr(err), _stream()), "kvq_quantize_nuq_k")
+    return codes, scales, outl, err
+
+
+def kvq_quantize_nuq_v(v, bits, group_ch, lut, n_out, err=None):
+    """v: [n_mats][n_tok][d] float16 -> (codes, scales [..][d/Gv],
+    outliers int32 [n_mats][n_tok][d/Gv][n_out], err)."""
+    _need_cuda(v)
+    if v.dtype != torch.float16 or v.dim() != 3:
+        raise KvqError(KVQ_E_ARG, "kvq_quantize_nuq_v: v must be float16 [n_mats][n_tok][d]")
+    n_mats, n_tok, d = v.shape
+    ng = d // group_ch if group_ch > 0 else 0
+    codes = torch.empty((n_mats, n_tok, max(kvq_words(d, bits), 0)),
+                        dtype=torch.int32, device=v.device)
+    scales = torch.empty((n_mats, n_tok, ng), dtype=torch.float32, device=v.device)
+    outl = torch.empty((n_mats, n_tok, ng, max(n_out, 0)), dtype=torch.int32, device=v.device)
+    if err is None:
+        err = torch.zeros(1, dtype=torch.int32, device=v.device)
+    keep, lp = _host_lut(lut, bits)
+    _check(lib().kvq_quantize_nuq_v(_ptr(v), n_mats, n_tok, d, bits, group_ch, lp,
+                                    n_out, _ptr(codes), _ptr(scales),
+                                    _ptr(outl) if outl.numel() else None,
+                                    _ptr(err), _stream()), "kvq_quantize_nuq_v")
+    return codes, scales, outl, err
+
+
+def kvq_quantize_v_qjl(v, bits, group_ch, jl, err=None):
+    """v: [n_mats][n_tok][d] f16/f32 (already rotated), jl [m][d] f32 ->
+    (codes, scales, sketch int32 [n_mats][n_tok][m/32], rnorm f32
+    [n_mats][n_tok], err)."""
+    _need_cuda(v, jl)
+    if v.dim() != 3 or jl.dim() != 2 or jl.dtype != torch.float32 or \
+            jl.shape[1] != v.shape[2]:
+        raise KvqError(KVQ_E_ARG, "kvq_quantize_v_qjl: v [n_mats][n_tok][d], jl [m][d] f32")
+    n_mats, n_tok, d = v.shape
+    m = jl.shape[0]
+    ng = d // group_ch if group_ch > 0 else 0
+    codes = torch.empty((n_mats, n_tok, max(kvq_words(d, bits), 0)),
+                        dtype=torch.int32, device=v.device)
+    scales = torch.empty((n_mats, n_tok, ng), dtype=torch.float32, device=v.device)
+    sketch = torch.empty((n_mats, n_tok, max(m // 32, 0)), dtype=torch.int32, device=v.device)
+    rnorm = torch.empty((n_mats, n_tok), dtype=torch.float32, device=v.device)
+    if err is None:
+        err = torch.zeros(1, dtype=torch.int32, device=v.device)
+    _check(lib().kvq_quantize_v_qjl(_ptr(v), _dtype(v), n_mats, n_tok, d, bits, group_ch,
+                                    _ptr(jl), m, _ptr(codes), _ptr(scales), _ptr(sketch),
+                                    _ptr(rnorm), _ptr(err), _stream()), "kvq_quantize_v_qjl")
+    return codes, scales, sketch, rnorm, err
+
+
+def ext_view(B, Hkv, D, n_tok, keys, values, k_bits, v_bits, G, Gv, k_lut=None,
+             v_lut=None, sketch=None, rnorm=None, jl=None, v_rotated=False):
+    """A kvq_ext_view over quantizer outputs ([B*Hkv][...] arrays).
+
+    keys:   (codes, scales) symmetric, or (codes, scales, outliers) with
+            k_lut for the codebook datatype;
+    values: (codes, scales) or (codes, scales, outliers) with v_lut;
+    sketch, rnorm, jl: the residual sketch of the values (optional)."""
+    v = ExtView()
+    v.batch, v.kv_heads, v.head_dim, v.n_tok = B, Hkv, D, n_tok
+    v.k_bits, v.group_tok, v.v_bits, v.group_ch = k_bits, G, v_bits, Gv
+    kc, ks = keys[0], keys[1]
+    v.k_codes, v.k_codes_stride = kc.data_ptr(), kc[0].numel()
+    v.k_scales, v.k_scales_stride = ks.data_ptr(), ks[0].numel()
+    if k_lut is not None:
+        v.k_nuq = 1
+        v.k_lut[:1 << k_bits] = [float(x) for x in k_lut]
+        if len(keys) > 2 and keys[2].numel():
+            v.k_n_out = keys[2].shape[-1]
+            v.k_outliers, v.k_outliers_stride = keys[2].data_ptr(), keys[2][0].numel()
+    vc, vs = values[0], values[1]
+    v.v_codes, v.v_codes_stride = vc.data_ptr(), vc[0].numel()
+    v.v_scales, v.v_scales_stride = vs.data_ptr(), vs[0].numel()
+    if v_lut is not None:
+        v.v_nuq = 1
+        v.v_lut[:1 << v_bits] = [float(x) for x in v_lut]
+        if len(values) > 2 and values[2].numel():
+            v.v_n_out = values[2].shape[-1]
+            v.v_outliers, v.v_outliers_stride = values[2].data_ptr(), values[2][0].numel()
+    if sketch is not None:
+        v.v_qjl, v.qjl_m = 1, jl.shape[0]
+        v.v_sketch, v.v_sketch_stride = sketch.data_ptr(), sketch[0].numel()
+        v.v_rnorm, v.v_rnorm_stride = rnorm.data_ptr(), rnorm[0].numel()
+        v.jl = jl.data_ptr()
+    v.v_rotated = int(bool(v_rotated))
+    return v
+
+
+def kvq_decode_ext_workspace_bytes(view, n_q_heads, n_splits=0):
+    return lib().kvq_decode_ext_workspace_bytes(ctypes.byref(view), n_q_heads, n_splits)
+
+
+def kvq_decode_attention_ext(view, q, sm_scale=None, n_splits=0, workspace=None, out=None):
+    """q: [B][Hq][D] f16/f32 -> out [B][Hq][D] float32."""
+    _need_cuda(q)
+    if q.dim() != 3 or q.shape[0] != view.batch or q.shape[2] != view.head_dim:
+        raise KvqError(KVQ_E_ARG, "kvq_decode_attention_ext: q must be [B][Hq][D] of the view")
+    B, hq, D = q.shape
+    if sm_scale is None:
+        sm_scale = 1.0 / D ** 0.5
+    ws_bytes = kvq_decode_ext_workspace_bytes(view, hq, n_splits)
+    if ws_bytes == 0:
+        raise KvqError(KVQ_E_ARG, "kvq_decode_ext_workspace_bytes")
+    if workspace is None:
+        workspace = torch.empty(ws_bytes, dtype=torch.uint8, device=q.device)
+    _need_cuda(workspace)
+    _need_bytes(workspace, ws_bytes, "kvq_decode_attention_ext", "workspace")
+    if out is None:
+        out = torch.empty((B, hq, D), dtype=torch.float32, device=q.device)
+    _need_cuda(out)
+    _need_shape(out, (B, hq, D), "kvq_decode_attention_ext", "out")
+    _check(lib().kvq_decode_attention_ext(
+        ctypes.byref(view), _ptr(q), _dtype(q), hq, sm_scale, _ptr(out), n_splits,
+        _ptr(workspace), workspace.numel() * workspace.element_size(), _stream()),
+        "kvq_decode_attention_ext")
+    return out

@@ -156,3 +156,35 @@ def test_rope_decode_argument_errors():
     empty = kvq.KvView()
     empty.batch, empty.kv_heads, empty.head_dim = 1, 1, 32
     assert call(rope(), view=empty) == kvq.KVQ_E_ARG     # no tokens
+
+
+def test_struct_layouts_match_the_header(tmp_path):
+    """The ctypes mirrors of the C structs have the header's size and field
+    offsets (a small C program built with gcc prints them)."""
+    import shutil
+    import subprocess
+    if not shutil.which("gcc"):
+        pytest.skip("gcc not available")
+    structs = {"kvq_cache_cfg": kvq.CacheCfg, "kvq_kv_view": kvq.KvView,
+               "kvq_ext_view": kvq.ExtView, "kvq_rope": kvq.Rope,
+               "kvq_export_bufs": kvq.ExportBufs}
+    lines = ['#include <stdio.h>', '#include <stddef.h>', f'#include "{HEADER}"',
+             "int main(void) {"]
+    for cname, py in structs.items():
+        lines.append(f'printf("{cname} size %zu\\n", sizeof({cname}));')
+        for fname, _ in py._fields_:
+            lines.append(f'printf("{cname} {fname} %zu\\n", offsetof({cname}, {fname}));')
+    lines.append("return 0; }")
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines))
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-o", str(exe), str(src)], check=True)
+    out = subprocess.run([str(exe)], check=True, capture_output=True, text=True).stdout
+    got = {}
+    for line in out.splitlines():
+        c, f, n = line.split()
+        got[(c, f)] = int(n)
+    for cname, py in structs.items():
+        assert got[(cname, "size")] == ctypes.sizeof(py), cname
+        for fname, _ in py._fields_:
+            assert got[(cname, fname)] == getattr(py, fname).offset, (cname, fname)

@@ -1,0 +1,249 @@
+"""GPU parity of the extended formats through the C ABI against the oracle.
+
+Non-uniform codebook datatype with per-vector dense-and-sparse outliers
+("KVQuant: Towards 10 Million Context Length LLM Inference with KV Cache
+Quantization", summary, "Approach", table "Measured effects reported in the
+paper") and the value-side 1-bit residual sketch of the KQV scheme
+("Statistical Inference and Quality Measures of KV Cache Quantisations
+Inspired by TurboQuant", "Quantization Schemes").  Codes, scales and
+outliers are bit-exact; sketch signs are bit-exact except where the float64
+dot product is within rounding of zero; attention within 2e-3 of the
+float64 oracle on the same reconstructions.
+"""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from oracle import attention, codec, nuq, qjl, rotation
+from quantized_decode_attention_02_amd import kvq
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+TOL = 2e-3
+
+
+def say(*a):
+    print(*a, flush=True)
+
+
+def u32(t):
+    return t.cpu().numpy().view(np.uint32)
+
+
+def inputs(seed, n_mats, n, d, spikes=True):
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((n_mats, n, d)).astype(np.float32)
+    x *= rng.uniform(0.05, 4, (n_mats, 1, d)).astype(np.float32)
+    if spikes:
+        m = rng.random(x.shape) < 0.01
+        x[m] *= rng.uniform(5, 40, int(m.sum())).astype(np.float32)
+    x = x.astype(np.float16)
+    x[0, 3, :] = 0                                   # a zero token row
+    x[0, :, 1] = 0                                   # a zero channel
+    if n > 20 and d > 8:
+        x[-1, 10, 5] = -x[-1, 11, 5]                 # equal magnitudes
+        x[-1, 12, :8] = np.float16(2.0 ** -20)       # fp16 subnormals
+    return x
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+@pytest.mark.parametrize("n_out", [0, 1, 3])
+@pytest.mark.parametrize("d,G,n", [(128, 128, 300), (64, 32, 97), (40, 7, 30)])
+def test_quantize_nuq_k_bit_exact(bits, n_out, d, G, n):
+    say("nuq_k", bits, n_out, d, G, n)
+    lut = synth.nuq_codebook(bits)
+    x = inputs(bits * 10 + n_out + d, 2, n, d)
+    codes, scales, outl, err = kvq.kvq_quantize_nuq_k(torch.from_numpy(x).to(DEV),
+                                                      bits, G, lut, n_out)
+    assert kvq.kvq_poll_error(err) == kvq.KVQ_OK
+    for m in range(2):
+        c, s, p, v = nuq.quantize_k(x[m], lut, G, n_out)
+        assert np.array_equal(u32(codes[m]), nuq.pack_codes(c, bits))
+        assert np.array_equal(scales[m].cpu().numpy(), s)
+        if n_out:
+            assert np.array_equal(u32(outl[m]), nuq.pack_outliers(p, v))
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+@pytest.mark.parametrize("n_out", [0, 1, 2])
+@pytest.mark.parametrize("d,Gv,n", [(128, 128, 100), (128, 32, 65), (48, 16, 33)])
+def test_quantize_nuq_v_bit_exact(bits, n_out, d, Gv, n):
+    say("nuq_v", bits, n_out, d, Gv, n)
+    lut = synth.nuq_codebook(bits)
+    x = inputs(bits * 7 + n_out + d, 2, n, d)
+    codes, scales, outl, err = kvq.kvq_quantize_nuq_v(torch.from_numpy(x).to(DEV),
+                                                      bits, Gv, lut, n_out)
+    assert kvq.kvq_poll_error(err) == kvq.KVQ_OK
+    for m in range(2):
+        c, s, p, v = nuq.quantize_v(x[m], lut, Gv, n_out)
+        assert np.array_equal(u32(codes[m]), nuq.pack_codes(c, bits))
+        assert np.array_equal(scales[m].cpu().numpy(), s)
+        if n_out:
+            assert np.array_equal(u32(outl[m]), nuq.pack_outliers(p, v))
+
+
+def test_nuq_rejects_bad_codebooks_and_nonfinite():
+    x = torch.ones((1, 8, 16), dtype=torch.float16, device=DEV)
+    for lut in ([-1.0, -0.5, 0.5, 1.0], [-1.0, 0.0, 0.1, 1.0], [1.0, 0.0, -0.5, -1.0]):
+        with pytest.raises(kvq.KvqError) as e:
+            kvq.kvq_quantize_nuq_v(x, 2, 16, np.array(lut, np.float32), 1)
+        assert e.value.status == kvq.KVQ_E_ARG
+    x[0, 2, 3] = float("inf")
+    _, _, _, err = kvq.kvq_quantize_nuq_k(x, 2, 8, synth.nuq_codebook(2), 1)
+    assert kvq.kvq_poll_error(err) == kvq.KVQ_E_NONFINITE
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4])
+@pytest.mark.parametrize("dtype", [np.float16, np.float32])
+def test_quantize_v_qjl(bits, dtype):
+    say("qjl", bits, dtype.__name__)
+    d, m, n, Gv = 128, 128, 200, 32
+    v = inputs(bits, 2, n, d, spikes=False)
+    vr = np.stack([rotation.wht(v[i]) for i in range(2)])
+    if dtype == np.float16:
+        vr = vr.astype(np.float16)
+    S = synth.jl_matrix(5, m, d)
+    codes, scales, sketch, rnorm, err = kvq.kvq_quantize_v_qjl(
+        torch.from_numpy(vr).to(DEV), bits, Gv, torch.from_numpy(S).to(DEV))
+    assert kvq.kvq_poll_error(err) == kvq.KVQ_OK
+    for i in range(2):
+        c, s, b, g, r = qjl.quantize_v(vr[i], bits, Gv, S)
+        assert np.array_equal(u32(codes[i]), codec.pack_rows(c, bits))
+        assert np.array_equal(scales[i].cpu().numpy(), s)
+        gg = rnorm[i].cpu().numpy()
+        assert np.all(np.abs(gg.astype(np.float64) - g) <= np.abs(g) * 2.0 ** -23)
+        # signs: equal wherever the float64 dot product is clear of rounding
+        got = u32(sketch[i])
+        want = qjl.pack_signs(b)
+        dots = r.astype(np.float64) @ S.astype(np.float64).T
+        mag = np.abs(r.astype(np.float64)) @ np.abs(S.astype(np.float64)).T
+        clear = (np.abs(dots) > d * 2.0 ** -50 * mag) | (mag == 0)   # 0 rows: +1 both
+        gb = (got[:, :, None] >> np.arange(32, dtype=np.uint32)) & 1
+        wb = (want[:, :, None] >> np.arange(32, dtype=np.uint32)) & 1
+        gb, wb = gb.reshape(n, m), wb.reshape(n, m)
+        assert np.array_equal(gb[clear], wb[clear])
+        assert np.mean(~clear) < 1e-3
+
+
+def oracle_ext(q, ks, vs, Hkv, vrot=False):
+    """Attention of each batch element over per-stream K_hat, V_hat lists."""
+    B, Hq, D = q.shape
+    out = []
+    for b in range(B):
+        kh = np.stack([ks[b * Hkv + h] for h in range(Hkv)])
+        vh = np.stack([vs[b * Hkv + h] for h in range(Hkv)])
+        o = attention.attention(q[b].astype(np.float64), kh, vh)
+        out.append(qjl.unrotate(o) if vrot else o)
+    return np.stack(out)
+
+
+# (B, Hq, Hkv, N, D, k: (bits, G, n_out) or ("sym", bits, G), v likewise or
+# ("qjl", bits, Gv, m))
+EXT_CASES = {
+    "nuq3_1pct_g4": (1, 8, 2, 1000, 128, ("nuq", 3, 128, 1), ("nuq", 3, 128, 1)),
+    "nuq2_mha_small_groups": (2, 2, 2, 333, 64, ("nuq", 2, 32, 2), ("nuq", 2, 16, 1)),
+    "nuq4_g5_no_outliers": (1, 10, 2, 700, 128, ("nuq", 4, 64, 0), ("nuq", 4, 64, 0)),
+    "sym_k4_qjl_v3": (1, 8, 2, 900, 128, ("sym", 4, 128), ("qjl", 3, 32, 128)),
+    "sym_k4_qjl_v2_m64": (2, 4, 2, 500, 64, ("sym", 4, 64), ("qjl", 2, 64, 64)),
+    "nuq_k_qjl_v": (1, 4, 1, 640, 128, ("nuq", 3, 128, 1), ("qjl", 3, 128, 128)),
+}
+
+
+def build_ext(name, seed=7):
+    B, Hq, Hkv, N, D, kspec, vspec = EXT_CASES[name]
+    q, k, v = synth.kv_inputs(seed, B, Hq, Hkv, N, D, outliers="fraction", frac=0.03)
+    kf = np.ascontiguousarray(k.reshape(B * Hkv, N, D))
+    vf = np.ascontiguousarray(v.reshape(B * Hkv, N, D))
+    vrot = vspec[0] == "qjl"
+    if kspec[0] == "nuq":
+        _, kb, G, no = kspec
+        lut_k = synth.nuq_codebook(kb)
+        keys = kvq.kvq_quantize_nuq_k(torch.from_numpy(kf).to(DEV), kb, G, lut_k, no)[:3]
+        kh = []
+        for i in range(B * Hkv):
+            c, s, p, vv = nuq.quantize_k(kf[i], lut_k, G, no)
+            kh.append(nuq.dequant_k(c, s, p, vv, lut_k, G))
+    else:
+        _, kb, G = kspec
+        lut_k = None
+        keys = kvq.kvq_quantize_k(torch.from_numpy(kf).to(DEV), kb, G)[:2]
+        kh = []
+        for i in range(B * Hkv):
+            c, s = codec.quantize_k(kf[i], kb, G)
+            kh.append(codec.dequant(c, codec.expand_k_scales(s, N, G)))
+    sk = rn = S_t = None
+    if vspec[0] == "nuq":
+        _, vb, Gv, no = vspec
+        lut_v = synth.nuq_codebook(vb)
+        values = kvq.kvq_quantize_nuq_v(torch.from_numpy(vf).to(DEV), vb, Gv, lut_v, no)[:3]
+        vh = []
+        for i in range(B * Hkv):
+            c, s, p, vv = nuq.quantize_v(vf[i], lut_v, Gv, no)
+            vh.append(nuq.dequant_v(c, s, p, vv, lut_v, Gv))
+    else:
+        _, vb, Gv, m = vspec
+        lut_v = None
+        S = synth.jl_matrix(seed, m, D)
+        S_t = torch.from_numpy(S).to(DEV)
+        vr = np.stack([rotation.wht(vf[i]) for i in range(B * Hkv)])
+        c_t, s_t, sk, rn, _ = kvq.kvq_quantize_v_qjl(torch.from_numpy(vr).to(DEV), vb, Gv, S_t)
+        values = (c_t, s_t)
+        vh = []
+        for i in range(B * Hkv):
+            c, s, b, g, r = qjl.quantize_v(vr[i], vb, Gv, S)
+            vh.append(qjl.dequant_v(c, s, b, g, S, Gv))
+    view = kvq.ext_view(B, Hkv, D, N, keys, values, kb, vb, G, Gv, k_lut=lut_k, v_lut=lut_v,
+                        sketch=sk, rnorm=rn, jl=S_t, v_rotated=vrot)
+    keep = (keys, values, sk, rn, S_t)
+    ref = oracle_ext(q, kh, vh, Hkv, vrot)
+    return q, view, ref, keep
+
+
+@pytest.mark.parametrize("name", list(EXT_CASES))
+def test_ext_decode_parity(name):
+    say("ext case", name)
+    q, view, ref, keep = build_ext(name)
+    qt = torch.from_numpy(q).to(DEV)
+    for splits in (0, 1, 3, 40):
+        out = kvq.kvq_decode_attention_ext(view, qt, n_splits=splits).cpu().numpy()
+        err = attention.max_row_relative_error(out, ref)
+        say(f"  splits={splits} err={err:.3e}")
+        assert err <= TOL
+    out32 = kvq.kvq_decode_attention_ext(view, qt.float()).cpu().numpy()
+    assert attention.max_row_relative_error(out32, ref) <= TOL
+
+
+def test_ext_decode_query_scale_range():
+    q, view, ref, keep = build_ext("nuq3_1pct_g4")
+    for qmul, sm in ((64.0, 0.02), (2.0 ** -8, 30.0)):
+        qs = (q.astype(np.float32) * qmul).astype(np.float16)
+        out = kvq.kvq_decode_attention_ext(view, torch.from_numpy(qs).to(DEV),
+                                           sm_scale=sm).cpu().numpy()
+        B, Hq, D = q.shape
+        # the oracle recomputed with this query and scale
+        _, _, Hkv, N, _, kspec, vspec = EXT_CASES["nuq3_1pct_g4"]
+        qq, k, v = synth.kv_inputs(7, B, Hq, Hkv, N, D, outliers="fraction", frac=0.03)
+        lut = synth.nuq_codebook(3)
+        kh = [nuq.dequant_k(*nuq.quantize_k(k[0, h], lut, 128, 1), lut, 128) for h in range(Hkv)]
+        vh = [nuq.dequant_v(*nuq.quantize_v(v[0, h], lut, 128, 1), lut, 128) for h in range(Hkv)]
+        r = attention.attention(qs[0].astype(np.float64), np.stack(kh), np.stack(vh), sm_scale=sm)
+        assert attention.max_row_relative_error(out[0], r) <= TOL
+
+
+def test_ext_view_rejections():
+    q, view, ref, keep = build_ext("nuq3_1pct_g4")
+    qt = torch.from_numpy(q).to(DEV)
+    bad = kvq.ExtView.from_buffer_copy(view)
+    bad.k_lut[1] = 0.3                      # not ascending / not an fp16 codebook
+    with pytest.raises(kvq.KvqError):
+        kvq.kvq_decode_attention_ext(bad, qt)
+    bad = kvq.ExtView.from_buffer_copy(view)
+    bad.k_n_out = 17
+    with pytest.raises(kvq.KvqError):
+        kvq.kvq_decode_attention_ext(bad, qt)
+    bad = kvq.ExtView.from_buffer_copy(view)
+    bad.head_dim = 256
+    with pytest.raises(kvq.KvqError):
+        kvq.kvq_decode_attention_ext(bad, torch.zeros((1, 8, 256), dtype=torch.float16,
+                                                      device=DEV))
