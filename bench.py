@@ -43,7 +43,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="1m_32layer",
                     choices=["1m_32layer", "gqa_128k", "gqa_128k_k2v4",
-                             "mixkvq_32k", "7b_layer_4k"])
+                             "mixkvq_32k", "7b_layer_4k",
+                             "kvquant_3bit_1pct_128k", "kqv_4bit_128k"])
     ap.add_argument("--layers", type=int, default=None,
                     help="layers of the 1m_32layer workload (default 32)")
     ap.add_argument("--seed", type=int, default=7)
@@ -270,6 +271,113 @@ def sub_workload(torch, kvq, dev, stream, name, args, flush_buf):
     return rec
 
 
+def ext_workload(torch, kvq, dev, stream, name, args, flush_buf):
+    """A next-row leg on the 128K GQA layer: the codebook datatype with 1%
+    per-vector outliers, or the KQV scheme (rotated keys; rotated values
+    with the 1-bit residual sketch).  Times the quantization of the whole
+    context (the prefill) and the decode call (events, Infinity Cache
+    evicted before each call)."""
+    w = dict(synth.WORKLOADS[name])
+    B, Hq, Hkv, N, D = w["B"], w["Hq"], w["Hkv"], w["N"], w["D"]
+    ikw = {k: w[k] for k in ("outliers", "frac", "fmin", "fmax", "sink_factor") if k in w}
+    qn, kn, vn = synth.kv_inputs(args.seed, B, Hq, Hkv, N, D, **ikw)
+    kt = torch.from_numpy(kn.reshape(B * Hkv, N, D)).to(dev)
+    vt = torch.from_numpy(vn.reshape(B * Hkv, N, D)).to(dev)
+    qt = torch.from_numpy(qn).to(dev)
+    del qn, kn, vn
+    jl = None
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    if w.get("k_nuq"):
+        lk, lv = synth.nuq_codebook(w["k_bits"]), synth.nuq_codebook(w["v_bits"])
+        # one untimed pass loads the quantizers' code
+        kvq.kvq_quantize_nuq_k(kt[:1, :256], w["k_bits"], w["G"], lk, w["n_out"])
+        kvq.kvq_quantize_nuq_v(vt[:1, :256], w["v_bits"], w["Gv"], lv, w["n_out"])
+        torch.cuda.synchronize()
+        e0.record(stream)
+        keys = kvq.kvq_quantize_nuq_k(kt, w["k_bits"], w["G"], lk, w["n_out"])[:3]
+        values = kvq.kvq_quantize_nuq_v(vt, w["v_bits"], w["Gv"], lv, w["n_out"])[:3]
+        e1.record(stream)
+        view = kvq.ext_view(B, Hkv, D, N, keys, values, w["k_bits"], w["v_bits"],
+                            w["G"], w["Gv"], k_lut=lk, v_lut=lv)
+        keep = (keys, values)
+        kernel = "decode_ext_kernel (codebook keys and values, outliers) + merge_ext_kernel"
+    else:
+        jl = torch.from_numpy(synth.jl_matrix(args.seed, w["qjl_m"], D)).to(dev)
+        kvq.kvq_quantize_k(kvq.kvq_hadamard(kt[:1, :256].contiguous(), out_dtype=torch.float32),
+                           w["k_bits"], w["G"])
+        kvq.kvq_quantize_v_qjl(kvq.kvq_hadamard(vt[:1, :256].contiguous(),
+                                                out_dtype=torch.float32), w["v_bits"], w["Gv"], jl)
+        torch.cuda.synchronize()
+        e0.record(stream)
+        kr = kvq.kvq_hadamard(kt, out_dtype=torch.float32)
+        keys = kvq.kvq_quantize_k(kr, w["k_bits"], w["G"])[:2]
+        del kr
+        vr = kvq.kvq_hadamard(vt, out_dtype=torch.float32)
+        c, sc, sk, rn, _ = kvq.kvq_quantize_v_qjl(vr, w["v_bits"], w["Gv"], jl)
+        e1.record(stream)
+        del vr
+        values = (c, sc)
+        qt = kvq.kvq_hadamard(qt, out_dtype=torch.float32)
+        view = kvq.ext_view(B, Hkv, D, N, keys, values, w["k_bits"], w["v_bits"],
+                            w["G"], w["Gv"], sketch=sk, rnorm=rn, jl=jl, v_rotated=True)
+        keep = (keys, values, sk, rn, jl)
+        kernel = "decode_ext_kernel (symmetric keys, values with the sketch) + merge_ext_kernel"
+    torch.cuda.synchronize()
+    quant_us = 1000 * e0.elapsed_time(e1)
+    del kt, vt
+    ws = torch.empty(kvq.kvq_decode_ext_workspace_bytes(view, Hq, 0), dtype=torch.uint8,
+                     device=dev)
+    out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
+    calls = []
+    for i in range(3 + 20):
+        evict(flush_buf)
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        kvq.kvq_decode_attention_ext(view, qt, workspace=ws, out=out)
+        b.record(stream)
+        if i >= 3:
+            calls.append((a, b))
+    torch.cuda.synchronize()
+    us = [1000 * a.elapsed_time(b) for a, b in calls]
+    med = float(np.median(us))
+    # bytes of one call: codes, scales, outliers, sketch words and norms,
+    # the query (and, for the sketch, the projection matrix once)
+    streams = B * Hkv
+    kw = 4 * math.ceil(D / (32 // w["k_bits"]))
+    vw = 4 * math.ceil(D / (32 // w["v_bits"]))
+    per = N * (kw + vw) + (N + w["G"] - 1) // w["G"] * D * 4 + N * (D // w["Gv"]) * 4
+    if w.get("k_nuq"):
+        per += (N + w["G"] - 1) // w["G"] * D * w["n_out"] * 4
+        per += N * (D // w["Gv"]) * w["n_out"] * 4
+    else:
+        per += N * (w["qjl_m"] // 8 + 4)
+    nbytes = streams * per + B * Hq * D * 2 + (w.get("qjl_m", 0) * D * 4)
+    g = Hq // Hkv
+    # the method's arithmetic per token and KV head: the dequantization of
+    # K and V (D multiplies each), the scores and the value sums (g D FMA
+    # each), and for the sketch the sign sums (g m adds)
+    fma = streams * N * (2 * D + 2 * g * D + g * w.get("qjl_m", 0))
+    cfg = {k: w[k] for k in w if k not in ("outliers", "fmin", "fmax")}
+    cfg["workload"] = name
+    del keep, ws, out, view
+    torch.cuda.empty_cache()
+    return {"us_per_call": {"mean": round(float(np.mean(us)), 2), "median": round(med, 2),
+                            "p10": round(float(np.percentile(us, 10)), 2),
+                            "p90": round(float(np.percentile(us, 90)), 2), "calls": len(us)},
+            "quantize_context_us": round(quant_us, 1),
+            "bytes_per_call": int(nbytes),
+            "achieved_gbs": round(nbytes / (med * 1e-6) / 1e9, 1),
+            "frac_hbm_peak": round(nbytes / (med * 1e-6) / 1e9 / PEAK_GBS, 4),
+            "roofline": {"bound": "alu", "fma_per_call": int(fma),
+                         "achieved_tflops": round(2 * fma / (med * 1e-6) / 1e12, 2),
+                         "peak_tflops": 78.6,
+                         "frac": round(2 * fma / (med * 1e-6) / 78.6e12, 4)},
+            "kernel": kernel, "config": cfg}
+
+
 def main():
     args = parse()
     if args.gpus != 1:
@@ -287,6 +395,13 @@ def main():
     torch.cuda.set_device(dev)
     stream = torch.cuda.current_stream()
     w = dict(synth.WORKLOADS[args.workload])
+    if args.workload in ("kvquant_3bit_1pct_128k", "kqv_4bit_128k"):
+        # a next-row leg on its own (the default run reports it beside the
+        # headline)
+        flush_buf = torch.zeros(1 << 30, dtype=torch.uint8, device=dev)
+        print(json.dumps({"workload": args.workload, **ext_workload(
+            torch, kvq, dev, stream, args.workload, args, flush_buf)}), flush=True)
+        return
     extra = {}
 
     if args.workload == "1m_32layer":
@@ -555,6 +670,14 @@ def main():
             res["workloads"][name] = sub_workload(torch, kvq, dev, stream, name,
                                                   args, flush_buf)
             print(f"# {name}: {res['workloads'][name]['us_per_call']['median']} "
+                  f"us per call ({time.time() - t0w:.1f}s)", file=sys.stderr,
+                  flush=True)
+        res["next_rows"] = {}
+        for name in ("kvquant_3bit_1pct_128k", "kqv_4bit_128k"):
+            t0w = time.time()
+            res["next_rows"][name] = ext_workload(torch, kvq, dev, stream, name,
+                                                  args, flush_buf)
+            print(f"# {name}: {res['next_rows'][name]['us_per_call']['median']} "
                   f"us per call ({time.time() - t0w:.1f}s)", file=sys.stderr,
                   flush=True)
     if not args.no_cpu_baseline:

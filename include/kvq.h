@@ -455,8 +455,8 @@ size_t kvq_decode_ext_workspace_bytes(const kvq_ext_view* v, int n_q_heads, int 
  * two error paths"), K_hat and V_hat the reconstructions above (the sketch
  * contributes sqrt(pi/2)/m * rnorm * S^T b per token; rotated values are
  * turned back).  q [B][n_q_heads][D] KVQ_F16 or KVQ_F32; out float32.
- * Requires head_dim <= 128, (n_q_heads / kv_heads) * head_dim <= 1024,
- * (n_q_heads / kv_heads) * qjl_m <= 1024, n_splits <= 4096, n_tok >= 1.  */
+ * Requires head_dim 32, 64 or 128, group_tok a multiple of 32, at most 8
+ * query heads per KV head, n_splits <= 4096, n_tok >= 1 (else KVQ_E_ARG). */
 kvq_status kvq_decode_attention_ext(const kvq_ext_view* v, const void* q, int dtype,
                                     int n_q_heads, float sm_scale, float* out, int n_splits,
                                     void* workspace, size_t ws_bytes, void* stream);

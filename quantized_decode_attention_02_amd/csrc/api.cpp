@@ -521,11 +521,13 @@ bool make_lut(const float* lut, int bits, ExtLut* out) {
 
 bool ext_view_ok(const kvq_ext_view* v, int n_q_heads) {
   if (!v) return false;
-  if (v->batch < 1 || v->kv_heads < 1 || v->head_dim < 1 || v->head_dim > 128) return false;
+  if (v->batch < 1 || v->kv_heads < 1) return false;
+  if (v->head_dim != 32 && v->head_dim != 64 && v->head_dim != 128) return false;
   if (v->n_tok < 1 || n_q_heads < 1 || n_q_heads % v->kv_heads) return false;
   const int g = n_q_heads / v->kv_heads;
-  if (g * v->head_dim > 1024) return false;
-  if (v->group_tok < 1 || v->group_ch < 1 || v->head_dim % v->group_ch) return false;
+  if (g > 8) return false;
+  if (v->group_tok < 1 || v->group_tok % 32 || v->group_ch < 1 || v->head_dim % v->group_ch)
+    return false;
   if (!v->k_codes || !v->k_scales || !v->v_codes || !v->v_scales) return false;
   if (v->k_nuq ? (v->k_bits < 2 || v->k_bits > 4) : !bits_ok(v->k_bits)) return false;
   if (v->v_nuq ? (v->v_bits < 2 || v->v_bits > 4) : !bits_ok(v->v_bits)) return false;
@@ -535,7 +537,7 @@ bool ext_view_ok(const kvq_ext_view* v, int n_q_heads) {
   if (v->v_n_out && !v->v_outliers) return false;
   if (v->v_qjl) {
     if (v->qjl_m < 32 || v->qjl_m > 256 || v->qjl_m % 32) return false;
-    if (g * v->qjl_m > 1024 || !v->v_sketch || !v->v_rnorm || !v->jl) return false;
+    if (g * v->qjl_m > 8 * 256 || !v->v_sketch || !v->v_rnorm || !v->jl) return false;
   }
   if (v->v_rotated && (v->head_dim & (v->head_dim - 1))) return false;
   if (!aligned(v->k_codes, 4) || !aligned(v->v_codes, 4) || !aligned(v->k_scales, 4) ||

@@ -303,12 +303,18 @@ quantize_v_qjl_kernel(const T* __restrict__ v, int64_t n_tok, int d, int bits, i
 
 // ---------------------------------------------------------------------------
 // Decode over an extended view: one workgroup per (split, KV head, batch);
-// chunks of kCT tokens; a chunk's keys are dequantized into LDS (codebook
-// or symmetric codes times the channel scale, plus the group's outliers),
-// scored by four lanes per (token, head), then its values the same way into
-// the same LDS rows; the sketch words and norms of the chunk go to LDS for
-// the per-head sign sums.  Partial record per (batch, head, split):
-// m (log2 units), l, o[D], z[M] (M = m of the sketch, 0 without one).
+// splits are whole 64-token chunks.  Thread tid owns channel c = tid % D of
+// the tokens tid / D, tid / D + 256 / D, ... of a chunk for the dequant
+// (the field's word and shift, the channel's scale and the codebook in LDS
+// are fixed per thread or per chunk, so no division runs per element);
+// the chunk's keys go to LDS, the group's outliers are added, four lanes
+// per token score it against every query head (a lane sums every fourth
+// channel: rows padded to D + 4 floats, so the 16 tokens x 4 lanes of a
+// wave hit distinct banks), the online softmax runs a wave per head, then
+// the values the same way, and thread (channel, head set) accumulates the
+// weighted sums; the sketch words and norms of the chunk go to LDS for the
+// per-head sign sums.  Partial record per (batch, head, split): m (log2
+// units), l, o[D], z[M] (M = m of the sketch, 0 without one).
 // ---------------------------------------------------------------------------
 struct ExtArgs {
   kvq_ext_view v;
@@ -318,48 +324,66 @@ struct ExtArgs {
   float* partials;
   int n_parts;
   int rec;            // D + 2 + M
+  int64_t per;        // tokens per split, a multiple of kCT
 };
 
-__device__ inline uint32_t field_of(const uint32_t* row, int c, int bits) {
-  const int pw = fields_per_word(bits);
-  return (row[c / pw] >> ((c % pw) * bits)) & ((1u << bits) - 1u);
-}
+// LDS words of the per-chunk staging areas (codes, scales, sketch words).
+struct ExtStage {
+  int kw, vw, ngv, mw;   // words per key / value row, value groups, sketch words
+};
 
-template <typename QT>
+template <typename QT, int D>
 __global__ void __launch_bounds__(kThreads)
 decode_ext_kernel(ExtArgs a, const QT* __restrict__ q) {
+  constexpr int Dp = D + 4;               // padded LDS row
+  constexpr int TPT = kThreads / D;       // token lanes of the dequant
   extern __shared__ __align__(16) float sm[];
   const kvq_ext_view& v = a.v;
-  const int D = v.head_dim, Dp = D + 1;
   const int g = a.Hq / v.kv_heads;
   const int M = v.v_qjl ? v.qjl_m : 0, MW = M / 32;
-  float* qs = sm;                       // [g][D]
-  float* buf = qs + g * D;              // [kCT][D + 1]
-  float* ps = buf + kCT * Dp;           // [g][kCT]
-  float* st = ps + g * kCT;             // [3][g]: m, l, alpha
-  float* gam = st + 3 * g;              // [kCT]
-  uint32_t* skw = (uint32_t*)(gam + kCT);  // [kCT][MW]
+  const int kb = v.k_bits, vb = v.v_bits;
+  const int kw_row = words_of(D, kb), vw_row = words_of(D, vb);
+  const int ngv = D / v.group_ch;
+  float* lut = sm;                        // [32]: key levels, value levels
+  float* qs = lut + 32;                   // [g][D]
+  float* buf = qs + g * D;                // [kCT][Dp]
+  float* ps = buf + kCT * Dp;             // [g][kCT]
+  float* st = ps + g * kCT;               // [3][g]: m, l, alpha
+  float* gam = st + 3 * g;                // [kCT]
+  float* ksl = gam + kCT;                 // [2][D]: scales of the chunk's key groups
+  float* vsl = ksl + 2 * D;               // [kCT][ngv]
+  uint32_t* skw = (uint32_t*)(vsl + kCT * ngv);  // [kCT][MW]
+  uint32_t* kcw = skw + kCT * MW;         // [kCT][kw_row]
+  uint32_t* vcw = kcw + kCT * kw_row;     // [kCT][vw_row]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int part = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int64_t s = (int64_t)b * v.kv_heads + kvh;
   const int64_t N = v.n_tok;
-  const int64_t per = (N + a.n_parts - 1) / a.n_parts;
-  const int64_t t_lo = min(N, (int64_t)part * per), t_hi = min(N, t_lo + per);
-  const int nk = fields_per_word(v.k_bits), nv = fields_per_word(v.v_bits);
-  const int wk = words_of(D, v.k_bits), wv = words_of(D, v.v_bits);
-  const int koff = v.k_nuq ? 0 : qmax_of(v.k_bits) + 1;
-  const int voff = v.v_nuq ? 0 : qmax_of(v.v_bits) + 1;
-  const int ngv = D / v.group_ch;
-  (void)nk; (void)nv;
+  const int64_t t_lo = min(N, (int64_t)part * a.per), t_hi = min(N, t_lo + a.per);
+  const int G = v.group_tok;
 
+  // per-thread constants of the dequant: channel c of tokens t0 + TPT j
+  const int c = tid % D, t0 = tid / D;
+  const int kword = c / fields_per_word(kb), kshift = (c % fields_per_word(kb)) * kb;
+  const int vword = c / fields_per_word(vb), vshift = (c % fields_per_word(vb)) * vb;
+  const uint32_t kmask = (1u << kb) - 1u, vmask = (1u << vb) - 1u;
+  const int vgrp = c / v.group_ch;
+  const float koff = v.k_nuq ? 0.0f : (float)(qmax_of(kb) + 1);
+  const float voff = v.v_nuq ? 0.0f : (float)(qmax_of(vb) + 1);
+
+  if (tid < 16) {
+    lut[tid] = v.k_nuq ? a.lk.lvl[tid] : 0.0f;
+    lut[16 + tid] = v.v_nuq ? a.lv.lvl[tid] : 0.0f;
+  }
   for (int i = tid; i < g * D; i += kThreads)
     qs[i] = ldx(q, ((int64_t)b * a.Hq + kvh * g) * D + i) * a.qscale;
   if (tid < g) {
     st[tid] = -INFINITY;
     st[g + tid] = 0.0f;
   }
-  // accumulators: output pairs (h, d) and sketch pairs (h, i) of this thread
-  float o[4] = {0.0f, 0.0f, 0.0f, 0.0f}, z[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+  float o[8], z[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) { o[k] = 0.0f; z[k] = 0.0f; }
   __syncthreads();
 
   const uint32_t* kc = v.k_codes + s * v.k_codes_stride;
@@ -371,42 +395,68 @@ decode_ext_kernel(ExtArgs a, const QT* __restrict__ q) {
 
   for (int64_t c0 = t_lo; c0 < t_hi; c0 += kCT) {
     const int n = (int)min((int64_t)kCT, t_hi - c0);
-    // ---- keys of the chunk
-    for (int i = tid; i < n * D; i += kThreads) {
-      const int t = i / D, c = i % D;
-      const int64_t tok = c0 + t;
-      const uint32_t code = field_of(kc + tok * wk, c, v.k_bits);
-      const float sc = ks[(tok / v.group_tok) * D + c];
-      const float lvl = v.k_nuq ? a.lk.lvl[code] : (float)((int)code - koff);
-      buf[t * Dp + c] = lvl * sc;
+    // ---- every load of the chunk at once, into LDS: the code rows (one
+    //      contiguous range each), the key scales of its (at most two)
+    //      groups, the value scales, the sketch words and norms
+    const int64_t g0 = c0 / G;
+    const int r0 = (int)(c0 - g0 * G);            // chunk start within its group
+    const int ng_chunk = (r0 + n > G) ? 2 : 1;
+    for (int i = tid; i < n * kw_row; i += kThreads) kcw[i] = kc[c0 * kw_row + i];
+    for (int i = tid; i < n * vw_row; i += kThreads) vcw[i] = vc[c0 * vw_row + i];
+    for (int i = tid; i < ng_chunk * D; i += kThreads) ksl[i] = ks[g0 * D + i];
+    for (int i = tid; i < n * ngv; i += kThreads) vsl[i] = vs[c0 * ngv + i];
+    if (M) {
+      for (int i = tid; i < n * MW; i += kThreads)
+        skw[i] = v.v_sketch[s * v.v_sketch_stride + c0 * MW + i];
+      for (int t = tid; t < n; t += kThreads) gam[t] = v.v_rnorm[s * v.v_rnorm_stride + c0 + t];
     }
     __syncthreads();
+    // ---- keys of the chunk: level (or centred code) times the channel's
+    //      scale of the token's group
+    for (int t = t0; t < n; t += TPT) {
+      const uint32_t code = (kcw[t * kw_row + kword] >> kshift) & kmask;
+      const float lvl = v.k_nuq ? lut[code] : (float)code - koff;
+      buf[t * Dp + c] = lvl * ksl[(r0 + t >= G ? D : 0) + c];
+    }
     if (ko) {
-      const int64_t g0 = c0 / v.group_tok, g1 = (c0 + n - 1) / v.group_tok;
       const int per_g = D * v.k_n_out;
-      for (int64_t gg = g0; gg <= g1; ++gg) {
+      __syncthreads();
+      for (int gi = 0; gi < ng_chunk; ++gi) {
         for (int i = tid; i < per_g; i += kThreads) {
-          const uint32_t e = ko[gg * per_g + i];
+          const uint32_t e = ko[(g0 + gi) * per_g + i];
           if ((e & 0x7FFFu) == 0) continue;               // +-0: nothing to add
-          const int64_t tok = gg * v.group_tok + (e >> 16);
+          const int64_t tok = (g0 + gi) * G + (e >> 16);
           if (tok < c0 || tok >= c0 + n) continue;
-          const int c = i / v.k_n_out;
-          buf[(tok - c0) * Dp + c] += h2f((uint16_t)(e & 0xFFFFu));
+          buf[(tok - c0) * Dp + i / v.k_n_out] += h2f((uint16_t)(e & 0xFFFFu));
         }
       }
-      __syncthreads();
     }
-    // ---- scores: four lanes per (token, head)
-    for (int i0 = 0; i0 < n * g * 4; i0 += kThreads) {
-      const int i = i0 + tid;
-      const int it = i >> 2, qd = i & 3;
-      const int t = it % n, h = it / n;
-      float acc = 0.0f;
-      if (i < n * g * 4)
-        for (int c = qd; c < D; c += 4) acc = __builtin_fmaf(qs[h * D + c], buf[t * Dp + c], acc);
-      acc += __shfl_xor(acc, 1);
-      acc += __shfl_xor(acc, 2);
-      if (i < n * g * 4 && qd == 0) ps[h * kCT + t] = acc;
+    __syncthreads();
+    // ---- scores: lane (token tid / 4, quarter tid % 4) sums channels
+    //      quarter, quarter + 4, ... for every head
+    {
+      const int t = tid >> 2, qd = tid & 3;
+      float acc[8];
+#pragma unroll
+      for (int h = 0; h < 8; ++h) acc[h] = 0.0f;
+      if (t < n) {
+#pragma unroll 4
+        for (int j = qd; j < D; j += 4) {
+          const float kv = buf[t * Dp + j];
+#pragma unroll
+          for (int h = 0; h < 8; ++h)
+            if (h < g) acc[h] = __builtin_fmaf(qs[h * D + j], kv, acc[h]);
+        }
+      }
+#pragma unroll
+      for (int h = 0; h < 8; ++h) {
+        if (h < g) {
+          float x = acc[h];
+          x += __shfl_xor(x, 1);
+          x += __shfl_xor(x, 2);
+          if (qd == 0 && t < n) ps[h * kCT + t] = x;
+        }
+      }
     }
     __syncthreads();
     // ---- online softmax: a wave per head (lane = token)
@@ -429,53 +479,48 @@ decode_ext_kernel(ExtArgs a, const QT* __restrict__ q) {
         st[2 * g + h] = alpha;
       }
     }
-    __syncthreads();
-    // ---- values of the chunk (into the same rows), sketch words and norms
-    for (int i = tid; i < n * D; i += kThreads) {
-      const int t = i / D, c = i % D;
-      const int64_t tok = c0 + t;
-      const uint32_t code = field_of(vc + tok * wv, c, v.v_bits);
-      const float sc = vs[tok * ngv + c / v.group_ch];
-      const float lvl = v.v_nuq ? a.lv.lvl[code] : (float)((int)code - voff);
-      buf[t * Dp + c] = lvl * sc;
+    // ---- values of the chunk (into the key rows: the scores are done)
+    for (int t = t0; t < n; t += TPT) {
+      const uint32_t code = (vcw[t * vw_row + vword] >> vshift) & vmask;
+      const float lvl = v.v_nuq ? lut[16 + code] : (float)code - voff;
+      buf[t * Dp + c] = lvl * vsl[t * ngv + vgrp];
     }
-    if (M) {
-      for (int i = tid; i < n * MW; i += kThreads) {
-        const int t = i / MW, w = i % MW;
-        skw[i] = v.v_sketch[s * v.v_sketch_stride + (c0 + t) * MW + w];
-      }
-      for (int t = tid; t < n; t += kThreads) gam[t] = v.v_rnorm[s * v.v_rnorm_stride + c0 + t];
-    }
-    __syncthreads();
     if (vo) {
       const int per_t = ngv * v.v_n_out;
+      __syncthreads();
       for (int i = tid; i < n * per_t; i += kThreads) {
-        const int t = i / per_t, r = i % per_t;
+        const int t = i / per_t, r = i - t * per_t;
         const uint32_t e = vo[(c0 + t) * per_t + r];
         if ((e & 0x7FFFu) == 0) continue;
-        const int c = (r / v.v_n_out) * v.group_ch + (int)(e >> 16);
-        buf[t * Dp + c] += h2f((uint16_t)(e & 0xFFFFu));
+        const int cc = (r / v.v_n_out) * v.group_ch + (int)(e >> 16);
+        buf[t * Dp + cc] += h2f((uint16_t)(e & 0xFFFFu));
       }
-      __syncthreads();
     }
-    // ---- weighted sums
+    __syncthreads();
+    // ---- weighted sums: channel c of heads t0, t0 + TPT, ...
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      const int i = tid + k * kThreads;
-      if (i < g * D) {
-        const int h = i / D, c = i % D;
+    for (int k = 0; k < 8; ++k) {
+      const int h = t0 + k * TPT;
+      if (h < g) {
         float acc = o[k] * st[2 * g + h];
+#pragma unroll 8
         for (int t = 0; t < n; ++t) acc = __builtin_fmaf(ps[h * kCT + t], buf[t * Dp + c], acc);
         o[k] = acc;
       }
-      if (i < g * M) {
-        const int h = i / M, j = i % M;
-        float acc = z[k] * st[2 * g + h];
-        for (int t = 0; t < n; ++t) {
-          const float w = ps[h * kCT + t] * gam[t];
-          acc += ((skw[t * MW + (j >> 5)] >> (j & 31)) & 1u) ? w : -w;
+    }
+    if (M) {
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int i = tid + k * kThreads;
+        if (i < g * M) {
+          const int h = i / M, j = i - h * M;
+          float acc = z[k] * st[2 * g + h];
+          for (int t = 0; t < n; ++t) {
+            const float w = ps[h * kCT + t] * gam[t];
+            acc += ((skw[t * MW + (j >> 5)] >> (j & 31)) & 1u) ? w : -w;
+          }
+          z[k] = acc;
         }
-        z[k] = acc;
       }
     }
     __syncthreads();
@@ -487,10 +532,11 @@ decode_ext_kernel(ExtArgs a, const QT* __restrict__ q) {
     out[tid * hstride + 1] = st[g + tid];
   }
 #pragma unroll
-  for (int k = 0; k < 4; ++k) {
+  for (int k = 0; k < 8; ++k) {
+    const int h = t0 + k * TPT;
+    if (h < g) out[h * hstride + 2 + c] = o[k];
     const int i = tid + k * kThreads;
-    if (i < g * D) out[(i / D) * hstride + 2 + i % D] = o[k];
-    if (i < g * M) out[(i / M) * hstride + 2 + D + i % M] = z[k];
+    if (M && i < g * M) out[(i / M) * hstride + 2 + D + i % M] = z[k];
   }
 }
 
@@ -527,11 +573,34 @@ merge_ext_kernel(const float* __restrict__ partials, int D, int M, int n_parts, 
   if (lane == 0) red[wave] = L;
   __syncthreads();
   L = red[0] + red[1] + red[2] + red[3];
-  for (int j = tid; j < D + M; j += kThreads) {
-    float x = 0.0f;
-    for (int i = 0; i < n_parts; ++i) x = __builtin_fmaf(wts[i], p[(int64_t)i * rec + 2 + j], x);
-    acc[j] = x;
+  // wave w sums partials w, w + 4, ... (lane l on entries l, l + 64, ...,
+  // eight partials in flight), then the four waves are added in LDS
+  __shared__ float part_sum[kThreads / 64][kMaxD + 256];
+  {
+    float x[8];
+#pragma unroll
+    for (int k = 0; k < 8; ++k) x[k] = 0.0f;
+    const int nj = D + M;
+    for (int i = wave; i < n_parts; i += 4 * 2) {
+      const bool two = i + 4 < n_parts;
+      const float w0 = wts[i], w1 = two ? wts[i + 4] : 0.0f;
+      const float* p0 = p + (int64_t)i * rec + 2;
+      const float* p1 = p + (int64_t)(two ? i + 4 : i) * rec + 2;
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const int j = lane + 64 * k;
+        if (j < nj) x[k] = __builtin_fmaf(w0, p0[j], __builtin_fmaf(w1, p1[j], x[k]));
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int j = lane + 64 * k;
+      if (j < nj) part_sum[wave][j] = x[k];
+    }
   }
+  __syncthreads();
+  for (int j = tid; j < D + M; j += kThreads)
+    acc[j] = part_sum[0][j] + part_sum[1][j] + part_sum[2][j] + part_sum[3][j];
   __syncthreads();
   if (M) {
     const float c = 1.2533141373155003f / (float)M;   // sqrt(pi/2) / m
@@ -603,38 +672,58 @@ hipError_t launch_quantize_v_qjl(const void* v, int f16, int64_t n_mats, int64_t
 
 size_t ext_decode_lds(const kvq_ext_view& v, int Hq) {
   const int g = Hq / v.kv_heads, D = v.head_dim, M = v.v_qjl ? v.qjl_m : 0;
-  return sizeof(float) * ((size_t)g * D + (size_t)kCT * (D + 1) + (size_t)g * kCT + 3 * (size_t)g +
-                          kCT + (size_t)kCT * (M / 32));
+  const size_t words = 32 + (size_t)g * D + (size_t)kCT * (D + 4) + (size_t)g * kCT + 3 * (size_t)g +
+                       kCT + 2 * (size_t)D + (size_t)kCT * (D / v.group_ch) + (size_t)kCT * (M / 32) +
+                       (size_t)kCT * words_of(D, v.k_bits) + (size_t)kCT * words_of(D, v.v_bits);
+  return sizeof(float) * words;
 }
 
+// Splits are whole chunks: about 1024 workgroups, at least one chunk each.
 int ext_decode_parts(const kvq_ext_view& v, int n_splits) {
-  if (n_splits > 0) return n_splits;
-  const int64_t streams = (int64_t)v.batch * v.kv_heads;
-  int64_t p = (1024 + streams - 1) / streams;
-  const int64_t by_len = (v.n_tok + kCT - 1) / kCT;
-  if (p > by_len) p = by_len;
+  const int64_t chunks = (v.n_tok + kCT - 1) / kCT;
+  int64_t p = n_splits;
+  if (p <= 0) {
+    const int64_t streams = (int64_t)v.batch * v.kv_heads;
+    p = (1024 + streams - 1) / streams;
+  }
+  if (p > chunks) p = chunks;
   if (p < 1) p = 1;
   if (p > 4096) p = 4096;
   return (int)p;
+}
+
+template <int D>
+hipError_t launch_decode_ext_d(const ExtArgs& a, const void* q, int f16, dim3 grid, size_t lds,
+                               hipStream_t s) {
+  const void* fn = f16 ? (const void*)decode_ext_kernel<uint16_t, D>
+                       : (const void*)decode_ext_kernel<float, D>;
+  if (lds > 64 * 1024) {
+    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  if (f16)
+    decode_ext_kernel<uint16_t, D><<<grid, kThreads, lds, s>>>(a, (const uint16_t*)q);
+  else
+    decode_ext_kernel<float, D><<<grid, kThreads, lds, s>>>(a, (const float*)q);
+  return hipGetLastError();
 }
 
 hipError_t launch_decode_ext(const kvq_ext_view& v, const ExtLut& lk, const ExtLut& lv,
                              const void* q, int f16, int Hq, float sm_scale, float* partials,
                              int n_parts, float* out, hipStream_t s) {
   const int M = v.v_qjl ? v.qjl_m : 0;
-  ExtArgs a{v, lk, lv, Hq, sm_scale * kLog2e, partials, n_parts, v.head_dim + 2 + M};
+  const int64_t chunks = (v.n_tok + kCT - 1) / kCT;
+  const int64_t per = (chunks + n_parts - 1) / n_parts * kCT;
+  ExtArgs a{v, lk, lv, Hq, sm_scale * kLog2e, partials, n_parts, v.head_dim + 2 + M, per};
   const size_t lds = ext_decode_lds(v, Hq);
   dim3 grid((unsigned)n_parts, (unsigned)v.kv_heads, (unsigned)v.batch);
-  const void* fn = f16 ? (const void*)decode_ext_kernel<uint16_t> : (const void*)decode_ext_kernel<float>;
-  if (lds > 64 * 1024) {
-    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-    if (e != hipSuccess) return e;
+  hipError_t e;
+  switch (v.head_dim) {
+    case 32: e = launch_decode_ext_d<32>(a, q, f16, grid, lds, s); break;
+    case 64: e = launch_decode_ext_d<64>(a, q, f16, grid, lds, s); break;
+    case 128: e = launch_decode_ext_d<128>(a, q, f16, grid, lds, s); break;
+    default: return hipErrorInvalidValue;
   }
-  if (f16)
-    decode_ext_kernel<uint16_t><<<grid, kThreads, lds, s>>>(a, (const uint16_t*)q);
-  else
-    decode_ext_kernel<float><<<grid, kThreads, lds, s>>>(a, (const float*)q);
-  hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   merge_ext_kernel<<<dim3((unsigned)(v.batch * Hq)), kThreads, sizeof(float) * (size_t)n_parts, s>>>(
       partials, v.head_dim, M, n_parts, a.rec, v.jl, v.v_rotated, out);

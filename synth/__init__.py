@@ -182,6 +182,18 @@ WORKLOADS = {
     "1m_32layer": dict(B=1, Hq=32, Hkv=32, N=1048576, D=128, S=1, G=128,
                        Gv=32, R=128, k_bits=2, v_bits=2, layers=32,
                        chunk=4096),
+    # the next rows on the 128K GQA layer: 3-bit codebook keys (per channel,
+    # 128-token groups) and values (per token) with 1% per-vector outliers;
+    # and the KQV scheme at a 4-bit budget (rotated keys at 4 bits, rotated
+    # values at 3 bits plus the 1-bit sketch of m = 128 rows)
+    "kvquant_3bit_1pct_128k": dict(B=1, Hq=32, Hkv=8, N=131072, D=128, G=128,
+                                   Gv=128, k_bits=3, v_bits=3, k_nuq=True,
+                                   v_nuq=True, n_out=1, outliers="fraction",
+                                   frac=0.02, fmin=10.0, fmax=30.0,
+                                   sink_factor=20.0),
+    "kqv_4bit_128k": dict(B=1, Hq=32, Hkv=8, N=131072, D=128, G=128, Gv=32,
+                          k_bits=4, v_bits=3, qjl_m=128, outliers="fraction",
+                          frac=0.02, fmin=10.0, fmax=30.0, sink_factor=20.0),
 }
 
 

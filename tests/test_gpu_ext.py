@@ -247,3 +247,71 @@ def test_ext_view_rejections():
     with pytest.raises(kvq.KvqError):
         kvq.kvq_decode_attention_ext(bad, torch.zeros((1, 8, 256), dtype=torch.float16,
                                                       device=DEV))
+
+
+@pytest.mark.parametrize("name", ["kvquant_3bit_1pct_128k", "kqv_4bit_128k"])
+def test_ext_fullsize_sampled_stream(name):
+    """The bench's next-row legs at full size (the 128K GQA layer), in the
+    launch configuration the bench times (automatic splits): the sampled
+    KV head's codes, scales, outliers (or sketch) against the oracle bit for
+    bit, and its query heads' outputs within 2e-3."""
+    w = synth.WORKLOADS[name]
+    B, Hq, Hkv, N, D = w["B"], w["Hq"], w["Hkv"], w["N"], w["D"]
+    g = Hq // Hkv
+    ikw = {k: w[k] for k in ("outliers", "frac", "fmin", "fmax", "sink_factor") if k in w}
+    q, k, v = synth.kv_inputs(7, B, Hq, Hkv, N, D, **ikw)
+    kt = torch.from_numpy(k.reshape(B * Hkv, N, D)).to(DEV)
+    vt = torch.from_numpy(v.reshape(B * Hkv, N, D)).to(DEV)
+    h = 5
+    say("ext fullsize", name, "stream", h)
+    if w.get("k_nuq"):
+        lk, lv = synth.nuq_codebook(w["k_bits"]), synth.nuq_codebook(w["v_bits"])
+        keys = kvq.kvq_quantize_nuq_k(kt, w["k_bits"], w["G"], lk, w["n_out"])[:3]
+        values = kvq.kvq_quantize_nuq_v(vt, w["v_bits"], w["Gv"], lv, w["n_out"])[:3]
+        view = kvq.ext_view(B, Hkv, D, N, keys, values, w["k_bits"], w["v_bits"], w["G"],
+                            w["Gv"], k_lut=lk, v_lut=lv)
+        qt = torch.from_numpy(q).to(DEV)
+        c, s, p, vv = nuq.quantize_k(k[0, h], lk, w["G"], w["n_out"])
+        assert np.array_equal(u32(keys[0][h]), nuq.pack_codes(c, w["k_bits"]))
+        assert np.array_equal(keys[1][h].cpu().numpy(), s)
+        assert np.array_equal(u32(keys[2][h]), nuq.pack_outliers(p, vv))
+        kh = nuq.dequant_k(c, s, p, vv, lk, w["G"])
+        c, s, p, vv = nuq.quantize_v(v[0, h], lv, w["Gv"], w["n_out"])
+        assert np.array_equal(u32(values[0][h]), nuq.pack_codes(c, w["v_bits"]))
+        assert np.array_equal(values[1][h].cpu().numpy(), s)
+        assert np.array_equal(u32(values[2][h]), nuq.pack_outliers(p, vv))
+        vh = nuq.dequant_v(c, s, p, vv, lv, w["Gv"])
+        qh = q[0, h * g:(h + 1) * g].astype(np.float64)
+        ref = attention.attention(qh, kh[None], vh[None])
+        keep = (keys, values)
+    else:
+        S = synth.jl_matrix(7, w["qjl_m"], D)
+        jl = torch.from_numpy(S).to(DEV)
+        kr = kvq.kvq_hadamard(kt, out_dtype=torch.float32)
+        keys = kvq.kvq_quantize_k(kr, w["k_bits"], w["G"])[:2]
+        vr = kvq.kvq_hadamard(vt, out_dtype=torch.float32)
+        c_t, s_t, sk, rn, _ = kvq.kvq_quantize_v_qjl(vr, w["v_bits"], w["Gv"], jl)
+        qt = kvq.kvq_hadamard(torch.from_numpy(q).to(DEV), out_dtype=torch.float32)
+        view = kvq.ext_view(B, Hkv, D, N, keys, (c_t, s_t), w["k_bits"], w["v_bits"],
+                            w["G"], w["Gv"], sketch=sk, rnorm=rn, jl=jl, v_rotated=True)
+        kr_h = rotation.wht(k[0, h])
+        assert np.array_equal(kr[h].cpu().numpy(), kr_h)
+        c, s = codec.quantize_k(kr_h, w["k_bits"], w["G"])
+        assert np.array_equal(u32(keys[0][h]), codec.pack_rows(c, w["k_bits"]))
+        assert np.array_equal(keys[1][h].cpu().numpy(), s)
+        kh = codec.dequant(c, codec.expand_k_scales(s, N, w["G"]))
+        vr_h = rotation.wht(v[0, h])
+        c, s, b, gam, r = qjl.quantize_v(vr_h, w["v_bits"], w["Gv"], S)
+        assert np.array_equal(u32(c_t[h]), codec.pack_rows(c, w["v_bits"]))
+        assert np.array_equal(s_t[h].cpu().numpy(), s)
+        gb = u32(sk[h])
+        assert np.mean(gb != qjl.pack_signs(b)) < 1e-4
+        vh = qjl.dequant_v(c, s, b, gam, S, w["Gv"])
+        qh = rotation.wht(q[0, h * g:(h + 1) * g]).astype(np.float64)
+        ref = qjl.unrotate(attention.attention(qh, kh[None], vh[None]))
+        keep = (keys, c_t, s_t, sk, rn, jl)
+    out = kvq.kvq_decode_attention_ext(view, qt).cpu().numpy()
+    err = attention.max_row_relative_error(out[0, h * g:(h + 1) * g], ref)
+    say(f"  decode err {err:.3e}")
+    assert err <= TOL
+    assert len(keep) >= 2
