@@ -511,8 +511,8 @@ def main():
     views = [c.kvq_cache_view() for c in caches]
     # room for a few more partials than the first step needs: the automatic
     # split count can grow by one as flushes add key groups
-    ws_bytes = 2 * max(kvq.kvq_decode_workspace_bytes(v, Hq, args.splits)
-                       for v in views) + 65536
+    ws_bytes = 2 * max(kvq.kvq_decode_workspace_bytes(v, Hq, sp)
+                       for v in views for sp in {args.splits, 0}) + 65536
     ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
     out = torch.empty((B, Hq, D), dtype=torch.float32, device=dev)
     flush_buf = None
