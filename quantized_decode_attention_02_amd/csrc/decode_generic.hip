@@ -30,6 +30,7 @@ constexpr int kRopeChunkTok = 32;
 template <bool ROPE>
 constexpr int chunk_tok() { return ROPE ? kRopeChunkTok : kChunkTok; }
 constexpr float kLog2e = 1.4426950408889634f;
+typedef float float4v __attribute__((ext_vector_type(4)));
 
 __device__ inline float h2f(uint16_t u) {
   return (float)__builtin_bit_cast(_Float16, u);
@@ -344,11 +345,15 @@ decode_generic_kernel(kvq_kv_view v, const QT* __restrict__ q, int Hq,
 }
 
 // out[b][h][:] = sum_p 2^(m_p - M) o_p / sum_p 2^(m_p - M) l_p, one
-// workgroup per (batch, query head).  One pass reads every (m, l) pair into
-// LDS; M and the weights follow from LDS; then wave w sums partials w, w + 4,
-// ... with lane l on channels 2l and 2l + 1 (eight partials in flight per
-// lane), and the four wave sums are added in LDS.
+// workgroup per (batch, query head).  The merge is latency-bound (a few
+// hundred partials of D + 2 floats per head), so every load of a pass is
+// issued before anything waits: thread (row r, column c) loads channels
+// 4c .. 4c + 3 of partials r, r + R, ... (kMergeK of them, R = 256 / C rows
+// for C = the power of two >= D / 4 columns) while the (m, l) pairs go to
+// LDS and M and the weights are formed; the R row sums are then added in
+// LDS.  More than R * kMergeK partials take further passes.
 constexpr int kMergeThreads = 256;
+constexpr int kMergeK = 16;
 __device__ inline float wave_max(float x) {
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) x = fmaxf(x, __shfl_xor(x, o));
@@ -359,18 +364,41 @@ __device__ inline float wave_sum(float x) {
   for (int o = 1; o < 64; o <<= 1) x += __shfl_xor(x, o);
   return x;
 }
+template <bool EVEN>  // D even: every channel pair is 8-byte aligned
 __global__ void __launch_bounds__(kMergeThreads)
-merge_kernel(const float* __restrict__ partials, int D, int n_parts,
+merge_kernel(const float* __restrict__ partials, int D, int n_parts, int cols_log2,
              float* __restrict__ out) {
   __shared__ float red[kMergeThreads / 64];
-  __shared__ float osum[kMergeThreads / 64][2 * 64];
-  extern __shared__ float ml[];  // [2][n_parts]: m, then weight; l in between
+  __shared__ float4v osum[kMergeThreads];
+  extern __shared__ float ml[];  // [2][n_parts]: m, then l, then the weight
   float* mm = ml;
   float* ww = ml + n_parts;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int col = tid & ((1 << cols_log2) - 1), row = tid >> cols_log2;
+  const int rows = kMergeThreads >> cols_log2;
   const int64_t bh = blockIdx.x;
   const int64_t stride = D + 2;
   const float* p = partials + bh * n_parts * stride;
+  const int c0 = 4 * col;
+  // this thread's channels c0 .. c0 + 3 of partial i (indexes clamped into
+  // the array: columns past D and partials past n_parts are never used)
+  auto load4 = [&](int i) {
+    const float* src = p + (int64_t)min(i, n_parts - 1) * stride + 2;
+    float4v x;
+    if (EVEN) {
+      const int cc = c0 < D ? c0 : 0;
+      const float2 a = *(const float2*)(src + cc), b = *(const float2*)(src + min(cc + 2, D - 2));
+      x = (float4v){a.x, a.y, b.x, b.y};
+    } else {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) x[j] = src[min(c0 + j, D - 1)];
+    }
+    return x;
+  };
+  const int per_pass = rows * kMergeK;
+  float4v x[kMergeK];
+#pragma unroll
+  for (int k = 0; k < kMergeK; ++k) x[k] = load4(row + rows * k);
   float M = -INFINITY;
   for (int i = tid; i < n_parts; i += kMergeThreads) {
     const float m = p[i * stride], l = p[i * stride + 1];
@@ -394,35 +422,25 @@ merge_kernel(const float* __restrict__ partials, int D, int n_parts,
   if (lane == 0) red[wave] = L;
   __syncthreads();
   L = red[0] + red[1] + red[2] + red[3];
-  for (int d0 = 0; d0 < D; d0 += 128) {
-    const int d = d0 + 2 * lane;
-    float a0 = 0.0f, a1 = 0.0f;
-    if (d < D) {
-      int i = wave;
-      for (; i + 28 < n_parts; i += 32) {
-        float x[8][2];
+  float4v acc = (float4v){0.0f, 0.0f, 0.0f, 0.0f};
+  for (int base = 0;;) {
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          x[k][0] = p[(i + 4 * k) * stride + 2 + d];
-          x[k][1] = d + 1 < D ? p[(i + 4 * k) * stride + 3 + d] : 0.0f;
-        }
-#pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          a0 = __builtin_fmaf(x[k][0], ww[i + 4 * k], a0);
-          a1 = __builtin_fmaf(x[k][1], ww[i + 4 * k], a1);
-        }
-      }
-      for (; i < n_parts; i += 4) {
-        a0 = __builtin_fmaf(p[i * stride + 2 + d], ww[i], a0);
-        if (d + 1 < D) a1 = __builtin_fmaf(p[i * stride + 3 + d], ww[i], a1);
-      }
+    for (int k = 0; k < kMergeK; ++k) {
+      const int i = base + row + rows * k;
+      if (i < n_parts) acc += x[k] * ww[i];
     }
-    osum[wave][2 * lane] = a0;
-    osum[wave][2 * lane + 1] = a1;
-    __syncthreads();
-    if (tid < 128 && d0 + tid < D)
-      out[bh * D + d0 + tid] = (osum[0][tid] + osum[1][tid] + osum[2][tid] + osum[3][tid]) / L;
-    __syncthreads();
+    base += per_pass;
+    if (base >= n_parts) break;
+#pragma unroll
+    for (int k = 0; k < kMergeK; ++k) x[k] = load4(base + row + rows * k);
+  }
+  osum[tid] = acc;
+  __syncthreads();
+  for (int d = tid; d < D; d += kMergeThreads) {
+    const int cc = d >> 2, e = d & 3;
+    float sum = 0.0f;
+    for (int r = 0; r < rows; ++r) sum += osum[(r << cols_log2) + cc][e];
+    out[bh * D + d] = sum / L;
   }
 }
 
@@ -479,12 +497,21 @@ hipError_t launch_decode_generic(const kvq_kv_view& v, const void* q, int f16,
 hipError_t launch_merge(const float* partials, int B, int Hq, int D,
                         int n_parts, float* out, hipStream_t s) {
   const size_t lds = 2 * sizeof(float) * (size_t)n_parts;
-  if (lds + 3 * 1024 > 64 * 1024) {
-    hipError_t e = hipFuncSetAttribute((const void*)merge_kernel,
+  if (lds + 5 * 1024 > 64 * 1024) {
+    hipError_t e = hipFuncSetAttribute((const void*)merge_kernel<true>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e == hipSuccess)
+      e = hipFuncSetAttribute((const void*)merge_kernel<false>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
-  merge_kernel<<<dim3((unsigned)(B * Hq)), kMergeThreads, lds, s>>>(partials, D, n_parts, out);
+  int cols_log2 = 0;
+  while ((4 << cols_log2) < D) ++cols_log2;  // D <= 256: at most 64 columns
+  const dim3 grid((unsigned)(B * Hq));
+  if (D % 2 == 0)
+    merge_kernel<true><<<grid, kMergeThreads, lds, s>>>(partials, D, n_parts, cols_log2, out);
+  else
+    merge_kernel<false><<<grid, kMergeThreads, lds, s>>>(partials, D, n_parts, cols_log2, out);
   return hipGetLastError();
 }
 

@@ -334,15 +334,24 @@ __device__ inline float row_sum16(float x) {
   return x;
 }
 
+// Lazy softmax rescale.  The running maximum m moves only when a tile's
+// largest score exceeds it by more than kLazy (log2 units), so most tiles
+// skip the rescale of the output accumulators; p = 2^(s - m) is then at
+// most 2^kLazy.  The result is the same function of (m, l, o): every
+// partial is exact with respect to the m it reports.
+constexpr int kLazy = 3;
 // Value prescale.  P' = p * v_scale / f is rounded to one fp16 number, so
-// a unit's value scales are multiplied by a power of two sigma_v = 2^(14 - e)
-// before P' is formed, e being the exponent of a recent unit's largest value
-// scale: the largest scale times sigma_v stays in [2^8, 2^15), which keeps
-// P' below the fp16 maximum and, down to p * v_scale / v_max = 2^-16, in the
-// normal range (relative rounding 2^-11).  The output accumulators carry the
-// same factor: when a unit's scales leave that window, e moves to the
-// unit's exponent and the accumulators are multiplied by the (exact) power
-// of two between the two factors; at the end they are divided by sigma_v.
+// a unit's value scales are multiplied by a power of two
+// sigma_v = 2^(14 - kLazy - e) before P' is formed, e being the exponent of
+// a recent unit's largest value scale: the largest scale times sigma_v
+// stays in [2^(8 - kLazy), 2^(15 - kLazy)), which keeps P' (p <= 2^kLazy)
+// below the fp16 maximum and, down to p * v_scale / v_max = 2^(kLazy - 16),
+// in the normal range (relative rounding 2^-11).  The output accumulators
+// carry the same factor: when a unit's scales leave that window, e moves to
+// the unit's exponent and the accumulators are multiplied by the (exact)
+// power of two between the two factors; at the end they are divided by
+// sigma_v.
+constexpr int kVTop = 14 - kLazy;
 // Exponent of the largest of the n value scales a wave holds (float4 j of
 // lane l is scale group l + 64 j); the result is wave-uniform.
 template <int K>
@@ -532,7 +541,7 @@ decode_mfma_kernel(MfmaArgs a) {
     load_scales(u_first);
   }
 
-  int ev = 0;            // sigma_v = 2^(14 - ev) (see unit_vscale_exp)
+  int ev = 0;            // sigma_v = 2^(kVTop - ev) (see unit_vscale_exp)
   bool ev_set = false;
   for (int u = u_first; u < u_hi; u += kWaves) {
     const int grp = u / upg;
@@ -550,7 +559,7 @@ decode_mfma_kernel(MfmaArgs a) {
         ev_set = true;
       }
     }
-    const float sig_v = pow2f(14 - ev);
+    const float sig_v = pow2f(kVTop - ev);
 #pragma unroll
     for (int j = 0; j < kVs4; ++j) {
       const int idx = lane + 64 * j;
@@ -644,7 +653,7 @@ decode_mfma_kernel(MfmaArgs a) {
       float tmax = amax * inv_sigma_k;
       tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
       tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-      if (__any(tmax > m_run)) {
+      if (__any(tmax > m_run + (float)kLazy)) {
         const float m_new = fmaxf(m_run, tmax);
         const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
         m_run = m_new;
@@ -716,7 +725,7 @@ decode_mfma_kernel(MfmaArgs a) {
   l_run += __shfl_xor(l_run, 16);
   l_run += __shfl_xor(l_run, 32);
   if (ev_set) {
-    const float r = pow2f(ev - 14);
+    const float r = pow2f(ev - kVTop);
 #pragma unroll
     for (int jb = 0; jb < 8; ++jb) o[jb] *= r;
   }
@@ -932,7 +941,7 @@ __global__ void __launch_bounds__(kThreads, (rs_waves<KB, VB, NC, HS>())) decode
   uint32_t magic = 0x64006400u;
   asm volatile("" : "+v"(magic));  // keep the fp16 magic in a VGPR
 
-  int ev = 0;            // sigma_v = 2^(14 - ev) (see unit_vscale_exp)
+  int ev = 0;            // sigma_v = 2^(kVTop - ev) (see unit_vscale_exp)
   bool ev_set = false;
 
   // Rolling prefetch (as in the column kernel above).  The first unit is
@@ -1115,7 +1124,7 @@ __global__ void __launch_bounds__(kThreads, (rs_waves<KB, VB, NC, HS>())) decode
             ev_set = true;
           }
         }
-        const float sig_v = pow2f(14 - ev);
+        const float sig_v = pow2f(kVTop - ev);
 #pragma unroll
         for (int j = 0; j < kVs4; ++j) {
           const int idx = lane + 64 * j;
@@ -1297,7 +1306,7 @@ __global__ void __launch_bounds__(kThreads, (rs_waves<KB, VB, NC, HS>())) decode
 #pragma unroll
       for (int hl = 0; hl < HS; ++hl) {
         tmx[hl] = row_max16(fmaxf(sc[0][hl], sc[1][hl])) * sk;
-        grow = grow || tmx[hl] > m_run[hl];
+        grow = grow || tmx[hl] > m_run[hl] + (float)kLazy;
       }
       if (__any(grow)) {
         float alpha[HS];
@@ -1379,7 +1388,7 @@ __global__ void __launch_bounds__(kThreads, (rs_waves<KB, VB, NC, HS>())) decode
 #pragma unroll
   for (int hl = 0; hl < HS; ++hl) l_part[hl] = row_sum16(l_part[hl]);
   if (ev_set) {
-    const float r = pow2f(ev - 14);
+    const float r = pow2f(ev - kVTop);
 #pragma unroll
     for (int jb = 0; jb < 8; ++jb) o[jb] *= r;
   }
