@@ -249,6 +249,21 @@ def sub_workload(torch, kvq, dev, stream, name, args, flush_buf):
     torch.cuda.synchronize()
     assert c.kvq_cache_check() == kvq.KVQ_OK
     us = [1000 * a.elapsed_time(b) for a, b in calls]
+    # the same cache read as keys stored before the rotary embedding
+    # (uniform or mixed keys: the dedicated rotary kernel)
+    view = c.kvq_cache_view()
+    rope_calls = []
+    for i in range(6):
+        evict(flush_buf)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        kvq.kvq_decode_attention_rope(view, q[0], workspace=ws, out=out)
+        e1.record(stream)
+        if i:
+            rope_calls.append((e0, e1))
+    torch.cuda.synchronize()
+    rope_us = float(np.median([1000 * a.elapsed_time(b) for a, b in rope_calls]))
     nbytes = stream_bytes(c.kvq_cache_view(), Hq)
     ceil = size_matched_ceiling(torch, kvq, dev, stream, nbytes, flush_buf)
     med = float(np.median(us))
@@ -262,6 +277,7 @@ def sub_workload(torch, kvq, dev, stream, name, args, flush_buf):
            "frac_peak": round(nbytes / (med * 1e-6) / 1e9 / PEAK_GBS, 4),
            "read_ceiling_same_bytes_gbs": round(ceil, 1),
            "frac_read_ceiling": round(nbytes / (med * 1e-6) / 1e9 / ceil, 4),
+           "rope_decode_us": round(rope_us, 2),
            "config": config}
     rec.update(extra)
     if "salience_select_us" in extra:

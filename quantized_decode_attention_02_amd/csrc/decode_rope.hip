@@ -1,7 +1,8 @@
 // Decode attention over keys cached before the rotary position embedding
 // ("KVQuant: Towards 10 Million Context Length LLM Inference with KV Cache
 // Quantization", "Approach": per-channel key quantization before RoPE), for
-// uniform int8 / int4 / int2 keys, int4 / int2 value tiles and D = 128.
+// uniform int8 / int4 / int2 keys or mixed bf16 / int4 / int2 keys (the
+// MixKVQ layout), int4 / int2 value tiles and D = 128.
 //
 // Cache-order token i sits at position pos0 + i.  Writing the position of a
 // quantized token as t0 + j, with t0 the position of the first token of its
@@ -129,14 +130,18 @@ __device__ constexpr int hi_e(int i) { return KB == 8 ? lo_e<KB>(i) + 2 : i + 4;
 // two words; lane channel e < 4 is 4c + e, e >= 4 is 64 + 4c + e - 4.
 template <int KB, bool INTER>
 struct KWords {
-  typedef typename std::conditional<KB == 8 || !INTER, u32x2, uint32_t>::type T;
+  typedef typename std::conditional<
+      KB == 0, u32x4, typename std::conditional<KB == 8 || !INTER, u32x2, uint32_t>::type>::type T;
 };
 
 // The lane's 8 codes as 4 fp16 pairs; pair i holds lane channels
 // (lo_e(i), hi_e(i)).
 template <int KB, bool INTER>
 __device__ inline void key_pairs(typename KWords<KB, INTER>::T w, int c, half2v p[4]) {
-  if constexpr (KB == 8) {
+  if constexpr (KB == 0) {
+    (void)w;
+    (void)c;
+  } else if constexpr (KB == 8) {
     p[0] = code_pair<8>(w[0]);
     p[1] = code_pair<8>(w[0] >> 8);
     p[2] = code_pair<8>(w[1]);
@@ -178,6 +183,7 @@ struct RopeLds {
   float2 tab[kRTile][kRNF];               // (cos, sin) of j * theta_f
   float2 qs[GQ][kRD];                     // (q_d, sigma q_e) * qscale
   float2 base[kRWaves][kRNF];             // (cos, sin) of t0 * theta_f
+  uint8_t inv[kRWaves][kRD];              // mixed keys: channel of each class position
   float pv[kRWaves][GQ][pv_slots<RS>()][kRTile];  // weight * value scale
   float comb[kRWaves][GQ][kRD + 2];       // per-wave (m, l, o)
 };
@@ -188,7 +194,7 @@ struct RopeLds {
 // The one-head kernel keeps the latter: it then fits three waves per SIMD.
 template <int KB, int VB, int GQ, bool INTER, typename QT, bool RS = (GQ >= 2)>
 __global__ void __launch_bounds__(kRThreads)
-__attribute__((amdgpu_waves_per_eu(RS ? 2 : 3)))
+__attribute__((amdgpu_waves_per_eu((RS || KB == 0) ? 2 : 3)))
 decode_rope_kernel(kvq_kv_view v, const QT* __restrict__ q, int Hq, float qscale,
                    RopeDev rope, float* __restrict__ partials, int n_parts, int part_stride,
                    int gv_shift, int h_off) {
@@ -245,6 +251,37 @@ decode_rope_kernel(kvq_kv_view v, const QT* __restrict__ q, int Hq, float qscale
   // lane channel e: its channel, and its frequency's offset from fbase
   auto chan = [&](int e) { return INTER ? 8 * c + e : (e < 4 ? 4 * c + e : kRNF + 4 * c + e - 4); };
   auto fi = [](int e) { return INTER ? e >> 1 : e & 3; };
+  // Mixed keys (KB == 0): a score is a sum over channels in any order, so
+  // lane c takes the class positions 8 c .. 8 c + 7 (bf16 positions first,
+  // then int4, then int2; every class a multiple of eight positions): eight
+  // consecutive entries of one class row, one load per token.  Per key
+  // group the lane looks up the channel and frequency of each position
+  // (the inverse of the group's class map) and the int positions' scales.
+  constexpr bool KM = KB == 0;
+  const int NB = KM ? v.n_bf16 : 0, N4 = KM ? v.n_int4 : 0, N2 = kRD - NB - N4;
+  const int kp0 = 8 * c;
+  const int kcls = kp0 < NB ? 0 : (kp0 < NB + N4 ? 1 : 2);  // bf16, int4, int2
+  const uint32_t* kmb = nullptr;  // the lane's class array (this stream)
+  uint32_t krw = 0, kwo = 0;      // its row words, the lane's first word
+  int k2sh = 0;                   // int2: bit offset of the lane's 16 bits
+  if constexpr (KM) {
+    if (kcls == 0) {
+      kmb = (const uint32_t*)(v.k_bf16 + s * v.k_bf16_stride);
+      krw = (uint32_t)NB / 2;
+      kwo = (uint32_t)kp0 / 2;
+    } else if (kcls == 1) {
+      kmb = v.k_int4 + s * v.k_int4_stride;
+      krw = (uint32_t)N4 / 8;
+      kwo = (uint32_t)(kp0 - NB) / 8;
+    } else {
+      kmb = v.k_int2 + s * v.k_int2_stride;
+      krw = (uint32_t)(N2 + 15) / 16;
+      kwo = (uint32_t)(kp0 - NB - N4) / 16;
+      k2sh = 16 * (((kp0 - NB - N4) / 8) & 1);
+    }
+  }
+  const uint8_t* kpos = KM ? v.k_pos + s * v.k_pos_stride : nullptr;
+  int dch[KM ? 8 : 1], dfr[KM ? 8 : 1];  // channel and frequency of each position
 
   float m_run[GQ], l_run[GQ], o[GQ][kRBlocks];
 #pragma unroll
@@ -267,7 +304,13 @@ decode_rope_kernel(kvq_kv_view v, const QT* __restrict__ q, int Hq, float qscale
 #pragma unroll
     for (int st = 0; st < kRSteps; ++st) {
       const uint32_t off = (row0 + 4 * st) * KWD + kcol;
-      if constexpr (!INTER) {
+      if constexpr (KM) {
+        const uint32_t o2 = (row0 + 4 * st) * krw + kwo;
+        if (kcls == 0)
+          kw[st] = ldnt((const u32x4*)(kmb + o2));
+        else
+          kw[st][0] = ldnt(kmb + o2);
+      } else if constexpr (!INTER) {
         kw[st][0] = ldnt(kc + off);
         kw[st][1] = ldnt(kc + off + kcol2);
       } else if constexpr (KB == 8) {
@@ -308,7 +351,18 @@ decode_rope_kernel(kvq_kv_view v, const QT* __restrict__ q, int Hq, float qscale
     const bool more = T + kRWaves < t_hi;
     const int64_t qt0 = T * kRTile;
     const int64_t grp = (uint32_t)qt0 / (uint32_t)v.group_tok;  // qt0 < 2^26
-    if (grp != cur_grp) {
+    if (KM && grp != cur_grp) {
+      cur_grp = grp;
+      for (int d = lane; d < kRD; d += 64) L.inv[wave][kpos[grp * kRD + d]] = (uint8_t)d;
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        dch[KM ? e : 0] = L.inv[wave][kp0 + e];
+        dfr[KM ? e : 0] = INTER ? dch[KM ? e : 0] >> 1 : dch[KM ? e : 0] & (kRNF - 1);
+        ks[e] = kcls == 0 ? 1.0f : ksc[grp * (N4 + N2) + kp0 + e - NB];
+      }
+      __builtin_amdgcn_wave_barrier();
+    } else if (!KM && grp != cur_grp) {
       cur_grp = grp;
       const float4v a = *(const float4v*)(ksc + grp * kRD + chan(0));
       const float4v bq = *(const float4v*)(ksc + grp * kRD + chan(4));
@@ -325,10 +379,10 @@ decode_rope_kernel(kvq_kv_view v, const QT* __restrict__ q, int Hq, float qscale
     float Q1[GQ][8], Q2[GQ][8];
 #pragma unroll
     for (int e = 0; e < 8; ++e) {
-      const float2 cs = L.base[wave][fbase + fi(e)];
+      const float2 cs = L.base[wave][KM ? dfr[KM ? e : 0] : fbase + fi(e)];
 #pragma unroll
       for (int h = 0; h < GQ; ++h) {
-        const float2 qq = L.qs[h][chan(e)];
+        const float2 qq = L.qs[h][KM ? dch[KM ? e : 0] : chan(e)];
         Q1[h][e] = ks[e] * (cs.x * qq.x + cs.y * qq.y);
         Q2[h][e] = ks[e] * (cs.x * qq.y - cs.y * qq.x);
       }
@@ -337,6 +391,38 @@ decode_rope_kernel(kvq_kv_view v, const QT* __restrict__ q, int Hq, float qscale
 #pragma unroll
     for (int st = 0; st < kRSteps; ++st) {
       const int j = 4 * st + r;
+      if constexpr (KM) {
+        // the lane's eight entries as floats (exact): bf16 values, or
+        // int4 / int2 codes minus their offsets
+        float x[8];
+        float2 t8[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) t8[e] = L.tab[j][dfr[KM ? e : 0]];
+        const u32x4 w = kw[st];
+        if (kcls == 0) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            x[2 * i] = __builtin_bit_cast(float, w[i] << 16);
+            x[2 * i + 1] = __builtin_bit_cast(float, w[i] & 0xFFFF0000u);
+          }
+        } else if (kcls == 1) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) x[e] = (float)(int)((w[0] >> (4 * e)) & 0xFu) - 8.0f;
+        } else {
+          const uint32_t y = w[0] >> k2sh;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) x[e] = (float)(int)((y >> (2 * e)) & 0x3u) - 2.0f;
+        }
+#pragma unroll
+        for (int h = 0; h < GQ; ++h) {
+          float acc = 0.0f;
+#pragma unroll
+          for (int e = 0; e < 8; ++e)
+            acc = __builtin_fmaf(x[e], t8[e].x * Q1[h][e] + t8[e].y * Q2[h][e], acc);
+          sc[h][st] = RS ? acc : row_sum16(acc);
+        }
+        continue;
+      }
       float2 t[4];
       const float4v* tp = (const float4v*)&L.tab[j][fbase];
 #pragma unroll
@@ -505,23 +591,38 @@ hipError_t launch_rope_g(const kvq_kv_view& v, const void* q, int f16, int Hq, f
                          const RopeDev& rope, float* partials, int n_parts, int part_stride,
                          int gv_shift, hipStream_t s) {
   const int g = Hq / v.kv_heads;
-  for (int h0 = 0; h0 < g; h0 += 2) {
-    hipError_t e;
-    if (h0 + 2 > g)
-      e = rope.interleaved
+  if constexpr (KB == 0) {
+    // mixed keys: one query head per launch (the per-lane channel map
+    // leaves no registers for a second head)
+    for (int h = 0; h < g; ++h) {
+      const hipError_t e =
+          rope.interleaved
               ? launch_rope_t<KB, VB, 1, true>(v, q, f16, Hq, qscale, rope, partials, n_parts,
-                                               part_stride, gv_shift, h0, s)
+                                               part_stride, gv_shift, h, s)
               : launch_rope_t<KB, VB, 1, false>(v, q, f16, Hq, qscale, rope, partials, n_parts,
-                                                part_stride, gv_shift, h0, s);
-    else
-      e = rope.interleaved
-              ? launch_rope_t<KB, VB, 2, true>(v, q, f16, Hq, qscale, rope, partials, n_parts,
-                                               part_stride, gv_shift, h0, s)
-              : launch_rope_t<KB, VB, 2, false>(v, q, f16, Hq, qscale, rope, partials, n_parts,
-                                                part_stride, gv_shift, h0, s);
-    if (e != hipSuccess) return e;
+                                                part_stride, gv_shift, h, s);
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
+  } else {
+    for (int h0 = 0; h0 < g; h0 += 2) {
+      hipError_t e;
+      if (h0 + 2 > g)
+        e = rope.interleaved
+                ? launch_rope_t<KB, VB, 1, true>(v, q, f16, Hq, qscale, rope, partials, n_parts,
+                                                 part_stride, gv_shift, h0, s)
+                : launch_rope_t<KB, VB, 1, false>(v, q, f16, Hq, qscale, rope, partials,
+                                                  n_parts, part_stride, gv_shift, h0, s);
+      else
+        e = rope.interleaved
+                ? launch_rope_t<KB, VB, 2, true>(v, q, f16, Hq, qscale, rope, partials, n_parts,
+                                                 part_stride, gv_shift, h0, s)
+                : launch_rope_t<KB, VB, 2, false>(v, q, f16, Hq, qscale, rope, partials,
+                                                  n_parts, part_stride, gv_shift, h0, s);
+      if (e != hipSuccess) return e;
+    }
+    return hipSuccess;
   }
-  return hipSuccess;
 }
 
 bool aligned_to(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
@@ -530,15 +631,25 @@ bool aligned_to(const void* p, uintptr_t a) { return ((uintptr_t)p % a) == 0; }
 
 bool rope_fast_eligible(const kvq_kv_view& v, int Hq) {
   const int g = Hq / v.kv_heads;
-  if (v.k_mixed || v.head_dim != kRD) return false;
-  if (v.k_bits != 2 && v.k_bits != 4 && v.k_bits != 8) return false;
+  if (v.head_dim != kRD) return false;
+  if (v.k_mixed) {
+    // whole eight-position lanes per class; 16-byte bf16 loads
+    const int nb = v.n_bf16, n4 = v.n_int4;
+    if (nb < 0 || n4 < 0 || nb % 8 || n4 % 8 || nb + n4 > kRD || !v.k_pos) return false;
+    if (nb && !(aligned_to(v.k_bf16, 16) && v.k_bf16_stride % 8 == 0)) return false;
+    if (n4 && !v.k_int4) return false;
+    if (nb + n4 < kRD && !v.k_int2) return false;
+  } else {
+    if (v.k_bits != 2 && v.k_bits != 4 && v.k_bits != 8) return false;
+    if (!(aligned_to(v.k_codes, 16) && v.k_codes_stride % 4 == 0 && aligned_to(v.k_scales, 16) &&
+          v.k_scales_stride % 4 == 0))
+      return false;
+  }
   if (v.v_bits != 2 && v.v_bits != 4) return false;
   if (v.v_layout != KVQ_V_TILE32 || v.group_tok % kRTile || v.group_ch < 16) return false;
   if (g < 1 || g > 8) return false;
   if (v.n_quant < kRTile || v.n_quant >= ((int64_t)1 << 26)) return false;  // 32-bit offsets
-  return aligned_to(v.k_codes, 16) && v.k_codes_stride % 4 == 0 && aligned_to(v.k_scales, 16) &&
-         v.k_scales_stride % 4 == 0 && aligned_to(v.v_codes, 16) && v.v_codes_stride % 4 == 0 &&
-         aligned_to(v.v_scales, 4);
+  return aligned_to(v.v_codes, 16) && v.v_codes_stride % 4 == 0 && aligned_to(v.v_scales, 4);
 }
 
 int rope_fast_parts(const kvq_kv_view& v, int Hq, int n_splits) {
@@ -577,6 +688,12 @@ hipError_t launch_decode_rope(const kvq_kv_view& v, const void* q, int f16, int 
   if (v.k_bits == KB && v.v_bits == VB)                                                     \
     e = launch_rope_g<KB, VB>(v, q, f16, Hq, qscale, rope, partials, n_parts, stride, gv_shift, \
                               s);                                                           \
+  else
+  if (v.k_mixed)
+    e = v.v_bits == 4 ? launch_rope_g<0, 4>(v, q, f16, Hq, qscale, rope, partials, n_parts, stride,
+                                            gv_shift, s)
+                      : launch_rope_g<0, 2>(v, q, f16, Hq, qscale, rope, partials, n_parts, stride,
+                                            gv_shift, s);
   else
   KVQ_ROPE_CASE(8, 4) KVQ_ROPE_CASE(8, 2) KVQ_ROPE_CASE(4, 4) KVQ_ROPE_CASE(4, 2)
   KVQ_ROPE_CASE(2, 4) KVQ_ROPE_CASE(2, 2) e = hipErrorInvalidValue;

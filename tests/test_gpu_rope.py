@@ -7,8 +7,10 @@ and runs float64 attention.  The decode output must be within 2e-3 (max row
 relative L2 error).  Cases span several 32-token tiles with a ragged fp16
 tail, both pair layouts, every key/value bit width the dedicated kernel
 takes, 1 to 5 and 8 query heads per KV head (run as head pairs and single
-heads), sinks, large position offsets, and views only the general kernel
-covers (mixed keys, row-layout values, head_dim 64).
+heads), sinks, large position offsets, mixed bf16 / int4 / int2 keys
+(the dedicated kernel's per-lane class positions, against the general
+kernel too), and views only the general kernel covers (row-layout values,
+head_dim 64, bf16 counts that are not a multiple of eight).
 """
 import numpy as np
 import pytest
@@ -105,6 +107,29 @@ def test_rope_general_views():
     run_case(D=64, seed=33, kb=4, vb=2, Gv=32)
     run_case(kb=3, vb=3, seed=34)
     run_case(qf32=True, seed=35, n_splits=3)
+
+
+@pytest.mark.parametrize("pairing", ["half", "interleaved"])
+@pytest.mark.parametrize("nb,n4,vb,g", [(8, 32, 2, 5), (0, 64, 4, 1), (16, 8, 2, 3),
+                                        (8, 120, 4, 2), (0, 0, 2, 4), (8, 0, 2, 1)])
+def test_rope_mixed_keys(pairing, nb, n4, vb, g):
+    # mixed keys take the dedicated kernel (whole eight-position classes);
+    # the general kernel must agree with it
+    seed = 60 + nb + n4 + vb + g
+    kw = dict(mixed=True, n_bf16=nb, n_int4=n4, kb=2, vb=vb, Hq=2 * g, Hkv=2, S=1,
+              N=1400, pairing=pairing, seed=seed, pos0=1000 * g + nb)
+    a = run_case(**kw)
+    b = run_case(flags=kvq.KVQ_DECODE_GENERIC, **kw)
+    assert np.max(np.abs(a - b)) <= 2e-3 * np.max(np.abs(a))
+
+
+def test_rope_mixed_keys_splits_and_fallback():
+    # explicit split counts (more splits than tiles included), batch 2
+    for n_splits in (1, 9, 300):
+        run_case(mixed=True, n_bf16=8, n_int4=32, kb=2, vb=2, B=2, Hq=4, Hkv=2, N=1300,
+                 G=64, n_splits=n_splits, seed=80 + n_splits)
+    # four bf16 channels: not whole lanes, so the general kernel
+    run_case(mixed=True, n_bf16=4, n_int4=32, kb=2, vb=2, Hq=4, Hkv=2, seed=90)
 
 
 def test_rope_tiny_and_tail_only():
