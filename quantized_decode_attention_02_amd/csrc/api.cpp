@@ -612,7 +612,7 @@ kvq_status kvq_quantize_v_qjl(const void* v, int dtype, int64_t n_mats, int64_t 
 
 size_t kvq_decode_ext_workspace_bytes(const kvq_ext_view* v, int n_q_heads, int n_splits) {
   if (!ext_view_ok(v, n_q_heads) || n_splits < 0 || n_splits > 4096) return 0;
-  const int parts = ext_decode_parts(*v, n_splits);
+  const int parts = ext_decode_parts(*v, n_q_heads, n_splits);
   const int M = v->v_qjl ? v->qjl_m : 0;
   return (size_t)v->batch * n_q_heads * parts * (v->head_dim + 2 + M) * sizeof(float);
 }
@@ -632,7 +632,7 @@ kvq_status kvq_decode_attention_ext(const kvq_ext_view* v, const void* q, int dt
   if (v->k_nuq && !make_lut(v->k_lut, v->k_bits, &lk)) return KVQ_E_ARG;
   if (v->v_nuq && !make_lut(v->v_lut, v->v_bits, &lv)) return KVQ_E_ARG;
   if (ext_decode_lds(*v, n_q_heads) > 160 * 1024) return KVQ_E_UNSUPPORTED;
-  const int parts = ext_decode_parts(*v, n_splits);
+  const int parts = ext_decode_parts(*v, n_q_heads, n_splits);
   return hip_status(launch_decode_ext(*v, lk, lv, q, dtype == KVQ_F16, n_q_heads, sm_scale,
                                       (float*)workspace, parts, out, (hipStream_t)stream));
 }

@@ -36,6 +36,9 @@ constexpr int kThreads = 256;
 constexpr int kRowsV = 32;    // token rows per workgroup of the value quantizers
 constexpr int kCT = 64;       // tokens per decode chunk
 constexpr float kLog2e = 1.4426950408889634f;
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef float float4v __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ inline float h2f(uint16_t u) { return (float)__builtin_bit_cast(_Float16, u); }
 __device__ inline bool f16_finite(uint16_t u) { return (u & 0x7C00u) != 0x7C00u; }
@@ -284,38 +287,82 @@ quantize_v_qjl_kernel(const T* __restrict__ v, int64_t n_tok, int d, int bits, i
     }
     rnorm[mat * n_tok + r0 + tid] = (float)sqrt(acc);
   }
+  // sign of <S_i, r> for every row r and sketch row i, in float64: thread
+  // (row tid / 8, lane group ig = tid % 8) accumulates sketch rows
+  // ih + 32 k + 4 ig + j (j < 4, k < 4) of a half of at most 128 sketch
+  // rows, over blocks of 32 channels of S staged transposed in LDS (rows
+  // of 132 floats); the 4-bit groups of a word are OR-ed over the row's
+  // eight lanes.
   const int mw = m / 32;
-  for (int r = wave; r < rows; r += kThreads / 64) {
-    for (int i0 = 0; i0 < m; i0 += 64) {
-      const int i = i0 + lane;
-      double dot = 0.0;
-      if (i < m) {
-        const float* srow = S + (int64_t)i * d;
-        for (int c = 0; c < d; ++c) dot += (double)srow[c] * (double)rs[r * d + c];
+  float* St = sc;  // [32][132], free after the codes
+  const int rr = tid >> 3, ig = tid & 7;
+  for (int ih = 0; ih < m; ih += 128) {
+    const int mi = min(128, m - ih);
+    double dot[4][4];
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) dot[k][j] = 0.0;
+    for (int cb = 0; cb < d; cb += 32) {
+      const int nc = min(32, d - cb);
+      __syncthreads();
+      for (int e = tid; e < 32 * mi; e += kThreads) {
+        const int i = e >> 5, cc = e & 31;
+        St[cc * 132 + i] = cc < nc ? S[(int64_t)(ih + i) * d + cb + cc] : 0.0f;
       }
-      const uint64_t bal = __ballot(i < m && dot >= 0.0);
-      uint32_t* out = sketch + (mat * n_tok + r0 + r) * mw + i0 / 32;
-      if (lane == 0) out[0] = (uint32_t)bal;
-      if (lane == 32 && i0 + 32 < m) out[1] = (uint32_t)(bal >> 32);
+      __syncthreads();
+      if (rr < rows) {
+        for (int cc = 0; cc < nc; ++cc) {
+          const double xr = rs[rr * d + cb + cc];
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            if (32 * k < mi) {
+              const float4v s4 = *(const float4v*)&St[cc * 132 + 32 * k + 4 * ig];
+#pragma unroll
+              for (int j = 0; j < 4; ++j) dot[k][j] = __builtin_fma((double)s4[j], xr, dot[k][j]);
+            }
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      if (32 * k < mi) {
+        uint32_t nib = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) nib |= (dot[k][j] >= 0.0 ? 1u : 0u) << (4 * ig + j);
+        nib |= __shfl_xor(nib, 1);
+        nib |= __shfl_xor(nib, 2);
+        nib |= __shfl_xor(nib, 4);
+        if (ig == 0 && rr < rows) sketch[(mat * n_tok + r0 + rr) * mw + ih / 32 + k] = nib;
+      }
     }
   }
 }
 
 // ---------------------------------------------------------------------------
 // Decode over an extended view: one workgroup per (split, KV head, batch);
-// splits are whole 64-token chunks.  Thread tid owns channel c = tid % D of
-// the tokens tid / D, tid / D + 256 / D, ... of a chunk for the dequant
-// (the field's word and shift, the channel's scale and the codebook in LDS
-// are fixed per thread or per chunk, so no division runs per element);
-// the chunk's keys go to LDS, the group's outliers are added, four lanes
-// per token score it against every query head (a lane sums every fourth
-// channel: rows padded to D + 4 floats, so the 16 tokens x 4 lanes of a
-// wave hit distinct banks), the online softmax runs a wave per head, then
-// the values the same way, and thread (channel, head set) accumulates the
-// weighted sums; the sketch words and norms of the chunk go to LDS for the
-// per-head sign sums.  Partial record per (batch, head, split): m (log2
-// units), l, o[D], z[M] (M = m of the sketch, 0 without one).
+// splits are whole 64-token chunks.  Per chunk, every load goes to LDS in one
+// pass (code rows, the key scales of its at most two groups, value scales,
+// sketch words transposed to word-major, norms).  Thread tid dequantizes
+// channel c = tid % D of the tokens tid / D, tid / D + 256 / D, ... (the
+// field's word and shift, the channel's key scales and the codebook are
+// fixed per thread or per chunk) into fp32 rows padded to D + 16 floats, and
+// the group's outliers are added.  Four lanes per token score it against
+// every query head with 16-byte reads of key rows and queries (lane
+// quarter qd takes channels 16 i + 4 qd .. + 3).  A wave per head runs the
+// online softmax over the chunk's tokens (one token per lane).  The values
+// are dequantized into the same rows, then thread (channel c, slice tid / D)
+// accumulates every head's weighted sum over its slice of the chunk's
+// tokens, reading four weights per 16-byte load; the slices are added at
+// the end.  The sketch's per-head sign sums z[h][j] = sum_t p gamma b are a
+// product of the weights (hi and lo fp16 limbs of p * gamma times a power of
+// two per chunk) with the +-1 sketch signs, on matrix cores: rows 2 h + limb,
+// 32 tokens per step, 16 sketch rows j per block, fp32 accumulation.
+// Partial record per (batch, head, split): m (log2 units), l, o[D], z[M]
+// (M = m of the sketch, 0 without one).
 // ---------------------------------------------------------------------------
+
 struct ExtArgs {
   kvq_ext_view v;
   ExtLut lk, lv;
@@ -327,16 +374,77 @@ struct ExtArgs {
   int64_t per;        // tokens per split, a multiple of kCT
 };
 
-// LDS words of the per-chunk staging areas (codes, scales, sketch words).
-struct ExtStage {
-  int kw, vw, ngv, mw;   // words per key / value row, value groups, sketch words
+constexpr int kExtPad = 16;  // floats of padding per fp32 row (16-byte rows, b128 reads)
+
+// The next chunk's words of one contiguous source range, held in registers
+// while the current chunk is computed: thread tid takes words tid + 256 k,
+// k < CAP; words past CAP * 256 are copied directly when stored.
+template <int CAP>
+struct Staged {
+  uint32_t r[CAP];
+  __device__ void load(const uint32_t* src, int cnt) {
+#pragma unroll
+    for (int k = 0; k < CAP; ++k) {
+      const int i = threadIdx.x + kThreads * k;
+      r[k] = i < cnt ? src[i] : 0u;
+    }
+  }
+  // dst[map(i)] = word i
+  template <typename F>
+  __device__ void store(const uint32_t* src, int cnt, uint32_t* dst, F map) const {
+#pragma unroll
+    for (int k = 0; k < CAP; ++k) {
+      const int i = threadIdx.x + kThreads * k;
+      if (i < cnt) dst[map(i)] = r[k];
+    }
+    for (int i = threadIdx.x + kThreads * CAP; i < cnt; i += kThreads) dst[map(i)] = src[i];
+  }
 };
 
+// Dequantize a chunk's code rows into fp32 rows of LDS: thread tid takes
+// the (token, word) items tid, tid + 256, ... of n rows of words_of(D, BITS)
+// words and writes every field of its word: level (codebook entry lut[code],
+// or code - off) times the scale sc(t, channel).
+template <int BITS, bool NUQ, int D, int DP, typename SC>
+__device__ inline void dequant_rows(const uint32_t* cw, int n, float* buf, const float* lut,
+                                    float off, SC sc) {
+  constexpr int FPW = 32 / BITS, WR = (D + FPW - 1) / FPW;
+  constexpr uint32_t MASK = (1u << BITS) - 1u;
+  for (int i = threadIdx.x; i < n * WR; i += kThreads) {
+    const int t = i / WR, w = i - t * WR;
+    const uint32_t word = cw[i];
+    float* row = buf + t * DP + w * FPW;
+#pragma unroll
+    for (int f = 0; f < FPW; ++f) {
+      if (w * FPW + f < D) {
+        const uint32_t code = (word >> (f * BITS)) & MASK;
+        const float lvl = NUQ ? lut[code] : (float)code - off;
+        row[f] = lvl * sc(t, w * FPW + f);
+      }
+    }
+  }
+}
+template <int D, int DP, typename SC>
+__device__ inline void dequant_rows_any(int bits, bool nuq, const uint32_t* cw, int n, float* buf,
+                                        const float* lut, float off, SC sc) {
+  if (nuq) {
+    if (bits == 2) dequant_rows<2, true, D, DP>(cw, n, buf, lut, off, sc);
+    else if (bits == 3) dequant_rows<3, true, D, DP>(cw, n, buf, lut, off, sc);
+    else dequant_rows<4, true, D, DP>(cw, n, buf, lut, off, sc);
+  } else {
+    if (bits == 2) dequant_rows<2, false, D, DP>(cw, n, buf, lut, off, sc);
+    else if (bits == 3) dequant_rows<3, false, D, DP>(cw, n, buf, lut, off, sc);
+    else if (bits == 4) dequant_rows<4, false, D, DP>(cw, n, buf, lut, off, sc);
+    else dequant_rows<8, false, D, DP>(cw, n, buf, lut, off, sc);
+  }
+}
+
 template <typename QT, int D>
-__global__ void __launch_bounds__(kThreads)
+__global__ void __launch_bounds__(kThreads, 3)  // three waves per SIMD, as the LDS allows
 decode_ext_kernel(ExtArgs a, const QT* __restrict__ q) {
-  constexpr int Dp = D + 4;               // padded LDS row
-  constexpr int TPT = kThreads / D;       // token lanes of the dequant
+  constexpr int Dp = D + kExtPad;
+  constexpr int TPT = kThreads / D;       // dequant token lanes; weighted-sum slices
+  constexpr int TS = kCT / TPT;           // tokens per slice
   extern __shared__ __align__(16) float sm[];
   const kvq_ext_view& v = a.v;
   const int g = a.Hq / v.kv_heads;
@@ -347,27 +455,30 @@ decode_ext_kernel(ExtArgs a, const QT* __restrict__ q) {
   float* lut = sm;                        // [32]: key levels, value levels
   float* qs = lut + 32;                   // [g][D]
   float* buf = qs + g * D;                // [kCT][Dp]
-  float* ps = buf + kCT * Dp;             // [g][kCT]
-  float* st = ps + g * kCT;               // [3][g]: m, l, alpha
-  float* gam = st + 3 * g;                // [kCT]
+  float* ps = buf + kCT * Dp;             // [g][kCT] weights
+  float* pg = ps + g * kCT;               // [g][kCT] weight * gamma * 2^-e (sketch)
+  float* st = pg + g * kCT;               // [4][8]: m, l, alpha; st[24] = 2^e
+  float* gam = st + 32;                   // [kCT]
   float* ksl = gam + kCT;                 // [2][D]: scales of the chunk's key groups
   float* vsl = ksl + 2 * D;               // [kCT][ngv]
-  uint32_t* skw = (uint32_t*)(vsl + kCT * ngv);  // [kCT][MW]
-  uint32_t* kcw = skw + kCT * MW;         // [kCT][kw_row]
+  uint32_t* skT = (uint32_t*)(vsl + ((kCT * ngv + 3) & ~3));  // [MW][kCT]
+  uint32_t* kcw = skT + kCT * MW;         // [kCT][kw_row]
   uint32_t* vcw = kcw + kCT * kw_row;     // [kCT][vw_row]
+  uint32_t* kol = vcw + kCT * vw_row;     // [2][D * k_n_out]: the groups' key outliers
+  uint32_t* vol = kol + 2 * D * v.k_n_out;  // [kCT][ngv * v_n_out]: value outliers
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lq = lane >> 4, ln = lane & 15;
   const int part = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int64_t s = (int64_t)b * v.kv_heads + kvh;
   const int64_t N = v.n_tok;
   const int64_t t_lo = min(N, (int64_t)part * a.per), t_hi = min(N, t_lo + a.per);
   const int G = v.group_tok;
 
-  // per-thread constants of the dequant: channel c of tokens t0 + TPT j
+  // per-thread constants of the dequant: channel c of tokens t0 + TPT j;
+  // the weighted sums: channel c of tokens t0 * TS .. t0 * TS + TS - 1
   const int c = tid % D, t0 = tid / D;
-  const int kword = c / fields_per_word(kb), kshift = (c % fields_per_word(kb)) * kb;
-  const int vword = c / fields_per_word(vb), vshift = (c % fields_per_word(vb)) * vb;
-  const uint32_t kmask = (1u << kb) - 1u, vmask = (1u << vb) - 1u;
-  const int vgrp = c / v.group_ch;
+  int gv_shift = 0;  // group_ch divides D, a power of two
+  while ((1 << gv_shift) < v.group_ch) ++gv_shift;
   const float koff = v.k_nuq ? 0.0f : (float)(qmax_of(kb) + 1);
   const float voff = v.v_nuq ? 0.0f : (float)(qmax_of(vb) + 1);
 
@@ -377,13 +488,17 @@ decode_ext_kernel(ExtArgs a, const QT* __restrict__ q) {
   }
   for (int i = tid; i < g * D; i += kThreads)
     qs[i] = ldx(q, ((int64_t)b * a.Hq + kvh * g) * D + i) * a.qscale;
-  if (tid < g) {
+  if (tid < 8) {
     st[tid] = -INFINITY;
-    st[g + tid] = 0.0f;
+    st[8 + tid] = 0.0f;
   }
-  float o[8], z[8];
+  float o[8];
 #pragma unroll
-  for (int k = 0; k < 8; ++k) { o[k] = 0.0f; z[k] = 0.0f; }
+  for (int k = 0; k < 8; ++k) o[k] = 0.0f;
+  // sketch sums: this wave's blocks of 16 sketch rows, nb = wave + 4 i
+  float4v zacc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) zacc[i] = (float4v){0.0f, 0.0f, 0.0f, 0.0f};
   __syncthreads();
 
   const uint32_t* kc = v.k_codes + s * v.k_codes_stride;
@@ -393,37 +508,81 @@ decode_ext_kernel(ExtArgs a, const QT* __restrict__ q) {
   const float* vs = v.v_scales + s * v.v_scales_stride;
   const uint32_t* vo = v.v_n_out ? v.v_outliers + s * v.v_outliers_stride : nullptr;
 
+  // Chunk loads: issued one chunk ahead into registers (so they overlap the
+  // current chunk's work), stored to LDS when the chunk starts.
+  const int per_g = D * v.k_n_out, per_t = ngv * v.v_n_out;
+  // (capacities for up to 4-bit codes, four value groups, four sketch
+  // words and one outlier per vector; larger views copy the rest directly)
+  Staged<(D >= 64 ? D / 32 : 1)> st_k, st_v;
+  Staged<1> st_ks, st_gam, st_vs, st_sk, st_ko, st_vo;
+  struct ChunkSrc {
+    const uint32_t *k, *v, *ks, *vs, *sk, *gam, *ko, *vo;
+    int nk, nv, nks, nvs, nsk, ngam, nko, nvo;
+  };
+  auto chunk_src = [&](int64_t c0) {
+    const int n = (int)min((int64_t)kCT, t_hi - c0);
+    const int64_t g0 = c0 / G;
+    const int ng = (c0 - g0 * G + n > G) ? 2 : 1;
+    ChunkSrc cs;
+    cs.k = kc + c0 * kw_row;                       cs.nk = n * kw_row;
+    cs.v = vc + c0 * vw_row;                       cs.nv = n * vw_row;
+    cs.ks = (const uint32_t*)(ks + g0 * D);        cs.nks = ng * D;
+    cs.vs = (const uint32_t*)(vs + c0 * ngv);      cs.nvs = n * ngv;
+    cs.sk = M ? v.v_sketch + s * v.v_sketch_stride + c0 * MW : nullptr;
+    cs.nsk = M ? n * MW : 0;
+    cs.gam = M ? (const uint32_t*)(v.v_rnorm + s * v.v_rnorm_stride + c0) : nullptr;
+    cs.ngam = M ? n : 0;
+    cs.ko = ko ? ko + g0 * per_g : nullptr;        cs.nko = ko ? ng * per_g : 0;
+    cs.vo = vo ? vo + c0 * per_t : nullptr;        cs.nvo = vo ? n * per_t : 0;
+    return cs;
+  };
+  auto stage_load = [&](const ChunkSrc& cs) {
+    st_k.load(cs.k, cs.nk);
+    st_v.load(cs.v, cs.nv);
+    st_ks.load(cs.ks, cs.nks);
+    st_vs.load(cs.vs, cs.nvs);
+    st_sk.load(cs.sk, cs.nsk);
+    st_gam.load(cs.gam, cs.ngam);
+    st_ko.load(cs.ko, cs.nko);
+    st_vo.load(cs.vo, cs.nvo);
+  };
+  auto ident = [](int i) { return i; };
+  ChunkSrc cur = chunk_src(t_lo);
+  if (t_lo < t_hi) stage_load(cur);
+
   for (int64_t c0 = t_lo; c0 < t_hi; c0 += kCT) {
     const int n = (int)min((int64_t)kCT, t_hi - c0);
-    // ---- every load of the chunk at once, into LDS: the code rows (one
-    //      contiguous range each), the key scales of its (at most two)
-    //      groups, the value scales, the sketch words and norms
     const int64_t g0 = c0 / G;
     const int r0 = (int)(c0 - g0 * G);            // chunk start within its group
     const int ng_chunk = (r0 + n > G) ? 2 : 1;
-    for (int i = tid; i < n * kw_row; i += kThreads) kcw[i] = kc[c0 * kw_row + i];
-    for (int i = tid; i < n * vw_row; i += kThreads) vcw[i] = vc[c0 * vw_row + i];
-    for (int i = tid; i < ng_chunk * D; i += kThreads) ksl[i] = ks[g0 * D + i];
-    for (int i = tid; i < n * ngv; i += kThreads) vsl[i] = vs[c0 * ngv + i];
-    if (M) {
-      for (int i = tid; i < n * MW; i += kThreads)
-        skw[i] = v.v_sketch[s * v.v_sketch_stride + c0 * MW + i];
-      for (int t = tid; t < n; t += kThreads) gam[t] = v.v_rnorm[s * v.v_rnorm_stride + c0 + t];
+    // ---- this chunk's words into LDS (sketch words transposed to
+    //      word-major), then the next chunk's loads
+    st_k.store(cur.k, cur.nk, kcw, ident);
+    st_v.store(cur.v, cur.nv, vcw, ident);
+    st_ks.store(cur.ks, cur.nks, (uint32_t*)ksl, ident);
+    st_vs.store(cur.vs, cur.nvs, (uint32_t*)vsl, ident);
+    st_sk.store(cur.sk, cur.nsk, skT, [&](int i) { return (i % MW) * kCT + i / MW; });
+    st_gam.store(cur.gam, cur.ngam, (uint32_t*)gam, ident);
+    st_ko.store(cur.ko, cur.nko, kol, ident);
+    st_vo.store(cur.vo, cur.nvo, vol, ident);
+    if (c0 + kCT < t_hi) {
+      cur = chunk_src(c0 + kCT);
+      stage_load(cur);
     }
     __syncthreads();
     // ---- keys of the chunk: level (or centred code) times the channel's
     //      scale of the token's group
-    for (int t = t0; t < n; t += TPT) {
-      const uint32_t code = (kcw[t * kw_row + kword] >> kshift) & kmask;
-      const float lvl = v.k_nuq ? lut[code] : (float)code - koff;
-      buf[t * Dp + c] = lvl * ksl[(r0 + t >= G ? D : 0) + c];
+    {
+      const int t_split = G - r0;  // first token of the second group
+      dequant_rows_any<D, Dp>(kb, v.k_nuq, kcw, n, buf, lut, koff, [&](int t, int ch) {
+        return ksl[(t >= t_split ? D : 0) + ch];
+      });
     }
     if (ko) {
-      const int per_g = D * v.k_n_out;
       __syncthreads();
       for (int gi = 0; gi < ng_chunk; ++gi) {
         for (int i = tid; i < per_g; i += kThreads) {
-          const uint32_t e = ko[(g0 + gi) * per_g + i];
+          const uint32_t e = kol[gi * per_g + i];
           if ((e & 0x7FFFu) == 0) continue;               // +-0: nothing to add
           const int64_t tok = (g0 + gi) * G + (e >> 16);
           if (tok < c0 || tok >= c0 + n) continue;
@@ -432,20 +591,28 @@ decode_ext_kernel(ExtArgs a, const QT* __restrict__ q) {
       }
     }
     __syncthreads();
-    // ---- scores: lane (token tid / 4, quarter tid % 4) sums channels
-    //      quarter, quarter + 4, ... for every head
+    // ---- scores: lane (token tid / 4, quarter qd = tid % 4) sums channels
+    //      16 i + 4 qd .. + 3 for every head
     {
       const int t = tid >> 2, qd = tid & 3;
       float acc[8];
 #pragma unroll
       for (int h = 0; h < 8; ++h) acc[h] = 0.0f;
       if (t < n) {
-#pragma unroll 4
-        for (int j = qd; j < D; j += 4) {
-          const float kv = buf[t * Dp + j];
 #pragma unroll
-          for (int h = 0; h < 8; ++h)
-            if (h < g) acc[h] = __builtin_fmaf(qs[h * D + j], kv, acc[h]);
+        for (int i = 0; i < D / 16; ++i) {
+          const int cc = 16 * i + 4 * qd;
+          const float4v kv = *(const float4v*)&buf[t * Dp + cc];
+#pragma unroll
+          for (int h = 0; h < 8; ++h) {
+            if (h < g) {
+              const float4v qv = *(const float4v*)&qs[h * D + cc];
+              acc[h] = __builtin_fmaf(qv[0], kv[0], acc[h]);
+              acc[h] = __builtin_fmaf(qv[1], kv[1], acc[h]);
+              acc[h] = __builtin_fmaf(qv[2], kv[2], acc[h]);
+              acc[h] = __builtin_fmaf(qv[3], kv[3], acc[h]);
+            }
+          }
         }
       }
 #pragma unroll
@@ -459,7 +626,19 @@ decode_ext_kernel(ExtArgs a, const QT* __restrict__ q) {
       }
     }
     __syncthreads();
-    // ---- online softmax: a wave per head (lane = token)
+    // ---- online softmax: a wave per head (lane = token); with the sketch,
+    //      the weights times gamma times 2^-e, e the exponent of the chunk's
+    //      largest gamma
+    float gsig = 1.0f;
+    if (M) {
+      float gm = lane < n ? gam[lane] : 0.0f;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) gm = fmaxf(gm, __shfl_xor(gm, off));
+      int e = gm > 0.0f ? (int)((__builtin_bit_cast(uint32_t, gm) >> 23) & 0xFF) - 127 : 0;
+      e = e < -100 ? -100 : (e > 100 ? 100 : e);
+      gsig = __builtin_bit_cast(float, (uint32_t)(127 - e) << 23);
+      if (tid == 0) st[24] = __builtin_bit_cast(float, (uint32_t)(127 + e) << 23);
+    }
     for (int h = wave; h < g; h += kThreads / 64) {
       const float x = lane < n ? ps[h * kCT + lane] : -INFINITY;
       float mx = x;
@@ -472,71 +651,146 @@ decode_ext_kernel(ExtArgs a, const QT* __restrict__ q) {
 #pragma unroll
       for (int off = 1; off < 64; off <<= 1) ls += __shfl_xor(ls, off);
       const float alpha = exp2f(m_old - m_new);
-      if (lane < n) ps[h * kCT + lane] = p;
+      ps[h * kCT + lane] = p;
+      if (M) pg[h * kCT + lane] = lane < n ? p * gam[lane] * gsig : 0.0f;
       if (lane == 0) {
         st[h] = m_new;
-        st[g + h] = st[g + h] * alpha + ls;
-        st[2 * g + h] = alpha;
+        st[8 + h] = st[8 + h] * alpha + ls;
+        st[16 + h] = alpha;
       }
     }
-    // ---- values of the chunk (into the key rows: the scores are done)
-    for (int t = t0; t < n; t += TPT) {
-      const uint32_t code = (vcw[t * vw_row + vword] >> vshift) & vmask;
-      const float lvl = v.v_nuq ? lut[16 + code] : (float)code - voff;
-      buf[t * Dp + c] = lvl * vsl[t * ngv + vgrp];
-    }
+    // ---- values of the chunk (into the key rows: the scores are done);
+    //      rows past n are cleared (their weights are 0)
+    dequant_rows_any<D, Dp>(vb, v.v_nuq, vcw, n, buf, lut + 16, voff, [&](int t, int ch) {
+      return vsl[t * ngv + (ch >> gv_shift)];
+    });
+    for (int i = tid; i < (kCT - n) * D; i += kThreads) buf[(n + i / D) * Dp + i % D] = 0.0f;
     if (vo) {
-      const int per_t = ngv * v.v_n_out;
       __syncthreads();
       for (int i = tid; i < n * per_t; i += kThreads) {
         const int t = i / per_t, r = i - t * per_t;
-        const uint32_t e = vo[(c0 + t) * per_t + r];
+        const uint32_t e = vol[i];
         if ((e & 0x7FFFu) == 0) continue;
         const int cc = (r / v.v_n_out) * v.group_ch + (int)(e >> 16);
         buf[t * Dp + cc] += h2f((uint16_t)(e & 0xFFFFu));
       }
     }
     __syncthreads();
-    // ---- weighted sums: channel c of heads t0, t0 + TPT, ...
+    // ---- weighted sums: channel c over this thread's token slice, every
+    //      head (four weights per 16-byte load)
+    {
+      const int tb = t0 * TS;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const int h = t0 + k * TPT;
-      if (h < g) {
-        float acc = o[k] * st[2 * g + h];
-#pragma unroll 8
-        for (int t = 0; t < n; ++t) acc = __builtin_fmaf(ps[h * kCT + t], buf[t * Dp + c], acc);
-        o[k] = acc;
+      for (int h = 0; h < 8; ++h)
+        if (h < g) o[h] *= st[16 + h];
+      if (tb < n) {
+#pragma unroll
+        for (int t = tb; t < tb + TS; t += 4) {
+          const float v0 = buf[t * Dp + c], v1 = buf[(t + 1) * Dp + c];
+          const float v2 = buf[(t + 2) * Dp + c], v3 = buf[(t + 3) * Dp + c];
+#pragma unroll
+          for (int h = 0; h < 8; ++h) {
+            if (h < g) {
+              const float4v w4 = *(const float4v*)&ps[h * kCT + t];
+              o[h] = __builtin_fmaf(w4[0], v0, o[h]);
+              o[h] = __builtin_fmaf(w4[1], v1, o[h]);
+              o[h] = __builtin_fmaf(w4[2], v2, o[h]);
+              o[h] = __builtin_fmaf(w4[3], v3, o[h]);
+            }
+          }
+        }
       }
     }
+    // ---- sketch sums on matrix cores: A = weight limbs (row 2 h + limb,
+    //      8 tokens per lane group), B = +-1 signs of sketch row j = 16 nb +
+    //      column; two 32-token steps per chunk
     if (M) {
+      half8 A[2];
+      const int ah = ln >> 1, limb = ln & 1;
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const int i = tid + k * kThreads;
-        if (i < g * M) {
-          const int h = i / M, j = i - h * M;
-          float acc = z[k] * st[2 * g + h];
-          for (int t = 0; t < n; ++t) {
-            const float w = ps[h * kCT + t] * gam[t];
-            acc += ((skw[t * MW + (j >> 5)] >> (j & 31)) & 1u) ? w : -w;
+      for (int k2 = 0; k2 < 2; ++k2) {
+        float x[8];
+        if (ah < g) {
+          const float4v x0 = *(const float4v*)&pg[ah * kCT + 32 * k2 + 8 * lq];
+          const float4v x1 = *(const float4v*)&pg[ah * kCT + 32 * k2 + 8 * lq + 4];
+          x[0] = x0[0]; x[1] = x0[1]; x[2] = x0[2]; x[3] = x0[3];
+          x[4] = x1[0]; x[5] = x1[1]; x[6] = x1[2]; x[7] = x1[3];
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) x[e] = 0.0f;
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const _Float16 hi = (_Float16)x[e];
+          A[k2][e] = limb ? (_Float16)(x[e] - (float)hi) : hi;
+        }
+      }
+      const float ginv = st[24];
+      float al[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int h = (4 * lq + r) >> 1;
+        al[r] = h < g ? st[16 + h] : 0.0f;
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int nb = wave + 4 * i;
+        if (nb < M / 16) {
+          const int j = 16 * nb + ln;
+          const uint32_t* wrow = skT + (j >> 5) * kCT;
+          const int bit = j & 31;
+          float4v zc = (float4v){0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+          for (int k2 = 0; k2 < 2; ++k2) {
+            const u32x4 w0 = *(const u32x4*)&wrow[32 * k2 + 8 * lq];
+            const u32x4 w1 = *(const u32x4*)&wrow[32 * k2 + 8 * lq + 4];
+            u32x4 bw;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const uint32_t wa = e < 2 ? w0[2 * e] : w1[2 * e - 4];
+              const uint32_t wb = e < 2 ? w0[2 * e + 1] : w1[2 * e - 3];
+              // +1 (0x3C00) where the bit is set, -1 (0xBC00) where clear
+              bw[e] = 0xBC00BC00u ^ (((wa >> bit) & 1u) << 15) ^ (((wb >> bit) & 1u) << 31);
+            }
+            zc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[k2], __builtin_bit_cast(half8, bw), zc,
+                                                         0, 0, 0);
           }
-          z[k] = acc;
+#pragma unroll
+          for (int r = 0; r < 4; ++r) zacc[i][r] = __builtin_fmaf(zacc[i][r], al[r], zc[r] * ginv);
         }
       }
     }
     __syncthreads();
   }
+  // ---- partial record: m, l; o summed over the slices; z from the limb rows
   float* out = a.partials + (((int64_t)b * a.Hq + kvh * g) * a.n_parts + part) * a.rec;
   const int64_t hstride = (int64_t)a.n_parts * a.rec;
   if (tid < g) {
     out[tid * hstride] = st[tid];
-    out[tid * hstride + 1] = st[g + tid];
+    out[tid * hstride + 1] = st[8 + tid];
   }
+  float* red = buf;  // [TPT][8][D]
 #pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    const int h = t0 + k * TPT;
-    if (h < g) out[h * hstride + 2 + c] = o[k];
-    const int i = tid + k * kThreads;
-    if (M && i < g * M) out[(i / M) * hstride + 2 + D + i % M] = z[k];
+  for (int h = 0; h < 8; ++h)
+    if (h < g) red[(t0 * 8 + h) * D + c] = o[h];
+  __syncthreads();
+  for (int h = t0; h < g; h += TPT) {
+    float sum = 0.0f;
+#pragma unroll
+    for (int sl = 0; sl < TPT; ++sl) sum += red[(sl * 8 + h) * D + c];
+    out[h * hstride + 2 + c] = sum;
+  }
+  if (M) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int nb = wave + 4 * i;
+      if (nb < M / 16) {
+        const int j = 16 * nb + ln;
+        const int h0 = 2 * lq, h1 = 2 * lq + 1;
+        if (h0 < g) out[h0 * hstride + 2 + D + j] = zacc[i][0] + zacc[i][1];
+        if (h1 < g) out[h1 * hstride + 2 + D + j] = zacc[i][2] + zacc[i][3];
+      }
+    }
   }
 }
 
@@ -603,12 +857,31 @@ merge_ext_kernel(const float* __restrict__ partials, int D, int M, int n_parts, 
     acc[j] = part_sum[0][j] + part_sum[1][j] + part_sum[2][j] + part_sum[3][j];
   __syncthreads();
   if (M) {
+    // S^T z: thread (d, quarter) sums sketch rows quarter, quarter + 4, ...
+    // (eight loads in flight), the four quarters are added in LDS
     const float c = 1.2533141373155003f / (float)M;   // sqrt(pi/2) / m
-    for (int d = tid; d < D; d += kThreads) {
-      float r = 0.0f;
-      for (int i = 0; i < M; ++i) r = __builtin_fmaf(S[(int64_t)i * D + d], acc[D + i], r);
-      acc[d] = __builtin_fmaf(c, r, acc[d]);
+    float* tq = &part_sum[0][0];                       // [4][kMaxD], free again
+    for (int idx = tid; idx < 4 * D; idx += kThreads) {
+      const int d = idx % D, quarter = idx / D;
+      float r0 = 0.0f, r1 = 0.0f;
+      int i = quarter;
+      for (; i + 28 < M; i += 32) {
+        float sv[8];
+#pragma unroll
+        for (int k = 0; k < 8; ++k) sv[k] = S[(int64_t)(i + 4 * k) * D + d];
+#pragma unroll
+        for (int k = 0; k < 8; k += 2) {
+          r0 = __builtin_fmaf(sv[k], acc[D + i + 4 * k], r0);
+          r1 = __builtin_fmaf(sv[k + 1], acc[D + i + 4 * k + 4], r1);
+        }
+      }
+      for (; i < M; i += 4) r0 = __builtin_fmaf(S[(int64_t)i * D + d], acc[D + i], r0);
+      tq[quarter * kMaxD + d] = r0 + r1;
     }
+    __syncthreads();
+    for (int d = tid; d < D; d += kThreads)
+      acc[d] = __builtin_fmaf(c, tq[d] + tq[kMaxD + d] + tq[2 * kMaxD + d] + tq[3 * kMaxD + d],
+                              acc[d]);
     __syncthreads();
   }
   for (int d = tid; d < D; d += kThreads) acc[d] = acc[d] / L;
@@ -672,19 +945,44 @@ hipError_t launch_quantize_v_qjl(const void* v, int f16, int64_t n_mats, int64_t
 
 size_t ext_decode_lds(const kvq_ext_view& v, int Hq) {
   const int g = Hq / v.kv_heads, D = v.head_dim, M = v.v_qjl ? v.qjl_m : 0;
-  const size_t words = 32 + (size_t)g * D + (size_t)kCT * (D + 4) + (size_t)g * kCT + 3 * (size_t)g +
-                       kCT + 2 * (size_t)D + (size_t)kCT * (D / v.group_ch) + (size_t)kCT * (M / 32) +
-                       (size_t)kCT * words_of(D, v.k_bits) + (size_t)kCT * words_of(D, v.v_bits);
+  const size_t ngv4 = ((size_t)kCT * (D / v.group_ch) + 3) & ~(size_t)3;
+  const size_t words = 32 + (size_t)g * D + (size_t)kCT * (D + kExtPad) + 2 * (size_t)g * kCT +
+                       32 + kCT + 2 * (size_t)D + ngv4 + (size_t)kCT * (M / 32) +
+                       (size_t)kCT * words_of(D, v.k_bits) + (size_t)kCT * words_of(D, v.v_bits) +
+                       2 * (size_t)D * v.k_n_out + (size_t)kCT * (D / v.group_ch) * v.v_n_out;
   return sizeof(float) * words;
 }
 
 // Splits are whole chunks: about 1024 workgroups, at least one chunk each.
-int ext_decode_parts(const kvq_ext_view& v, int n_splits) {
+// Splits per (batch, KV head): one round of the workgroups the compute
+// units hold at once (LDS and registers of the kernel for this view), at
+// most one per 64-token chunk.
+int ext_decode_parts(const kvq_ext_view& v, int Hq, int n_splits) {
   const int64_t chunks = (v.n_tok + kCT - 1) / kCT;
   int64_t p = n_splits;
   if (p <= 0) {
+    static int cus = 0;
+    if (cus == 0) {
+      int dev = 0, n = 0;
+      cus = (hipGetDevice(&dev) == hipSuccess &&
+             hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+             n > 0)
+                ? n
+                : 256;
+    }
+    const size_t lds = ext_decode_lds(v, Hq);
+    const void* fn = v.head_dim == 32   ? (const void*)decode_ext_kernel<uint16_t, 32>
+                     : v.head_dim == 64 ? (const void*)decode_ext_kernel<uint16_t, 64>
+                                        : (const void*)decode_ext_kernel<uint16_t, 128>;
+    int wgs = 0;
+    if ((lds > 64 * 1024 &&
+         hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) !=
+             hipSuccess) ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&wgs, fn, kThreads, lds) != hipSuccess ||
+        wgs < 1)
+      wgs = 1;
     const int64_t streams = (int64_t)v.batch * v.kv_heads;
-    p = (1024 + streams - 1) / streams;
+    p = ((int64_t)cus * wgs) / streams;
   }
   if (p > chunks) p = chunks;
   if (p < 1) p = 1;

@@ -200,7 +200,7 @@ hipError_t launch_quantize_v_qjl(const void* v, int f16, int64_t n_mats, int64_t
                                  float* scales, uint32_t* sketch, float* rnorm, uint32_t* err,
                                  hipStream_t s);
 size_t ext_decode_lds(const kvq_ext_view& v, int Hq);
-int ext_decode_parts(const kvq_ext_view& v, int n_splits);
+int ext_decode_parts(const kvq_ext_view& v, int Hq, int n_splits);
 // Decode over an extended view: partials [B][Hq][n_parts][D + 2 + M], then
 // the merge (with the sketch term and the inverse rotation) into out.
 hipError_t launch_decode_ext(const kvq_ext_view& v, const ExtLut& lk, const ExtLut& lv,
