@@ -304,7 +304,7 @@ def oracle_decode(q, oc, Hkv, sm_scale=None):
     return np.stack(outs)
 
 
-def split_bound(q, oc, Hkv, weight_round, chain, sm_scale=None):
+def split_bound(q, oc, Hkv, weight_round, chain, sm_scale=None, denorm=0.0):
     """Per output row, a bound on |o(n_splits = a) - o(n_splits = b)|_2
     from the arithmetic of the kernels, evaluated on the oracle's K_hat,
     V_hat in float64.
@@ -318,9 +318,14 @@ def split_bound(q, oc, Hkv, weight_round, chain, sm_scale=None):
     most eta / (1 - eta) * sum_t p_t |v_td - o_d| / sum_t p_t.  Float32
     accumulation along a chain of at most `chain` additions (tiles of one
     accumulator, partial merges) adds chain 2^-24 (sum p |v| / sum p + |o|).
-    P' values below the fp16 normal range add an absolute 2^-30 max|v|
-    per token at most.  The difference of two split counts is at most
-    twice the sum.
+    Where P' is one fp16 number, a P' below the fp16 normal range is off by
+    at most 2^-25 in P' units; P' = p v_scale sigma_v / f with the unit's
+    largest scale times sigma_v at least 2^5 (the prescale window's bottom)
+    and |code| v_scale <= max|v|, so a token adds at most
+    2^-25 f qmax v_scale / 2^5 <= 2^-30 f max|v| to a channel: `denorm`
+    = 2^-30 f_max (f_max the largest slot factor of the value operand, 64
+    for 2-bit and 16 for 4-bit values), 0 for float32 weights.  The
+    difference of two split counts is at most twice the sum.
     """
     B, Hq, D = q.shape
     g = Hq // Hkv
@@ -340,7 +345,7 @@ def split_bound(q, oc, Hkv, weight_round, chain, sm_scale=None):
             n = kh.shape[0]
             rows.append(2 * (eta / (1 - eta) * np.linalg.norm(dev) +
                              chain * 2.0 ** -24 * np.linalg.norm(mag) +
-                             n * 2.0 ** -30 * np.abs(vh).max() * np.sqrt(D)))
+                             n * denorm * np.abs(vh).max() * np.sqrt(D)))
     return np.array(rows).reshape(B, Hq)
 
 
@@ -349,12 +354,14 @@ def assert_split_invariance(outs, q, oc, Hkv, n_tok, sm_scale=None):
     the general kernel keeps float32 weights; the general kernel's chain is
     at most the tokens of one partial, the matrix-core one the tiles of one
     wave plus the merges."""
-    for flags, wr, chain in ((kvq.KVQ_DECODE_AUTO, 2.0 ** -11, n_tok // 32 + 64),
-                             (kvq.KVQ_DECODE_GENERIC, 2.0 ** -24, n_tok + 64)):
+    f_max = 64 if oc.cfg.v_bits == 2 else 16
+    for flags, wr, chain, dn in ((kvq.KVQ_DECODE_AUTO, 2.0 ** -11, n_tok // 32 + 64,
+                                  2.0 ** -30 * f_max),
+                                 (kvq.KVQ_DECODE_GENERIC, 2.0 ** -24, n_tok + 64, 0.0)):
         keys = sorted(s for f, s in outs if f == flags)
         if len(keys) < 2:
             continue
-        bound = split_bound(q, oc, Hkv, wr, chain, sm_scale)
+        bound = split_bound(q, oc, Hkv, wr, chain, sm_scale, dn)
         a = outs[(flags, keys[0])]
         for s in keys[1:]:
             diff = np.linalg.norm(outs[(flags, s)] - a, axis=-1)
