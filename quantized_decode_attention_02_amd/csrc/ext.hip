@@ -794,6 +794,497 @@ decode_ext_kernel(ExtArgs a, const QT* __restrict__ q) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Matrix-core form of the extended decode (g * D / Gv <= 16 query-head and
+// value-group columns, g <= 8).  Same workgroup, split and chunk structure
+// as decode_ext_kernel; per 64-token chunk:
+//  - dequant: thread tid decodes its staged code words (key and value rows,
+//    loaded one chunk ahead) field by field into fp16 levels through a
+//    per-kind table of the 2^bits levels (codebook entries, or code - off;
+//    both exact in fp16): keys into rows Lk[t][c], values transposed into
+//    LvT[c][t];
+//  - scores on v_mfma_f32_16x16x32_f16: wave w takes tokens 16 w .. + 15;
+//    A = Q' = q * sm_scale * log2(e) * (key scale of the token's group) *
+//    2^(13 - e_q - e_k) as hi and lo fp16 limbs (rows 2 h + limb, rebuilt
+//    when the wave's group changes), B = the key levels; the key outliers
+//    are added to the scores with LDS atomics (q times the exact value);
+//  - softmax: a wave per head; the value operand P'[h * ngv + grp][t] =
+//    p * v_scale * 2^(14 - e_v) in fp16 (e_v the chunk's largest value-scale
+//    exponent), so P' < 2^15;
+//  - values on v_mfma_f32_16x16x32_f16: wave w takes channel blocks w,
+//    w + 4 (A = LvT rows, B = P'), a fresh accumulator per chunk folded into
+//    the running one as o = o * alpha + o_chunk * 2^(e_v - 14); column
+//    (h, grp) is kept only on the channels of group grp; value outliers go
+//    to an fp32 LDS accumulator (scaled by alpha per chunk) with atomics;
+//  - sketch sums as in decode_ext_kernel.
+// ---------------------------------------------------------------------------
+constexpr int kLkPad = 8;    // halves of padding per fp16 key row
+constexpr int kLvStride = kCT + 8;  // halves per transposed value row and P' row
+
+template <int D>
+struct ExtMLayout {
+  // byte offsets of the LDS arrays (every one 16-byte aligned)
+  int lut, qs, lk, lv, ps, pg, pv, oc, st, gam, ksl, vsl, skT, kol, vol, total;
+  __host__ __device__ ExtMLayout(int g, int ngv, int MW, int per_g, int per_t) {
+    int o = 0;
+    auto take = [&](int bytes) { const int at = o; o += (bytes + 15) & ~15; return at; };
+    lut = take(2 * 256 * 2);
+    qs = take(g * D * 4);
+    lk = take(kCT * (D + kLkPad) * 2);
+    lv = take(D * kLvStride * 2);
+    ps = take(g * kCT * 4);
+    pg = take(g * kCT * 4);
+    pv = take(16 * kLvStride * 2);
+    oc = take(g * D * 4);
+    st = take(32 * 4);
+    gam = take(kCT * 4);
+    ksl = take(2 * D * 4);
+    vsl = take(kCT * ngv * 4);
+    skT = take(MW * kCT * 4);
+    kol = take(2 * per_g * 4);
+    vol = take(kCT * per_t * 4);
+    total = o;
+  }
+};
+
+template <int BITS, int D, typename ST>
+__device__ inline void dequant_word(uint32_t word, int w, const uint16_t* lut, ST store) {
+  constexpr int FPW = 32 / BITS;
+  constexpr uint32_t MASK = (1u << BITS) - 1u;
+#pragma unroll
+  for (int f = 0; f < FPW; ++f)
+    if (w * FPW + f < D) store(w * FPW + f, lut[(word >> (f * BITS)) & MASK]);
+}
+template <int D, typename ST>
+__device__ inline void dequant_word_any(int bits, uint32_t word, int w, const uint16_t* lut,
+                                        ST store) {
+  if (bits == 2) dequant_word<2, D>(word, w, lut, store);
+  else if (bits == 3) dequant_word<3, D>(word, w, lut, store);
+  else if (bits == 4) dequant_word<4, D>(word, w, lut, store);
+  else dequant_word<8, D>(word, w, lut, store);
+}
+
+__device__ inline int fexp(float x) {  // exponent of a positive normal float
+  int e = (int)((__builtin_bit_cast(uint32_t, x) >> 23) & 0xFF) - 127;
+  return e < -100 ? -100 : (e > 100 ? 100 : e);
+}
+__device__ inline float p2(int k) { return __builtin_bit_cast(float, (uint32_t)(127 + k) << 23); }
+
+template <typename QT, int D>
+__global__ void __launch_bounds__(kThreads, 3)
+decode_ext_mfma_kernel(ExtArgs a, const QT* __restrict__ q) {
+  constexpr int KB = D / 32;              // 32-channel blocks of the score contraction
+  constexpr int LkS = D + kLkPad;         // halves per key row
+  extern __shared__ __align__(16) unsigned char smem[];
+  const kvq_ext_view& v = a.v;
+  const int g = a.Hq / v.kv_heads;
+  const int M = v.v_qjl ? v.qjl_m : 0, MW = M / 32;
+  const int kb = v.k_bits, vb = v.v_bits;
+  const int kw_row = words_of(D, kb), vw_row = words_of(D, vb);
+  const int ngv = D / v.group_ch;
+  const int per_g = D * v.k_n_out, per_t = ngv * v.v_n_out;
+  const ExtMLayout<D> L(g, ngv, MW, per_g, per_t);
+  uint16_t* lutK = (uint16_t*)(smem + L.lut);
+  uint16_t* lutV = lutK + 256;
+  float* qs = (float*)(smem + L.qs);
+  uint16_t* Lk = (uint16_t*)(smem + L.lk);
+  uint16_t* LvT = (uint16_t*)(smem + L.lv);
+  float* ps = (float*)(smem + L.ps);
+  float* pg = (float*)(smem + L.pg);
+  uint16_t* Pv = (uint16_t*)(smem + L.pv);
+  float* OC = (float*)(smem + L.oc);
+  float* st = (float*)(smem + L.st);      // m[8], l[8], alpha[8]; [24] 2^e_gamma; [25] 2^(e_v-14)
+  float* gam = (float*)(smem + L.gam);
+  float* ksl = (float*)(smem + L.ksl);
+  float* vsl = (float*)(smem + L.vsl);
+  uint32_t* skT = (uint32_t*)(smem + L.skT);
+  uint32_t* kol = (uint32_t*)(smem + L.kol);
+  uint32_t* vol = (uint32_t*)(smem + L.vol);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lq = lane >> 4, ln = lane & 15;
+  const int part = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  const int64_t s = (int64_t)b * v.kv_heads + kvh;
+  const int64_t N = v.n_tok;
+  const int64_t t_lo = min(N, (int64_t)part * a.per), t_hi = min(N, t_lo + a.per);
+  const int G = v.group_tok;
+
+  // level tables (fp16 bit patterns), queries, state, cleared P' columns and
+  // value-outlier accumulators
+  for (int u = tid; u < 512; u += kThreads) {
+    const bool isk = u < 256;
+    const int uu = u & 255, bits = isk ? kb : vb;
+    float lv = 0.0f;
+    if (uu < (1 << bits)) {
+      const bool nuq = isk ? v.k_nuq : v.v_nuq;
+      lv = nuq ? (isk ? a.lk.lvl[uu] : a.lv.lvl[uu]) : (float)(uu - qmax_of(bits) - 1);
+    }
+    lutK[u] = __builtin_bit_cast(uint16_t, (_Float16)lv);
+  }
+  for (int i = tid; i < g * D; i += kThreads) {
+    qs[i] = ldx(q, ((int64_t)b * a.Hq + kvh * g) * D + i) * a.qscale;
+    OC[i] = 0.0f;
+  }
+  for (int i = tid; i < 16 * kLvStride; i += kThreads) Pv[i] = 0;
+  if (tid < 8) {
+    st[tid] = -INFINITY;
+    st[8 + tid] = 0.0f;
+  }
+  __syncthreads();
+  // largest |q * sm_scale * log2 e| of the workgroup's heads (power of two)
+  int eq;
+  {
+    float mx = 0.0f;
+    for (int i = lane; i < g * D; i += 64) mx = fmaxf(mx, fabsf(qs[i]));
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+    eq = mx > 0.0f ? fexp(mx) : 0;
+  }
+
+  // per-wave state: Q' limbs of the wave's current key group, value and
+  // sketch accumulators
+  half8 qa[KB];
+  int64_t qgrp = -1;
+  float qsc = 0.0f;                        // 2^(e_q + e_k - 13): score units
+  const int nblk = D / 16;                 // 16-channel value blocks
+  float4v ot[2];                           // blocks wave, wave + 4
+#pragma unroll
+  for (int i = 0; i < 2; ++i) ot[i] = (float4v){0.0f, 0.0f, 0.0f, 0.0f};
+  float4v zacc[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) zacc[i] = (float4v){0.0f, 0.0f, 0.0f, 0.0f};
+
+  const uint32_t* kc = v.k_codes + s * v.k_codes_stride;
+  const float* ks = v.k_scales + s * v.k_scales_stride;
+  const uint32_t* ko = v.k_n_out ? v.k_outliers + s * v.k_outliers_stride : nullptr;
+  const uint32_t* vc = v.v_codes + s * v.v_codes_stride;
+  const float* vs = v.v_scales + s * v.v_scales_stride;
+  const uint32_t* vo = v.v_n_out ? v.v_outliers + s * v.v_outliers_stride : nullptr;
+
+  Staged<(D >= 64 ? D / 32 : 1)> st_k, st_v;
+  Staged<1> st_ks, st_gam, st_vs, st_sk, st_ko, st_vo;
+  struct ChunkSrc {
+    const uint32_t *k, *v, *ks, *vs, *sk, *gam, *ko, *vo;
+    int nk, nv, nks, nvs, nsk, ngam, nko, nvo;
+  };
+  auto chunk_src = [&](int64_t c0) {
+    const int n = (int)min((int64_t)kCT, t_hi - c0);
+    const int64_t g0 = c0 / G;
+    const int ng = (c0 - g0 * G + n > G) ? 2 : 1;
+    ChunkSrc cs;
+    cs.k = kc + c0 * kw_row;                       cs.nk = n * kw_row;
+    cs.v = vc + c0 * vw_row;                       cs.nv = n * vw_row;
+    cs.ks = (const uint32_t*)(ks + g0 * D);        cs.nks = ng * D;
+    cs.vs = (const uint32_t*)(vs + c0 * ngv);      cs.nvs = n * ngv;
+    cs.sk = M ? v.v_sketch + s * v.v_sketch_stride + c0 * MW : nullptr;
+    cs.nsk = M ? n * MW : 0;
+    cs.gam = M ? (const uint32_t*)(v.v_rnorm + s * v.v_rnorm_stride + c0) : nullptr;
+    cs.ngam = M ? n : 0;
+    cs.ko = ko ? ko + g0 * per_g : nullptr;        cs.nko = ko ? ng * per_g : 0;
+    cs.vo = vo ? vo + c0 * per_t : nullptr;        cs.nvo = vo ? n * per_t : 0;
+    return cs;
+  };
+  auto stage_load = [&](const ChunkSrc& cs) {
+    st_k.load(cs.k, cs.nk);
+    st_v.load(cs.v, cs.nv);
+    st_ks.load(cs.ks, cs.nks);
+    st_vs.load(cs.vs, cs.nvs);
+    st_sk.load(cs.sk, cs.nsk);
+    st_gam.load(cs.gam, cs.ngam);
+    st_ko.load(cs.ko, cs.nko);
+    st_vo.load(cs.vo, cs.nvo);
+  };
+  auto ident = [](int i) { return i; };
+  ChunkSrc cur = chunk_src(t_lo);
+  if (t_lo < t_hi) stage_load(cur);
+
+  for (int64_t c0 = t_lo; c0 < t_hi; c0 += kCT) {
+    const int n = (int)min((int64_t)kCT, t_hi - c0);
+    const int64_t g0 = c0 / G;
+    const int r0 = (int)(c0 - g0 * G);            // chunk start within its group
+    const int ng_chunk = (r0 + n > G) ? 2 : 1;
+    // ---- dequant this chunk's code words (staged registers, the rest from
+    //      memory) into fp16 levels; the other staged words into LDS; then
+    //      the next chunk's loads
+    {
+      auto kstore = [&](int i, uint32_t word) {
+        const int t = i / kw_row, w = i - t * kw_row;
+        uint16_t* row = Lk + t * LkS;
+        dequant_word_any<D>(kb, word, w, lutK, [&](int ch, uint16_t h) { row[ch] = h; });
+      };
+      auto vstore = [&](int i, uint32_t word) {
+        const int t = i / vw_row, w = i - t * vw_row;
+        dequant_word_any<D>(vb, word, w, lutV,
+                            [&](int ch, uint16_t h) { LvT[ch * kLvStride + t] = h; });
+      };
+      constexpr int CK = D >= 64 ? D / 32 : 1;
+      // one word at a time (unrolling the items would keep every field's
+      // table read in flight at once)
+#pragma unroll 1
+      for (int k = 0; k < CK; ++k) {
+        const int i = tid + kThreads * k;
+        uint32_t wk = 0;
+#pragma unroll
+        for (int k2 = 0; k2 < CK; ++k2)
+          if (k2 == k) wk = st_k.r[k2];
+        if (i < cur.nk) kstore(i, wk);
+      }
+#pragma unroll 1
+      for (int k = 0; k < CK; ++k) {
+        const int i = tid + kThreads * k;
+        uint32_t wv = 0;
+#pragma unroll
+        for (int k2 = 0; k2 < CK; ++k2)
+          if (k2 == k) wv = st_v.r[k2];
+        if (i < cur.nv) vstore(i, wv);
+      }
+      for (int i = tid + kThreads * CK; i < cur.nk; i += kThreads) kstore(i, cur.k[i]);
+      for (int i = tid + kThreads * CK; i < cur.nv; i += kThreads) vstore(i, cur.v[i]);
+      // value columns past n: zero (their weights are 0; LDS may hold NaN)
+      for (int i = tid; i < (kCT - n) * D; i += kThreads)
+        LvT[(i % D) * kLvStride + n + i / D] = 0;
+    }
+    st_ks.store(cur.ks, cur.nks, (uint32_t*)ksl, ident);
+    st_vs.store(cur.vs, cur.nvs, (uint32_t*)vsl, ident);
+    st_sk.store(cur.sk, cur.nsk, skT, [&](int i) { return (i % MW) * kCT + i / MW; });
+    st_gam.store(cur.gam, cur.ngam, (uint32_t*)gam, ident);
+    st_ko.store(cur.ko, cur.nko, kol, ident);
+    st_vo.store(cur.vo, cur.nvo, vol, ident);
+    if (c0 + kCT < t_hi) {
+      cur = chunk_src(c0 + kCT);
+      stage_load(cur);
+    }
+    __syncthreads();
+    // ---- scores: wave w, tokens 16 w .. 16 w + 15
+    if (16 * wave < n) {  // (a partial chunk may leave a wave without tokens)
+      const int tw = 16 * wave;
+      const int gi = (r0 + tw >= G) ? 1 : 0;  // its tokens' group: one per 16 tokens
+      if (g0 + gi != qgrp) {
+        // Q' of the key group: q times the channel's scale times
+        // 2^(13 - e_q - e_k), hi and lo fp16 limbs (row ln = 2 h + limb)
+        qgrp = g0 + gi;
+        const float* kss = ksl + gi * D;
+        float km = 0.0f;
+        for (int c = lane; c < D; c += 64) km = fmaxf(km, kss[c]);
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) km = fmaxf(km, __shfl_xor(km, off));
+        const int ek = km > 0.0f ? fexp(km) : 0;
+        const float sg = p2(13 - eq - ek);
+        qsc = p2(eq + ek - 13);
+        const int h = ln >> 1, limb = ln & 1;
+#pragma unroll
+        for (int k = 0; k < KB; ++k) {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const int c = 32 * k + 8 * lq + e;
+            const float x = h < g ? qs[h * D + c] * kss[c] * sg : 0.0f;
+            const _Float16 hi = (_Float16)x;
+            qa[k][e] = limb ? (_Float16)(x - (float)hi) : hi;
+          }
+        }
+      }
+      float4v acc = (float4v){0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int k = 0; k < KB; ++k) {
+        const half8 kbv = *(const half8*)&Lk[(tw + ln) * LkS + 32 * k + 8 * lq];
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[k], kbv, acc, 0, 0, 0);
+      }
+      // lane (token tw + ln, lq): rows 4 lq .. 4 lq + 3 = heads 2 lq, 2 lq + 1
+      const int t = tw + ln, h0 = 2 * lq;
+      if (t < n) {
+        if (h0 < g) ps[h0 * kCT + t] = (acc[0] + acc[1]) * qsc;
+        if (h0 + 1 < g) ps[(h0 + 1) * kCT + t] = (acc[2] + acc[3]) * qsc;
+      }
+    }
+    if (ko) {
+      // key outliers: q . (exact value) added to the scores
+      __syncthreads();
+      for (int i = tid; i < ng_chunk * per_g; i += kThreads) {
+        const uint32_t e = kol[i];
+        if ((e & 0x7FFFu) == 0) continue;
+        const int gi = i / per_g, c = (i - gi * per_g) / v.k_n_out;
+        const int64_t tok = (g0 + gi) * G + (e >> 16) - c0;
+        if (tok < 0 || tok >= n) continue;
+        const float val = h2f((uint16_t)(e & 0xFFFFu));
+        for (int h = 0; h < g; ++h) atomicAdd(&ps[h * kCT + (int)tok], qs[h * D + c] * val);
+      }
+    }
+    __syncthreads();
+    // ---- online softmax: a wave per head (lane = token); P' for the value
+    //      operand, gamma-weighted weights for the sketch
+    float gsig = 1.0f;
+    if (M) {
+      float gm = lane < n ? gam[lane] : 0.0f;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) gm = fmaxf(gm, __shfl_xor(gm, off));
+      const int e = gm > 0.0f ? fexp(gm) : 0;
+      gsig = p2(-e);
+      if (tid == 0) st[24] = p2(e);
+    }
+    int ev;
+    {
+      float vm = 0.0f;
+      for (int j = 0; j < ngv; ++j) vm = fmaxf(vm, lane < n ? vsl[lane * ngv + j] : 0.0f);
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) vm = fmaxf(vm, __shfl_xor(vm, off));
+      ev = vm > 0.0f ? fexp(vm) : 0;
+    }
+    const float vsig = p2(14 - ev);
+    if (tid == 0) st[25] = p2(ev - 14);
+    for (int h = wave; h < g; h += kThreads / 64) {
+      const float x = lane < n ? ps[h * kCT + lane] : -INFINITY;
+      float mx = x;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+      const float m_old = st[h];
+      const float m_new = fmaxf(m_old, mx);
+      const float p = lane < n ? exp2f(x - m_new) : 0.0f;
+      float ls = p;
+#pragma unroll
+      for (int off = 1; off < 64; off <<= 1) ls += __shfl_xor(ls, off);
+      const float alpha = exp2f(m_old - m_new);
+      ps[h * kCT + lane] = p;
+      if (M) pg[h * kCT + lane] = lane < n ? p * gam[lane] * gsig : 0.0f;
+      for (int j = 0; j < ngv; ++j) {
+        const float pv = lane < n ? p * vsl[lane * ngv + j] * vsig : 0.0f;
+        Pv[(h * ngv + j) * kLvStride + lane] = __builtin_bit_cast(uint16_t, (_Float16)pv);
+      }
+      if (lane == 0) {
+        st[h] = m_new;
+        st[8 + h] = st[8 + h] * alpha + ls;
+        st[16 + h] = alpha;
+      }
+    }
+    __syncthreads();
+    if (vo) {
+      // value outliers: the fp32 side accumulator follows the softmax
+      for (int i = tid; i < g * D; i += kThreads) OC[i] *= st[16 + i / D];
+      __syncthreads();
+      for (int i = tid; i < n * per_t; i += kThreads) {
+        const uint32_t e = vol[i];
+        if ((e & 0x7FFFu) == 0) continue;
+        const int t = i / per_t, r = i - t * per_t;
+        const int cc = (r / v.v_n_out) * v.group_ch + (int)(e >> 16);
+        const float val = h2f((uint16_t)(e & 0xFFFFu));
+        for (int h = 0; h < g; ++h) atomicAdd(&OC[h * D + cc], ps[h * kCT + t] * val);
+      }
+    }
+    // ---- values: channel blocks wave, wave + 4 of 16 channels; columns
+    //      (head, value group); two 32-token steps
+    {
+      const float vun = st[25];
+      const int col = ln;
+      const int hc = col / ngv;
+      const float al = (hc < g) ? st[16 + hc] : 0.0f;
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int jb = wave + 4 * i;
+        if (jb < nblk) {
+          float4v oc = (float4v){0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+          for (int k2 = 0; k2 < 2; ++k2) {
+            const half8 av = *(const half8*)&LvT[(16 * jb + ln) * kLvStride + 32 * k2 + 8 * lq];
+            const half8 bv = *(const half8*)&Pv[col * kLvStride + 32 * k2 + 8 * lq];
+            oc = __builtin_amdgcn_mfma_f32_16x16x32_f16(av, bv, oc, 0, 0, 0);
+          }
+#pragma unroll
+          for (int r = 0; r < 4; ++r) ot[i][r] = __builtin_fmaf(ot[i][r], al, oc[r] * vun);
+        }
+      }
+    }
+    // ---- sketch sums (as in decode_ext_kernel)
+    if (M) {
+      half8 A[2];
+      const int ah = ln >> 1, limb = ln & 1;
+#pragma unroll
+      for (int k2 = 0; k2 < 2; ++k2) {
+        float x[8];
+        if (ah < g) {
+          const float4v x0 = *(const float4v*)&pg[ah * kCT + 32 * k2 + 8 * lq];
+          const float4v x1 = *(const float4v*)&pg[ah * kCT + 32 * k2 + 8 * lq + 4];
+          x[0] = x0[0]; x[1] = x0[1]; x[2] = x0[2]; x[3] = x0[3];
+          x[4] = x1[0]; x[5] = x1[1]; x[6] = x1[2]; x[7] = x1[3];
+        } else {
+#pragma unroll
+          for (int e = 0; e < 8; ++e) x[e] = 0.0f;
+        }
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const _Float16 hi = (_Float16)x[e];
+          A[k2][e] = limb ? (_Float16)(x[e] - (float)hi) : hi;
+        }
+      }
+      const float ginv = st[24];
+      float alr[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int h = (4 * lq + r) >> 1;
+        alr[r] = h < g ? st[16 + h] : 0.0f;
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int nb = wave + 4 * i;
+        if (nb < M / 16) {
+          const int j = 16 * nb + ln;
+          const uint32_t* wrow = skT + (j >> 5) * kCT;
+          const int bit = j & 31;
+          float4v zc = (float4v){0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+          for (int k2 = 0; k2 < 2; ++k2) {
+            const u32x4 w0 = *(const u32x4*)&wrow[32 * k2 + 8 * lq];
+            const u32x4 w1 = *(const u32x4*)&wrow[32 * k2 + 8 * lq + 4];
+            u32x4 bw;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const uint32_t wa = e < 2 ? w0[2 * e] : w1[2 * e - 4];
+              const uint32_t wb = e < 2 ? w0[2 * e + 1] : w1[2 * e - 3];
+              bw[e] = 0xBC00BC00u ^ (((wa >> bit) & 1u) << 15) ^ (((wb >> bit) & 1u) << 31);
+            }
+            zc = __builtin_amdgcn_mfma_f32_16x16x32_f16(A[k2], __builtin_bit_cast(half8, bw), zc,
+                                                         0, 0, 0);
+          }
+#pragma unroll
+          for (int r = 0; r < 4; ++r) zacc[i][r] = __builtin_fmaf(zacc[i][r], alr[r], zc[r] * ginv);
+        }
+      }
+    }
+    __syncthreads();
+  }
+  // ---- partial record: m, l; o (column of the channel's value group) plus
+  //      the outlier accumulator; z from the limb rows
+  float* out = a.partials + (((int64_t)b * a.Hq + kvh * g) * a.n_parts + part) * a.rec;
+  const int64_t hstride = (int64_t)a.n_parts * a.rec;
+  if (tid < g) {
+    out[tid * hstride] = st[tid];
+    out[tid * hstride + 1] = st[8 + tid];
+  }
+  {
+    const int col = ln, hc = col / ngv, gc = col % ngv;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int jb = wave + 4 * i;
+      if (jb < nblk && hc < g) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const int c = 16 * jb + 4 * lq + r;
+          if (c / v.group_ch == gc) out[hc * hstride + 2 + c] = ot[i][r] + OC[hc * D + c];
+        }
+      }
+    }
+  }
+  if (M) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int nb = wave + 4 * i;
+      if (nb < M / 16) {
+        const int j = 16 * nb + ln;
+        const int h0 = 2 * lq, h1 = 2 * lq + 1;
+        if (h0 < g) out[h0 * hstride + 2 + D + j] = zacc[i][0] + zacc[i][1];
+        if (h1 < g) out[h1 * hstride + 2 + D + j] = zacc[i][2] + zacc[i][3];
+      }
+    }
+  }
+}
+
 // out = turn(O + sqrt(pi/2)/m S^T Z) / L over the partials of one (batch,
 // query head): O, Z and L summed with the log-sum-exp weights; turn is the
 // normalized Walsh-Hadamard transform when the values were stored rotated.
@@ -943,14 +1434,50 @@ hipError_t launch_quantize_v_qjl(const void* v, int f16, int64_t n_mats, int64_t
   return hipGetLastError();
 }
 
+// Whether the matrix-core form runs: at most 16 (query head, value group)
+// columns of the value product.
+bool ext_mfma(const kvq_ext_view& v, int Hq) {
+  const int g = Hq / v.kv_heads;
+  return g <= 8 && g * (v.head_dim / v.group_ch) <= 16;
+}
+
 size_t ext_decode_lds(const kvq_ext_view& v, int Hq) {
   const int g = Hq / v.kv_heads, D = v.head_dim, M = v.v_qjl ? v.qjl_m : 0;
+  if (ext_mfma(v, Hq)) {
+    const int ngv = D / v.group_ch, per_g = D * v.k_n_out, per_t = ngv * v.v_n_out;
+    switch (D) {
+      case 32: return (size_t)ExtMLayout<32>(g, ngv, M / 32, per_g, per_t).total;
+      case 64: return (size_t)ExtMLayout<64>(g, ngv, M / 32, per_g, per_t).total;
+      default: return (size_t)ExtMLayout<128>(g, ngv, M / 32, per_g, per_t).total;
+    }
+  }
   const size_t ngv4 = ((size_t)kCT * (D / v.group_ch) + 3) & ~(size_t)3;
   const size_t words = 32 + (size_t)g * D + (size_t)kCT * (D + kExtPad) + 2 * (size_t)g * kCT +
                        32 + kCT + 2 * (size_t)D + ngv4 + (size_t)kCT * (M / 32) +
                        (size_t)kCT * words_of(D, v.k_bits) + (size_t)kCT * words_of(D, v.v_bits) +
                        2 * (size_t)D * v.k_n_out + (size_t)kCT * (D / v.group_ch) * v.v_n_out;
   return sizeof(float) * words;
+}
+
+const void* ext_kernel_fn(const kvq_ext_view& v, int Hq, bool f16) {
+  const bool m = ext_mfma(v, Hq);
+  switch (v.head_dim) {
+    case 32:
+      return m ? (f16 ? (const void*)decode_ext_mfma_kernel<uint16_t, 32>
+                      : (const void*)decode_ext_mfma_kernel<float, 32>)
+               : (f16 ? (const void*)decode_ext_kernel<uint16_t, 32>
+                      : (const void*)decode_ext_kernel<float, 32>);
+    case 64:
+      return m ? (f16 ? (const void*)decode_ext_mfma_kernel<uint16_t, 64>
+                      : (const void*)decode_ext_mfma_kernel<float, 64>)
+               : (f16 ? (const void*)decode_ext_kernel<uint16_t, 64>
+                      : (const void*)decode_ext_kernel<float, 64>);
+    default:
+      return m ? (f16 ? (const void*)decode_ext_mfma_kernel<uint16_t, 128>
+                      : (const void*)decode_ext_mfma_kernel<float, 128>)
+               : (f16 ? (const void*)decode_ext_kernel<uint16_t, 128>
+                      : (const void*)decode_ext_kernel<float, 128>);
+  }
 }
 
 // Splits are whole chunks: about 1024 workgroups, at least one chunk each.
@@ -971,9 +1498,7 @@ int ext_decode_parts(const kvq_ext_view& v, int Hq, int n_splits) {
                 : 256;
     }
     const size_t lds = ext_decode_lds(v, Hq);
-    const void* fn = v.head_dim == 32   ? (const void*)decode_ext_kernel<uint16_t, 32>
-                     : v.head_dim == 64 ? (const void*)decode_ext_kernel<uint16_t, 64>
-                                        : (const void*)decode_ext_kernel<uint16_t, 128>;
+    const void* fn = ext_kernel_fn(v, Hq, true);
     int wgs = 0;
     if ((lds > 64 * 1024 &&
          hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds) !=
@@ -990,20 +1515,15 @@ int ext_decode_parts(const kvq_ext_view& v, int Hq, int n_splits) {
   return (int)p;
 }
 
-template <int D>
-hipError_t launch_decode_ext_d(const ExtArgs& a, const void* q, int f16, dim3 grid, size_t lds,
+hipError_t launch_decode_ext_k(const ExtArgs& a, const void* q, int f16, dim3 grid, size_t lds,
                                hipStream_t s) {
-  const void* fn = f16 ? (const void*)decode_ext_kernel<uint16_t, D>
-                       : (const void*)decode_ext_kernel<float, D>;
+  const void* fn = ext_kernel_fn(a.v, a.Hq, f16 != 0);
   if (lds > 64 * 1024) {
     hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
   }
-  if (f16)
-    decode_ext_kernel<uint16_t, D><<<grid, kThreads, lds, s>>>(a, (const uint16_t*)q);
-  else
-    decode_ext_kernel<float, D><<<grid, kThreads, lds, s>>>(a, (const float*)q);
-  return hipGetLastError();
+  void* args[] = {(void*)&a, (void*)&q};
+  return hipLaunchKernel(fn, grid, dim3(kThreads), args, lds, s);
 }
 
 hipError_t launch_decode_ext(const kvq_ext_view& v, const ExtLut& lk, const ExtLut& lv,
@@ -1016,12 +1536,8 @@ hipError_t launch_decode_ext(const kvq_ext_view& v, const ExtLut& lk, const ExtL
   const size_t lds = ext_decode_lds(v, Hq);
   dim3 grid((unsigned)n_parts, (unsigned)v.kv_heads, (unsigned)v.batch);
   hipError_t e;
-  switch (v.head_dim) {
-    case 32: e = launch_decode_ext_d<32>(a, q, f16, grid, lds, s); break;
-    case 64: e = launch_decode_ext_d<64>(a, q, f16, grid, lds, s); break;
-    case 128: e = launch_decode_ext_d<128>(a, q, f16, grid, lds, s); break;
-    default: return hipErrorInvalidValue;
-  }
+  if (v.head_dim != 32 && v.head_dim != 64 && v.head_dim != 128) return hipErrorInvalidValue;
+  e = launch_decode_ext_k(a, q, f16, grid, lds, s);
   if (e != hipSuccess) return e;
   merge_ext_kernel<<<dim3((unsigned)(v.batch * Hq)), kThreads, sizeof(float) * (size_t)n_parts, s>>>(
       partials, v.head_dim, M, n_parts, a.rec, v.jl, v.v_rotated, out);

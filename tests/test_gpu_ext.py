@@ -147,6 +147,11 @@ EXT_CASES = {
     "sym_k4_qjl_v3": (1, 8, 2, 900, 128, ("sym", 4, 128), ("qjl", 3, 32, 128)),
     "sym_k4_qjl_v2_m64": (2, 4, 2, 500, 64, ("sym", 4, 64), ("qjl", 2, 64, 64)),
     "nuq_k_qjl_v": (1, 4, 1, 640, 128, ("nuq", 3, 128, 1), ("qjl", 3, 128, 128)),
+    # 8-bit symmetric keys (a 256-entry level table), D = 32, value outliers
+    # in groups of 8 channels
+    "sym_k8_d32_nuq_v4": (1, 6, 2, 450, 32, ("sym", 8, 32), ("nuq", 4, 8, 1)),
+    # g * D / Gv = 32 columns: the vector-ALU form of the decode
+    "valu_g8_gv32": (1, 16, 2, 500, 128, ("nuq", 3, 64, 1), ("nuq", 3, 32, 1)),
 }
 
 
