@@ -41,6 +41,39 @@ typedef float float4v __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ inline float h2f(uint16_t u) { return (float)__builtin_bit_cast(_Float16, u); }
+
+// Wave-wide max and sum: four DPP row rotations (8, 4, 2, 1 lanes) leave
+// every lane of a 16-lane row with its row's result; the four rows are
+// combined through readlane (a few cycles each, against the LDS round trip
+// of a shuffle per step).
+template <int CTRL>
+__device__ inline float dppf(float x) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+__device__ inline float rdl(float x, int l) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), l));
+}
+__device__ inline float wave_max64(float x) {
+  x = fmaxf(x, dppf<0x128>(x));
+  x = fmaxf(x, dppf<0x124>(x));
+  x = fmaxf(x, dppf<0x122>(x));
+  x = fmaxf(x, dppf<0x121>(x));
+  return fmaxf(fmaxf(rdl(x, 0), rdl(x, 16)), fmaxf(rdl(x, 32), rdl(x, 48)));
+}
+__device__ inline float wave_sum64(float x) {
+  x += dppf<0x128>(x);
+  x += dppf<0x124>(x);
+  x += dppf<0x122>(x);
+  x += dppf<0x121>(x);
+  return (rdl(x, 0) + rdl(x, 16)) + (rdl(x, 32) + rdl(x, 48));
+}
+// Sum over the four lanes of a quad (DPP quad permutations).
+__device__ inline float quad_sum(float x) {
+  x += dppf<0xB1>(x);  // quad_perm [1, 0, 3, 2]
+  x += dppf<0x4E>(x);  // quad_perm [2, 3, 0, 1]
+  return x;
+}
 __device__ inline bool f16_finite(uint16_t u) { return (u & 0x7C00u) != 0x7C00u; }
 
 // Level index of q: the number of midpoints strictly below q (a midpoint
@@ -619,8 +652,7 @@ decode_ext_kernel(ExtArgs a, const QT* __restrict__ q) {
       for (int h = 0; h < 8; ++h) {
         if (h < g) {
           float x = acc[h];
-          x += __shfl_xor(x, 1);
-          x += __shfl_xor(x, 2);
+          x = quad_sum(x);
           if (qd == 0 && t < n) ps[h * kCT + t] = x;
         }
       }
@@ -632,8 +664,7 @@ decode_ext_kernel(ExtArgs a, const QT* __restrict__ q) {
     float gsig = 1.0f;
     if (M) {
       float gm = lane < n ? gam[lane] : 0.0f;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) gm = fmaxf(gm, __shfl_xor(gm, off));
+      gm = wave_max64(gm);
       int e = gm > 0.0f ? (int)((__builtin_bit_cast(uint32_t, gm) >> 23) & 0xFF) - 127 : 0;
       e = e < -100 ? -100 : (e > 100 ? 100 : e);
       gsig = __builtin_bit_cast(float, (uint32_t)(127 - e) << 23);
@@ -642,14 +673,12 @@ decode_ext_kernel(ExtArgs a, const QT* __restrict__ q) {
     for (int h = wave; h < g; h += kThreads / 64) {
       const float x = lane < n ? ps[h * kCT + lane] : -INFINITY;
       float mx = x;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+      mx = wave_max64(mx);
       const float m_old = st[h];
       const float m_new = fmaxf(m_old, mx);
       const float p = lane < n ? exp2f(x - m_new) : 0.0f;
       float ls = p;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) ls += __shfl_xor(ls, off);
+      ls = wave_sum64(ls);
       const float alpha = exp2f(m_old - m_new);
       ps[h * kCT + lane] = p;
       if (M) pg[h * kCT + lane] = lane < n ? p * gam[lane] * gsig : 0.0f;
@@ -824,7 +853,7 @@ constexpr int kLvStride = kCT + 8;  // halves per transposed value row and P' ro
 template <int D>
 struct ExtMLayout {
   // byte offsets of the LDS arrays (every one 16-byte aligned)
-  int lut, qs, lk, lv, ps, pg, pv, oc, st, gam, ksl, vsl, skT, kol, vol, total;
+  int lut, qs, lk, lv, ps, pg, pv, oc, corr, st, gam, ksl, vsl, skT, vol, total;
   __host__ __device__ ExtMLayout(int g, int ngv, int MW, int per_g, int per_t) {
     int o = 0;
     auto take = [&](int bytes) { const int at = o; o += (bytes + 15) & ~15; return at; };
@@ -836,12 +865,12 @@ struct ExtMLayout {
     pg = take(g * kCT * 4);
     pv = take(16 * kLvStride * 2);
     oc = take(g * D * 4);
+    corr = take(g * kCT * 4);
     st = take(32 * 4);
     gam = take(kCT * 4);
     ksl = take(2 * D * 4);
     vsl = take(kCT * ngv * 4);
     skT = take(MW * kCT * 4);
-    kol = take(2 * per_g * 4);
     vol = take(kCT * per_t * 4);
     total = o;
   }
@@ -898,8 +927,8 @@ decode_ext_mfma_kernel(ExtArgs a, const QT* __restrict__ q) {
   float* ksl = (float*)(smem + L.ksl);
   float* vsl = (float*)(smem + L.vsl);
   uint32_t* skT = (uint32_t*)(smem + L.skT);
-  uint32_t* kol = (uint32_t*)(smem + L.kol);
   uint32_t* vol = (uint32_t*)(smem + L.vol);
+  float* corr = (float*)(smem + L.corr);  // [g][kCT] key-outlier score terms
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int lq = lane >> 4, ln = lane & 15;
   const int part = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
@@ -925,6 +954,7 @@ decode_ext_mfma_kernel(ExtArgs a, const QT* __restrict__ q) {
     OC[i] = 0.0f;
   }
   for (int i = tid; i < 16 * kLvStride; i += kThreads) Pv[i] = 0;
+  for (int i = tid; i < g * kCT; i += kThreads) corr[i] = 0.0f;
   if (tid < 8) {
     st[tid] = -INFINITY;
     st[8 + tid] = 0.0f;
@@ -935,8 +965,7 @@ decode_ext_mfma_kernel(ExtArgs a, const QT* __restrict__ q) {
   {
     float mx = 0.0f;
     for (int i = lane; i < g * D; i += 64) mx = fmaxf(mx, fabsf(qs[i]));
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+    mx = wave_max64(mx);
     eq = mx > 0.0f ? fexp(mx) : 0;
   }
 
@@ -1047,8 +1076,17 @@ decode_ext_mfma_kernel(ExtArgs a, const QT* __restrict__ q) {
     st_vs.store(cur.vs, cur.nvs, (uint32_t*)vsl, ident);
     st_sk.store(cur.sk, cur.nsk, skT, [&](int i) { return (i % MW) * kCT + i / MW; });
     st_gam.store(cur.gam, cur.ngam, (uint32_t*)gam, ident);
-    st_ko.store(cur.ko, cur.nko, kol, ident);
     st_vo.store(cur.vo, cur.nvo, vol, ident);
+    // key outliers: q . (exact value) into the score terms of their tokens
+    for (int i = tid; i < cur.nko; i += kThreads) {
+      const uint32_t e = i < kThreads ? st_ko.r[0] : cur.ko[i];
+      if ((e & 0x7FFFu) == 0) continue;
+      const int gi = i / per_g, c = (i - gi * per_g) / v.k_n_out;
+      const int64_t tok = (g0 + gi) * G + (e >> 16) - c0;
+      if (tok < 0 || tok >= n) continue;
+      const float val = h2f((uint16_t)(e & 0xFFFFu));
+      for (int h = 0; h < g; ++h) atomicAdd(&corr[h * kCT + (int)tok], qs[h * D + c] * val);
+    }
     if (c0 + kCT < t_hi) {
       cur = chunk_src(c0 + kCT);
       stage_load(cur);
@@ -1065,8 +1103,7 @@ decode_ext_mfma_kernel(ExtArgs a, const QT* __restrict__ q) {
         const float* kss = ksl + gi * D;
         float km = 0.0f;
         for (int c = lane; c < D; c += 64) km = fmaxf(km, kss[c]);
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) km = fmaxf(km, __shfl_xor(km, off));
+        km = wave_max64(km);
         const int ek = km > 0.0f ? fexp(km) : 0;
         const float sg = p2(13 - eq - ek);
         qsc = p2(eq + ek - 13);
@@ -1091,21 +1128,15 @@ decode_ext_mfma_kernel(ExtArgs a, const QT* __restrict__ q) {
       // lane (token tw + ln, lq): rows 4 lq .. 4 lq + 3 = heads 2 lq, 2 lq + 1
       const int t = tw + ln, h0 = 2 * lq;
       if (t < n) {
-        if (h0 < g) ps[h0 * kCT + t] = (acc[0] + acc[1]) * qsc;
-        if (h0 + 1 < g) ps[(h0 + 1) * kCT + t] = (acc[2] + acc[3]) * qsc;
-      }
-    }
-    if (ko) {
-      // key outliers: q . (exact value) added to the scores
-      __syncthreads();
-      for (int i = tid; i < ng_chunk * per_g; i += kThreads) {
-        const uint32_t e = kol[i];
-        if ((e & 0x7FFFu) == 0) continue;
-        const int gi = i / per_g, c = (i - gi * per_g) / v.k_n_out;
-        const int64_t tok = (g0 + gi) * G + (e >> 16) - c0;
-        if (tok < 0 || tok >= n) continue;
-        const float val = h2f((uint16_t)(e & 0xFFFFu));
-        for (int h = 0; h < g; ++h) atomicAdd(&ps[h * kCT + (int)tok], qs[h * D + c] * val);
+        // the outlier terms of this chunk are consumed and cleared here
+        if (h0 < g) {
+          ps[h0 * kCT + t] = (acc[0] + acc[1]) * qsc + corr[h0 * kCT + t];
+          corr[h0 * kCT + t] = 0.0f;
+        }
+        if (h0 + 1 < g) {
+          ps[(h0 + 1) * kCT + t] = (acc[2] + acc[3]) * qsc + corr[(h0 + 1) * kCT + t];
+          corr[(h0 + 1) * kCT + t] = 0.0f;
+        }
       }
     }
     __syncthreads();
@@ -1114,8 +1145,7 @@ decode_ext_mfma_kernel(ExtArgs a, const QT* __restrict__ q) {
     float gsig = 1.0f;
     if (M) {
       float gm = lane < n ? gam[lane] : 0.0f;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) gm = fmaxf(gm, __shfl_xor(gm, off));
+      gm = wave_max64(gm);
       const int e = gm > 0.0f ? fexp(gm) : 0;
       gsig = p2(-e);
       if (tid == 0) st[24] = p2(e);
@@ -1124,8 +1154,7 @@ decode_ext_mfma_kernel(ExtArgs a, const QT* __restrict__ q) {
     {
       float vm = 0.0f;
       for (int j = 0; j < ngv; ++j) vm = fmaxf(vm, lane < n ? vsl[lane * ngv + j] : 0.0f);
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) vm = fmaxf(vm, __shfl_xor(vm, off));
+      vm = wave_max64(vm);
       ev = vm > 0.0f ? fexp(vm) : 0;
     }
     const float vsig = p2(14 - ev);
@@ -1133,14 +1162,12 @@ decode_ext_mfma_kernel(ExtArgs a, const QT* __restrict__ q) {
     for (int h = wave; h < g; h += kThreads / 64) {
       const float x = lane < n ? ps[h * kCT + lane] : -INFINITY;
       float mx = x;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+      mx = wave_max64(mx);
       const float m_old = st[h];
       const float m_new = fmaxf(m_old, mx);
       const float p = lane < n ? exp2f(x - m_new) : 0.0f;
       float ls = p;
-#pragma unroll
-      for (int off = 1; off < 64; off <<= 1) ls += __shfl_xor(ls, off);
+      ls = wave_sum64(ls);
       const float alpha = exp2f(m_old - m_new);
       ps[h * kCT + lane] = p;
       if (M) pg[h * kCT + lane] = lane < n ? p * gam[lane] * gsig : 0.0f;
@@ -1148,6 +1175,8 @@ decode_ext_mfma_kernel(ExtArgs a, const QT* __restrict__ q) {
         const float pv = lane < n ? p * vsl[lane * ngv + j] * vsig : 0.0f;
         Pv[(h * ngv + j) * kLvStride + lane] = __builtin_bit_cast(uint16_t, (_Float16)pv);
       }
+      if (vo)  // the value-outlier side accumulator follows the softmax
+        for (int c = lane; c < D; c += 64) OC[h * D + c] *= alpha;
       if (lane == 0) {
         st[h] = m_new;
         st[8 + h] = st[8 + h] * alpha + ls;
@@ -1156,9 +1185,6 @@ decode_ext_mfma_kernel(ExtArgs a, const QT* __restrict__ q) {
     }
     __syncthreads();
     if (vo) {
-      // value outliers: the fp32 side accumulator follows the softmax
-      for (int i = tid; i < g * D; i += kThreads) OC[i] *= st[16 + i / D];
-      __syncthreads();
       for (int i = tid; i < n * per_t; i += kThreads) {
         const uint32_t e = vol[i];
         if ((e & 0x7FFFu) == 0) continue;
@@ -1300,8 +1326,7 @@ merge_ext_kernel(const float* __restrict__ partials, int D, int M, int n_parts, 
   float mx = -INFINITY;
   for (int i = tid; i < n_parts; i += kThreads)
     if (p[(int64_t)i * rec + 1] > 0.0f) mx = fmaxf(mx, p[(int64_t)i * rec]);
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+  mx = wave_max64(mx);
   if (lane == 0) red[wave] = mx;
   __syncthreads();
   const float Mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
@@ -1313,8 +1338,7 @@ merge_ext_kernel(const float* __restrict__ partials, int D, int M, int n_parts, 
     wts[i] = w;
     L += w * l;
   }
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) L += __shfl_xor(L, off);
+  L = wave_sum64(L);
   if (lane == 0) red[wave] = L;
   __syncthreads();
   L = red[0] + red[1] + red[2] + red[3];
