@@ -849,6 +849,50 @@ decode_ext_kernel(ExtArgs a, const QT* __restrict__ q) {
 // ---------------------------------------------------------------------------
 constexpr int kLkPad = 8;    // halves of padding per fp16 key row
 constexpr int kLvStride = kCT + 8;  // halves per transposed value row and P' row
+constexpr int kLvSpare = 8;  // spare channel rows past D of the transposed values
+
+// Dequantize a chunk's code words to fp16 levels through the table: word i
+// is token i / WR, word i % WR; keys land as rows (D + kLkPad halves per
+// token), values transposed (kLvStride halves per channel).  The first CK
+// words of each thread come from registers, the rest from memory.  A row's
+// last word may hold unused fields past D (3-bit codes); their levels land
+// in the key row's padding or in the spare channel rows, which no operand
+// reads, so no field needs a bounds test.
+template <int BITS, int D, int CK, bool TR>
+__device__ inline void deq_chunk(const uint32_t (&r)[CK], const uint32_t* src, int cnt,
+                                 const uint16_t* lut, uint16_t* dst) {
+  constexpr int FPW = 32 / BITS, WR = (D + FPW - 1) / FPW;
+  constexpr uint32_t MASK = (1u << BITS) - 1u;
+  static_assert(WR * FPW - D <= (TR ? kLvSpare : kLkPad), "fields past D must fit the padding");
+  auto one = [&](int i, uint32_t word) {
+    const int t = i / WR, w = i - t * WR;
+    uint16_t* o = TR ? dst + w * FPW * kLvStride + t : dst + t * (D + kLkPad) + w * FPW;
+#pragma unroll
+    for (int f = 0; f < FPW; ++f) o[TR ? f * kLvStride : f] = lut[(word >> (f * BITS)) & MASK];
+  };
+  // one word at a time (unrolled, every field's table read would be in
+  // flight at once)
+#pragma unroll 1
+  for (int k = 0; k < CK; ++k) {
+    uint32_t wk = 0;
+#pragma unroll
+    for (int k2 = 0; k2 < CK; ++k2)
+      if (k2 == k) wk = r[k2];
+    const int i = threadIdx.x + kThreads * k;
+    if (i < cnt) one(i, wk);
+  }
+  for (int i = threadIdx.x + kThreads * CK; i < cnt; i += kThreads) one(i, src[i]);
+}
+template <int D, int CK, bool TR>
+__device__ inline void deq_chunk_any(int bits, const uint32_t (&r)[CK], const uint32_t* src,
+                                     int cnt, const uint16_t* lut, uint16_t* dst) {
+  switch (bits) {
+    case 2: deq_chunk<2, D, CK, TR>(r, src, cnt, lut, dst); break;
+    case 3: deq_chunk<3, D, CK, TR>(r, src, cnt, lut, dst); break;
+    case 4: deq_chunk<4, D, CK, TR>(r, src, cnt, lut, dst); break;
+    default: deq_chunk<8, D, CK, TR>(r, src, cnt, lut, dst); break;
+  }
+}
 
 template <int D>
 struct ExtMLayout {
@@ -860,7 +904,7 @@ struct ExtMLayout {
     lut = take(2 * 256 * 2);
     qs = take(g * D * 4);
     lk = take(kCT * (D + kLkPad) * 2);
-    lv = take(D * kLvStride * 2);
+    lv = take((D + kLvSpare) * kLvStride * 2);
     ps = take(g * kCT * 4);
     pg = take(g * kCT * 4);
     pv = take(16 * kLvStride * 2);
@@ -875,23 +919,6 @@ struct ExtMLayout {
     total = o;
   }
 };
-
-template <int BITS, int D, typename ST>
-__device__ inline void dequant_word(uint32_t word, int w, const uint16_t* lut, ST store) {
-  constexpr int FPW = 32 / BITS;
-  constexpr uint32_t MASK = (1u << BITS) - 1u;
-#pragma unroll
-  for (int f = 0; f < FPW; ++f)
-    if (w * FPW + f < D) store(w * FPW + f, lut[(word >> (f * BITS)) & MASK]);
-}
-template <int D, typename ST>
-__device__ inline void dequant_word_any(int bits, uint32_t word, int w, const uint16_t* lut,
-                                        ST store) {
-  if (bits == 2) dequant_word<2, D>(word, w, lut, store);
-  else if (bits == 3) dequant_word<3, D>(word, w, lut, store);
-  else if (bits == 4) dequant_word<4, D>(word, w, lut, store);
-  else dequant_word<8, D>(word, w, lut, store);
-}
 
 __device__ inline int fexp(float x) {  // exponent of a positive normal float
   int e = (int)((__builtin_bit_cast(uint32_t, x) >> 23) & 0xFF) - 127;
@@ -1035,39 +1062,9 @@ decode_ext_mfma_kernel(ExtArgs a, const QT* __restrict__ q) {
     //      memory) into fp16 levels; the other staged words into LDS; then
     //      the next chunk's loads
     {
-      auto kstore = [&](int i, uint32_t word) {
-        const int t = i / kw_row, w = i - t * kw_row;
-        uint16_t* row = Lk + t * LkS;
-        dequant_word_any<D>(kb, word, w, lutK, [&](int ch, uint16_t h) { row[ch] = h; });
-      };
-      auto vstore = [&](int i, uint32_t word) {
-        const int t = i / vw_row, w = i - t * vw_row;
-        dequant_word_any<D>(vb, word, w, lutV,
-                            [&](int ch, uint16_t h) { LvT[ch * kLvStride + t] = h; });
-      };
       constexpr int CK = D >= 64 ? D / 32 : 1;
-      // one word at a time (unrolling the items would keep every field's
-      // table read in flight at once)
-#pragma unroll 1
-      for (int k = 0; k < CK; ++k) {
-        const int i = tid + kThreads * k;
-        uint32_t wk = 0;
-#pragma unroll
-        for (int k2 = 0; k2 < CK; ++k2)
-          if (k2 == k) wk = st_k.r[k2];
-        if (i < cur.nk) kstore(i, wk);
-      }
-#pragma unroll 1
-      for (int k = 0; k < CK; ++k) {
-        const int i = tid + kThreads * k;
-        uint32_t wv = 0;
-#pragma unroll
-        for (int k2 = 0; k2 < CK; ++k2)
-          if (k2 == k) wv = st_v.r[k2];
-        if (i < cur.nv) vstore(i, wv);
-      }
-      for (int i = tid + kThreads * CK; i < cur.nk; i += kThreads) kstore(i, cur.k[i]);
-      for (int i = tid + kThreads * CK; i < cur.nv; i += kThreads) vstore(i, cur.v[i]);
+      deq_chunk_any<D, CK, false>(kb, st_k.r, cur.k, cur.nk, lutK, Lk);
+      deq_chunk_any<D, CK, true>(vb, st_v.r, cur.v, cur.nv, lutV, LvT);
       // value columns past n: zero (their weights are 0; LDS may hold NaN)
       for (int i = tid; i < (kCT - n) * D; i += kThreads)
         LvT[(i % D) * kLvStride + n + i / D] = 0;
