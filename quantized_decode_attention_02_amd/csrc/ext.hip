@@ -552,10 +552,12 @@ decode_ext_kernel(ExtArgs a, const QT* __restrict__ q) {
     const uint32_t *k, *v, *ks, *vs, *sk, *gam, *ko, *vo;
     int nk, nv, nks, nvs, nsk, ngam, nko, nvo;
   };
-  auto chunk_src = [&](int64_t c0) {
+  // chunk c0 starts at token r0 of key group g0 (chunks start at multiples
+  // of 64 and G is a multiple of 32, so a chunk spans at most two groups;
+  // g0 and r0 are carried from chunk to chunk instead of divided out)
+  auto chunk_src = [&](int64_t c0, int64_t g0, int r0) {
     const int n = (int)min((int64_t)kCT, t_hi - c0);
-    const int64_t g0 = c0 / G;
-    const int ng = (c0 - g0 * G + n > G) ? 2 : 1;
+    const int ng = (r0 + n > G) ? 2 : 1;
     ChunkSrc cs;
     cs.k = kc + c0 * kw_row;                       cs.nk = n * kw_row;
     cs.v = vc + c0 * vw_row;                       cs.nv = n * vw_row;
@@ -580,13 +582,20 @@ decode_ext_kernel(ExtArgs a, const QT* __restrict__ q) {
     st_vo.load(cs.vo, cs.nvo);
   };
   auto ident = [](int i) { return i; };
-  ChunkSrc cur = chunk_src(t_lo);
+  int64_t g_cur = t_lo / G;
+  int r_cur = (int)(t_lo - g_cur * G);
+  ChunkSrc cur = chunk_src(t_lo, g_cur, r_cur);
   if (t_lo < t_hi) stage_load(cur);
 
   for (int64_t c0 = t_lo; c0 < t_hi; c0 += kCT) {
     const int n = (int)min((int64_t)kCT, t_hi - c0);
-    const int64_t g0 = c0 / G;
-    const int r0 = (int)(c0 - g0 * G);            // chunk start within its group
+    const int64_t g0 = g_cur;
+    const int r0 = r_cur;                          // chunk start within its group
+    r_cur += kCT;
+    while (r_cur >= G) {
+      r_cur -= G;
+      ++g_cur;
+    }
     const int ng_chunk = (r0 + n > G) ? 2 : 1;
     // ---- this chunk's words into LDS (sketch words transposed to
     //      word-major), then the next chunk's loads
@@ -599,7 +608,7 @@ decode_ext_kernel(ExtArgs a, const QT* __restrict__ q) {
     st_ko.store(cur.ko, cur.nko, kol, ident);
     st_vo.store(cur.vo, cur.nvo, vol, ident);
     if (c0 + kCT < t_hi) {
-      cur = chunk_src(c0 + kCT);
+      cur = chunk_src(c0 + kCT, g_cur, r_cur);
       stage_load(cur);
     }
     __syncthreads();
@@ -1022,10 +1031,12 @@ decode_ext_mfma_kernel(ExtArgs a, const QT* __restrict__ q) {
     const uint32_t *k, *v, *ks, *vs, *sk, *gam, *ko, *vo;
     int nk, nv, nks, nvs, nsk, ngam, nko, nvo;
   };
-  auto chunk_src = [&](int64_t c0) {
+  // chunk c0 starts at token r0 of key group g0 (chunks start at multiples
+  // of 64 and G is a multiple of 32, so a chunk spans at most two groups;
+  // g0 and r0 are carried from chunk to chunk instead of divided out)
+  auto chunk_src = [&](int64_t c0, int64_t g0, int r0) {
     const int n = (int)min((int64_t)kCT, t_hi - c0);
-    const int64_t g0 = c0 / G;
-    const int ng = (c0 - g0 * G + n > G) ? 2 : 1;
+    const int ng = (r0 + n > G) ? 2 : 1;
     ChunkSrc cs;
     cs.k = kc + c0 * kw_row;                       cs.nk = n * kw_row;
     cs.v = vc + c0 * vw_row;                       cs.nv = n * vw_row;
@@ -1050,13 +1061,20 @@ decode_ext_mfma_kernel(ExtArgs a, const QT* __restrict__ q) {
     st_vo.load(cs.vo, cs.nvo);
   };
   auto ident = [](int i) { return i; };
-  ChunkSrc cur = chunk_src(t_lo);
+  int64_t g_cur = t_lo / G;
+  int r_cur = (int)(t_lo - g_cur * G);
+  ChunkSrc cur = chunk_src(t_lo, g_cur, r_cur);
   if (t_lo < t_hi) stage_load(cur);
 
   for (int64_t c0 = t_lo; c0 < t_hi; c0 += kCT) {
     const int n = (int)min((int64_t)kCT, t_hi - c0);
-    const int64_t g0 = c0 / G;
-    const int r0 = (int)(c0 - g0 * G);            // chunk start within its group
+    const int64_t g0 = g_cur;
+    const int r0 = r_cur;                          // chunk start within its group
+    r_cur += kCT;
+    while (r_cur >= G) {
+      r_cur -= G;
+      ++g_cur;
+    }
     const int ng_chunk = (r0 + n > G) ? 2 : 1;
     // ---- dequant this chunk's code words (staged registers, the rest from
     //      memory) into fp16 levels; the other staged words into LDS; then
@@ -1085,7 +1103,7 @@ decode_ext_mfma_kernel(ExtArgs a, const QT* __restrict__ q) {
       for (int h = 0; h < g; ++h) atomicAdd(&corr[h * kCT + (int)tok], qs[h * D + c] * val);
     }
     if (c0 + kCT < t_hi) {
-      cur = chunk_src(c0 + kCT);
+      cur = chunk_src(c0 + kCT, g_cur, r_cur);
       stage_load(cur);
     }
     __syncthreads();
