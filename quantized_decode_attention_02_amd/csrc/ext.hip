@@ -860,24 +860,29 @@ constexpr int kLkPad = 8;    // halves of padding per fp16 key row
 constexpr int kLvStride = kCT + 8;  // halves per transposed value row and P' row
 constexpr int kLvSpare = 8;  // spare channel rows past D of the transposed values
 
-// Dequantize a chunk's code words to fp16 levels through the table: word i
-// is token i / WR, word i % WR; keys land as rows (D + kLkPad halves per
-// token), values transposed (kLvStride halves per channel).  The first CK
-// words of each thread come from registers, the rest from memory.  A row's
-// last word may hold unused fields past D (3-bit codes); their levels land
-// in the key row's padding or in the spare channel rows, which no operand
-// reads, so no field needs a bounds test.
-template <int BITS, int D, int CK, bool TR>
-__device__ inline void deq_chunk(const uint32_t (&r)[CK], const uint32_t* src, int cnt,
-                                 const uint16_t* lut, uint16_t* dst) {
+// Key code words of a chunk to fp16 level rows (D + kLkPad halves per
+// token) through the tables: word i is token i / WR, word i % WR; the first
+// CK words of each thread come from registers, the rest from memory.  Codes
+// of up to 4 bits go two neighbouring fields at a time through the pair
+// table.  A row's last word may hold unused fields past D (3-bit codes):
+// their levels land in the row's padding, which no operand reads, so no
+// field needs a bounds test.
+template <int BITS, int D, int CK>
+__device__ inline void deq_keys(const uint32_t (&r)[CK], const uint32_t* src, int cnt,
+                                const uint16_t* lut, const uint32_t* lut2, uint16_t* dst) {
   constexpr int FPW = 32 / BITS, WR = (D + FPW - 1) / FPW;
-  constexpr uint32_t MASK = (1u << BITS) - 1u;
-  static_assert(WR * FPW - D <= (TR ? kLvSpare : kLkPad), "fields past D must fit the padding");
+  constexpr uint32_t MASK = (1u << BITS) - 1u, PMASK = (1u << (2 * BITS)) - 1u;
+  static_assert(WR * FPW - D <= kLkPad, "fields past D must fit the row padding");
   auto one = [&](int i, uint32_t word) {
     const int t = i / WR, w = i - t * WR;
-    uint16_t* o = TR ? dst + w * FPW * kLvStride + t : dst + t * (D + kLkPad) + w * FPW;
+    uint16_t* o = dst + t * (D + kLkPad) + w * FPW;
+    if (BITS <= 4) {
 #pragma unroll
-    for (int f = 0; f < FPW; ++f) o[TR ? f * kLvStride : f] = lut[(word >> (f * BITS)) & MASK];
+      for (int f = 0; f < FPW; f += 2) *(uint32_t*)(o + f) = lut2[(word >> (f * BITS)) & PMASK];
+    } else {
+#pragma unroll
+      for (int f = 0; f < FPW; ++f) o[f] = lut[(word >> (f * BITS)) & MASK];
+    }
   };
   // one word at a time (unrolled, every field's table read would be in
   // flight at once)
@@ -892,25 +897,97 @@ __device__ inline void deq_chunk(const uint32_t (&r)[CK], const uint32_t* src, i
   }
   for (int i = threadIdx.x + kThreads * CK; i < cnt; i += kThreads) one(i, src[i]);
 }
-template <int D, int CK, bool TR>
-__device__ inline void deq_chunk_any(int bits, const uint32_t (&r)[CK], const uint32_t* src,
-                                     int cnt, const uint16_t* lut, uint16_t* dst) {
+template <int D, int CK>
+__device__ inline void deq_keys_any(int bits, const uint32_t (&r)[CK], const uint32_t* src,
+                                    int cnt, const uint16_t* lut, const uint32_t* lut2,
+                                    uint16_t* dst) {
   switch (bits) {
-    case 2: deq_chunk<2, D, CK, TR>(r, src, cnt, lut, dst); break;
-    case 3: deq_chunk<3, D, CK, TR>(r, src, cnt, lut, dst); break;
-    case 4: deq_chunk<4, D, CK, TR>(r, src, cnt, lut, dst); break;
-    default: deq_chunk<8, D, CK, TR>(r, src, cnt, lut, dst); break;
+    case 2: deq_keys<2, D, CK>(r, src, cnt, lut, lut2, dst); break;
+    case 3: deq_keys<3, D, CK>(r, src, cnt, lut, lut2, dst); break;
+    case 4: deq_keys<4, D, CK>(r, src, cnt, lut, lut2, dst); break;
+    default: deq_keys<8, D, CK>(r, src, cnt, lut, lut2, dst); break;
+  }
+}
+
+// Value code words by token pairs: pair item j is word w = j % WP of tokens
+// 2p and 2p + 1 (p = j / WP, WP the power of two at or above the words per
+// row, items with w past the row idle), so that the transposed level rows
+// (kLvStride halves per channel) take both tokens of a channel in one
+// 4-byte store.  The second word of a pair past the chunk's n tokens reads
+// as 0 and its level is stored as 0.  Unused fields past D land in the
+// spare channel rows.
+__host__ __device__ constexpr int ceil_log2(int x) { return x <= 1 ? 0 : 1 + ceil_log2((x + 1) / 2); }
+template <int CP>
+__device__ inline void load_vpairs(uint32_t (&r)[CP][2], const uint32_t* src, int n, int wr,
+                                   int lg) {
+#pragma unroll
+  for (int k = 0; k < CP; ++k) {
+    const int j = threadIdx.x + kThreads * k;
+    const int p = j >> lg, w = j & ((1 << lg) - 1);
+    const int at = 2 * p * wr + w;
+    const bool ok = w < wr && 2 * p < n;
+    r[k][0] = ok ? src[at] : 0u;
+    r[k][1] = (ok && 2 * p + 1 < n) ? src[at + wr] : 0u;
+  }
+}
+template <int BITS, int D, int CP>
+__device__ inline void deq_vpairs(const uint32_t (&r)[CP][2], const uint32_t* src, int n,
+                                  const uint16_t* lut, const uint32_t* lut2, uint16_t* LvT) {
+  constexpr int FPW = 32 / BITS, WR = (D + FPW - 1) / FPW, LG = ceil_log2(WR), WP = 1 << LG;
+  constexpr uint32_t MASK = (1u << BITS) - 1u;
+  static_assert(WR * FPW - D <= kLvSpare, "fields past D must fit the spare rows");
+  const int cnt = ((n + 1) >> 1) * WP;
+  auto one = [&](int j, uint32_t wa, uint32_t wb) {
+    const int p = j >> LG, w = j & (WP - 1);
+    const uint32_t keep = 2 * p + 1 < n ? 0xFFFFFFFFu : 0xFFFFu;
+    uint16_t* o = LvT + w * FPW * kLvStride + 2 * p;
+#pragma unroll
+    for (int f = 0; f < FPW; ++f) {
+      const uint32_t ca = (wa >> (f * BITS)) & MASK, cb = (wb >> (f * BITS)) & MASK;
+      const uint32_t lv = BITS <= 4 ? lut2[ca | cb << BITS] : lut[ca] | (uint32_t)lut[cb] << 16;
+      *(uint32_t*)(o + f * kLvStride) = lv & keep;
+    }
+  };
+#pragma unroll 1
+  for (int k = 0; k < CP; ++k) {
+    uint32_t wa = 0, wb = 0;
+#pragma unroll
+    for (int k2 = 0; k2 < CP; ++k2)
+      if (k2 == k) {
+        wa = r[k2][0];
+        wb = r[k2][1];
+      }
+    const int j = threadIdx.x + kThreads * k;
+    if (j < cnt && (WP == WR || (j & (WP - 1)) < WR)) one(j, wa, wb);
+  }
+  for (int j = threadIdx.x + kThreads * CP; j < cnt; j += kThreads) {
+    const int p = j >> LG, w = j & (WP - 1);
+    if (WP != WR && w >= WR) continue;
+    const int at = 2 * p * WR + w;
+    one(j, src[at], 2 * p + 1 < n ? src[at + WR] : 0u);
+  }
+}
+template <int D, int CP>
+__device__ inline void deq_vpairs_any(int bits, const uint32_t (&r)[CP][2], const uint32_t* src,
+                                      int n, const uint16_t* lut, const uint32_t* lut2,
+                                      uint16_t* LvT) {
+  switch (bits) {
+    case 2: deq_vpairs<2, D, CP>(r, src, n, lut, lut2, LvT); break;
+    case 3: deq_vpairs<3, D, CP>(r, src, n, lut, lut2, LvT); break;
+    case 4: deq_vpairs<4, D, CP>(r, src, n, lut, lut2, LvT); break;
+    default: deq_vpairs<8, D, CP>(r, src, n, lut, lut2, LvT); break;
   }
 }
 
 template <int D>
 struct ExtMLayout {
   // byte offsets of the LDS arrays (every one 16-byte aligned)
-  int lut, qs, lk, lv, ps, pg, pv, oc, corr, st, gam, ksl, vsl, skT, vol, total;
+  int lut, lut2, qs, lk, lv, ps, pg, pv, oc, corr, st, gam, ksl, vsl, skT, vol, total;
   __host__ __device__ ExtMLayout(int g, int ngv, int MW, int per_g, int per_t) {
     int o = 0;
     auto take = [&](int bytes) { const int at = o; o += (bytes + 15) & ~15; return at; };
     lut = take(2 * 256 * 2);
+    lut2 = take(2 * 256 * 4);
     qs = take(g * D * 4);
     lk = take(kCT * (D + kLkPad) * 2);
     lv = take((D + kLvSpare) * kLvStride * 2);
@@ -946,11 +1023,14 @@ decode_ext_mfma_kernel(ExtArgs a, const QT* __restrict__ q) {
   const int M = v.v_qjl ? v.qjl_m : 0, MW = M / 32;
   const int kb = v.k_bits, vb = v.v_bits;
   const int kw_row = words_of(D, kb), vw_row = words_of(D, vb);
+  const int vlg = ceil_log2(vw_row);  // value pair items per token pair: 2^vlg
   const int ngv = D / v.group_ch;
   const int per_g = D * v.k_n_out, per_t = ngv * v.v_n_out;
   const ExtMLayout<D> L(g, ngv, MW, per_g, per_t);
   uint16_t* lutK = (uint16_t*)(smem + L.lut);
   uint16_t* lutV = lutK + 256;
+  uint32_t* lut2K = (uint32_t*)(smem + L.lut2);  // level pairs: code a | code b << bits
+  uint32_t* lut2V = lut2K + 256;
   float* qs = (float*)(smem + L.qs);
   uint16_t* Lk = (uint16_t*)(smem + L.lk);
   uint16_t* LvT = (uint16_t*)(smem + L.lv);
@@ -975,15 +1055,20 @@ decode_ext_mfma_kernel(ExtArgs a, const QT* __restrict__ q) {
 
   // level tables (fp16 bit patterns), queries, state, cleared P' columns and
   // value-outlier accumulators
+  auto level = [&](bool isk, int code) {
+    const int bits = isk ? kb : vb;
+    float lv = 0.0f;
+    if (code < (1 << bits)) {
+      const bool nuq = isk ? v.k_nuq : v.v_nuq;
+      lv = nuq ? (isk ? a.lk.lvl[code] : a.lv.lvl[code]) : (float)(code - qmax_of(bits) - 1);
+    }
+    return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)lv);
+  };
   for (int u = tid; u < 512; u += kThreads) {
     const bool isk = u < 256;
     const int uu = u & 255, bits = isk ? kb : vb;
-    float lv = 0.0f;
-    if (uu < (1 << bits)) {
-      const bool nuq = isk ? v.k_nuq : v.v_nuq;
-      lv = nuq ? (isk ? a.lk.lvl[uu] : a.lv.lvl[uu]) : (float)(uu - qmax_of(bits) - 1);
-    }
-    lutK[u] = __builtin_bit_cast(uint16_t, (_Float16)lv);
+    lutK[u] = (uint16_t)level(isk, uu);
+    lut2K[u] = bits <= 4 ? level(isk, uu & ((1 << bits) - 1)) | level(isk, uu >> bits) << 16 : 0u;
   }
   for (int i = tid; i < g * D; i += kThreads) {
     qs[i] = ldx(q, ((int64_t)b * a.Hq + kvh * g) * D + i) * a.qscale;
@@ -1025,11 +1110,13 @@ decode_ext_mfma_kernel(ExtArgs a, const QT* __restrict__ q) {
   const float* vs = v.v_scales + s * v.v_scales_stride;
   const uint32_t* vo = v.v_n_out ? v.v_outliers + s * v.v_outliers_stride : nullptr;
 
-  Staged<(D >= 64 ? D / 32 : 1)> st_k, st_v;
+  Staged<(D >= 64 ? D / 32 : 1)> st_k;
+  constexpr int CP = D >= 128 ? D / 64 : 1;  // value word pairs per thread in registers
+  uint32_t rv[CP][2];
   Staged<1> st_ks, st_gam, st_vs, st_sk, st_ko, st_vo;
   struct ChunkSrc {
     const uint32_t *k, *v, *ks, *vs, *sk, *gam, *ko, *vo;
-    int nk, nv, nks, nvs, nsk, ngam, nko, nvo;
+    int n, nk, nv, nks, nvs, nsk, ngam, nko, nvo;
   };
   // chunk c0 starts at token r0 of key group g0 (chunks start at multiples
   // of 64 and G is a multiple of 32, so a chunk spans at most two groups;
@@ -1038,6 +1125,7 @@ decode_ext_mfma_kernel(ExtArgs a, const QT* __restrict__ q) {
     const int n = (int)min((int64_t)kCT, t_hi - c0);
     const int ng = (r0 + n > G) ? 2 : 1;
     ChunkSrc cs;
+    cs.n = n;
     cs.k = kc + c0 * kw_row;                       cs.nk = n * kw_row;
     cs.v = vc + c0 * vw_row;                       cs.nv = n * vw_row;
     cs.ks = (const uint32_t*)(ks + g0 * D);        cs.nks = ng * D;
@@ -1052,7 +1140,7 @@ decode_ext_mfma_kernel(ExtArgs a, const QT* __restrict__ q) {
   };
   auto stage_load = [&](const ChunkSrc& cs) {
     st_k.load(cs.k, cs.nk);
-    st_v.load(cs.v, cs.nv);
+    load_vpairs<CP>(rv, cs.v, cs.n, vw_row, vlg);
     st_ks.load(cs.ks, cs.nks);
     st_vs.load(cs.vs, cs.nvs);
     st_sk.load(cs.sk, cs.nsk);
@@ -1081,11 +1169,13 @@ decode_ext_mfma_kernel(ExtArgs a, const QT* __restrict__ q) {
     //      the next chunk's loads
     {
       constexpr int CK = D >= 64 ? D / 32 : 1;
-      deq_chunk_any<D, CK, false>(kb, st_k.r, cur.k, cur.nk, lutK, Lk);
-      deq_chunk_any<D, CK, true>(vb, st_v.r, cur.v, cur.nv, lutV, LvT);
-      // value columns past n: zero (their weights are 0; LDS may hold NaN)
-      for (int i = tid; i < (kCT - n) * D; i += kThreads)
-        LvT[(i % D) * kLvStride + n + i / D] = 0;
+      deq_keys_any<D, CK>(kb, st_k.r, cur.k, cur.nk, lutK, lut2K, Lk);
+      deq_vpairs_any<D, CP>(vb, rv, cur.v, n, lutV, lut2V, LvT);
+      // value columns past the last token pair: zero (their weights are 0;
+      // LDS may hold NaN)
+      const int ne = (n + 1) & ~1;
+      for (int i = tid; i < (kCT - ne) * D; i += kThreads)
+        LvT[(i % D) * kLvStride + ne + i / D] = 0;
     }
     st_ks.store(cur.ks, cur.nks, (uint32_t*)ksl, ident);
     st_vs.store(cur.vs, cur.nvs, (uint32_t*)vsl, ident);

@@ -152,6 +152,12 @@ EXT_CASES = {
     "sym_k8_d32_nuq_v4": (1, 6, 2, 450, 32, ("sym", 8, 32), ("nuq", 4, 8, 1)),
     # g * D / Gv = 32 columns: the vector-ALU form of the decode
     "valu_g8_gv32": (1, 16, 2, 500, 128, ("nuq", 3, 64, 1), ("nuq", 3, 32, 1)),
+    # an odd number of tokens in the last chunk (41; value codes go through
+    # the level tables by token pairs) at D = 128
+    "nuq3_odd_tail_d128": (1, 8, 2, 1001, 128, ("nuq", 3, 128, 1), ("nuq", 3, 128, 1)),
+    # 8-bit values (more value words per chunk than the staged registers
+    # hold) with the sketch, 2-bit keys, odd tail (9 tokens)
+    "sym_k2_qjl_v8_odd": (1, 4, 2, 777, 128, ("sym", 2, 64), ("qjl", 8, 32, 64)),
 }
 
 
