@@ -1006,6 +1006,22 @@ struct ExtMLayout {
   }
 };
 
+// x / d for x >= 0, d >= 1 and x * d < 2^32: the high word of x times
+// ceil(2^32 / d) (a 33-bit multiplier: its low word and its top bit).  With
+// ceil(2^32 / d) = (2^32 + r) / d, 0 <= r < d, the product is x / d plus
+// x r / (d 2^32) < 1 / d, so its integer part is the quotient.
+struct FastDiv {
+  uint32_t m, top;
+  __device__ explicit FastDiv(uint32_t d) {
+    const uint64_t mm = ((1ull << 32) + d - 1) / d;
+    m = (uint32_t)mm;
+    top = (uint32_t)(mm >> 32);
+  }
+  __device__ int operator()(int x) const {
+    return (int)(__umulhi((uint32_t)x, m) + (top ? (uint32_t)x : 0u));
+  }
+};
+
 __device__ inline int fexp(float x) {  // exponent of a positive normal float
   int e = (int)((__builtin_bit_cast(uint32_t, x) >> 23) & 0xFF) - 127;
   return e < -100 ? -100 : (e > 100 ? 100 : e);
@@ -1024,9 +1040,12 @@ decode_ext_mfma_kernel(ExtArgs a, const QT* __restrict__ q) {
   const int kb = v.k_bits, vb = v.v_bits;
   const int kw_row = words_of(D, kb), vw_row = words_of(D, vb);
   const int vlg = ceil_log2(vw_row);  // value pair items per token pair: 2^vlg
+  // divisions by runtime sizes in the chunk loop
+  const FastDiv div_mw(MW > 0 ? MW : 1), div_kno(v.k_n_out > 0 ? v.k_n_out : 1);
   const int ngv = D / v.group_ch;
   const int per_g = D * v.k_n_out, per_t = ngv * v.v_n_out;
   const ExtMLayout<D> L(g, ngv, MW, per_g, per_t);
+  const FastDiv div_pt(per_t > 0 ? per_t : 1), div_vno(v.v_n_out > 0 ? v.v_n_out : 1);
   uint16_t* lutK = (uint16_t*)(smem + L.lut);
   uint16_t* lutV = lutK + 256;
   uint32_t* lut2K = (uint32_t*)(smem + L.lut2);  // level pairs: code a | code b << bits
@@ -1096,6 +1115,7 @@ decode_ext_mfma_kernel(ExtArgs a, const QT* __restrict__ q) {
   int64_t qgrp = -1;
   float qsc = 0.0f;                        // 2^(e_q + e_k - 13): score units
   const int nblk = D / 16;                 // 16-channel value blocks
+  const int col_head = ln / ngv;           // head of value-operand column ln
   float4v ot[2];                           // blocks wave, wave + 4
 #pragma unroll
   for (int i = 0; i < 2; ++i) ot[i] = (float4v){0.0f, 0.0f, 0.0f, 0.0f};
@@ -1179,14 +1199,18 @@ decode_ext_mfma_kernel(ExtArgs a, const QT* __restrict__ q) {
     }
     st_ks.store(cur.ks, cur.nks, (uint32_t*)ksl, ident);
     st_vs.store(cur.vs, cur.nvs, (uint32_t*)vsl, ident);
-    st_sk.store(cur.sk, cur.nsk, skT, [&](int i) { return (i % MW) * kCT + i / MW; });
+    st_sk.store(cur.sk, cur.nsk, skT, [&](int i) {
+      const int w = div_mw(i);
+      return (i - w * MW) * kCT + w;
+    });
     st_gam.store(cur.gam, cur.ngam, (uint32_t*)gam, ident);
     st_vo.store(cur.vo, cur.nvo, vol, ident);
     // key outliers: q . (exact value) into the score terms of their tokens
     for (int i = tid; i < cur.nko; i += kThreads) {
       const uint32_t e = i < kThreads ? st_ko.r[0] : cur.ko[i];
       if ((e & 0x7FFFu) == 0) continue;
-      const int gi = i / per_g, c = (i - gi * per_g) / v.k_n_out;
+      const int gi = i >= per_g ? 1 : 0;  // (at most two groups per chunk)
+      const int c = div_kno(i - gi * per_g);
       const int64_t tok = (g0 + gi) * G + (e >> 16) - c0;
       if (tok < 0 || tok >= n) continue;
       const float val = h2f((uint16_t)(e & 0xFFFFu));
@@ -1293,8 +1317,8 @@ decode_ext_mfma_kernel(ExtArgs a, const QT* __restrict__ q) {
       for (int i = tid; i < n * per_t; i += kThreads) {
         const uint32_t e = vol[i];
         if ((e & 0x7FFFu) == 0) continue;
-        const int t = i / per_t, r = i - t * per_t;
-        const int cc = (r / v.v_n_out) * v.group_ch + (int)(e >> 16);
+        const int t = div_pt(i), r = i - t * per_t;
+        const int cc = div_vno(r) * v.group_ch + (int)(e >> 16);
         const float val = h2f((uint16_t)(e & 0xFFFFu));
         for (int h = 0; h < g; ++h) atomicAdd(&OC[h * D + cc], ps[h * kCT + t] * val);
       }
@@ -1304,8 +1328,7 @@ decode_ext_mfma_kernel(ExtArgs a, const QT* __restrict__ q) {
     {
       const float vun = st[25];
       const int col = ln;
-      const int hc = col / ngv;
-      const float al = (hc < g) ? st[16 + hc] : 0.0f;
+      const float al = (col_head < g) ? st[16 + col_head] : 0.0f;
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         const int jb = wave + 4 * i;
