@@ -39,6 +39,7 @@ constexpr float kLog2e = 1.4426950408889634f;
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float float4v __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 
 __device__ inline float h2f(uint16_t u) { return (float)__builtin_bit_cast(_Float16, u); }
 
@@ -857,6 +858,7 @@ decode_ext_kernel(ExtArgs a, const QT* __restrict__ q) {
 //  - sketch sums as in decode_ext_kernel.
 // ---------------------------------------------------------------------------
 constexpr int kLkPad = 8;    // halves of padding per fp16 key row
+constexpr int kQbPad = 8;    // halves of padding per Q' row
 constexpr int kLvStride = kCT + 8;  // halves per transposed value row and P' row
 constexpr int kLvSpare = 8;  // spare channel rows past D of the transposed values
 
@@ -982,20 +984,23 @@ __device__ inline void deq_vpairs_any(int bits, const uint32_t (&r)[CP][2], cons
 template <int D>
 struct ExtMLayout {
   // byte offsets of the LDS arrays (every one 16-byte aligned)
-  int lut, lut2, qs, lk, lv, ps, pg, pv, oc, corr, st, gam, ksl, vsl, skT, vol, total;
-  __host__ __device__ ExtMLayout(int g, int ngv, int MW, int per_g, int per_t) {
+  int lut, lut2, qs, qb, lk, lv, ps, pg, pv, oc, corr, st, gam, ksl, vsl, skT, vol, total;
+  // pair-table entries of a code width (none for 8 bits)
+  __host__ __device__ static int pairs(int bits) { return bits <= 4 ? 1 << (2 * bits) : 0; }
+  __host__ __device__ ExtMLayout(int g, int ngv, int MW, int per_g, int per_t, int kb, int vb) {
     int o = 0;
     auto take = [&](int bytes) { const int at = o; o += (bytes + 15) & ~15; return at; };
     lut = take(2 * 256 * 2);
-    lut2 = take(2 * 256 * 4);
+    lut2 = take((pairs(kb) + pairs(vb)) * 4);
     qs = take(g * D * 4);
+    qb = take(2 * g * (D + kQbPad) * 2);
     lk = take(kCT * (D + kLkPad) * 2);
     lv = take((D + kLvSpare) * kLvStride * 2);
     ps = take(g * kCT * 4);
     pg = take(g * kCT * 4);
     pv = take(16 * kLvStride * 2);
     oc = take(g * D * 4);
-    corr = take(g * kCT * 4);
+    corr = take(per_g > 0 ? g * kCT * 4 : 0);  // only with key outliers
     st = take(32 * 4);
     gam = take(kCT * 4);
     ksl = take(2 * D * 4);
@@ -1033,6 +1038,7 @@ __global__ void __launch_bounds__(kThreads, 3)
 decode_ext_mfma_kernel(ExtArgs a, const QT* __restrict__ q) {
   constexpr int KB = D / 32;              // 32-channel blocks of the score contraction
   constexpr int LkS = D + kLkPad;         // halves per key row
+  constexpr int kQbS = D + kQbPad;        // halves per Q' row
   extern __shared__ __align__(16) unsigned char smem[];
   const kvq_ext_view& v = a.v;
   const int g = a.Hq / v.kv_heads;
@@ -1044,13 +1050,14 @@ decode_ext_mfma_kernel(ExtArgs a, const QT* __restrict__ q) {
   const FastDiv div_mw(MW > 0 ? MW : 1), div_kno(v.k_n_out > 0 ? v.k_n_out : 1);
   const int ngv = D / v.group_ch;
   const int per_g = D * v.k_n_out, per_t = ngv * v.v_n_out;
-  const ExtMLayout<D> L(g, ngv, MW, per_g, per_t);
+  const ExtMLayout<D> L(g, ngv, MW, per_g, per_t, kb, vb);
   const FastDiv div_pt(per_t > 0 ? per_t : 1), div_vno(v.v_n_out > 0 ? v.v_n_out : 1);
   uint16_t* lutK = (uint16_t*)(smem + L.lut);
   uint16_t* lutV = lutK + 256;
   uint32_t* lut2K = (uint32_t*)(smem + L.lut2);  // level pairs: code a | code b << bits
-  uint32_t* lut2V = lut2K + 256;
+  uint32_t* lut2V = lut2K + ExtMLayout<D>::pairs(kb);
   float* qs = (float*)(smem + L.qs);
+  _Float16* qb = (_Float16*)(smem + L.qb);
   uint16_t* Lk = (uint16_t*)(smem + L.lk);
   uint16_t* LvT = (uint16_t*)(smem + L.lv);
   float* ps = (float*)(smem + L.ps);
@@ -1083,18 +1090,22 @@ decode_ext_mfma_kernel(ExtArgs a, const QT* __restrict__ q) {
     }
     return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)lv);
   };
-  for (int u = tid; u < 512; u += kThreads) {
-    const bool isk = u < 256;
-    const int uu = u & 255, bits = isk ? kb : vb;
-    lutK[u] = (uint16_t)level(isk, uu);
-    lut2K[u] = bits <= 4 ? level(isk, uu & ((1 << bits) - 1)) | level(isk, uu >> bits) << 16 : 0u;
+  for (int u = tid; u < 512; u += kThreads) lutK[u] = (uint16_t)level(u < 256, u & 255);
+  {
+    const int pk = ExtMLayout<D>::pairs(kb), pv = ExtMLayout<D>::pairs(vb);
+    for (int u = tid; u < pk + pv; u += kThreads) {
+      const bool isk = u < pk;
+      const int uu = isk ? u : u - pk, bits = isk ? kb : vb;
+      lut2K[u] = level(isk, uu & ((1 << bits) - 1)) | level(isk, uu >> bits) << 16;
+    }
   }
   for (int i = tid; i < g * D; i += kThreads) {
     qs[i] = ldx(q, ((int64_t)b * a.Hq + kvh * g) * D + i) * a.qscale;
     OC[i] = 0.0f;
   }
   for (int i = tid; i < 16 * kLvStride; i += kThreads) Pv[i] = 0;
-  for (int i = tid; i < g * kCT; i += kThreads) corr[i] = 0.0f;
+  if (v.k_n_out)
+    for (int i = tid; i < g * kCT; i += kThreads) corr[i] = 0.0f;
   if (tid < 8) {
     st[tid] = -INFINITY;
     st[8 + tid] = 0.0f;
@@ -1112,7 +1123,8 @@ decode_ext_mfma_kernel(ExtArgs a, const QT* __restrict__ q) {
   // per-wave state: Q' limbs of the wave's current key group, value and
   // sketch accumulators
   half8 qa[KB];
-  int64_t qgrp = -1;
+  int64_t qgrp = -1;                       // key group of the wave's qa
+  int64_t qb_grp = -1;                     // key group of the Q' rows in LDS
   float qsc = 0.0f;                        // 2^(e_q + e_k - 13): score units
   const int nblk = D / 16;                 // 16-channel value blocks
   const int col_head = ln / ngv;           // head of value-operand column ln
@@ -1221,33 +1233,43 @@ decode_ext_mfma_kernel(ExtArgs a, const QT* __restrict__ q) {
       stage_load(cur);
     }
     __syncthreads();
-    // ---- scores: wave w, tokens 16 w .. 16 w + 15
-    if (16 * wave < n) {  // (a partial chunk may leave a wave without tokens)
-      const int tw = 16 * wave;
-      const int gi = (r0 + tw >= G) ? 1 : 0;  // its tokens' group: one per 16 tokens
-      if (g0 + gi != qgrp) {
-        // Q' of the key group: q times the channel's scale times
-        // 2^(13 - e_q - e_k), hi and lo fp16 limbs (row ln = 2 h + limb)
-        qgrp = g0 + gi;
+    // ---- Q' of the chunk's key groups: q times the channel's scale times
+    //      2^(13 - e_q - e_k) in hi and lo fp16 limbs, built once per group
+    //      by the workgroup into LDS (row 2 h + limb); each wave loads the
+    //      rows of its tokens' group as its A operand (rows past 2 g are 0)
+    const int tw = 16 * wave;
+    const int gw = (r0 + tw >= G) ? 1 : 0;  // the wave's key group: one per 16 tokens
+    for (int gi = 0; gi < ng_chunk; ++gi) {
+      if (g0 + gi != qb_grp) {
+        if (gi > 0) __syncthreads();  // the first group's rows are loaded
         const float* kss = ksl + gi * D;
         float km = 0.0f;
         for (int c = lane; c < D; c += 64) km = fmaxf(km, kss[c]);
         km = wave_max64(km);
         const int ek = km > 0.0f ? fexp(km) : 0;
         const float sg = p2(13 - eq - ek);
-        qsc = p2(eq + ek - 13);
-        const int h = ln >> 1, limb = ln & 1;
-#pragma unroll
-        for (int k = 0; k < KB; ++k) {
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const int c = 32 * k + 8 * lq + e;
-            const float x = h < g ? qs[h * D + c] * kss[c] * sg : 0.0f;
-            const _Float16 hi = (_Float16)x;
-            qa[k][e] = limb ? (_Float16)(x - (float)hi) : hi;
-          }
+        if (tid == 0) st[26] = p2(eq + ek - 13);
+        for (int i = tid; i < g * (D / 2); i += kThreads) {
+          const int h = i / (D / 2), c = 2 * (i - h * (D / 2));
+          const float x0 = qs[h * D + c] * kss[c] * sg, x1 = qs[h * D + c + 1] * kss[c + 1] * sg;
+          const _Float16 h0 = (_Float16)x0, h1 = (_Float16)x1;
+          *(half2v*)&qb[2 * h * kQbS + c] = (half2v){h0, h1};
+          *(half2v*)&qb[(2 * h + 1) * kQbS + c] =
+              (half2v){(_Float16)(x0 - (float)h0), (_Float16)(x1 - (float)h1)};
         }
+        __syncthreads();
+        qb_grp = g0 + gi;
       }
+      if (gw == gi && g0 + gi != qgrp) {
+        qgrp = g0 + gi;
+        qsc = st[26];
+#pragma unroll
+        for (int k = 0; k < KB; ++k)
+          qa[k] = ln < 2 * g ? *(const half8*)&qb[ln * kQbS + 32 * k + 8 * lq] : (half8){};
+      }
+    }
+    // ---- scores: wave w, tokens 16 w .. 16 w + 15
+    if (16 * wave < n) {  // (a partial chunk may leave a wave without tokens)
       float4v acc = (float4v){0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int k = 0; k < KB; ++k) {
@@ -1258,14 +1280,19 @@ decode_ext_mfma_kernel(ExtArgs a, const QT* __restrict__ q) {
       const int t = tw + ln, h0 = 2 * lq;
       if (t < n) {
         // the outlier terms of this chunk are consumed and cleared here
-        if (h0 < g) {
-          ps[h0 * kCT + t] = (acc[0] + acc[1]) * qsc + corr[h0 * kCT + t];
-          corr[h0 * kCT + t] = 0.0f;
+        float c0v = 0.0f, c1v = 0.0f;
+        if (ko) {
+          if (h0 < g) {
+            c0v = corr[h0 * kCT + t];
+            corr[h0 * kCT + t] = 0.0f;
+          }
+          if (h0 + 1 < g) {
+            c1v = corr[(h0 + 1) * kCT + t];
+            corr[(h0 + 1) * kCT + t] = 0.0f;
+          }
         }
-        if (h0 + 1 < g) {
-          ps[(h0 + 1) * kCT + t] = (acc[2] + acc[3]) * qsc + corr[(h0 + 1) * kCT + t];
-          corr[(h0 + 1) * kCT + t] = 0.0f;
-        }
+        if (h0 < g) ps[h0 * kCT + t] = (acc[0] + acc[1]) * qsc + c0v;
+        if (h0 + 1 < g) ps[(h0 + 1) * kCT + t] = (acc[2] + acc[3]) * qsc + c1v;
       }
     }
     __syncthreads();
@@ -1598,9 +1625,10 @@ size_t ext_decode_lds(const kvq_ext_view& v, int Hq) {
   if (ext_mfma(v, Hq)) {
     const int ngv = D / v.group_ch, per_g = D * v.k_n_out, per_t = ngv * v.v_n_out;
     switch (D) {
-      case 32: return (size_t)ExtMLayout<32>(g, ngv, M / 32, per_g, per_t).total;
-      case 64: return (size_t)ExtMLayout<64>(g, ngv, M / 32, per_g, per_t).total;
-      default: return (size_t)ExtMLayout<128>(g, ngv, M / 32, per_g, per_t).total;
+      case 32: return (size_t)ExtMLayout<32>(g, ngv, M / 32, per_g, per_t, v.k_bits, v.v_bits).total;
+      case 64: return (size_t)ExtMLayout<64>(g, ngv, M / 32, per_g, per_t, v.k_bits, v.v_bits).total;
+      default:
+        return (size_t)ExtMLayout<128>(g, ngv, M / 32, per_g, per_t, v.k_bits, v.v_bits).total;
     }
   }
   const size_t ngv4 = ((size_t)kCT * (D / v.group_ch) + 3) & ~(size_t)3;
