@@ -1469,15 +1469,36 @@ decode_ext_mfma_kernel(ExtArgs a, const QT* __restrict__ q) {
 // out = turn(O + sqrt(pi/2)/m S^T Z) / L over the partials of one (batch,
 // query head): O, Z and L summed with the log-sum-exp weights; turn is the
 // normalized Walsh-Hadamard transform when the values were stored rotated.
+// Latency-bound (one workgroup per query head), so every pass keeps many
+// loads in flight: thread (row group rg, float2 column c) sums partials rg,
+// rg + R, ... of its column, and its first kMergeK loads are issued before
+// the (m, l) pass that yields their weights.
+constexpr int kMergeExtK = 16;
 __global__ void __launch_bounds__(kThreads)
 merge_ext_kernel(const float* __restrict__ partials, int D, int M, int n_parts, int rec,
                  const float* __restrict__ S, int rotated, float* __restrict__ out) {
+  typedef float float2v __attribute__((ext_vector_type(2)));
   __shared__ float red[kThreads / 64];
   __shared__ float acc[kMaxD + 256];
+  __shared__ float2v psum[kThreads];
   extern __shared__ float wts[];   // [n_parts]
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int64_t bh = blockIdx.x;
   const float* p = partials + bh * n_parts * rec;
+  const int C = (D + M) / 2;             // float2 columns of (o, z) (D + M is even)
+  const int R = kThreads / C;            // row groups (C <= 192)
+  const int col = tid % C, rg = tid / C;
+  const bool act = rg < R;
+  // a part's (o, z) at float offset 2 of its record (rec is even, so the
+  // float2 loads are aligned); parts past the end are clamped, their weight
+  // is taken as 0
+  auto ld = [&](int i) {
+    const int ic = i < n_parts ? i : n_parts - 1;
+    return *(const float2v*)(p + (int64_t)ic * rec + 2 + 2 * col);
+  };
+  float2v pre[kMergeExtK];
+#pragma unroll
+  for (int k = 0; k < kMergeExtK; ++k) pre[k] = act ? ld(rg + R * k) : (float2v){0.0f, 0.0f};
   float mx = -INFINITY;
   for (int i = tid; i < n_parts; i += kThreads)
     if (p[(int64_t)i * rec + 1] > 0.0f) mx = fmaxf(mx, p[(int64_t)i * rec]);
@@ -1497,61 +1518,65 @@ merge_ext_kernel(const float* __restrict__ partials, int D, int M, int n_parts, 
   if (lane == 0) red[wave] = L;
   __syncthreads();
   L = red[0] + red[1] + red[2] + red[3];
-  // wave w sums partials w, w + 4, ... (lane l on entries l, l + 64, ...,
-  // eight partials in flight), then the four waves are added in LDS
-  __shared__ float part_sum[kThreads / 64][kMaxD + 256];
-  {
-    float x[8];
+  if (act) {
+    float2v sum = (float2v){0.0f, 0.0f};
 #pragma unroll
-    for (int k = 0; k < 8; ++k) x[k] = 0.0f;
-    const int nj = D + M;
-    for (int i = wave; i < n_parts; i += 4 * 2) {
-      const bool two = i + 4 < n_parts;
-      const float w0 = wts[i], w1 = two ? wts[i + 4] : 0.0f;
-      const float* p0 = p + (int64_t)i * rec + 2;
-      const float* p1 = p + (int64_t)(two ? i + 4 : i) * rec + 2;
+    for (int k = 0; k < kMergeExtK; ++k) {
+      const int i = rg + R * k;
+      const float w = i < n_parts ? wts[i] : 0.0f;
+      sum[0] = __builtin_fmaf(w, pre[k][0], sum[0]);
+      sum[1] = __builtin_fmaf(w, pre[k][1], sum[1]);
+    }
+    for (int i0 = rg + R * kMergeExtK; i0 < n_parts; i0 += R * kMergeExtK) {
+      float2v x[kMergeExtK];
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
-        const int j = lane + 64 * k;
-        if (j < nj) x[k] = __builtin_fmaf(w0, p0[j], __builtin_fmaf(w1, p1[j], x[k]));
+      for (int k = 0; k < kMergeExtK; ++k) x[k] = ld(i0 + R * k);
+#pragma unroll
+      for (int k = 0; k < kMergeExtK; ++k) {
+        const int i = i0 + R * k;
+        const float w = i < n_parts ? wts[i] : 0.0f;
+        sum[0] = __builtin_fmaf(w, x[k][0], sum[0]);
+        sum[1] = __builtin_fmaf(w, x[k][1], sum[1]);
       }
     }
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const int j = lane + 64 * k;
-      if (j < nj) part_sum[wave][j] = x[k];
-    }
+    psum[tid] = sum;
   }
   __syncthreads();
-  for (int j = tid; j < D + M; j += kThreads)
-    acc[j] = part_sum[0][j] + part_sum[1][j] + part_sum[2][j] + part_sum[3][j];
+  for (int j = tid; j < C; j += kThreads) {
+    float2v t = (float2v){0.0f, 0.0f};
+    for (int r = 0; r < R; ++r) t += psum[r * C + j];
+    acc[2 * j] = t[0];
+    acc[2 * j + 1] = t[1];
+  }
   __syncthreads();
   if (M) {
-    // S^T z: thread (d, quarter) sums sketch rows quarter, quarter + 4, ...
-    // (eight loads in flight), the four quarters are added in LDS
+    // S^T z: thread (d, slice) sums the sketch rows of its slice (every
+    // P-th row), kMergeExtK loads in flight; the slices are added in LDS
     const float c = 1.2533141373155003f / (float)M;   // sqrt(pi/2) / m
-    float* tq = &part_sum[0][0];                       // [4][kMaxD], free again
-    for (int idx = tid; idx < 4 * D; idx += kThreads) {
-      const int d = idx % D, quarter = idx / D;
-      float r0 = 0.0f, r1 = 0.0f;
-      int i = quarter;
-      for (; i + 28 < M; i += 32) {
-        float sv[8];
+    float* tq = (float*)psum;                          // [P][D], free again
+    const int P = kThreads / D, d = tid % D, sl = tid / D;
+    float r0 = 0.0f, r1 = 0.0f;
+    for (int i0 = sl; i0 < M; i0 += P * kMergeExtK) {
+      float sv[kMergeExtK];
 #pragma unroll
-        for (int k = 0; k < 8; ++k) sv[k] = S[(int64_t)(i + 4 * k) * D + d];
-#pragma unroll
-        for (int k = 0; k < 8; k += 2) {
-          r0 = __builtin_fmaf(sv[k], acc[D + i + 4 * k], r0);
-          r1 = __builtin_fmaf(sv[k + 1], acc[D + i + 4 * k + 4], r1);
-        }
+      for (int k = 0; k < kMergeExtK; ++k) {
+        const int i = i0 + P * k;
+        sv[k] = i < M ? S[(int64_t)i * D + d] : 0.0f;
       }
-      for (; i < M; i += 4) r0 = __builtin_fmaf(S[(int64_t)i * D + d], acc[D + i], r0);
-      tq[quarter * kMaxD + d] = r0 + r1;
+#pragma unroll
+      for (int k = 0; k < kMergeExtK; k += 2) {
+        const int i = i0 + P * k, i1 = i + P;
+        r0 = __builtin_fmaf(sv[k], i < M ? acc[D + i] : 0.0f, r0);
+        r1 = __builtin_fmaf(sv[k + 1], i1 < M ? acc[D + i1] : 0.0f, r1);
+      }
     }
+    tq[sl * D + d] = r0 + r1;
     __syncthreads();
-    for (int d = tid; d < D; d += kThreads)
-      acc[d] = __builtin_fmaf(c, tq[d] + tq[kMaxD + d] + tq[2 * kMaxD + d] + tq[3 * kMaxD + d],
-                              acc[d]);
+    for (int dd = tid; dd < D; dd += kThreads) {
+      float t = 0.0f;
+      for (int q = 0; q < P; ++q) t += tq[q * D + dd];
+      acc[dd] = __builtin_fmaf(c, t, acc[dd]);
+    }
     __syncthreads();
   }
   for (int d = tid; d < D; d += kThreads) acc[d] = acc[d] / L;
