@@ -1277,7 +1277,10 @@ decode_ext_mfma_kernel(ExtArgs a, const QT* __restrict__ q) {
         acc = __builtin_amdgcn_mfma_f32_16x16x32_f16(qa[k], kbv, acc, 0, 0, 0);
       }
       // lane (token tw + ln, lq): rows 4 lq .. 4 lq + 3 = heads 2 lq, 2 lq + 1
-      const int t = tw + ln, h0 = 2 * lq;
+      int t = tw + ln, h0 = 2 * lq;
+      // (recomputed here: hoisted out of the loop, the LDS addresses below
+      // get spilled, and their reload waits for the next chunk's loads)
+      asm volatile("" : "+v"(t), "+v"(h0));
       if (t < n) {
         // the outlier terms of this chunk are consumed and cleared here
         float c0v = 0.0f, c1v = 0.0f;
