@@ -326,6 +326,13 @@ __device__ inline float max_ror(float x) {
 __device__ inline float row_max16(float x) {
   return max_ror<1>(max_ror<2>(max_ror<4>(max_ror<8>(x))));
 }
+// Largest of a scale row held as float4s by lanes 0-31 (lanes 32-63 hold
+// zeros; scales are >= 0).
+__device__ inline float row_max_lanes32(float4v x) {
+  const float m = row_max16(fmaxf(fmaxf(x[0], x[1]), fmaxf(x[2], x[3])));
+  return fmaxf(__builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, m), 0)),
+               __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, m), 16)));
+}
 __device__ inline float row_sum16(float x) {
   x += dpp_f<0x128>(x);
   x += dpp_f<0x124>(x);
@@ -423,7 +430,6 @@ decode_mfma_kernel(MfmaArgs a) {
   // units split as evenly as possible over the splits
   const int u_lo = (int)((int64_t)split * n_units / a.n_splits);
   const int u_hi = (int)((int64_t)(split + 1) * n_units / a.n_splits);
-  const float* kg = v.k_gmax + s * v.k_gmax_stride;
 
   // This lane's query values on its key MFMA k-slots, times the inverse of
   // each slot's factor, sm_scale * log2(e) and a power of two sigma_q that
@@ -505,7 +511,6 @@ decode_mfma_kernel(MfmaArgs a) {
   u32x4 vw[kUnitTiles][VB == 4 ? 2 : 1];
   float4v vsn[kVs4];
   float4v ksn = (float4v){0.0f, 0.0f, 0.0f, 0.0f};
-  float kgn = 0.0f;
   auto load_tile = [&](int unit, int i) {
     const int64_t t32 = (int64_t)(unit * ut + i) * 32;
 #pragma unroll
@@ -529,16 +534,20 @@ decode_mfma_kernel(MfmaArgs a) {
       const int idx = lane + 64 * j;
       if (idx < n_vs4) vsn[j] = ldnt(src + idx);
     }
+    // (the group's largest scale is taken from this row when it is
+    // committed: a separate uniform load of it would be moved to a scalar
+    // register at once, and that move waits for every load in flight, the
+    // prefetched tiles included)
     if (lane < kD / 4) ksn = ((const float4v*)(ks + (int64_t)(unit / upg) * kD))[lane];
-    kgn = kg[unit / upg];
   };
   float* my_ks = S.ks[wave];
   const int u_first = u_lo + wave;
   if (u_first < u_hi) {
+    // scales first, then the tiles: the order of the loop's own requests
+    load_scales(u_first);
 #pragma unroll
     for (int i = 0; i < kUnitTiles; ++i)
       if (i < ut) load_tile(u_first, i);
-    load_scales(u_first);
   }
 
   int ev = 0;            // sigma_v = 2^(kVTop - ev) (see unit_vscale_exp)
@@ -566,7 +575,9 @@ decode_mfma_kernel(MfmaArgs a) {
       if (idx < n_vs4) ((float4v*)my_vs)[idx] = vsn[j] * sig_v;
     }
     // sigma_g: power of two bringing the group's largest scale below 2^13
-    int exg = (int)((__builtin_bit_cast(uint32_t, kgn) >> 23) & 0xFF) - 127;
+    // (the group's largest scale, from the scale row itself)
+    const float kgv = row_max_lanes32(ksn);
+    int exg = (int)((__builtin_bit_cast(uint32_t, kgv) >> 23) & 0xFF) - 127;
     exg = exg < -100 ? -100 : exg;
     const float sigma_g = __builtin_bit_cast(float, (uint32_t)(127 + 12 - exg) << 23);
     const float inv_sigma_g = __builtin_bit_cast(float, (uint32_t)(127 - 12 + exg) << 23);
@@ -995,7 +1006,11 @@ __global__ void __launch_bounds__(kThreads, (rs_waves<KB, VB, NC, HS>())) decode
       if (idx < n_vs4) vsn[j] = ldnt(src + idx);
     }
     if (lane < ksrow / 4) ksn = ((const float4v*)(ks + (int64_t)(unit / upg) * ksrow))[lane];
-    kgn = kg[unit / upg];
+    // (uniform keys take the group's largest scale from the scale row
+    // itself when it is committed: a separate uniform load of it would be
+    // moved to a scalar register at once, and that move waits for every
+    // load in flight, the prefetched tiles included)
+    if (KM) kgn = kg[unit / upg];
     if (KM) kpn = ((const uint16_t*)(kpp + (int64_t)(unit / upg) * kD))[lane];
   };
   // A step of the wave covers kStep tiles: one unit, or kStep / ut units
@@ -1021,13 +1036,17 @@ __global__ void __launch_bounds__(kThreads, (rs_waves<KB, VB, NC, HS>())) decode
       for (int c = 0; c < 8; ++c) qraw[c] = *(const u32x4*)((const float*)a.q + base + 4 * c);
     }
   }
-  if (u_first < u_hi) {
-    load_scales(u_first);
+  // Every request names a valid unit (n_units >= 1 here): past u_hi, or for
+  // a wave without units, the index is clamped and the data is not used.
+  // The requests are then the same on every path, so the compiler's wait
+  // counts stay exact instead of falling back to waiting for every load in
+  // flight at each unit start.
+  const int u_last = n_units - 1;
+  load_scales(u_first < u_last ? u_first : u_last);
 #pragma unroll
-    for (int i = 0; i < kSlots; ++i) {
-      const int uu = u_first + kWaves * (i / ut);
-      if (uu < u_hi) load_tile(uu, i % ut, i);
-    }
+  for (int i = 0; i < kSlots; ++i) {
+    const int uu = u_first + kWaves * (i / ut);
+    load_tile(uu < u_last ? uu : u_last, i % ut, i);
   }
 
   // This lane's query values (head a_head, channels of lane group lq) on
@@ -1107,7 +1126,9 @@ __global__ void __launch_bounds__(kThreads, (rs_waves<KB, VB, NC, HS>())) decode
     for (int i = 0; i < kStep; ++i) {
       const int uc = u + kWaves * (i / ut);  // this tile's unit
       if (i % ut == 0) {
-        if (i > 0 && uc >= u_hi) break;
+        // (a step's later unit past the end ends the wave's loop: the
+        // next step would start past it too)
+        if (i > 0 && uc >= u_hi) goto units_done;
         // ---- unit start: commit the unit's scales, request the next
         //      unit's, and build Q' for the unit's key group (every unit,
         //      so that Q' is not carried from one unit to the next, which
@@ -1130,7 +1151,8 @@ __global__ void __launch_bounds__(kThreads, (rs_waves<KB, VB, NC, HS>())) decode
           const int idx = lane + 64 * j;
           if (idx < n_vs4) ((float4v*)my_vs)[idx] = vsn[j] * sig_v;
         }
-        int exg = (int)((__builtin_bit_cast(uint32_t, kgn) >> 23) & 0xFF) - 127;
+        const float kgv = KM ? kgn : row_max_lanes32(ksn);
+        int exg = (int)((__builtin_bit_cast(uint32_t, kgv) >> 23) & 0xFF) - 127;
         exg = exg < -100 ? -100 : exg;
         const float sigma_g = __builtin_bit_cast(float, (uint32_t)(127 + 12 - exg) << 23);
         const float inv_sigma_g = __builtin_bit_cast(float, (uint32_t)(127 - 12 + exg) << 23);
@@ -1157,7 +1179,7 @@ __global__ void __launch_bounds__(kThreads, (rs_waves<KB, VB, NC, HS>())) decode
         }
         __builtin_amdgcn_wave_barrier();
         // scales of the wave's next unit
-        if (uc + kWaves < u_hi) load_scales(uc + kWaves);
+        load_scales(uc + kWaves < u_last ? uc + kWaves : u_last);
         {
           isk = inv_sigma_q * inv_sigma_g * 16777216.0f;
           // one limb per lane: the high part, or the rounding residual
@@ -1374,14 +1396,15 @@ __global__ void __launch_bounds__(kThreads, (rs_waves<KB, VB, NC, HS>())) decode
       // refill the slot with the wave's tile kSlots places later
       if (i + kSlots < kStep) {
         const int uf = u + kWaves * ((i + kSlots) / ut);
-        if (uf < u_hi) load_tile(uf, (i + kSlots) % ut, i % kSlots);
+        load_tile(uf < u_last ? uf : u_last, (i + kSlots) % ut, i % kSlots);
       } else {
         const int uf = un + kWaves * ((i + kSlots - kStep) / ut);
-        if (uf < u_hi) load_tile(uf, (i + kSlots - kStep) % ut, i % kSlots);
+        load_tile(uf < u_last ? uf : u_last, (i + kSlots - kStep) % ut, i % kSlots);
       }
     }
     __builtin_amdgcn_wave_barrier();
   }
+units_done:
 
   // ---- per-wave state to LDS (after every wave is done with its P' buffer);
   //      the output divided by sigma_v
