@@ -964,7 +964,9 @@ __global__ void __launch_bounds__(kThreads, (rs_waves<KB, VB, NC, HS>())) decode
   constexpr int kSlots = KM ? 2 : kUnitTiles;
   u32x4 kw[kSlots][2];
   u32x4 vw[kSlots][VB == 4 ? 2 : 1];
-  u32x4 kb16[KM ? kSlots : 1][2];  // mixed keys: the token's bf16 channels
+  // mixed keys: the token's bf16 channels (0-3 and 4-7, each loaded on
+  // its own into its own registers)
+  u32x2 kb16lo[KM ? kSlots : 1][2], kb16hi[KM ? kSlots : 1][2];
   float4v vsn[kVs4];
   float4v ksn = (float4v){0.0f, 0.0f, 0.0f, 0.0f};
   float kgn = 0.0f;
@@ -979,14 +981,15 @@ __global__ void __launch_bounds__(kThreads, (rs_waves<KB, VB, NC, HS>())) decode
         // 2 (kb - n4b) + lq / 2
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) kw[slot][h][kb] = ldnt(&kbase[kb][tok * kstride[kb] + kwi[kb]]);
-        if (NB == 8) {
-          kb16[KM ? slot : 0][h] = ldnt((const u32x4*)(kbp + tok * 8));
-        } else if (NB == 4) {
-          const u32x2 b2 = ldnt((const u32x2*)(kbp + tok * 4));
-          kb16[KM ? slot : 0][h] = (u32x4){b2[0], b2[1], 0u, 0u};
-        } else {
-          kb16[KM ? slot : 0][h] = (u32x4){0u, 0u, 0u, 0u};
-        }
+        // (the class sizes act as lane conditions, so every path issues
+        // the same requests and the compiler's wait counts stay exact)
+        int nbv = NB;
+        asm volatile("" : "+v"(nbv));
+        u32x2 lo = {0u, 0u}, hi = {0u, 0u};
+        if (nbv >= 4) lo = ldnt((const u32x2*)(kbp + tok * nbv));
+        if (nbv == 8) hi = ldnt((const u32x2*)(kbp + tok * 8 + 4));
+        kb16lo[KM ? slot : 0][h] = lo;
+        kb16hi[KM ? slot : 0][h] = hi;
       } else if (KB == 4) {
         kw[slot][h] = ldnt((const u32x4*)(kc + tok * 16 + 4 * lq));
       } else {
@@ -1010,7 +1013,12 @@ __global__ void __launch_bounds__(kThreads, (rs_waves<KB, VB, NC, HS>())) decode
     // itself when it is committed: a separate uniform load of it would be
     // moved to a scalar register at once, and that move waits for every
     // load in flight, the prefetched tiles included)
-    if (KM) kgn = kg[unit / upg];
+    if (KM) {
+      // (a lane-varying index keeps this one in a vector register)
+      int gi = unit / upg;
+      asm volatile("" : "+v"(gi));
+      kgn = kg[gi];
+    }
     if (KM) kpn = ((const uint16_t*)(kpp + (int64_t)(unit / upg) * kD))[lane];
   };
   // A step of the wave covers kStep tiles: one unit, or kStep / ut units
@@ -1310,7 +1318,8 @@ __global__ void __launch_bounds__(kThreads, (rs_waves<KB, VB, NC, HS>())) decode
           // the bf16 channels: the token's bf16 row is the key operand
           // (k-slots past NB, and every slot of lane groups 1-3, meet zero
           // query limbs)
-          const bf16x8 kbf = __builtin_bit_cast(bf16x8, kb16[KM ? i % kSlots : 0][h]);
+          const u32x2 lo = kb16lo[KM ? i % kSlots : 0][h], hi = kb16hi[KM ? i % kSlots : 0][h];
+          const bf16x8 kbf = __builtin_bit_cast(bf16x8, (u32x4){lo[0], lo[1], hi[0], hi[1]});
           acc[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qbA, kbf, acc[h], 0, 0, 0);
           acc[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qbB, kbf, acc[h], 0, 0, 0);
         }
