@@ -807,6 +807,16 @@ decode_mfma_kernel(MfmaArgs a) {
 // does not round it away without bias over thousands of tiles.
 constexpr int kPlStride = 40;  // halves per P' row: 32 + 8 against bank conflicts
 
+// Requests of the row-score kernel past the wave's last unit read this block
+// of zeros (8 KB: the largest span a request's lane offsets cover is a
+// unit's value scales, 4 KB).  Every path then issues the same requests, so
+// the compiler's wait counts stay exact (a skipped request makes it fall
+// back to waiting for every load in flight at each unit start), and the
+// block stays in cache.  (Not const: the compiler would fold loads from a
+// known-zero array away and bring the skipped requests back.  Nothing
+// writes it; a device variable starts zeroed.)
+__device__ __align__(16) uint32_t kPastZeros[2048];
+
 template <int NC, bool KM>
 struct RsLds {
   float vs[kWaves][kUnitTiles * 32 * NC];
@@ -971,44 +981,58 @@ __global__ void __launch_bounds__(kThreads, (rs_waves<KB, VB, NC, HS>())) decode
   float4v ksn = (float4v){0.0f, 0.0f, 0.0f, 0.0f};
   float kgn = 0.0f;
   uint32_t kpn = 0;  // mixed keys: class positions of channels 2 lane, 2 lane + 1
+  // (a unit past the wave's last reads kPastZeros at the same lane offsets;
+  // for mixed keys, whose many arrays would each need that choice, it reads
+  // the split's last unit again, which its own wave reads at about the
+  // same time)
+  const int u_again = u_hi > 0 ? u_hi - 1 : 0;
   auto load_tile = [&](int unit, int i, int slot) {
-    const int64_t t32 = (int64_t)(unit * ut + i) * 32;
+    const bool past = unit >= u_hi;
+    const int64_t t32 = (int64_t)((KM && past ? u_again : unit) * ut + i) * 32;
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      const int64_t tok = t32 + 16 * h + ln;
+      const int r = 16 * h + ln;  // token of the tile
       if (KM) {
         // word of MFMA block kb: int4 word 4 kb + lq, or int2 word
         // 2 (kb - n4b) + lq / 2
 #pragma unroll
-        for (int kb = 0; kb < 4; ++kb) kw[slot][h][kb] = ldnt(&kbase[kb][tok * kstride[kb] + kwi[kb]]);
+        for (int kb = 0; kb < 4; ++kb)
+          kw[slot][h][kb] = ldnt(&kbase[kb][(t32 + r) * kstride[kb] + kwi[kb]]);
         // (the class sizes act as lane conditions, so every path issues
         // the same requests and the compiler's wait counts stay exact)
         int nbv = NB;
         asm volatile("" : "+v"(nbv));
+        const uint16_t* bb = kbp + (t32 + r) * nbv;
         u32x2 lo = {0u, 0u}, hi = {0u, 0u};
-        if (nbv >= 4) lo = ldnt((const u32x2*)(kbp + tok * nbv));
-        if (nbv == 8) hi = ldnt((const u32x2*)(kbp + tok * 8 + 4));
+        if (nbv >= 4) lo = ldnt((const u32x2*)bb);
+        if (nbv == 8) hi = ldnt((const u32x2*)(bb + 4));
         kb16lo[KM ? slot : 0][h] = lo;
         kb16hi[KM ? slot : 0][h] = hi;
       } else if (KB == 4) {
-        kw[slot][h] = ldnt((const u32x4*)(kc + tok * 16 + 4 * lq));
+        const uint32_t* b = past ? kPastZeros : kc + t32 * 16;
+        kw[slot][h] = ldnt((const u32x4*)(b + r * 16 + 4 * lq));
       } else {
-        const u32x2 w2 = ldnt((const u32x2*)(kc + tok * 8 + 2 * lq));
+        const uint32_t* b = past ? kPastZeros : kc + t32 * 8;
+        const u32x2 w2 = ldnt((const u32x2*)(b + r * 8 + 2 * lq));
         kw[slot][h] = (u32x4){w2[0], w2[1], 0u, 0u};
       }
     }
-    const int64_t tw = (int64_t)(unit * ut + i) * (32 * VB * kD / 32);
-    vw[slot][0] = ldnt((const u32x4*)(vc + tw + lane * 4));
-    if (VB == 4) vw[slot][VB == 4 ? 1 : 0] = ldnt((const u32x4*)(vc + tw + 256 + lane * 4));
+    const uint32_t* vb = (!KM && past) ? kPastZeros : vc + t32 * (VB * kD / 32);
+    vw[slot][0] = ldnt((const u32x4*)(vb + lane * 4));
+    if (VB == 4) vw[slot][VB == 4 ? 1 : 0] = ldnt((const u32x4*)(vb + 256 + lane * 4));
   };
   auto load_scales = [&](int unit) {
-    const float4v* src = (const float4v*)(vs + (int64_t)unit * ut * 32 * NC);
+    const bool past = !KM && unit >= u_hi;
+    if (KM && unit >= u_hi) unit = u_again;
+    const float4v* src =
+        (const float4v*)(past ? (const float*)kPastZeros : vs + (int64_t)unit * ut * 32 * NC);
 #pragma unroll
     for (int j = 0; j < kVs4; ++j) {
       const int idx = lane + 64 * j;
       if (idx < n_vs4) vsn[j] = ldnt(src + idx);
     }
-    if (lane < ksrow / 4) ksn = ((const float4v*)(ks + (int64_t)(unit / upg) * ksrow))[lane];
+    const float* ksr = past ? (const float*)kPastZeros : ks + (int64_t)(unit / upg) * ksrow;
+    if (lane < ksrow / 4) ksn = ((const float4v*)ksr)[lane];
     // (uniform keys take the group's largest scale from the scale row
     // itself when it is committed: a separate uniform load of it would be
     // moved to a scalar register at once, and that move waits for every
@@ -1018,8 +1042,8 @@ __global__ void __launch_bounds__(kThreads, (rs_waves<KB, VB, NC, HS>())) decode
       int gi = unit / upg;
       asm volatile("" : "+v"(gi));
       kgn = kg[gi];
+      kpn = ((const uint16_t*)(kpp + (int64_t)(unit / upg) * kD))[lane];
     }
-    if (KM) kpn = ((const uint16_t*)(kpp + (int64_t)(unit / upg) * kD))[lane];
   };
   // A step of the wave covers kStep tiles: one unit, or kStep / ut units
   // (u, u + 4, ...) when units are shorter than the slot ring, so the code
@@ -1044,18 +1068,13 @@ __global__ void __launch_bounds__(kThreads, (rs_waves<KB, VB, NC, HS>())) decode
       for (int c = 0; c < 8; ++c) qraw[c] = *(const u32x4*)((const float*)a.q + base + 4 * c);
     }
   }
-  // Every request names a valid unit (n_units >= 1 here): past u_hi, or for
-  // a wave without units, the index is clamped and the data is not used.
-  // The requests are then the same on every path, so the compiler's wait
-  // counts stay exact instead of falling back to waiting for every load in
-  // flight at each unit start.
-  const int u_last = n_units - 1;
-  load_scales(u_first < u_last ? u_first : u_last);
+  // Every request is issued on every path (past the wave's last unit, or
+  // for a wave without units, it reads kPastZeros or, for mixed keys, the
+  // split's last unit), scales first, then the tiles: the order of the
+  // loop's own requests.
+  load_scales(u_first);
 #pragma unroll
-  for (int i = 0; i < kSlots; ++i) {
-    const int uu = u_first + kWaves * (i / ut);
-    load_tile(uu < u_last ? uu : u_last, i % ut, i);
-  }
+  for (int i = 0; i < kSlots; ++i) load_tile(u_first + kWaves * (i / ut), i % ut, i);
 
   // This lane's query values (head a_head, channels of lane group lq) on
   // its key k-slots, times the inverse slot factor, sm_scale * log2(e) and
@@ -1187,7 +1206,7 @@ __global__ void __launch_bounds__(kThreads, (rs_waves<KB, VB, NC, HS>())) decode
         }
         __builtin_amdgcn_wave_barrier();
         // scales of the wave's next unit
-        load_scales(uc + kWaves < u_last ? uc + kWaves : u_last);
+        load_scales(uc + kWaves);
         {
           isk = inv_sigma_q * inv_sigma_g * 16777216.0f;
           // one limb per lane: the high part, or the rounding residual
@@ -1405,10 +1424,10 @@ __global__ void __launch_bounds__(kThreads, (rs_waves<KB, VB, NC, HS>())) decode
       // refill the slot with the wave's tile kSlots places later
       if (i + kSlots < kStep) {
         const int uf = u + kWaves * ((i + kSlots) / ut);
-        load_tile(uf < u_last ? uf : u_last, (i + kSlots) % ut, i % kSlots);
+        load_tile(uf, (i + kSlots) % ut, i % kSlots);
       } else {
         const int uf = un + kWaves * ((i + kSlots - kStep) / ut);
-        load_tile(uf < u_last ? uf : u_last, (i + kSlots - kStep) % ut, i % kSlots);
+        load_tile(uf, (i + kSlots - kStep) % ut, i % kSlots);
       }
     }
     __builtin_amdgcn_wave_barrier();
