@@ -318,7 +318,8 @@ def ext_workload(torch, kvq, dev, stream, name, args, flush_buf):
         view = kvq.ext_view(B, Hkv, D, N, keys, values, w["k_bits"], w["v_bits"],
                             w["G"], w["Gv"], k_lut=lk, v_lut=lv)
         keep = (keys, values)
-        kernel = "decode_ext_kernel (codebook keys and values, outliers) + merge_ext_kernel"
+        kernel = ("decode_ext_mfma_kernel (codebook keys and values, outliers) + "
+                  "merge_ext_kernel")
     else:
         jl = torch.from_numpy(synth.jl_matrix(args.seed, w["qjl_m"], D)).to(dev)
         kvq.kvq_quantize_k(kvq.kvq_hadamard(kt[:1, :256].contiguous(), out_dtype=torch.float32),
@@ -339,7 +340,8 @@ def ext_workload(torch, kvq, dev, stream, name, args, flush_buf):
         view = kvq.ext_view(B, Hkv, D, N, keys, values, w["k_bits"], w["v_bits"],
                             w["G"], w["Gv"], sketch=sk, rnorm=rn, jl=jl, v_rotated=True)
         keep = (keys, values, sk, rn, jl)
-        kernel = "decode_ext_kernel (symmetric keys, values with the sketch) + merge_ext_kernel"
+        kernel = ("decode_ext_mfma_kernel (symmetric keys, values with the sketch) + "
+                  "merge_ext_kernel")
     torch.cuda.synchronize()
     quant_us = 1000 * e0.elapsed_time(e1)
     del kt, vt
