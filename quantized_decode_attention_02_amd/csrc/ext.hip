@@ -1328,14 +1328,28 @@ decode_ext_mfma_kernel(ExtArgs a, const QT* __restrict__ q) {
       float ls = p;
       ls = wave_sum64(ls);
       const float alpha = exp2f(m_old - m_new);
-      ps[h * kCT + lane] = p;
       if (M) pg[h * kCT + lane] = lane < n ? p * gam[lane] * gsig : 0.0f;
       for (int j = 0; j < ngv; ++j) {
         const float pv = lane < n ? p * vsl[lane * ngv + j] * vsig : 0.0f;
         Pv[(h * ngv + j) * kLvStride + lane] = __builtin_bit_cast(uint16_t, (_Float16)pv);
       }
-      if (vo)  // the value-outlier side accumulator follows the softmax
+      if (vo) {
+        // the value-outlier side accumulator of head h follows the softmax,
+        // then takes this chunk's outliers, p_t * value (this wave only
+        // touches row h; lanes that meet on a channel add atomically)
         for (int c = lane; c < D; c += 64) OC[h * D + c] *= alpha;
+        for (int i0 = 0; i0 < n * per_t; i0 += 64) {
+          const int i = i0 + lane;
+          const bool in = i < n * per_t;
+          const uint32_t e = in ? vol[i] : 0u;
+          const int t = in ? div_pt(i) : 0;
+          const float pt = __shfl(p, t);
+          if (in && (e & 0x7FFFu) != 0) {
+            const int cc = div_vno(i - t * per_t) * v.group_ch + (int)(e >> 16);
+            atomicAdd(&OC[h * D + cc], pt * h2f((uint16_t)(e & 0xFFFFu)));
+          }
+        }
+      }
       if (lane == 0) {
         st[h] = m_new;
         st[8 + h] = st[8 + h] * alpha + ls;
@@ -1343,16 +1357,6 @@ decode_ext_mfma_kernel(ExtArgs a, const QT* __restrict__ q) {
       }
     }
     __syncthreads();
-    if (vo) {
-      for (int i = tid; i < n * per_t; i += kThreads) {
-        const uint32_t e = vol[i];
-        if ((e & 0x7FFFu) == 0) continue;
-        const int t = div_pt(i), r = i - t * per_t;
-        const int cc = div_vno(r) * v.group_ch + (int)(e >> 16);
-        const float val = h2f((uint16_t)(e & 0xFFFFu));
-        for (int h = 0; h < g; ++h) atomicAdd(&OC[h * D + cc], ps[h * kCT + t] * val);
-      }
-    }
     // ---- values: channel blocks wave, wave + 4 of 16 channels; columns
     //      (head, value group); two 32-token steps
     {
