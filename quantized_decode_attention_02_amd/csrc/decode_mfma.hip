@@ -817,7 +817,7 @@ constexpr int kPlStride = 40;  // halves per P' row: 32 + 8 against bank conflic
 // writes it; a device variable starts zeroed.)
 __device__ __align__(16) uint32_t kPastZeros[2048];
 
-template <int NC, bool KM>
+template <int NC, bool KM, int QR>
 struct RsLds {
   float vs[kWaves][kUnitTiles * 32 * NC];
   float ks[kWaves][kD];
@@ -831,12 +831,18 @@ struct RsLds {
   float l[kWaves][8];
   union alignas(16) {
     float o[kWaves][8][kD + 1];
-    _Float16 pl[kWaves][16][kPlStride];
+    struct {
+      _Float16 pl[kWaves][16][kPlStride];
+      // uniform keys: each wave's Q' limbs in the A layout, by key MFMA,
+      // lane group and distinct row (2 head + limb; QR rows), four words
+      // of fp16 pairs per entry
+      u32x4 qp[KM ? 1 : kWaves][4][4][KM ? 1 : QR];
+    } t;
   } u;
 };
-template <int NC, bool KM>
+template <int NC, bool KM, int QR>
 constexpr size_t rs_lds_bytes() {
-  return sizeof(RsLds<NC, KM>) > sizeof(RowsLds) ? sizeof(RsLds<NC, KM>) : sizeof(RowsLds);
+  return sizeof(RsLds<NC, KM, QR>) > sizeof(RowsLds) ? sizeof(RsLds<NC, KM, QR>) : sizeof(RowsLds);
 }
 
 // KB: uniform key bits (4 or 2), or 0 for mixed keys (bf16 / int4 / int2
@@ -853,7 +859,8 @@ constexpr int rs_waves() {
 template <int KB, int VB, int NC, int HS, int UT>
 __global__ void __launch_bounds__(kThreads, (rs_waves<KB, VB, NC, HS>())) decode_rs_kernel(MfmaArgs a) {
   constexpr bool KM = KB == 0;  // mixed-precision keys
-  __shared__ __align__(16) unsigned char lds_raw[rs_lds_bytes<NC, KM>()];
+  constexpr int QR = HS == 1 ? 2 : 16;  // distinct Q' rows (head, limb)
+  __shared__ __align__(16) unsigned char lds_raw[rs_lds_bytes<NC, KM, QR>()];
   const PartIndex pi = part_index(a);
   const int part = pi.part, kvh = pi.kvh, b = pi.b;
   const int n_fp = a.n_parts - a.n_splits;
@@ -862,7 +869,7 @@ __global__ void __launch_bounds__(kThreads, (rs_waves<KB, VB, NC, HS>())) decode
     return;
   }
   const int split = part - n_fp;
-  RsLds<NC, KM>& S = *(RsLds<NC, KM>*)lds_raw;
+  RsLds<NC, KM, QR>& S = *(RsLds<NC, KM, QR>*)lds_raw;
   const kvq_kv_view& v = a.v;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
@@ -899,7 +906,7 @@ __global__ void __launch_bounds__(kThreads, (rs_waves<KB, VB, NC, HS>())) decode
   const float* vs = v.v_scales + s * v.v_scales_stride;
   float* my_vs = S.vs[wave];
   float* my_ks = S.ks[wave];
-  _Float16(*my_pl)[kPlStride] = S.u.pl[wave];
+  _Float16(*my_pl)[kPlStride] = S.u.t.pl[wave];
   // mixed keys: class sizes, packed row words, and the MFMA blocks (the
   // first n4b take int4 positions, the rest int2 positions, 32 each)
   const int NB = KM ? v.n_bf16 : 0, N4 = KM ? v.n_int4 : 0, N2 = kD - NB - N4;
@@ -1270,29 +1277,35 @@ __global__ void __launch_bounds__(kThreads, (rs_waves<KB, VB, NC, HS>())) decode
               }
             }
           } else {
-          const float* kss = my_ks + 32 * lq;
-          float ksv[32];
-#pragma unroll
-          for (int c = 0; c < 32; c += 4) {
-            const float4v t4 = *(const float4v*)(kss + c);
-            ksv[c] = t4[0]; ksv[c + 1] = t4[1]; ksv[c + 2] = t4[2]; ksv[c + 3] = t4[3];
+          // Q' limbs: the A operand repeats each (head, limb) row over the
+          // row groups and the limb lanes share the high part, so the wave
+          // forms each distinct product once: lane (kb, lq, i) = (lane >> 4,
+          // (lane >> 2) & 3, lane & 3) takes slot pair i of key MFMA kb and
+          // lane group lq for every distinct head (nh of them), stores the
+          // high and low limbs in LDS, and every lane then reads its four
+          // operands (the same products and roundings as forming them in
+          // place)
+          (void)lmask;
+          const int nh = HS == 1 ? 1 : 2 * rgd;
+          const int bkb = lane >> 4, blq = (lane >> 2) & 3, bi = lane & 3;
+          const int c0 = 32 * blq + k_slot_channel<KB == 0 ? 4 : KB>(bkb, bi, 0);
+          const float k0 = my_ks[c0], k1 = my_ks[c0 + (KB == 4 ? 4 : 8)];
+          const float* qsrc = (const float*)&S.qf[2 * bkb + (bi >> 1)][16 * blq] + 2 * (bi & 1);
+          uint32_t* qdst = (uint32_t*)&S.u.t.qp[wave][bkb][blq][0] + bi;
+          for (int hh = 0; hh < nh; ++hh) {
+            // lane 2 hh of each lane group holds head hh (limb 0) in qf
+            const float2 qq = *(const float2*)(qsrc + 8 * hh);
+            const float x0 = qq.x * k0, x1 = qq.y * k1;
+            const half2v hi = {(_Float16)x0, (_Float16)x1};
+            const half2v lo = {(_Float16)(x0 - (float)hi[0]), (_Float16)(x1 - (float)hi[1])};
+            qdst[8 * hh] = __builtin_bit_cast(uint32_t, hi);
+            qdst[8 * hh + 4] = __builtin_bit_cast(uint32_t, lo);
           }
+          __builtin_amdgcn_wave_barrier();
+          const int qrow = HS == 1 ? limb : 2 * a_head + limb;
 #pragma unroll
-          for (int kb = 0; kb < 4; ++kb) {
-            const float4v q0 = S.qf[2 * kb][lane], q1 = S.qf[2 * kb + 1][lane];
-            const float qk[8] = {q0[0], q0[1], q0[2], q0[3], q1[0], q1[1], q1[2], q1[3]};
-            u32x4 r;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const float x0 = qk[2 * i] * ksv[k_slot_channel<KB == 0 ? 4 : KB>(kb, i, 0)];
-              const float x1 = qk[2 * i + 1] * ksv[k_slot_channel<KB == 0 ? 4 : KB>(kb, i, 1)];
-              const half2v hi = {(_Float16)x0, (_Float16)x1};
-              const half2v hsel = __builtin_bit_cast(half2v, __builtin_bit_cast(uint32_t, hi) & lmask);
-              const half2v res = {(_Float16)(x0 - (float)hsel[0]), (_Float16)(x1 - (float)hsel[1])};
-              r[i] = __builtin_bit_cast(uint32_t, res);
-            }
-            qa[kb] = __builtin_bit_cast(half8, r);
-          }
+          for (int kb = 0; kb < 4; ++kb)
+            qa[kb] = __builtin_bit_cast(half8, S.u.t.qp[wave][kb][lq][qrow]);
           const half8 aoff = k_offset_operand<KB == 0 ? 4 : KB>();
           float4v c = (float4v){0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
