@@ -966,8 +966,22 @@ __global__ void __launch_bounds__(kThreads, (rs_waves<KB, VB, NC, HS>())) decode
   float4v o[8];
 #pragma unroll
   for (int jb = 0; jb < 8; ++jb) o[jb] = (float4v){0.0f, 0.0f, 0.0f, 0.0f};
+  // Raw value operands (RV): 2-bit value codes masked in place, as fp16
+  // denormals (f * u * 2^-24, exact), like the key operands; their offset
+  // term 2^-24 * off * sum_t f_t P'_t goes to ocorr through one more MFMA
+  // per tile (every row of it holds its column's term) and is taken out of
+  // o at the start of each step, so that the offset never piles up over
+  // more than one step's tokens; o carries the factor 2^-24 to the end.
+  // Taken for mixed keys and for 2-bit keys with one head slot, where it
+  // runs faster (1M-token MHA layer 464 -> 450 us, MixKVQ 32K x 8 85 -> 82
+  // us per call); with 4-bit keys it ran slower (the 128K GQA layer 41.7 ->
+  // 44.5 us) and with two head slots the three-wave variants spill.  The
+  // other variants keep the magic-number operands with the offset
+  // subtracted per code.
+  constexpr bool RV = VB == 2 && (KB == 0 || (KB == 2 && HS == 1));
+  float4v ocorr = (float4v){0.0f, 0.0f, 0.0f, 0.0f};
   uint32_t magic = 0x64006400u;
-  asm volatile("" : "+v"(magic));  // keep the fp16 magic in a VGPR
+  if (!RV) asm volatile("" : "+v"(magic));  // keep the fp16 magic in a VGPR
 
   int ev = 0;            // sigma_v = 2^(kVTop - ev) (see unit_vscale_exp)
   bool ev_set = false;
@@ -1156,6 +1170,11 @@ __global__ void __launch_bounds__(kThreads, (rs_waves<KB, VB, NC, HS>())) decode
 
   for (int u = u_first; u < u_hi; u += kWaves * ups) {
     const int un = u + kWaves * ups;  // first unit of the next step
+    if (RV) {
+#pragma unroll
+      for (int jb = 0; jb < 8; ++jb) o[jb] -= ocorr;
+      ocorr = (float4v){0.0f, 0.0f, 0.0f, 0.0f};
+    }
 #pragma unroll
     for (int i = 0; i < kStep; ++i) {
       const int uc = u + kWaves * (i / ut);  // this tile's unit
@@ -1174,6 +1193,7 @@ __global__ void __launch_bounds__(kThreads, (rs_waves<KB, VB, NC, HS>())) decode
               const float r = pow2f(ev - e);
 #pragma unroll
               for (int jb = 0; jb < 8; ++jb) o[jb] *= r;
+              if (RV) ocorr *= r;
             }
             ev = e;
             ev_set = true;
@@ -1392,6 +1412,7 @@ __global__ void __launch_bounds__(kThreads, (rs_waves<KB, VB, NC, HS>())) decode
         }
 #pragma unroll
         for (int jb = 0; jb < 8; ++jb) o[jb] *= av;
+        if (RV) ocorr *= av;
       }
       // p / f(slot pair) for the value operand, sums of the unscaled p
       float p[2][HS];
@@ -1401,13 +1422,30 @@ __global__ void __launch_bounds__(kThreads, (rs_waves<KB, VB, NC, HS>())) decode
         p[1][hl] = __builtin_amdgcn_exp2f(__builtin_fmaf(sc[1][hl], sk, cm[1][hl]));
         l_part[hl] = __builtin_fmaf(p[0][hl], f0, __builtin_fmaf(p[1][hl], f1, l_part[hl]));
       }
-      // ---- P' = p * v_scale into the value B layout
+      // ---- P' = p * v_scale into the value B layout, with no lane
+      //      conditions: rows of heads at or past g feed only output columns
+      //      that are never kept, and a lane whose value group c is past NC
+      //      (possible only when g * NC < 16) writes row 15, which then
+      //      belongs to no head below g.  (2-bit keys with 4-bit values and
+      //      two head slots keep the lane conditions: without them those
+      //      variants spill at three waves per SIMD.)
+      constexpr bool kNoLaneIf = !(KB == 2 && VB == 4 && HS == 2);
       const float* vrow = my_vs + ((i % ut) * 32 + ln) * NC;
 #pragma unroll
       for (int j = 0; j < NC; ++j) {
         if (j >= niter) break;
         const int c = rep_idx + j * rep;
-        if (c < NC) {
+        if (kNoLaneIf) {
+          const bool cok = c < NC;
+          const int cr = cok ? c : NC - 1;
+          const float vs0 = vrow[cr], vs1 = vrow[16 * NC + cr];
+#pragma unroll
+          for (int hl = 0; hl < HS; ++hl) {
+            _Float16* row = my_pl[cok ? s_head[hl] * NC + c : 15];
+            row[kpos] = (_Float16)(p[0][hl] * vs0);
+            row[kpos + 4] = (_Float16)(p[1][hl] * vs1);
+          }
+        } else if (c < NC) {
           const float vs0 = vrow[c], vs1 = vrow[16 * NC + c];
 #pragma unroll
           for (int hl = 0; hl < HS; ++hl) {
@@ -1425,7 +1463,10 @@ __global__ void __launch_bounds__(kThreads, (rs_waves<KB, VB, NC, HS>())) decode
 #pragma unroll
       for (int jb = 0; jb < 8; ++jb) {
         half8 A;
-        if (VB == 2) {
+        if (RV) {
+          const uint32_t word = vw[i % kSlots][0][jb >> 1];
+          A = int2_key_operand((jb & 1) ? (word >> 8) : word);
+        } else if (VB == 2) {
           const uint32_t word = vw[i % kSlots][0][jb >> 1];
           A = int2_operand((jb & 1) ? (word >> 8) : word, magic);
         } else {
@@ -1433,6 +1474,7 @@ __global__ void __launch_bounds__(kThreads, (rs_waves<KB, VB, NC, HS>())) decode
         }
         o[jb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, pb, o[jb], 0, 0, 0);
       }
+      if (RV) ocorr = __builtin_amdgcn_mfma_f32_16x16x32_f16(k_offset_operand<2>(), pb, ocorr, 0, 0, 0);
       __builtin_amdgcn_wave_barrier();
       // refill the slot with the wave's tile kSlots places later
       if (i + kSlots < kStep) {
@@ -1452,9 +1494,10 @@ units_done:
 #pragma unroll
   for (int hl = 0; hl < HS; ++hl) l_part[hl] = row_sum16(l_part[hl]);
   if (ev_set) {
-    const float r = pow2f(ev - kVTop);
+    // (2-bit values: the last step's offset term out, and 2^24); 1 / sigma_v
+    const float r = pow2f(ev - kVTop + (RV ? 24 : 0));
 #pragma unroll
-    for (int jb = 0; jb < 8; ++jb) o[jb] *= r;
+    for (int jb = 0; jb < 8; ++jb) o[jb] = (RV ? o[jb] - ocorr : o[jb]) * r;
   }
   __syncthreads();
   if (ln == 0 && lq < rgd) {
