@@ -966,22 +966,8 @@ __global__ void __launch_bounds__(kThreads, (rs_waves<KB, VB, NC, HS>())) decode
   float4v o[8];
 #pragma unroll
   for (int jb = 0; jb < 8; ++jb) o[jb] = (float4v){0.0f, 0.0f, 0.0f, 0.0f};
-  // Raw value operands (RV): 2-bit value codes masked in place, as fp16
-  // denormals (f * u * 2^-24, exact), like the key operands; their offset
-  // term 2^-24 * off * sum_t f_t P'_t goes to ocorr through one more MFMA
-  // per tile (every row of it holds its column's term) and is taken out of
-  // o at the start of each step, so that the offset never piles up over
-  // more than one step's tokens; o carries the factor 2^-24 to the end.
-  // Taken for mixed keys and for 2-bit keys with one head slot, where it
-  // runs faster (1M-token MHA layer 464 -> 450 us, MixKVQ 32K x 8 85 -> 82
-  // us per call); with 4-bit keys it ran slower (the 128K GQA layer 41.7 ->
-  // 44.5 us) and with two head slots the three-wave variants spill.  The
-  // other variants keep the magic-number operands with the offset
-  // subtracted per code.
-  constexpr bool RV = VB == 2 && (KB == 0 || (KB == 2 && HS == 1));
-  float4v ocorr = (float4v){0.0f, 0.0f, 0.0f, 0.0f};
   uint32_t magic = 0x64006400u;
-  if (!RV) asm volatile("" : "+v"(magic));  // keep the fp16 magic in a VGPR
+  asm volatile("" : "+v"(magic));  // keep the fp16 magic in a VGPR
 
   int ev = 0;            // sigma_v = 2^(kVTop - ev) (see unit_vscale_exp)
   bool ev_set = false;
@@ -1170,11 +1156,6 @@ __global__ void __launch_bounds__(kThreads, (rs_waves<KB, VB, NC, HS>())) decode
 
   for (int u = u_first; u < u_hi; u += kWaves * ups) {
     const int un = u + kWaves * ups;  // first unit of the next step
-    if (RV) {
-#pragma unroll
-      for (int jb = 0; jb < 8; ++jb) o[jb] -= ocorr;
-      ocorr = (float4v){0.0f, 0.0f, 0.0f, 0.0f};
-    }
 #pragma unroll
     for (int i = 0; i < kStep; ++i) {
       const int uc = u + kWaves * (i / ut);  // this tile's unit
@@ -1193,7 +1174,6 @@ __global__ void __launch_bounds__(kThreads, (rs_waves<KB, VB, NC, HS>())) decode
               const float r = pow2f(ev - e);
 #pragma unroll
               for (int jb = 0; jb < 8; ++jb) o[jb] *= r;
-              if (RV) ocorr *= r;
             }
             ev = e;
             ev_set = true;
@@ -1412,7 +1392,6 @@ __global__ void __launch_bounds__(kThreads, (rs_waves<KB, VB, NC, HS>())) decode
         }
 #pragma unroll
         for (int jb = 0; jb < 8; ++jb) o[jb] *= av;
-        if (RV) ocorr *= av;
       }
       // p / f(slot pair) for the value operand, sums of the unscaled p
       float p[2][HS];
@@ -1463,10 +1442,7 @@ __global__ void __launch_bounds__(kThreads, (rs_waves<KB, VB, NC, HS>())) decode
 #pragma unroll
       for (int jb = 0; jb < 8; ++jb) {
         half8 A;
-        if (RV) {
-          const uint32_t word = vw[i % kSlots][0][jb >> 1];
-          A = int2_key_operand((jb & 1) ? (word >> 8) : word);
-        } else if (VB == 2) {
+        if (VB == 2) {
           const uint32_t word = vw[i % kSlots][0][jb >> 1];
           A = int2_operand((jb & 1) ? (word >> 8) : word, magic);
         } else {
@@ -1474,7 +1450,6 @@ __global__ void __launch_bounds__(kThreads, (rs_waves<KB, VB, NC, HS>())) decode
         }
         o[jb] = __builtin_amdgcn_mfma_f32_16x16x32_f16(A, pb, o[jb], 0, 0, 0);
       }
-      if (RV) ocorr = __builtin_amdgcn_mfma_f32_16x16x32_f16(k_offset_operand<2>(), pb, ocorr, 0, 0, 0);
       __builtin_amdgcn_wave_barrier();
       // refill the slot with the wave's tile kSlots places later
       if (i + kSlots < kStep) {
@@ -1494,10 +1469,9 @@ units_done:
 #pragma unroll
   for (int hl = 0; hl < HS; ++hl) l_part[hl] = row_sum16(l_part[hl]);
   if (ev_set) {
-    // (2-bit values: the last step's offset term out, and 2^24); 1 / sigma_v
-    const float r = pow2f(ev - kVTop + (RV ? 24 : 0));
+    const float r = pow2f(ev - kVTop);
 #pragma unroll
-    for (int jb = 0; jb < 8; ++jb) o[jb] = (RV ? o[jb] - ocorr : o[jb]) * r;
+    for (int jb = 0; jb < 8; ++jb) o[jb] *= r;
   }
   __syncthreads();
   if (ln == 0 && lq < rgd) {

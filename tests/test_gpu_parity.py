@@ -304,8 +304,7 @@ def oracle_decode(q, oc, Hkv, sm_scale=None):
     return np.stack(outs)
 
 
-def split_bound(q, oc, Hkv, weight_round, chain, sm_scale=None, denorm=0.0,
-                raw_gv=0):
+def split_bound(q, oc, Hkv, weight_round, chain, sm_scale=None, denorm=0.0):
     """Per output row, a bound on |o(n_splits = a) - o(n_splits = b)|_2
     from the arithmetic of the kernels, evaluated on the oracle's K_hat,
     V_hat in float64.
@@ -325,13 +324,8 @@ def split_bound(q, oc, Hkv, weight_round, chain, sm_scale=None, denorm=0.0,
     and |code| v_scale <= max|v|, so a token adds at most
     2^-25 f qmax v_scale / 2^5 <= 2^-30 f max|v| to a channel: `denorm`
     = 2^-30 f_max (f_max the largest slot factor of the value operand, 64
-    for 2-bit and 16 for 4-bit values), 0 for float32 weights.  Where the
-    value operands are 2-bit codes in offset binary (raw_gv = Gv: the
-    matrix-core path adds code + 2 times P' and takes the offset term out
-    once per four-tile step), the accumulator holds up to |v| + 2 s per
-    token, s the token's value scale, which is the largest |v_hat| of its
-    value group (every nonzero group reaches +-qmax = 1).  The difference
-    of two split counts is at most twice the sum.
+    for 2-bit and 16 for 4-bit values), 0 for float32 weights.  The
+    difference of two split counts is at most twice the sum.
     """
     B, Hq, D = q.shape
     g = Hq // Hkv
@@ -345,11 +339,7 @@ def split_bound(q, oc, Hkv, weight_round, chain, sm_scale=None, denorm=0.0,
             p = np.exp(s - s.max())
             o = p @ vh / p.sum()
             dev = (p @ np.abs(vh - o)) / p.sum()
-            av = np.abs(vh)
-            if raw_gv:
-                s_t = av.reshape(av.shape[0], -1, raw_gv).max(axis=2)
-                av = av + 2.0 * np.repeat(s_t, raw_gv, axis=1)
-            mag = (p @ av) / p.sum() + np.abs(o)
+            mag = (p @ np.abs(vh)) / p.sum() + np.abs(o)
             ds = (2.0 ** -20 + D * 2.0 ** -24) * sm * (np.abs(kh) @ np.abs(qq))
             eta = weight_round + float(ds.max())
             n = kh.shape[0]
@@ -365,15 +355,13 @@ def assert_split_invariance(outs, q, oc, Hkv, n_tok, sm_scale=None):
     at most the tokens of one partial, the matrix-core one the tiles of one
     wave plus the merges."""
     f_max = 64 if oc.cfg.v_bits == 2 else 16
-    raw = oc.cfg.Gv if oc.cfg.v_bits == 2 else 0
-    for flags, wr, chain, dn, rg in (
-            (kvq.KVQ_DECODE_AUTO, 2.0 ** -11, n_tok // 32 + n_tok // 128 + 64,
-             2.0 ** -30 * f_max, raw),
-            (kvq.KVQ_DECODE_GENERIC, 2.0 ** -24, n_tok + 64, 0.0, 0)):
+    for flags, wr, chain, dn in ((kvq.KVQ_DECODE_AUTO, 2.0 ** -11, n_tok // 32 + 64,
+                                  2.0 ** -30 * f_max),
+                                 (kvq.KVQ_DECODE_GENERIC, 2.0 ** -24, n_tok + 64, 0.0)):
         keys = sorted(s for f, s in outs if f == flags)
         if len(keys) < 2:
             continue
-        bound = split_bound(q, oc, Hkv, wr, chain, sm_scale, dn, rg)
+        bound = split_bound(q, oc, Hkv, wr, chain, sm_scale, dn)
         a = outs[(flags, keys[0])]
         for s in keys[1:]:
             diff = np.linalg.norm(outs[(flags, s)] - a, axis=-1)
@@ -492,9 +480,8 @@ def test_uniform_weights_long_wave(name):
     """q = 0 gives every token the same weight, so the output is the mean
     of V_hat over the whole context, far smaller than the values or the
     weight sums.  With one split each wave sums a quarter of the context
-    (hundreds of four-tile steps); the matrix-core path carries the 2-bit
-    value codes in offset binary through its accumulator within a step, so
-    a cancellation error would show here first."""
+    (hundreds of tiles into one accumulator), so any drift of the value
+    sums relative to their terms would show here first."""
     say("uniform weights", name)
     q, oc, gc, Hkv = build_both(name, LONG_CASES)
     view = gc.kvq_cache_view()
