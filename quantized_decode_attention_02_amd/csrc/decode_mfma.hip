@@ -821,7 +821,10 @@ template <int NC, bool KM, int QR>
 struct RsLds {
   float vs[kWaves][kUnitTiles * 32 * NC];
   float ks[kWaves][kD];
-  float4v qf[8][64];
+  // lane l's query values at column l + l / 16: the Q' build reads one
+  // column of each lane group per lane, and the padding puts the four lane
+  // groups in distinct banks
+  float4v qf[8][64 + 4];
   // mixed keys: q * sm_scale * log2(e) * sigma_q by channel; rows padded
   // to 132 floats so that the heads of one channel fall in distinct banks
   // (the Q' gather reads one channel of up to eight heads per instruction)
@@ -835,8 +838,9 @@ struct RsLds {
       _Float16 pl[kWaves][16][kPlStride];
       // uniform keys: each wave's Q' limbs in the A layout, by key MFMA,
       // lane group and distinct row (2 head + limb; QR rows), four words
-      // of fp16 pairs per entry
-      u32x4 qp[KM ? 1 : kWaves][4][4][KM ? 1 : QR];
+      // of fp16 pairs per entry; 16 rows are padded to 17 so that the four
+      // lane groups' stores fall in distinct banks
+      u32x4 qp[KM ? 1 : kWaves][4][4][KM ? 1 : (QR == 16 ? 17 : QR)];
     } t;
   } u;
 };
@@ -1144,8 +1148,8 @@ __global__ void __launch_bounds__(kThreads, (rs_waves<KB, VB, NC, HS>())) decode
           for (int e = 0; e < 2; ++e)
             qf[2 * i + e] = qv[k_slot_channel<KB == 0 ? 4 : KB>(kb, i, e)] * sigma_q *
                             (1.0f / (float)(1 << slot_log2f<KB == 0 ? 4 : KB>(i)));
-        S.qf[2 * kb][lane] = (float4v){qf[0], qf[1], qf[2], qf[3]};
-        S.qf[2 * kb + 1][lane] = (float4v){qf[4], qf[5], qf[6], qf[7]};
+        S.qf[2 * kb][lane + (lane >> 4)] = (float4v){qf[0], qf[1], qf[2], qf[3]};
+        S.qf[2 * kb + 1][lane + (lane >> 4)] = (float4v){qf[4], qf[5], qf[6], qf[7]};
       }
     }
   }
@@ -1290,7 +1294,7 @@ __global__ void __launch_bounds__(kThreads, (rs_waves<KB, VB, NC, HS>())) decode
           const int bkb = lane >> 4, blq = (lane >> 2) & 3, bi = lane & 3;
           const int c0 = 32 * blq + k_slot_channel<KB == 0 ? 4 : KB>(bkb, bi, 0);
           const float k0 = my_ks[c0], k1 = my_ks[c0 + (KB == 4 ? 4 : 8)];
-          const float* qsrc = (const float*)&S.qf[2 * bkb + (bi >> 1)][16 * blq] + 2 * (bi & 1);
+          const float* qsrc = (const float*)&S.qf[2 * bkb + (bi >> 1)][17 * blq] + 2 * (bi & 1);
           uint32_t* qdst = (uint32_t*)&S.u.t.qp[wave][bkb][blq][0] + bi;
           for (int hh = 0; hh < nh; ++hh) {
             // lane 2 hh of each lane group holds head hh (limb 0) in qf
