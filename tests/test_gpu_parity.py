@@ -215,6 +215,13 @@ CACHE_CASES = {
     "k2v2_g32_mha": (dict(D=128, S=1, G=32, Gv=128, R=32, k_bits=2,
                           v_bits=2), 1, 2, 2, 1000, [1000],
                      dict(outliers="fraction", frac=0.02, sink_factor=20.0)),
+    # g = 6 and 7: the last head slots of the row groups (heads 6 and 7, or
+    # 7) hold no query head, so their P' rows and output columns are unused
+    "k4v2_g6": (dict(D=128, S=1, G=64, Gv=64, R=64, k_bits=4, v_bits=2),
+                1, 12, 2, 800, [800], dict(outliers="per_head", n_out=2)),
+    "k2v2_g7_nc1": (dict(D=128, S=0, G=128, Gv=128, R=128, k_bits=2,
+                         v_bits=2), 1, 7, 1, 900, [900],
+                    dict(outliers="none")),
 }
 MIXED_CASES = {
     "mixkvq_small": (dict(D=128, S=0, G=128, Gv=64, R=128, k_bits=2,
