@@ -354,15 +354,31 @@ decode_generic_kernel(kvq_kv_view v, const QT* __restrict__ q, int Hq,
 // LDS.  More than R * kMergeK partials take further passes.
 constexpr int kMergeThreads = 256;
 constexpr int kMergeK = 16;
+// Wave reductions for the merge: four DPP row rotations (8, 4, 2, 1) give
+// every lane its 16-lane row's result, and the four rows are combined from
+// scalar reads (a chain of VALU steps instead of six cross-lane LDS
+// permutes); the result is the same in every lane.
+template <int CTRL>
+__device__ inline float row_rot(float x) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, false));
+}
+__device__ inline float lane_f(float x, int l) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), l));
+}
 __device__ inline float wave_max(float x) {
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) x = fmaxf(x, __shfl_xor(x, o));
-  return x;
+  x = fmaxf(x, row_rot<0x128>(x));
+  x = fmaxf(x, row_rot<0x124>(x));
+  x = fmaxf(x, row_rot<0x122>(x));
+  x = fmaxf(x, row_rot<0x121>(x));
+  return fmaxf(fmaxf(lane_f(x, 0), lane_f(x, 16)), fmaxf(lane_f(x, 32), lane_f(x, 48)));
 }
 __device__ inline float wave_sum(float x) {
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) x += __shfl_xor(x, o);
-  return x;
+  x += row_rot<0x128>(x);
+  x += row_rot<0x124>(x);
+  x += row_rot<0x122>(x);
+  x += row_rot<0x121>(x);
+  return (lane_f(x, 0) + lane_f(x, 16)) + (lane_f(x, 32) + lane_f(x, 48));
 }
 template <bool EVEN>  // D even: every channel pair is 8-byte aligned
 __global__ void __launch_bounds__(kMergeThreads)
